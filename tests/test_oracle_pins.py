@@ -1,0 +1,408 @@
+"""Pins for the fp64 reference (CPU only).
+
+The reference is checked against things other than itself:
+  * scalar brute force (tests/brute.py) on tiny inputs, with random LayerNorm
+    affine terms, random gate/output biases and random masks that include a
+    fully masked row and a single-key row;
+  * closed forms: uniform softmax (zero query weights and zero bias give the
+    masked mean of v), the half gate (zero gate weights give sigmoid(0)=1/2),
+    a single kept key, a fully masked query (out = b_o exactly), the sharp
+    limit of one dominant logit, LayerNorm of a known vector;
+  * a library routine: torch scaled_dot_product_attention in float64;
+  * invariants: END(Z, M) = START(Z^T, M^T)^T, equivariance under a residue
+    permutation, row-sliced evaluation equals the unsliced call;
+  * a hand-checkable worked example (tests/golden/worked_example_i2.json);
+  * planted mistakes: mutated copies of reference pieces must fail a pin.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import brute
+import oracle
+from oracle import pairattn_oracle as O
+from pair_representation_attention_amd import inputs
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _tri_case(I=6, c=8, H=2, d=4, mask="random", seed=11, dtype="f32"):
+    return inputs.make_tri_case(I=I, c=c, H=H, d=d, dtype=dtype, mask=mask, seed=seed,
+                                affine=True, biases=True)
+
+
+# ----------------------------------------------------------------------------
+# brute force
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("orientation", [0, 1])
+@pytest.mark.parametrize("mask", ["random", "pad", "none"])
+def test_tri_matches_brute_force(orientation, mask):
+    case = _tri_case(I=7, mask=mask, seed=5 + orientation)
+    p = case.params_start.as_dict()
+    ref = np.array(brute.tri(case.z, case.mask, p, case.H, orientation))
+    got = oracle.tri_fwd(case.z, case.mask, p, case.H, orientation)
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_tri_matches_brute_force_i8_full_width():
+    """I=8 with the production head shape (H=4, d=32, c=128)."""
+    case = inputs.make_tri_case(I=8, c=128, H=4, d=32, dtype="bf16", mask="random", seed=8,
+                                affine=True, biases=True)
+    p = case.params_start.as_dict()
+    for ori in (0, 1):
+        ref = np.array(brute.tri(case.z, case.mask, p, 4, ori))
+        got = oracle.tri_fwd(case.z, case.mask, p, 4, ori)
+        assert np.max(np.abs(got - ref)) < 1e-12
+
+
+@pytest.mark.parametrize("mask", ["bernoulli", "columns", "none"])
+def test_msa_matches_brute_force(mask):
+    case = inputs.make_msa_case(S=3, I=6, c_m=8, c_z=6, H=2, d=4, dtype="f32", mask=mask, seed=3,
+                                affine=True, biases=True)
+    if case.mask is not None:
+        case.mask[1, :] = 0          # a fully masked sequence
+    p = case.params.as_dict()
+    ref = np.array(brute.msa(case.m, case.z, case.mask, p, 2))
+    got = oracle.msa_row(case.m, case.z, case.mask, p, 2)
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_points_and_rows_match_brute_force():
+    case = _tri_case(I=6, seed=21)
+    p = case.params_start.as_dict()
+    for ori in (0, 1):
+        ref = np.array(brute.tri(case.z, case.mask, p, case.H, ori))
+        pts = [(0, 0), (1, 4), (5, 2), (3, 3), (2, 5)]
+        got = oracle.tri_points(case.z, case.mask, p, case.H, ori, pts)
+        for n, (a, b) in enumerate(pts):
+            assert np.max(np.abs(got[n] - ref[a][b])) < 1e-12
+    ref = np.array(brute.tri(case.z, case.mask, p, case.H, 0))
+    bias = oracle.attention_bias(case.z, p, case.H, oracle.START)
+    rows = oracle.tri_rows(case.z[2:5], bias, case.mask[2:5], p, case.H)
+    assert np.max(np.abs(rows - ref[2:5])) < 1e-12
+
+
+# ----------------------------------------------------------------------------
+# closed forms
+# ----------------------------------------------------------------------------
+def _ln_np(x, g, b, eps):
+    x = np.asarray(x, np.float64)
+    mu = x.mean(-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * g + b
+
+
+def test_layer_norm_known_vector():
+    x = np.array([1.0, 2.0, 3.0, 4.0])
+    # mean 2.5, biased variance 1.25
+    want = (x - 2.5) / math.sqrt(1.25 + 1e-5)
+    got = oracle.layer_norm(x, np.ones(4), np.zeros(4), 1e-5)
+    assert np.max(np.abs(got - want)) < 1e-15
+    got2 = oracle.layer_norm(x, np.full(4, 2.0), np.full(4, -1.0), 0.0)
+    assert np.max(np.abs(got2 - (2.0 * (x - 2.5) / math.sqrt(1.25) - 1.0))) < 1e-15
+
+
+@pytest.mark.parametrize("orientation", [0, 1])
+def test_uniform_softmax_closed_form(orientation):
+    """W_q = 0 and W_b = 0: every logit is 0, o = mean of v over kept keys."""
+    case = _tri_case(I=9, c=16, H=2, d=8, mask="random", seed=31)
+    p = case.params_start.as_dict()
+    p["w_q"] = np.zeros_like(p["w_q"])
+    p["w_b"] = np.zeros_like(p["w_b"])
+    z = np.asarray(case.z, np.float64)
+    keep = case.mask != 0
+    xh = _ln_np(z, p["ln_gamma"], p["ln_beta"], p["eps"])
+    v = xh @ p["w_v"]
+    gpre = xh @ p["w_g"]
+    I = case.I
+    want = np.empty((I, I, z.shape[-1]))
+    for a in range(I):
+        for b in range(I):
+            if orientation == 0:
+                kk = keep[a, :]
+                o = v[a, kk].mean(0) if kk.any() else np.zeros(v.shape[-1])
+            else:
+                kk = keep[:, b]
+                o = v[kk, b].mean(0) if kk.any() else np.zeros(v.shape[-1])
+            g = 1.0 / (1.0 + np.exp(-(gpre[a, b] + p["b_g"])))
+            want[a, b] = (g * o) @ p["w_o"] + p["b_o"]
+    got = oracle.tri_fwd(case.z, case.mask, p, case.H, orientation)
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
+def test_half_gate_identity_output():
+    """W_g = 0, b_g = 0, W_o = identity, b_o = 0 (c = H*d): out = o / 2."""
+    case = inputs.make_tri_case(I=5, c=8, H=2, d=4, dtype="f32", mask="none", seed=3)
+    p = case.params_start.as_dict()
+    p["w_g"] = np.zeros_like(p["w_g"])
+    p["b_g"] = np.zeros_like(p["b_g"])
+    p["w_o"] = np.eye(8)
+    p["b_o"] = np.zeros(8)
+    p["w_q"] = np.zeros_like(p["w_q"])
+    p["w_b"] = np.zeros_like(p["w_b"])
+    xh = _ln_np(case.z, p["ln_gamma"], p["ln_beta"], p["eps"])
+    v = xh @ p["w_v"]
+    want = 0.5 * np.broadcast_to(v.mean(1, keepdims=True), v.shape)
+    got = oracle.tri_start(case.z, None, p, 2)
+    assert np.max(np.abs(got - want)) < 1e-13
+
+
+def test_single_kept_key_and_fully_masked_row():
+    case = _tri_case(I=6, c=8, H=2, d=4, mask="none", seed=44)
+    p = case.params_start.as_dict()
+    I = case.I
+    mask = np.zeros((I, I), np.uint8)
+    mask[0, 3] = 1            # row 0 keeps only key 3
+    mask[2, :] = 1            # row 2 keeps everything; row 1 keeps nothing
+    got = oracle.tri_start(case.z, mask, p, case.H)
+    xh = _ln_np(case.z, p["ln_gamma"], p["ln_beta"], p["eps"])
+    v = xh @ p["w_v"]
+    gpre = xh @ p["w_g"]
+    g = 1.0 / (1.0 + np.exp(-(gpre + p["b_g"])))
+    want0 = (g[0] * v[0, 3][None, :]) @ p["w_o"] + p["b_o"]
+    assert np.max(np.abs(got[0] - want0)) < 1e-12
+    # fully masked row: o = 0 so out = b_o exactly
+    assert np.array_equal(got[1], np.broadcast_to(np.asarray(p["b_o"], np.float64), got[1].shape))
+    for r in range(3, I):
+        assert np.array_equal(got[r], np.broadcast_to(np.asarray(p["b_o"], np.float64), got[r].shape))
+
+
+def test_sharp_limit_one_dominant_logit():
+    """A key whose logit exceeds every other by >= 60 takes all the weight."""
+    case = _tri_case(I=6, c=8, H=2, d=4, mask="none", seed=52)
+    p = case.params_start.as_dict()
+    p["w_q"] = np.zeros_like(p["w_q"])
+    p["ln_gamma"] = np.ones(8)
+    p["ln_beta"] = np.zeros(8)
+    pattern = np.array([1.0, -1.0] * 4)
+    z = np.array(case.z, np.float64)
+    z[:, 4, :] = 50.0 * pattern            # LN of this pair is +-1 exactly up to eps
+    p["w_b"] = np.stack([pattern, pattern], axis=1) * (1000.0 / 8.0)
+    got = oracle.tri_start(z, None, p, 2)
+    xh = _ln_np(z, p["ln_gamma"], p["ln_beta"], p["eps"])
+    Bk = xh @ p["w_b"]                     # [I, I, H]
+    gap = Bk[:, 4, :][:, None, :] - np.delete(Bk, 4, axis=1)
+    assert gap.min() > 60.0
+    v = xh @ p["w_v"]
+    g = 1.0 / (1.0 + np.exp(-(xh @ p["w_g"] + p["b_g"])))
+    want = (g * v[:, 4][:, None, :]) @ p["w_o"] + p["b_o"]
+    assert np.max(np.abs(got - want)) < 10 * np.exp(-60.0) * (1 + np.abs(v).max() * np.abs(p["w_o"]).sum(0).max())
+
+
+def test_against_torch_sdpa_float64():
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    case = _tri_case(I=10, c=16, H=2, d=8, mask="pad", seed=61)
+    p = case.params_start.as_dict()
+    mask = case.mask.copy()
+    # SDPA returns NaN for a query with no key; keep every row non-empty here
+    mask[np.where(mask.sum(1) == 0)[0], 0] = 1
+    got = oracle.tri_start(case.z, mask, p, case.H)
+    t = lambda a: torch.as_tensor(np.asarray(a, np.float64))
+    z = t(case.z)
+    xh = F.layer_norm(z, (z.shape[-1],), t(p["ln_gamma"]), t(p["ln_beta"]), eps=p["eps"])
+    H, d = 2, 8
+    I = case.I
+    q = (xh @ t(p["w_q"])).reshape(I, I, H, d).permute(0, 2, 1, 3)   # [i, h, j, d]
+    k = (xh @ t(p["w_k"])).reshape(I, I, H, d).permute(0, 2, 1, 3)
+    v = (xh @ t(p["w_v"])).reshape(I, I, H, d).permute(0, 2, 1, 3)
+    B = (xh @ t(p["w_b"])).permute(2, 0, 1)                            # [h, j, k]
+    maskterm = torch.where(t(mask) != 0, 0.0, -math.inf)               # [i, k]
+    attn_bias = B[None] + maskterm[:, None, None, :]
+    o = F.scaled_dot_product_attention(q, k, v, attn_mask=attn_bias, scale=1.0 / math.sqrt(d))
+    o = o.permute(0, 2, 1, 3).reshape(I, I, H * d)
+    g = torch.sigmoid(xh @ t(p["w_g"]) + t(p["b_g"]))
+    want = (g * o) @ t(p["w_o"]) + t(p["b_o"])
+    assert np.max(np.abs(got - want.numpy())) < 1e-10
+
+
+# ----------------------------------------------------------------------------
+# invariants
+# ----------------------------------------------------------------------------
+def test_end_equals_start_on_transpose():
+    case = _tri_case(I=8, mask="random", seed=71)
+    p = case.params_start.as_dict()
+    end = oracle.tri_end(case.z, case.mask, p, case.H)
+    zt = np.ascontiguousarray(np.transpose(case.z, (1, 0, 2)))
+    start_t = oracle.tri_start(zt, case.mask.T.copy(), p, case.H)
+    assert np.max(np.abs(end - np.transpose(start_t, (1, 0, 2)))) < 1e-12
+
+
+@pytest.mark.parametrize("orientation", [0, 1])
+def test_permutation_equivariance_tri(orientation):
+    case = _tri_case(I=9, mask="random", seed=81)
+    p = case.params_start.as_dict()
+    pi = np.random.default_rng(5).permutation(case.I)
+    base = oracle.tri_fwd(case.z, case.mask, p, case.H, orientation)
+    zp = case.z[pi][:, pi]
+    mp = case.mask[pi][:, pi]
+    perm = oracle.tri_fwd(zp, mp, p, case.H, orientation)
+    assert np.max(np.abs(perm - base[pi][:, pi])) < 1e-12
+
+
+def test_permutation_equivariance_msa():
+    case = inputs.make_msa_case(S=4, I=7, c_m=8, c_z=6, H=2, d=4, dtype="f32", seed=9,
+                                affine=True, biases=True)
+    p = case.params.as_dict()
+    rng = np.random.default_rng(6)
+    pi = rng.permutation(case.I)
+    sg = rng.permutation(case.S)
+    base = oracle.msa_row(case.m, case.z, case.mask, p, 2)
+    perm = oracle.msa_row(case.m[sg][:, pi], case.z[pi][:, pi], case.mask[sg][:, pi], p, 2)
+    assert np.max(np.abs(perm - base[sg][:, pi])) < 1e-12
+
+
+def test_row_sliced_equals_unsliced():
+    """Chunking the attention rows (threshold/unit slicing) changes nothing."""
+    with open(os.path.join(GOLDEN, "slicing_example.json")) as f:
+        sl = json.load(f)
+    case = _tri_case(I=13, c=8, H=2, d=4, mask="random", seed=91)
+    p = case.params_start.as_dict()
+    full = oracle.tri_start(case.z, case.mask, p, case.H)
+    bias = oracle.attention_bias(case.z, p, case.H, oracle.START)
+    # same proportions as the page's example, scaled to a 13-row input:
+    # rows above a threshold are cut into fixed-size units, remainder last
+    unit = max(1, case.I * sl["unit"] // sl["rows"])
+    parts = []
+    for r0 in range(0, case.I, unit):
+        r1 = min(case.I, r0 + unit)
+        parts.append(oracle.tri_rows(case.z[r0:r1], bias, case.mask[r0:r1], p, case.H))
+    assert np.max(np.abs(np.concatenate(parts) - full)) < 1e-13
+    # slicing the query axis also commutes
+    qs = [np.arange(0, 5), np.arange(5, 13)]
+    qparts = [oracle.tri_start(case.z, case.mask, p, case.H, queries=q) for q in qs]
+    assert np.max(np.abs(np.concatenate(qparts, axis=1) - full)) < 1e-13
+
+
+def test_slicing_example_numbers():
+    """The page's tensor example: 5120 x 1 x 1 x 64 fp32 is 1.25 MiB; unit 320."""
+    with open(os.path.join(GOLDEN, "slicing_example.json")) as f:
+        sl = json.load(f)
+    assert sl["rows"] * sl["width"] * 4 == int(sl["initial_mib"] * 2 ** 20)
+    assert sl["rows"] % sl["unit"] == 0 and sl["rows"] > sl["threshold"]
+
+
+def test_worked_example_i2():
+    """Hand-checkable I=2 example: LN gives exactly +-1, logits are integers."""
+    with open(os.path.join(GOLDEN, "worked_example_i2.json")) as f:
+        ex = json.load(f)
+    z = np.array(ex["z"], np.float64)
+    p = {k: np.array(v, np.float64) for k, v in ex["params"].items()}
+    p["eps"] = 0.0
+    got = oracle.tri_start(z, None, p, 1)
+    # closed form: with c=2, zero LN beta and eps=0, LN(z[a,b]) = s_ab (1, -1)
+    s = np.sign(z[..., 0] - z[..., 1])
+    wq, wk, wv, wg, wb, wo = (p[n] for n in ("w_q", "w_k", "w_v", "w_g", "w_b", "w_o"))
+    proj = lambda w: s[..., None] * (w[0] - w[1])          # [2, 2, out]
+    q, k, v, gp, B = proj(wq), proj(wk), proj(wv), proj(wg), proj(wb)[..., 0]
+    want = np.empty((2, 2, 2))
+    for i in range(2):
+        for j in range(2):
+            lg = [q[i, j, 0] * k[i, kk, 0] + B[j, kk] for kk in range(2)]
+            m = max(lg)
+            e = [math.exp(x - m) for x in lg]
+            o = (e[0] * v[i, 0, 0] + e[1] * v[i, 1, 0]) / (e[0] + e[1])
+            gate = 1.0 / (1.0 + math.exp(-(gp[i, j, 0] + p["b_g"][0])))
+            want[i, j] = gate * o * wo[0] + p["b_o"]
+    for n, row in enumerate(ex["logits_start"]):
+        i, j, kk, val = row
+        assert q[i, j, 0] * k[i, kk, 0] + B[j, kk] == val
+    assert np.max(np.abs(got - want)) < 1e-14
+
+
+# ----------------------------------------------------------------------------
+# planted mistakes: a mutated reference must fail the brute-force pin
+# ----------------------------------------------------------------------------
+def _brute_gap(monkeypatch_ctx=None):
+    case = _tri_case(I=6, c=8, H=2, d=4, mask="random", seed=101)
+    p = case.params_start.as_dict()
+    worst = 0.0
+    for ori in (0, 1):
+        ref = np.array(brute.tri(case.z, case.mask, p, case.H, ori))
+        got = oracle.tri_fwd(case.z, case.mask, p, case.H, ori)
+        worst = max(worst, float(np.max(np.abs(got - ref))))
+    mcase = inputs.make_msa_case(S=2, I=5, c_m=8, c_z=6, H=2, d=4, dtype="f32", seed=7,
+                                 affine=True, biases=True)
+    mp = mcase.params.as_dict()
+    ref = np.array(brute.msa(mcase.m, mcase.z, mcase.mask, mp, 2))
+    got = oracle.msa_row(mcase.m, mcase.z, mcase.mask, mp, 2)
+    return max(worst, float(np.max(np.abs(got - ref))))
+
+
+def _ln_unbiased(x, gamma, beta, eps):
+    x = np.asarray(x, np.float64)
+    return (x - x.mean(-1, keepdims=True)) / np.sqrt(x.var(-1, ddof=1, keepdims=True) + eps) * gamma + beta
+
+
+def _ln_no_eps(x, gamma, beta, eps):
+    x = np.asarray(x, np.float64)
+    return (x - x.mean(-1, keepdims=True)) / np.sqrt(x.var(-1, keepdims=True)) * gamma + beta
+
+
+def _ln_no_affine(x, gamma, beta, eps):
+    x = np.asarray(x, np.float64)
+    return (x - x.mean(-1, keepdims=True)) / np.sqrt(x.var(-1, keepdims=True) + eps)
+
+
+def _gate_no_bg(o, g_pre, p):
+    return (O.sigmoid(g_pre) * o) @ np.asarray(p["w_o"], np.float64) + np.asarray(p["b_o"], np.float64)
+
+
+def _gate_no_bo(o, g_pre, p):
+    return (O.sigmoid(g_pre + np.asarray(p["b_g"], np.float64)) * o) @ np.asarray(p["w_o"], np.float64)
+
+
+def _gate_flipped(o, g_pre, p):
+    return (O.sigmoid(-(g_pre + np.asarray(p["b_g"], np.float64))) * o) @ np.asarray(p["w_o"], np.float64) \
+        + np.asarray(p["b_o"], np.float64)
+
+
+def _softmax_ignores_mask(logits, keep):
+    x = logits - logits.max(-1, keepdims=True)
+    e = np.exp(x)
+    return e / e.sum(-1, keepdims=True)
+
+
+_orig_attention_bias = O.attention_bias
+
+
+def _bias_transposed(z, p, H, orientation=0, ln_prefix="ln", queries=None):
+    other = 1 - orientation if ln_prefix == "ln" else orientation
+    b = _orig_attention_bias(z, p, H, other, ln_prefix, None)
+    b = np.ascontiguousarray(b.transpose(0, 2, 1))
+    return b if queries is None else b[:, np.asarray(queries), :]
+
+
+class _NoSqrtMath:
+    def __getattr__(self, name):
+        return getattr(math, name)
+
+    @staticmethod
+    def sqrt(x):
+        return 1.0
+
+
+MUTANTS = {
+    "layer_norm_unbiased_variance": ("layer_norm", _ln_unbiased),
+    "layer_norm_without_eps": ("layer_norm", _ln_no_eps),
+    "layer_norm_without_affine": ("layer_norm", _ln_no_affine),
+    "gate_without_b_g": ("gated_output", _gate_no_bg),
+    "output_without_b_o": ("gated_output", _gate_no_bo),
+    "gate_sign_flipped": ("gated_output", _gate_flipped),
+    "softmax_ignores_mask": ("masked_softmax_weights", _softmax_ignores_mask),
+    "bias_transposed": ("attention_bias", _bias_transposed),
+    "logit_scale_dropped": ("math", _NoSqrtMath()),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    assert _brute_gap() < 1e-12
+    attr, repl = MUTANTS[name]
+    monkeypatch.setattr(O, attr, repl)
+    assert _brute_gap() > 1e-6, f"mutant {name} was not detected"
