@@ -1,0 +1,493 @@
+// bf16-interface kernels for gated pair-biased attention on gfx950.
+//
+// Inputs, weights and outputs are bf16.  Every MFMA operand inside the path
+// (normalised activations, packed weights, q, k, v, softmax weights, gated
+// o) is stored as fp16, which gfx950 multiplies at the same rate as bf16 but
+// with 11 instead of 8 significant bits; accumulation, LayerNorm statistics,
+// the bias and the softmax run in fp32.  Values headed for fp16 are
+// saturated at +-65504.
+//
+// The attention of every supported operation is cast as "row attention":
+// nrows independent rows, each with P positions that are both the queries
+// and the keys, H heads of width 32, and a bias[h][query][key] shared by all
+// rows.  The orientation (starting node, ending node, MSA rows) only changes
+// how a (row, position) pair is addressed in the input, mask and output,
+// which every kernel takes as strides.  The ending node is thus read with
+// strided loads of Z and written with strided stores; Z is never transposed.
+//
+// Workspace layouts (Pp = P rounded up to 32; padded positions hold zeros):
+//   q  [nrows][H][Pp][32] fp16, scaled by log2(e)/sqrt(d)
+//   k  [nrows][H][Pp][32] fp16
+//   v  [nrows][H][32][Pp] fp16 (positions fastest)
+//   g  [nrows][P][H*32]  fp16, sigmoid already applied
+//   bias [H][P][P] float, natural-log units
+#include "pa_device.h"
+
+namespace pa {
+
+// --------------------------------------------------------------------------
+// weight packing: transposed fp16 copies so that every MFMA operand lane
+// reads 16 contiguous bytes.  bf16 -> fp16 is exact for magnitudes in
+// [2^-14, 65504]; smaller weights keep an absolute error below 2^-25.
+//   wT  [4*HD][C_IN]  rows: q cols, k cols, v cols, g cols
+//   woT [C_OUT][HD]
+// --------------------------------------------------------------------------
+__global__ void pack_weights_kernel(const bf16* __restrict__ wq, const bf16* __restrict__ wk,
+                                    const bf16* __restrict__ wv, const bf16* __restrict__ wg,
+                                    const bf16* __restrict__ wo, f16* __restrict__ wT,
+                                    f16* __restrict__ woT, int c_in, int hd, int c_out) {
+  const int64_t n_w = (int64_t)4 * hd * c_in;
+  const int64_t n_o = (int64_t)c_out * hd;
+  const int64_t total = n_w + n_o;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    if (i < n_w) {
+      const int row = (int)(i / c_in), k = (int)(i % c_in);
+      const int t = row / hd, col = row % hd;
+      const bf16* src = t == 0 ? wq : t == 1 ? wk : t == 2 ? wv : wg;
+      wT[i] = f2h_sat(bf2f(src[(int64_t)k * hd + col]));
+    } else {
+      const int64_t j = i - n_w;
+      const int c = (int)(j / hd), k = (int)(j % hd);
+      woT[j] = f2h_sat(bf2f(wo[(int64_t)k * c_out + c]));
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// LayerNorm of a tile of 32 positions of one row into LDS (fp16, row pitch
+// C_IN + 8 elements).  Positions >= P are written as zeros.
+// --------------------------------------------------------------------------
+template <int C_IN, int NT>
+__device__ __forceinline__ void ln_tile_to_lds(const bf16* __restrict__ x, int64_t xs_r, int64_t xs_p,
+                                               int r, int p0, int P, const bf16* __restrict__ gamma,
+                                               const bf16* __restrict__ beta, float eps, f16* xs) {
+  constexpr int TPP = C_IN / 8;           // threads per position (8 channels each)
+  constexpr int PPP = NT / TPP;           // positions per pass
+  static_assert(TPP <= 64 && (64 % TPP) == 0, "channel groups must tile a wave");
+  const int tid = threadIdx.x;
+  const int sub = tid % TPP;
+#pragma unroll
+  for (int base = 0; base < 32; base += PPP) {
+    const int pl = base + tid / TPP;
+    if (PPP <= 32 || pl < 32) {
+      const int p = p0 + pl;
+      float v[8];
+      if (p < P) {
+        const bf16x8 raw = ld16(x + (int64_t)r * xs_r + (int64_t)p * xs_p + sub * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = bf2f(raw[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+      }
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += v[e];
+      const float mean = group_sum<TPP>(s) * (1.0f / C_IN);
+      float s2 = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = v[e] - mean;
+        s2 += t * t;
+      }
+      const float var = group_sum<TPP>(s2) * (1.0f / C_IN);
+      const float rstd = 1.0f / __builtin_sqrtf(var + eps);
+      const bf16x8 gm = ld16(gamma + sub * 8);
+      const bf16x8 bt = ld16(beta + sub * 8);
+      f16x8 y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        y[e] = (p < P) ? f2h_sat((v[e] - mean) * rstd * bf2f(gm[e]) + bf2f(bt[e])) : f2h(0.0f);
+      *reinterpret_cast<f16x8*>(xs + pl * (C_IN + 8) + sub * 8) = y;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Fused LayerNorm + projections.  One workgroup of 8 waves loops over tiles
+// of 32 positions of one row; each wave keeps its 64 (or 96) weight columns
+// in registers for the whole kernel.
+//   MODE 0: q, k, v, g          MODE 1: q, k, v, g and the pair bias
+//   MODE 2: pair bias only (wave 0 computes, the other waves only normalise)
+// Column group blockIdx.y selects 512 of the 4*HD projection columns.
+// --------------------------------------------------------------------------
+template <int C_IN, int HD, int MODE>
+__global__ __launch_bounds__(512) void proj_kernel(
+    const bf16* __restrict__ x, int64_t xs_r, int64_t xs_p, const bf16* __restrict__ gamma,
+    const bf16* __restrict__ beta, float eps, const f16* __restrict__ wT, const bf16* __restrict__ wb,
+    const bf16* __restrict__ b_g, float q_scale, f16* __restrict__ q_ws, f16* __restrict__ k_ws,
+    f16* __restrict__ v_ws, f16* __restrict__ g_ws, float* __restrict__ bias, int nrows, int P, int Pp,
+    int H) {
+  constexpr int NT = 512;
+  constexpr int KS = C_IN / 16;          // MFMA K-steps
+  constexpr bool HAS_QKVG = MODE != 2;
+  constexpr bool HAS_BIAS = MODE != 0;
+  __shared__ __attribute__((aligned(16))) f16 xs[32 * (C_IN + 8)];
+
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int lq = lane & 31, g = lane >> 5;
+  const int colbase = blockIdx.y * 512 + wave * 64;    // first of this wave's 64 columns
+  const int tensor = colbase / HD;                     // 0 q, 1 k, 2 v, 3 g
+  const bool bias_wave = HAS_BIAS && blockIdx.y == 0 && wave == 0;
+
+  f16x8 W[2][KS];
+  f16x8 WB[KS];
+  if (HAS_QKVG) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int t = 0; t < KS; ++t) W[mb][t] = ld16(wT + (int64_t)(colbase + mb * 32 + lq) * C_IN + t * 16 + g * 8);
+  }
+  if (bias_wave) {   // w_b is [C_IN][H]; rows >= H of the operand are zero
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) WB[t][e] = lq < H ? f2h_sat(bf2f(wb[(int64_t)(t * 16 + g * 8 + e) * H + lq])) : f2h(0.0f);
+  }
+
+  const int tiles_per_row = Pp / 32;
+  const int64_t ntiles = (int64_t)tiles_per_row * nrows;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int r = (int)(tile / tiles_per_row);
+    const int p0 = (int)(tile % tiles_per_row) * 32;
+    __syncthreads();   // previous tile's LDS reads are done
+    ln_tile_to_lds<C_IN, NT>(x, xs_r, xs_p, r, p0, P, gamma, beta, eps, xs);
+    __syncthreads();
+
+    if (HAS_QKVG) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        f32x16 acc = {};
+        if (tensor == 2) {   // v: out = X W, rows = positions, columns = channels
+#pragma unroll
+          for (int t = 0; t < KS; ++t) acc = mfma32(ld16(xs + lq * (C_IN + 8) + t * 16 + g * 8), W[mb][t], acc);
+        } else {             // q, k, g: out^T = W^T X^T, rows = channels, columns = positions
+#pragma unroll
+          for (int t = 0; t < KS; ++t) acc = mfma32(W[mb][t], ld16(xs + lq * (C_IN + 8) + t * 16 + g * 8), acc);
+        }
+        const int col = colbase + mb * 32 - tensor * HD;   // first column within the tensor
+        const int h = col / 32;
+        if (tensor == 0 || tensor == 1) {
+          f16* dst = (tensor == 0 ? q_ws : k_ws) + (((int64_t)r * H + h) * Pp + p0 + lq) * 32;
+          const float sc = tensor == 0 ? q_scale : 1.0f;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            f16x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = f2h_sat(acc[jj * 4 + e] * sc);
+            st8(dst + jj * 8 + g * 4, o);
+          }
+        } else if (tensor == 2) {
+          f16* dst = v_ws + (((int64_t)r * H + h) * 32 + lq) * Pp + p0;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            f16x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = f2h_sat(acc[jj * 4 + e]);
+            st8(dst + jj * 8 + g * 4, o);
+          }
+        } else {
+          const int p = p0 + lq;
+          if (p < P) {
+            f16* dst = g_ws + ((int64_t)r * P + p) * HD + col;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              f16x4 o;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int d = jj * 8 + g * 4 + e;
+                const float bg = b_g != nullptr ? bf2f(b_g[col + d]) : 0.0f;
+                const float t = acc[jj * 4 + e] + bg;
+                o[e] = f2h(1.0f / (1.0f + __expf(-t)));
+              }
+              st8(dst + jj * 8 + g * 4, o);
+            }
+          }
+        }
+      }
+    }
+    if (bias_wave) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int t = 0; t < KS; ++t) acc = mfma32(WB[t], ld16(xs + lq * (C_IN + 8) + t * 16 + g * 8), acc);
+      const int p = p0 + lq;
+      if (p < P) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int hh = acc_row(j, g);
+          if (hh < H) bias[((int64_t)hh * P + r) * P + p] = acc[j];
+        }
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Flash-style attention with the pair bias as the MFMA accumulator input,
+// online softmax in fp32 and the gate + output projection fused in.
+//
+// Workgroup = H waves (one per head) sharing 32 query positions and R rows.
+// Per 32-key block a wave computes S^T = K Q^T + bias^T (two MFMAs, the bias
+// tile loaded once and reused for the R rows), updates the running max and
+// sum, and accumulates O^T += V^T P^T (two MFMAs).  Keys are loaded in the
+// order pi(m) (bits 2 and 3 of m swapped) so that the S^T accumulator
+// registers are directly the B operand of the P.V product: register j of a
+// lane in half g then holds key (j/8)*16 + g*8 + j%8 of the block.
+// --------------------------------------------------------------------------
+template <int H, int C_OUT, int R>
+__global__ __launch_bounds__(H * 64) void attn_kernel(
+    const f16* __restrict__ q_ws, const f16* __restrict__ k_ws, const f16* __restrict__ v_ws,
+    const f16* __restrict__ g_ws, const float* __restrict__ bias, const uint8_t* __restrict__ mask,
+    int64_t ms_r, int64_t ms_k, const f16* __restrict__ woT, const bf16* __restrict__ b_o,
+    bf16* __restrict__ out, int64_t os_r, int64_t os_p, int nrows, int P, int Pp) {
+  constexpr int HD = H * 32;
+  constexpr int KO = HD / 16;                 // K-steps of the output projection
+  constexpr int CB = C_OUT / 32;              // output channel blocks
+  constexpr int CB_PER_WAVE = (CB + H - 1) / H;
+  constexpr int OP = HD + 8;                  // LDS pitch of the gated o tile
+  __shared__ __attribute__((aligned(16))) f16 o_lds[32 * OP];
+
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int lq = lane & 31, g = lane >> 5;
+  const int h = wave;
+  const int q0 = blockIdx.x * 32;
+  const int r0 = blockIdx.y * R;
+  const int nkb = Pp / 32;
+  const float NEG_INF = -__builtin_inff();
+
+  // query operands (B of S^T = K Q^T), one per row, loaded once
+  f16x8 Qop[R][2];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const int r = min(r0 + rr, nrows - 1);
+    const f16* base = q_ws + (((int64_t)r * H + h) * Pp + q0 + lq) * 32 + g * 8;
+    Qop[rr][0] = ld16(base);
+    Qop[rr][1] = ld16(base + 16);
+  }
+  f32x16 O[R];
+  float m_run[R], l_run[R];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    O[rr] = f32x16{};
+    m_run[rr] = NEG_INF;
+    l_run[rr] = 0.0f;
+  }
+
+  const int qrow = min(q0 + lq, P - 1);
+  const float* brow = bias + ((int64_t)h * P + qrow) * P;
+  const int kperm = (lq & ~12) | ((lq & 4) << 1) | ((lq & 8) >> 1);   // pi(lq)
+
+  const bool bias_vec = (P & 3) == 0;   // bias rows 16-byte aligned
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int kbase = kb * 32;
+    const bool tail = kbase + 32 > P;
+    f32x16 Bt;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int k0 = kbase + u * 16 + g * 8;
+      if (!tail && bias_vec) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(brow + k0);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(brow + k0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Bt[u * 8 + e] = a[e] * kLog2e;
+          Bt[u * 8 + 4 + e] = b[e] * kLog2e;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Bt[u * 8 + e] = brow[min(k0 + e, P - 1)] * kLog2e;
+      }
+    }
+
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const int r = min(r0 + rr, nrows - 1);
+      const int64_t rh = (int64_t)r * H + h;
+      const f16* kp = k_ws + (rh * Pp + kbase + kperm) * 32 + g * 8;
+      const f16x8 K0 = ld16(kp), K1 = ld16(kp + 16);
+      const f16* vp = v_ws + (rh * 32 + lq) * Pp + kbase + g * 8;
+      const f16x8 V0 = ld16(vp), V1 = ld16(vp + 16);
+
+      f32x16 S = mfma32(K0, Qop[rr][0], Bt);
+      S = mfma32(K1, Qop[rr][1], S);
+
+      if (tail || mask != nullptr) {
+        const uint8_t* mrow = mask != nullptr ? mask + (int64_t)r * ms_r : nullptr;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = kbase + (j >> 3) * 16 + g * 8 + (j & 7);
+          bool keep = key < P;
+          if (keep && mrow != nullptr) keep = mrow[(int64_t)key * ms_k] != 0;
+          S[j] = keep ? S[j] : NEG_INF;
+        }
+      }
+
+      float bmax = S[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) bmax = fmaxf(bmax, S[j]);
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+      const float m_new = fmaxf(m_run[rr], bmax);
+      const float m_use = m_new == NEG_INF ? 0.0f : m_new;
+      const float alpha = fast_exp2(m_run[rr] - m_use);
+      m_run[rr] = m_new;
+
+      float psum = 0.0f;
+      f16x8 P0, P1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = fast_exp2(S[j] - m_use);
+        psum += p;
+        P0[j] = f2h(p);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = fast_exp2(S[8 + j] - m_use);
+        psum += p;
+        P1[j] = f2h(p);
+      }
+      l_run[rr] = l_run[rr] * alpha + psum;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) O[rr][j] *= alpha;
+      O[rr] = mfma32(V0, P0, O[rr]);
+      O[rr] = mfma32(V1, P1, O[rr]);
+    }
+  }
+
+  // ---- epilogue: normalise, gate, output projection ----
+  f16x8 Wo[CB_PER_WAVE][KO];
+#pragma unroll
+  for (int i = 0; i < CB_PER_WAVE; ++i) {
+    const int cb = wave + i * H;
+    if (cb < CB) {
+#pragma unroll
+      for (int t = 0; t < KO; ++t) Wo[i][t] = ld16(woT + (int64_t)(cb * 32 + lq) * HD + t * 16 + g * 8);
+    }
+  }
+  const int q = q0 + lq;
+  const int qc = min(q, P - 1);
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const int r = r0 + rr;
+    if (r >= nrows) break;
+    const float ltot = l_run[rr] + __shfl_xor(l_run[rr], 32, 64);
+    const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+    const f16* gp = g_ws + ((int64_t)r * P + qc) * HD + h * 32;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const f16x4 gv = *reinterpret_cast<const f16x4*>(gp + jj * 8 + g * 4);
+      f16x4 ov;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[e] = f2h_sat(O[rr][jj * 4 + e] * inv * (float)gv[e]);
+      st8(o_lds + lq * OP + h * 32 + jj * 8 + g * 4, ov);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < CB_PER_WAVE; ++i) {
+      const int cb = wave + i * H;
+      if (cb < CB) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int t = 0; t < KO; ++t) acc = mfma32(Wo[i][t], ld16(o_lds + lq * OP + t * 16 + g * 8), acc);
+        if (q < P) {
+          bf16* dst = out + (int64_t)r * os_r + (int64_t)q * os_p + cb * 32;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            bf16x4 ov;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int c = jj * 8 + g * 4 + e;
+              const float bo = b_o != nullptr ? bf2f(b_o[cb * 32 + c]) : 0.0f;
+              ov[e] = f2bf(acc[jj * 4 + e] + bo);
+            }
+            st8(dst + jj * 8 + g * 4, ov);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace pa
+
+// ----------------------------------------------------------------------------
+// launchers (called from the host API in pairattn_api.hip)
+// ----------------------------------------------------------------------------
+#include "pa_launch.h"
+
+namespace pa {
+
+hipError_t launch_pack_bf16(const PackArgs& a, hipStream_t s) {
+  const int64_t total = (int64_t)4 * a.hd * a.c_in + (int64_t)a.c_out * a.hd;
+  const int threads = 256;
+  const int blocks = (int)std::min<int64_t>((total + threads - 1) / threads, 4096);
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(blocks), dim3(threads), 0, s, (const bf16*)a.wq, (const bf16*)a.wk,
+                     (const bf16*)a.wv, (const bf16*)a.wg, (const bf16*)a.wo, (f16*)a.wT, (f16*)a.woT, a.c_in,
+                     a.hd, a.c_out);
+  return hipGetLastError();
+}
+
+template <int C_IN, int HD, int MODE>
+static hipError_t proj_dispatch(const ProjArgs& a, int grid_x, int grid_y, hipStream_t s) {
+  hipLaunchKernelGGL((proj_kernel<C_IN, HD, MODE>), dim3(grid_x, grid_y), dim3(512), 0, s, (const bf16*)a.x, a.xs_r,
+                     a.xs_p, (const bf16*)a.gamma, (const bf16*)a.beta, a.eps, (const f16*)a.wT,
+                     (const bf16*)a.wb, (const bf16*)a.b_g, a.q_scale, (f16*)a.q_ws, (f16*)a.k_ws,
+                     (f16*)a.v_ws, (f16*)a.g_ws, a.bias, a.nrows, a.P, a.Pp, a.H);
+  return hipGetLastError();
+}
+
+template <int C_IN, int MODE>
+static hipError_t proj_dispatch_hd(const ProjArgs& a, int grid_x, int grid_y, hipStream_t s) {
+  if (MODE == 2) return proj_dispatch<C_IN, 128, 2>(a, grid_x, 1, s);
+  if (a.hd == 128) return proj_dispatch<C_IN, 128, MODE>(a, grid_x, grid_y, s);
+  if (a.hd == 256) return proj_dispatch<C_IN, 256, MODE>(a, grid_x, grid_y, s);
+  return hipErrorInvalidValue;
+}
+
+template <int MODE>
+static hipError_t proj_dispatch_c(const ProjArgs& a, int grid_x, int grid_y, hipStream_t s) {
+  switch (a.c_in) {
+    case 64: return proj_dispatch_hd<64, MODE>(a, grid_x, grid_y, s);
+    case 128: return proj_dispatch_hd<128, MODE>(a, grid_x, grid_y, s);
+    case 256: return proj_dispatch_hd<256, MODE>(a, grid_x, grid_y, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_proj_bf16(const ProjArgs& a, int mode, int num_cu, hipStream_t s) {
+  const int64_t ntiles = (int64_t)(a.Pp / 32) * a.nrows;
+  const int grid_y = mode == 2 ? 1 : (4 * a.hd) / 512;
+  const int grid_x = (int)std::max<int64_t>(1, std::min<int64_t>(ntiles, (int64_t)num_cu * 2));
+  switch (mode) {
+    case 0: return proj_dispatch_c<0>(a, grid_x, grid_y, s);
+    case 1: return proj_dispatch_c<1>(a, grid_x, grid_y, s);
+    case 2: return proj_dispatch_c<2>(a, grid_x, grid_y, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int H, int C_OUT>
+static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
+  constexpr int R = 4;
+  dim3 grid(a.Pp / 32, (a.nrows + R - 1) / R);
+  hipLaunchKernelGGL((attn_kernel<H, C_OUT, R>), grid, dim3(H * 64), 0, s, (const f16*)a.q_ws, (const f16*)a.k_ws,
+                     (const f16*)a.v_ws, (const f16*)a.g_ws, a.bias, a.mask, a.ms_r, a.ms_k, (const f16*)a.woT,
+                     (const bf16*)a.b_o, (bf16*)a.out, a.os_r, a.os_p, a.nrows, a.P, a.Pp);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
+  if (a.H == 4) {
+    if (a.c_out == 64) return attn_dispatch<4, 64>(a, s);
+    if (a.c_out == 128) return attn_dispatch<4, 128>(a, s);
+    if (a.c_out == 256) return attn_dispatch<4, 256>(a, s);
+  } else if (a.H == 8) {
+    if (a.c_out == 64) return attn_dispatch<8, 64>(a, s);
+    if (a.c_out == 128) return attn_dispatch<8, 128>(a, s);
+    if (a.c_out == 256) return attn_dispatch<8, 256>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -1,0 +1,50 @@
+// Host-side argument bundles and launchers of the pair-attention kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <algorithm>
+
+namespace pa {
+
+struct PackArgs {
+  const void *wq, *wk, *wv, *wg, *wo;  // natural layouts
+  void *wT, *woT;                      // packed copies in the workspace
+  int c_in, hd, c_out;
+};
+
+// LayerNorm + projection of nrows x P positions.  Element (r, p, c) of the
+// input is x[r*xs_r + p*xs_p + c].
+struct ProjArgs {
+  const void* x;
+  int64_t xs_r, xs_p;
+  const void *gamma, *beta;
+  float eps;
+  const void* wT;                // bf16 path: packed q|k|v|g weights
+  const void *wq, *wk, *wv, *wg; // fp32 path: natural layouts
+  const void *wb, *b_g;          // both paths: w_b [c_in][H], gate bias [H*32]
+  float q_scale;
+  void *q_ws, *k_ws, *v_ws, *g_ws;
+  float* bias;                   // [H][P][P] (row = attention row index r)
+  int c_in, hd, H, nrows, P, Pp;
+};
+
+struct AttnArgs {
+  const void *q_ws, *k_ws, *v_ws, *g_ws;
+  const float* bias;             // [H][P][P], natural-log units
+  const uint8_t* mask;           // key kept iff mask[r*ms_r + k*ms_k] != 0 (NULL = all)
+  int64_t ms_r, ms_k;
+  const void *woT, *wo, *b_o;    // woT for bf16, wo (natural) for fp32
+  void* out;                     // element (r, p, c) at out[r*os_r + p*os_p + c]
+  int64_t os_r, os_p;
+  int H, c_out, nrows, P, Pp;
+};
+
+hipError_t launch_pack_bf16(const PackArgs& a, hipStream_t s);
+// mode 0: q,k,v,g   1: q,k,v,g + bias   2: bias only
+hipError_t launch_proj_bf16(const ProjArgs& a, int mode, int num_cu, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+
+hipError_t launch_proj_f32(const ProjArgs& a, int mode, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
+
+}  // namespace pa

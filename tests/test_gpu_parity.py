@@ -1,0 +1,196 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
+
+Run on an MI355X:  python -m pytest tests -m gpu
+"""
+import numpy as np
+import pytest
+
+import oracle
+from pair_representation_attention_amd import inputs
+from parity_common import check, gpu_to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from pair_representation_attention_amd import lib
+    lib.load()   # raises if the HIP library is missing: no fallback
+    yield
+
+
+def _dev():
+    from pair_representation_attention_amd import device
+    return device
+
+
+# ----------------------------------------------------------------------------
+# small shapes: full output against the oracle, tails and masks
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("I", [1, 7, 33, 64, 100])
+@pytest.mark.parametrize("mask", ["none", "random"])
+def test_tri_small_shapes(dtype, I, mask):
+    case = inputs.make_tri_case(I=I, c=128, H=4, d=32, dtype=dtype, mask=mask, seed=100 + I,
+                                affine=True, biases=True)
+    dev = _dev()
+    for ori, p in ((0, case.params_start), (1, case.params_end)):
+        run = dev.TriRunner(case.z, case.mask, p, 4, dtype)
+        got = gpu_to_f64(run(ori))
+        torch.cuda.synchronize()
+        ref = oracle.tri_fwd(case.z, case.mask, p.as_dict(), 4, ori)
+        check(got, ref, dtype, f"tri I={I} ori={ori} mask={mask}")
+
+
+@pytest.mark.parametrize("c,H", [(64, 4), (256, 8), (128, 8)])
+def test_tri_other_widths(c, H):
+    case = inputs.make_tri_case(I=45, c=c, H=H, d=32, dtype="bf16", mask="random", seed=7 + c + H,
+                                affine=True, biases=True)
+    dev = _dev()
+    for ori, p in ((0, case.params_start), (1, case.params_end)):
+        got = gpu_to_f64(dev.TriRunner(case.z, case.mask, p, H, "bf16")(ori))
+        ref = oracle.tri_fwd(case.z, case.mask, p.as_dict(), H, ori)
+        check(got, ref, "bf16", f"tri c={c} H={H} ori={ori}")
+
+
+# ----------------------------------------------------------------------------
+# workload configurations
+# ----------------------------------------------------------------------------
+def test_cfg_tri_fp32_i64():
+    cfg = inputs.CONFIGS["tri_fp32_i64"]
+    case = inputs.make_tri_case(I=cfg["I"], c=cfg["c"], H=cfg["H"], d=cfg["d"], dtype=cfg["dtype"],
+                                mask=cfg["mask"], seed=cfg["seed"])
+    dev = _dev()
+    for ori, p in ((0, case.params_start), (1, case.params_end)):
+        got = gpu_to_f64(dev.TriRunner(case.z, case.mask, p, 4, "f32")(ori))
+        ref = oracle.tri_fwd(case.z, case.mask, p.as_dict(), 4, ori)
+        check(got, ref, "f32", f"cfg tri_fp32_i64 ori={ori}")
+
+
+def _sample(I, n, rng):
+    s = set([0, I - 1, I // 2]) | set(rng.choice(I, size=min(n, I), replace=False).tolist())
+    return np.array(sorted(s))
+
+
+def test_cfg_tri_bf16_i384_padded():
+    cfg = inputs.CONFIGS["tri_bf16_i384_pad"]
+    case = inputs.make_tri_case(I=cfg["I"], c=cfg["c"], H=cfg["H"], d=cfg["d"], dtype=cfg["dtype"],
+                                mask=cfg["mask"], seed=cfg["seed"])
+    dev = _dev()
+    rng = np.random.default_rng(0)
+    rows = np.concatenate([_sample(case.I, 10, rng), [350, 383]])   # includes padded residues
+    for ori, p in ((0, case.params_start), (1, case.params_end)):
+        got = gpu_to_f64(dev.TriRunner(case.z, case.mask, p, 4, "bf16")(ori))
+        if ori == 0:
+            ref = oracle.tri_start(case.z, case.mask, p.as_dict(), 4, rows=rows)
+            g = got[rows]
+        else:
+            ref = oracle.tri_end(case.z, case.mask, p.as_dict(), 4, cols=rows)
+            g = got[:, rows]
+        check(g, ref, "bf16", f"cfg tri_bf16_i384_pad ori={ori}")
+        # padded residues: every key masked -> out = b_o (= 0 here)
+        pad = case.mask.sum(1) == 0
+        assert np.all(got[pad] == 0.0) if ori == 0 else np.all(got[:, pad] == 0.0)
+
+
+def test_cfg_msa_bf16():
+    cfg = inputs.CONFIGS["msa_bf16_s512_i384"]
+    case = inputs.make_msa_case(S=cfg["S"], I=cfg["I"], c_m=cfg["c_m"], c_z=cfg["c_z"], H=cfg["H"], d=cfg["d"],
+                                dtype=cfg["dtype"], mask=cfg["mask"], seed=cfg["seed"])
+    dev = _dev()
+    got = gpu_to_f64(dev.MsaRunner(case.m, case.z, case.mask, case.params, 8, "bf16")())
+    rng = np.random.default_rng(1)
+    seqs = _sample(case.S, 8, rng)
+    ref = oracle.msa_row(case.m, case.z, case.mask, case.params.as_dict(), 8, seqs=seqs)
+    check(got[seqs], ref, "bf16", "cfg msa_bf16_s512_i384")
+
+
+@pytest.mark.parametrize("mask", ["bernoulli", "columns", "none"])
+def test_msa_small(mask):
+    case = inputs.make_msa_case(S=5, I=37, c_m=256, c_z=128, H=8, d=32, dtype="bf16", mask=mask, seed=17,
+                                affine=True, biases=True)
+    if case.mask is not None:
+        case.mask[2, :] = 0
+    got = gpu_to_f64(_dev().MsaRunner(case.m, case.z, case.mask, case.params, 8, "bf16")())
+    ref = oracle.msa_row(case.m, case.z, case.mask, case.params.as_dict(), 8)
+    check(got, ref, "bf16", f"msa small mask={mask}")
+
+
+def test_msa_small_fp32():
+    case = inputs.make_msa_case(S=4, I=21, c_m=64, c_z=64, H=4, d=32, dtype="f32", mask="bernoulli", seed=19,
+                                affine=True, biases=True)
+    got = gpu_to_f64(_dev().MsaRunner(case.m, case.z, case.mask, case.params, 4, "f32")())
+    ref = oracle.msa_row(case.m, case.z, case.mask, case.params.as_dict(), 4)
+    check(got, ref, "f32", "msa small fp32")
+
+
+def test_cfg_tri_bf16_i1536_sampled():
+    cfg = inputs.CONFIGS["tri_bf16_i1536"]
+    case = inputs.make_tri_case(I=cfg["I"], c=cfg["c"], H=cfg["H"], d=cfg["d"], dtype=cfg["dtype"],
+                                mask=cfg["mask"], seed=cfg["seed"])
+    dev = _dev()
+    rng = np.random.default_rng(2)
+    rows = np.array([0, 777, 1535])
+    for ori, p in ((0, case.params_start), (1, case.params_end)):
+        out = dev.TriRunner(case.z, case.mask, p, 4, "bf16")(ori)
+        if ori == 0:
+            got = gpu_to_f64(out[torch.as_tensor(rows, device=out.device)])
+            ref = oracle.tri_start(case.z, None, p.as_dict(), 4, rows=rows)
+        else:
+            got = gpu_to_f64(out[:, torch.as_tensor(rows, device=out.device)])
+            ref = oracle.tri_end(case.z, None, p.as_dict(), 4, cols=rows)
+        check(got, ref, "bf16", f"cfg tri_bf16_i1536 ori={ori} rows={rows.tolist()}")
+        del out
+
+
+# ----------------------------------------------------------------------------
+# properties of the GPU path
+# ----------------------------------------------------------------------------
+def test_end_equals_start_on_transpose_bitwise():
+    case = inputs.make_tri_case(I=77, c=128, H=4, d=32, dtype="bf16", mask="random", seed=5, affine=True,
+                                biases=True)
+    dev = _dev()
+    p = case.params_start
+    end = dev.TriRunner(case.z, case.mask, p, 4, "bf16")(1).clone()
+    zt = np.ascontiguousarray(case.z.transpose(1, 0, 2))
+    st = dev.TriRunner(zt, np.ascontiguousarray(case.mask.T), p, 4, "bf16")(0)
+    assert torch.equal(end, st.transpose(0, 1))
+
+
+def test_rows_block_equals_full_start():
+    case = inputs.make_tri_case(I=96, c=128, H=4, d=32, dtype="bf16", mask="random", seed=6, affine=True,
+                                biases=True)
+    dev = _dev()
+    p = case.params_start
+    full = dev.TriRunner(case.z, case.mask, p, 4, "bf16")(0).clone()
+    zf = dev.to_device(case.z, "bf16")
+    r0, r1 = 33, 70
+    rr = dev.RowsRunner(zf, zf[r0:r1].contiguous(), dev.mask_to_device(case.mask[r0:r1]), p, 4, "bf16")
+    got = rr()
+    assert torch.equal(got, full[r0:r1])
+    ref = oracle.tri_start(case.z, case.mask, p.as_dict(), 4, rows=np.arange(r0, r1))
+    check(gpu_to_f64(got), ref, "bf16", "rows block I=96")
+
+
+def test_bias_entry_point_matches_oracle():
+    case = inputs.make_tri_case(I=50, c=128, H=4, d=32, dtype="bf16", mask="none", seed=8, affine=True)
+    dev = _dev()
+    zf = dev.to_device(case.z, "bf16")
+    rr = dev.RowsRunner(zf, zf[:2].contiguous(), None, case.params_start, 4, "bf16")
+    b = rr.compute_bias().cpu().numpy()
+    ref = oracle.attention_bias(case.z, case.params_start.as_dict(), 4, oracle.START)
+    # bias = bf16(LN(z)) . w_b with fp32 accumulation
+    assert np.max(np.abs(b - ref)) < 3e-2
+
+
+def test_deterministic_bitwise():
+    case = inputs.make_tri_case(I=130, c=128, H=4, d=32, dtype="bf16", mask="random", seed=9)
+    dev = _dev()
+    run = dev.TriRunner(case.z, case.mask, case.params_start, 4, "bf16")
+    a = run(0).clone()
+    for _ in range(2):
+        assert torch.equal(run(0), a)
