@@ -15,12 +15,11 @@
 // which every kernel takes as strides.  The ending node is thus read with
 // strided loads of Z and written with strided stores; Z is never transposed.
 //
-// Workspace layouts (Pp = P rounded up to 32; padded positions hold zeros):
-//   q  [nrows][H][Pp][32] fp16, scaled by log2(e)/sqrt(d)
-//   k  [nrows][H][Pp][32] fp16
-//   v  [nrows][H][32][Pp] fp16 (positions fastest)
-//   g  [nrows][P][H*32]  fp16, sigmoid already applied
-//   bias [H][P][P] float, natural-log units
+// Workspace (Pp = P rounded up to 32; padded positions hold zeros); q, k, v
+// and the bias use the operand-ordered layouts of pa_device.h:
+//   q, k, v  nrows*H*Pp*32 fp16 (q scaled by log2(e)/sqrt(d))
+//   g        [nrows][P][H*32] fp16, sigmoid already applied
+//   bias     H*Pp*Pp float, log2 units (natural bias * log2(e)), zero padding
 #include "pa_device.h"
 
 namespace pa {
@@ -117,8 +116,8 @@ __global__ __launch_bounds__(512) void proj_kernel(
     const bf16* __restrict__ x, int64_t xs_r, int64_t xs_p, const bf16* __restrict__ gamma,
     const bf16* __restrict__ beta, float eps, const f16* __restrict__ wT, const bf16* __restrict__ wb,
     const bf16* __restrict__ b_g, float q_scale, f16* __restrict__ q_ws, f16* __restrict__ k_ws,
-    f16* __restrict__ v_ws, f16* __restrict__ g_ws, float* __restrict__ bias, int nrows, int P, int Pp,
-    int H) {
+    f16* __restrict__ v_ws, f16* __restrict__ g_ws, float* __restrict__ bias, int bias_swizzled, float bias_scale,
+    int nrows, int P, int Pp, int H) {
   constexpr int NT = 512;
   constexpr int KS = C_IN / 16;          // MFMA K-steps
   constexpr bool HAS_QKVG = MODE != 2;
@@ -168,24 +167,25 @@ __global__ __launch_bounds__(512) void proj_kernel(
         }
         const int col = colbase + mb * 32 - tensor * HD;   // first column within the tensor
         const int h = col / 32;
-        if (tensor == 0 || tensor == 1) {
-          f16* dst = (tensor == 0 ? q_ws : k_ws) + (((int64_t)r * H + h) * Pp + p0 + lq) * 32;
+        const int64_t rh = (int64_t)r * H + h;
+        const int nb = Pp / 32;
+        if (tensor == 0 || tensor == 1) {   // lane = position p0+lq; registers = 4 runs of 4 channels
           const float sc = tensor == 0 ? q_scale : 1.0f;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             f16x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = f2h_sat(acc[jj * 4 + e] * sc);
-            st8(dst + jj * 8 + g * 4, o);
+            const int d0 = jj * 8 + g * 4;
+            st8((tensor == 0 ? q_ws + q_off(rh, nb, p0 + lq, d0) : k_ws + k_off(rh, nb, p0 + lq, d0)), o);
           }
-        } else if (tensor == 2) {
-          f16* dst = v_ws + (((int64_t)r * H + h) * 32 + lq) * Pp + p0;
+        } else if (tensor == 2) {           // lane = channel lq; registers = 4 runs of 4 positions
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             f16x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = f2h_sat(acc[jj * 4 + e]);
-            st8(dst + jj * 8 + g * 4, o);
+            st8(v_ws + v_off(rh, nb, p0 + jj * 8 + g * 4, lq), o);
           }
         } else {
           const int p = p0 + lq;
@@ -212,200 +212,39 @@ __global__ __launch_bounds__(512) void proj_kernel(
 #pragma unroll
       for (int t = 0; t < KS; ++t) acc = mfma32(WB[t], ld16(xs + lq * (C_IN + 8) + t * 16 + g * 8), acc);
       const int p = p0 + lq;
-      if (p < P) {
+      if (bias_swizzled) {   // attention layout: log2 units, padded to Pp x Pp with zeros
+        const int nb = Pp / 32;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int hh = acc_row(j, g);
-          if (hh < H) bias[((int64_t)hh * P + r) * P + p] = acc[j];
+          if (hh < H) {
+            bias[b_off(hh, nb, r, p)] = p < P ? acc[j] * bias_scale : 0.0f;
+            if (r == P - 1)   // the padded query rows get zeros at the same keys
+              for (int rp = P; rp < Pp; ++rp) bias[b_off(hh, nb, rp, p)] = 0.0f;
+          }
+        }
+      } else if (p < P) {    // caller layout [H][P][P]
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int hh = acc_row(j, g);
+          if (hh < H) bias[((int64_t)hh * P + r) * P + p] = acc[j] * bias_scale;
         }
       }
     }
   }
 }
 
-// --------------------------------------------------------------------------
-// Flash-style attention with the pair bias as the MFMA accumulator input,
-// online softmax in fp32 and the gate + output projection fused in.
-//
-// Workgroup = H waves (one per head) sharing 32 query positions and R rows.
-// Per 32-key block a wave computes S^T = K Q^T + bias^T (two MFMAs, the bias
-// tile loaded once and reused for the R rows), updates the running max and
-// sum, and accumulates O^T += V^T P^T (two MFMAs).  Keys are loaded in the
-// order pi(m) (bits 2 and 3 of m swapped) so that the S^T accumulator
-// registers are directly the B operand of the P.V product: register j of a
-// lane in half g then holds key (j/8)*16 + g*8 + j%8 of the block.
-// --------------------------------------------------------------------------
-template <int H, int C_OUT, int R>
-__global__ __launch_bounds__(H * 64) void attn_kernel(
-    const f16* __restrict__ q_ws, const f16* __restrict__ k_ws, const f16* __restrict__ v_ws,
-    const f16* __restrict__ g_ws, const float* __restrict__ bias, const uint8_t* __restrict__ mask,
-    int64_t ms_r, int64_t ms_k, const f16* __restrict__ woT, const bf16* __restrict__ b_o,
-    bf16* __restrict__ out, int64_t os_r, int64_t os_p, int nrows, int P, int Pp) {
-  constexpr int HD = H * 32;
-  constexpr int KO = HD / 16;                 // K-steps of the output projection
-  constexpr int CB = C_OUT / 32;              // output channel blocks
-  constexpr int CB_PER_WAVE = (CB + H - 1) / H;
-  constexpr int OP = HD + 8;                  // LDS pitch of the gated o tile
-  __shared__ __attribute__((aligned(16))) f16 o_lds[32 * OP];
-
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int lq = lane & 31, g = lane >> 5;
-  const int h = wave;
-  const int q0 = blockIdx.x * 32;
-  const int r0 = blockIdx.y * R;
-  const int nkb = Pp / 32;
-  const float NEG_INF = -__builtin_inff();
-
-  // query operands (B of S^T = K Q^T), one per row, loaded once
-  f16x8 Qop[R][2];
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    const int r = min(r0 + rr, nrows - 1);
-    const f16* base = q_ws + (((int64_t)r * H + h) * Pp + q0 + lq) * 32 + g * 8;
-    Qop[rr][0] = ld16(base);
-    Qop[rr][1] = ld16(base + 16);
-  }
-  f32x16 O[R];
-  float m_run[R], l_run[R];
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    O[rr] = f32x16{};
-    m_run[rr] = NEG_INF;
-    l_run[rr] = 0.0f;
-  }
-
-  const int qrow = min(q0 + lq, P - 1);
-  const float* brow = bias + ((int64_t)h * P + qrow) * P;
-  const int kperm = (lq & ~12) | ((lq & 4) << 1) | ((lq & 8) >> 1);   // pi(lq)
-
-  const bool bias_vec = (P & 3) == 0;   // bias rows 16-byte aligned
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int kbase = kb * 32;
-    const bool tail = kbase + 32 > P;
-    f32x16 Bt;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int k0 = kbase + u * 16 + g * 8;
-      if (!tail && bias_vec) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(brow + k0);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(brow + k0 + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          Bt[u * 8 + e] = a[e] * kLog2e;
-          Bt[u * 8 + 4 + e] = b[e] * kLog2e;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Bt[u * 8 + e] = brow[min(k0 + e, P - 1)] * kLog2e;
-      }
-    }
-
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-      const int r = min(r0 + rr, nrows - 1);
-      const int64_t rh = (int64_t)r * H + h;
-      const f16* kp = k_ws + (rh * Pp + kbase + kperm) * 32 + g * 8;
-      const f16x8 K0 = ld16(kp), K1 = ld16(kp + 16);
-      const f16* vp = v_ws + (rh * 32 + lq) * Pp + kbase + g * 8;
-      const f16x8 V0 = ld16(vp), V1 = ld16(vp + 16);
-
-      f32x16 S = mfma32(K0, Qop[rr][0], Bt);
-      S = mfma32(K1, Qop[rr][1], S);
-
-      if (tail || mask != nullptr) {
-        const uint8_t* mrow = mask != nullptr ? mask + (int64_t)r * ms_r : nullptr;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = kbase + (j >> 3) * 16 + g * 8 + (j & 7);
-          bool keep = key < P;
-          if (keep && mrow != nullptr) keep = mrow[(int64_t)key * ms_k] != 0;
-          S[j] = keep ? S[j] : NEG_INF;
-        }
-      }
-
-      float bmax = S[0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) bmax = fmaxf(bmax, S[j]);
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-      const float m_new = fmaxf(m_run[rr], bmax);
-      const float m_use = m_new == NEG_INF ? 0.0f : m_new;
-      const float alpha = fast_exp2(m_run[rr] - m_use);
-      m_run[rr] = m_new;
-
-      float psum = 0.0f;
-      f16x8 P0, P1;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = fast_exp2(S[j] - m_use);
-        psum += p;
-        P0[j] = f2h(p);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = fast_exp2(S[8 + j] - m_use);
-        psum += p;
-        P1[j] = f2h(p);
-      }
-      l_run[rr] = l_run[rr] * alpha + psum;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) O[rr][j] *= alpha;
-      O[rr] = mfma32(V0, P0, O[rr]);
-      O[rr] = mfma32(V1, P1, O[rr]);
-    }
-  }
-
-  // ---- epilogue: normalise, gate, output projection ----
-  f16x8 Wo[CB_PER_WAVE][KO];
-#pragma unroll
-  for (int i = 0; i < CB_PER_WAVE; ++i) {
-    const int cb = wave + i * H;
-    if (cb < CB) {
-#pragma unroll
-      for (int t = 0; t < KO; ++t) Wo[i][t] = ld16(woT + (int64_t)(cb * 32 + lq) * HD + t * 16 + g * 8);
-    }
-  }
-  const int q = q0 + lq;
-  const int qc = min(q, P - 1);
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    const int r = r0 + rr;
-    if (r >= nrows) break;
-    const float ltot = l_run[rr] + __shfl_xor(l_run[rr], 32, 64);
-    const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-    const f16* gp = g_ws + ((int64_t)r * P + qc) * HD + h * 32;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const f16x4 gv = *reinterpret_cast<const f16x4*>(gp + jj * 8 + g * 4);
-      f16x4 ov;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ov[e] = f2h_sat(O[rr][jj * 4 + e] * inv * (float)gv[e]);
-      st8(o_lds + lq * OP + h * 32 + jj * 8 + g * 4, ov);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < CB_PER_WAVE; ++i) {
-      const int cb = wave + i * H;
-      if (cb < CB) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int t = 0; t < KO; ++t) acc = mfma32(Wo[i][t], ld16(o_lds + lq * OP + t * 16 + g * 8), acc);
-        if (q < P) {
-          bf16* dst = out + (int64_t)r * os_r + (int64_t)q * os_p + cb * 32;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            bf16x4 ov;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int c = jj * 8 + g * 4 + e;
-              const float bo = b_o != nullptr ? bf2f(b_o[cb * 32 + c]) : 0.0f;
-              ov[e] = f2bf(acc[jj * 4 + e] + bo);
-            }
-            st8(dst + jj * 8 + g * 4, ov);
-          }
-        }
-      }
-    }
-    __syncthreads();
+// Copy of a caller-provided bias [H][P][P] (natural-log units) into the
+// attention layout (operand order, log2 units, zero padding to Pp x Pp).
+__global__ void bias_to_attn_layout_kernel(const float* __restrict__ src, float* __restrict__ dst, int H, int P,
+                                           int Pp) {
+  const int64_t total = (int64_t)H * Pp * Pp;
+  const int nb = Pp / 32;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int h = (int)(i / ((int64_t)Pp * Pp));
+    const int64_t rem = i % ((int64_t)Pp * Pp);
+    const int q = (int)(rem / Pp), k = (int)(rem % Pp);
+    dst[b_off(h, nb, q, k)] = (q < P && k < P) ? src[((int64_t)h * P + q) * P + k] * kLog2e : 0.0f;
   }
 }
 
@@ -417,6 +256,13 @@ __global__ __launch_bounds__(H * 64) void attn_kernel(
 #include "pa_launch.h"
 
 namespace pa {
+
+hipError_t launch_bias_to_attn_layout(const float* src, float* dst, int H, int P, int Pp, hipStream_t s) {
+  const int64_t total = (int64_t)H * Pp * Pp;
+  const int blocks = (int)std::min<int64_t>((total + 255) / 256, 8192);
+  hipLaunchKernelGGL(bias_to_attn_layout_kernel, dim3(blocks), dim3(256), 0, s, src, dst, H, P, Pp);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_bf16(const PackArgs& a, hipStream_t s) {
   const int64_t total = (int64_t)4 * a.hd * a.c_in + (int64_t)a.c_out * a.hd;
@@ -433,7 +279,7 @@ static hipError_t proj_dispatch(const ProjArgs& a, int grid_x, int grid_y, hipSt
   hipLaunchKernelGGL((proj_kernel<C_IN, HD, MODE>), dim3(grid_x, grid_y), dim3(512), 0, s, (const bf16*)a.x, a.xs_r,
                      a.xs_p, (const bf16*)a.gamma, (const bf16*)a.beta, a.eps, (const f16*)a.wT,
                      (const bf16*)a.wb, (const bf16*)a.b_g, a.q_scale, (f16*)a.q_ws, (f16*)a.k_ws,
-                     (f16*)a.v_ws, (f16*)a.g_ws, a.bias, a.nrows, a.P, a.Pp, a.H);
+                     (f16*)a.v_ws, (f16*)a.g_ws, a.bias, a.bias_swizzled, a.bias_scale, a.nrows, a.P, a.Pp, a.H);
   return hipGetLastError();
 }
 
@@ -465,29 +311,6 @@ hipError_t launch_proj_bf16(const ProjArgs& a, int mode, int num_cu, hipStream_t
     case 2: return proj_dispatch_c<2>(a, grid_x, grid_y, s);
     default: return hipErrorInvalidValue;
   }
-}
-
-template <int H, int C_OUT>
-static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
-  constexpr int R = 4;
-  dim3 grid(a.Pp / 32, (a.nrows + R - 1) / R);
-  hipLaunchKernelGGL((attn_kernel<H, C_OUT, R>), grid, dim3(H * 64), 0, s, (const f16*)a.q_ws, (const f16*)a.k_ws,
-                     (const f16*)a.v_ws, (const f16*)a.g_ws, a.bias, a.mask, a.ms_r, a.ms_k, (const f16*)a.woT,
-                     (const bf16*)a.b_o, (bf16*)a.out, a.os_r, a.os_p, a.nrows, a.P, a.Pp);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
-  if (a.H == 4) {
-    if (a.c_out == 64) return attn_dispatch<4, 64>(a, s);
-    if (a.c_out == 128) return attn_dispatch<4, 128>(a, s);
-    if (a.c_out == 256) return attn_dispatch<4, 256>(a, s);
-  } else if (a.H == 8) {
-    if (a.c_out == 64) return attn_dispatch<8, 64>(a, s);
-    if (a.c_out == 128) return attn_dispatch<8, 128>(a, s);
-    if (a.c_out == 256) return attn_dispatch<8, 256>(a, s);
-  }
-  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

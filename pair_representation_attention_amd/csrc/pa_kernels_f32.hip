@@ -17,8 +17,8 @@ __global__ __launch_bounds__(256) void proj_f32_kernel(
     const float* __restrict__ beta, float eps, const float* __restrict__ wq, const float* __restrict__ wk,
     const float* __restrict__ wv, const float* __restrict__ wg, const float* __restrict__ wb,
     const float* __restrict__ b_g, float q_scale, float* __restrict__ q_ws, float* __restrict__ k_ws,
-    float* __restrict__ v_ws, float* __restrict__ g_ws, float* __restrict__ bias, int c_in, int hd, int H,
-    int nrows, int P, int mode) {
+    float* __restrict__ v_ws, float* __restrict__ g_ws, float* __restrict__ bias, float bias_scale, int c_in, int hd,
+    int H, int nrows, int P, int mode) {
   extern __shared__ float xs[];   // [32][c_in + 1]
   const int pitch = c_in + 1;
   const int r = blockIdx.y;
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void proj_f32_kernel(
       const int hh = col - nq;
       float acc = 0.0f;
       for (int k = 0; k < c_in; ++k) acc = fmaf(xr[k], wb[(int64_t)k * H + hh], acc);
-      bias[((int64_t)hh * P + r) * P + p] = acc;
+      bias[((int64_t)hh * P + r) * P + p] = acc * bias_scale;
     }
   }
 }
@@ -127,8 +127,8 @@ hipError_t launch_proj_f32(const ProjArgs& a, int mode, hipStream_t s) {
   hipLaunchKernelGGL(proj_f32_kernel, grid, dim3(256), lds, s, (const float*)a.x, a.xs_r, a.xs_p,
                      (const float*)a.gamma, (const float*)a.beta, a.eps, (const float*)a.wq, (const float*)a.wk,
                      (const float*)a.wv, (const float*)a.wg, (const float*)a.wb, (const float*)a.b_g, a.q_scale,
-                     (float*)a.q_ws, (float*)a.k_ws, (float*)a.v_ws, (float*)a.g_ws, a.bias, a.c_in, a.hd, a.H,
-                     a.nrows, a.P, mode);
+                     (float*)a.q_ws, (float*)a.k_ws, (float*)a.v_ws, (float*)a.g_ws, a.bias, a.bias_scale, a.c_in,
+                     a.hd, a.H, a.nrows, a.P, mode);
   return hipGetLastError();
 }
 

@@ -63,13 +63,16 @@ Layout make_layout(int64_t nrows, int64_t P, int64_t c_in, int64_t c_out, int64_
     L.k = take((size_t)nrows * H * Pp * 32 * 2);
     L.v = take((size_t)nrows * H * 32 * Pp * 2);
     L.g = take((size_t)nrows * P * hd * 2);
+    // the attention reads the bias in operand order, Pp x Pp, log2 units; a
+    // caller-provided bias (row block) is converted into this buffer as well
+    L.bias = take((size_t)H * Pp * Pp * 4);
   } else {
     L.q = take((size_t)nrows * P * hd * 4);
     L.k = take((size_t)nrows * P * hd * 4);
     L.v = take((size_t)nrows * P * hd * 4);
     L.g = take((size_t)nrows * P * hd * 4);
+    if (with_bias) L.bias = take((size_t)H * P * P * 4);
   }
-  if (with_bias) L.bias = take((size_t)H * P * P * 4);
   L.total = off;
   return L;
 }
@@ -365,8 +368,12 @@ static int run_row_attention(const pairattn_params* p, const Layout& L, hipStrea
   const int64_t hd = H * 32;
   const bool bf = p->dtype == PAIRATTN_BF16;
   const int Pp = (int)pad32(P);
-  float* bias_ws = bias_given != nullptr ? nullptr : reinterpret_cast<float*>(ws_at(p, L.bias));
-  const float* bias = bias_given != nullptr ? bias_given : bias_ws;
+  // bf16 path: the attention reads the workspace bias ([H][P][Pp], log2 units);
+  // fp32 path: [H][P][P] natural units, the caller's own array for row blocks
+  float* bias_ws = (bf || bias_given == nullptr) ? reinterpret_cast<float*>(ws_at(p, L.bias)) : nullptr;
+  const float* bias = (bf || bias_given == nullptr) ? bias_ws : bias_given;
+  const int bias_swz = bf ? 1 : 0;
+  const float bias_scale = bf ? 1.4426950408889634f : 1.0f;
 
   pa::ProjArgs pj{};
   pj.x = x;
@@ -386,6 +393,8 @@ static int run_row_attention(const pairattn_params* p, const Layout& L, hipStrea
   pj.v_ws = ws_at(p, L.v);
   pj.g_ws = ws_at(p, L.g);
   pj.bias = bias_ws;
+  pj.bias_swizzled = bias_swz;
+  pj.bias_scale = bias_scale;
   pj.c_in = (int)c;
   pj.hd = (int)hd;
   pj.H = (int)H;
@@ -418,6 +427,8 @@ static int run_row_attention(const pairattn_params* p, const Layout& L, hipStrea
     pb.eps = p->ln_eps;
     pb.wb = p->w_b;
     pb.bias = bias_ws;
+    pb.bias_swizzled = bias_swz;
+    pb.bias_scale = bias_scale;
     pb.c_in = (int)zb_c;
     pb.hd = (int)hd;
     pb.H = (int)H;
@@ -427,6 +438,10 @@ static int run_row_attention(const pairattn_params* p, const Layout& L, hipStrea
     if (bf) PA_TRY(hip_status(pa::launch_proj_bf16(pb, 2, num_cu, s), "pair-bias launch"));
     else PA_TRY(hip_status(pa::launch_proj_f32(pb, 2, s), "pair-bias launch"));
     tm_mark(s, "pair_bias");
+  }
+  if (bf && bias_given != nullptr) {   // row block: caller's bias -> attention layout
+    PA_TRY(hip_status(pa::launch_bias_to_attn_layout(bias_given, bias_ws, (int)H, (int)P, Pp, s), "bias copy launch"));
+    tm_mark(s, "bias_copy");
   }
 
   pa::AttnArgs at{};
@@ -512,6 +527,8 @@ int pairattn_tri_bias(const void* z, const pairattn_params* p, float* bias, int6
   pb.eps = p->ln_eps;
   pb.wb = p->w_b;
   pb.bias = bias;
+  pb.bias_swizzled = 0;
+  pb.bias_scale = 1.0f;
   pb.c_in = (int)c_z;
   pb.hd = (int)(H * 32);
   pb.H = (int)H;

@@ -61,9 +61,12 @@ def test_workspace_sizes():
     assert lib.pairattn_tri_workspace_bytes(8, 128, 4, 32, 7) == 0
     assert lib.pairattn_msa_workspace_bytes(512, 384, 256, 128, 8, 32, lib.PAIRATTN_BF16) > 0
     assert lib.pairattn_rows_workspace_bytes(512, 4096, 128, 4, 32, lib.PAIRATTN_BF16) > 0
-    # the row-block workspace carries no bias
-    assert lib.pairattn_rows_workspace_bytes(64, 64, 128, 4, 32, lib.PAIRATTN_BF16) < \
+    # a block of 16 rows needs less than all 64 rows
+    assert lib.pairattn_rows_workspace_bytes(16, 64, 128, 4, 32, lib.PAIRATTN_BF16) < \
         lib.pairattn_tri_workspace_bytes(64, 128, 4, 32, lib.PAIRATTN_BF16)
+    # the fp32 row block reads the caller's bias in place
+    assert lib.pairattn_rows_workspace_bytes(64, 64, 128, 4, 32, lib.PAIRATTN_F32) < \
+        lib.pairattn_tri_workspace_bytes(64, 128, 4, 32, lib.PAIRATTN_F32)
 
 
 def _tri_ok_params(I=64, c=128, H=4, dtype=lib.PAIRATTN_BF16):
