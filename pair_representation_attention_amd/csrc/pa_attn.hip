@@ -52,9 +52,9 @@ __device__ __forceinline__ f16x8 lds_f16x8(const char* p) { return *reinterpret_
 template <int H, int C_OUT>
 __global__ __launch_bounds__(512, 1) void attn_kernel(
     const f16* __restrict__ q_ws, const f16* __restrict__ k_ws, const f16* __restrict__ v_ws,
-    const f16* __restrict__ g_ws, const float* __restrict__ bias, const uint8_t* __restrict__ mask,
-    int64_t ms_r, int64_t ms_k, const f16* __restrict__ woT, const bf16* __restrict__ b_o,
-    bf16* __restrict__ out, int64_t os_r, int64_t os_p, int nrows, int P, int Pp, int n_qp, int n_rg) {
+    const f16* __restrict__ g_ws, const float* __restrict__ bias, const uint32_t* __restrict__ mask_bits,
+    const f16* __restrict__ woT, const bf16* __restrict__ b_o, bf16* __restrict__ out, int64_t os_r,
+    int64_t os_p, int nrows, int P, int Pp, int n_qp, int n_rg) {
   static_assert(H == 4 || H == 8, "4 or 8 heads");
   constexpr int HD = H * 32;
   constexpr int QB = H == 4 ? 2 : 1;        // query blocks per wave
@@ -145,25 +145,43 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c) g2lds16(bias + b_chunk(btile_h, nkb, btile_qb, kb, c) + lane * 4, bt + c * 1024);
   };
-  // mask term of the keys this lane feeds to the S^T MFMA (row rr, block kb)
-  auto mask_term = [&](int rr, int kb) -> f16 {
-    const int key = kb * 32 + kp_lane;
-    bool keep = key < P;
-    if (mask != nullptr) keep = keep && mask[(int64_t)rows_c[rr] * ms_r + (int64_t)min(key, P - 1) * ms_k] != 0;
-    return keep ? HZERO : HNEG_INF;
+  // keep bits: word (row, kb) of mask_bits holds bit b = key kb*32+b kept
+  auto load_bits = [&](int rr, int kb) -> uint32_t {
+    return mask_bits[(int64_t)rows_c[rr] * nkb + kb];
+  };
+  auto km_operand = [&](uint32_t bits) -> f16x8 {
+    f16x8 km;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) km[e] = HZERO;
+    if (g == 0) {
+      km[0] = HONE;
+      km[1] = HONE;
+      km[2] = ((bits >> kp_lane) & 1u) ? HZERO : HNEG_INF;
+    }
+    return km;
   };
 
   stage(0, 0);
-  f16 mt_next[RW];
+  uint32_t bits_next[RW];
 #pragma unroll
-  for (int rr = 0; rr < RW; ++rr) mt_next[rr] = mask_term(rr, 0);
+  for (int rr = 0; rr < RW; ++rr) bits_next[rr] = load_bits(rr, 0);
 
+  constexpr int NU = RW * QB;   // units per key block
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
     wait_vm0();
     __syncthreads();
 
-    // operands of this block from LDS
+    // operands of this block from LDS: K/V first, then the bias tiles
+    f16x8 K[RW][2], V[RW][2], KM[RW];
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) {
+      K[rr][0] = lds_f16x8(kv_lds + rr * 2048 + lane * 16);
+      K[rr][1] = lds_f16x8(kv_lds + rr * 2048 + 1024 + lane * 16);
+      V[rr][0] = lds_f16x8(kv_lds + 4096 + rr * 2048 + lane * 16);
+      V[rr][1] = lds_f16x8(kv_lds + 4096 + rr * 2048 + 1024 + lane * 16);
+      KM[rr] = km_operand(bits_next[rr]);
+    }
     f32x16 Bt[QB];
 #pragma unroll
     for (int qq = 0; qq < QB; ++qq) {
@@ -175,93 +193,91 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
         for (int e = 0; e < 4; ++e) Bt[qq][c * 4 + e] = v[e];
       }
     }
-    f16x8 K[RW][2], V[RW][2], KM[RW];
-#pragma unroll
-    for (int rr = 0; rr < RW; ++rr) {
-      K[rr][0] = lds_f16x8(kv_lds + rr * 2048 + lane * 16);
-      K[rr][1] = lds_f16x8(kv_lds + rr * 2048 + 1024 + lane * 16);
-      V[rr][0] = lds_f16x8(kv_lds + 4096 + rr * 2048 + lane * 16);
-      V[rr][1] = lds_f16x8(kv_lds + 4096 + rr * 2048 + 1024 + lane * 16);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) KM[rr][e] = HZERO;
-      if (g == 0) {
-        KM[rr][0] = HONE;
-        KM[rr][1] = HONE;
-        KM[rr][2] = mt_next[rr];
-      }
-    }
-    wait_lgkm0();
+    // the K/V reads (issued first; LDS returns in order) are complete once at
+    // most the 4*QB bias reads are outstanding: the K/V area can be refilled
+    if constexpr (QB == 2) asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory");
     if (kb + 1 < nkb) {
       stage(kb + 1, buf ^ 1);
 #pragma unroll
-      for (int rr = 0; rr < RW; ++rr) mt_next[rr] = mask_term(rr, kb + 1);
+      for (int rr = 0; rr < RW; ++rr) bits_next[rr] = load_bits(rr, kb + 1);
     }
 
+    auto qk = [&](int rr, int qq) -> f32x16 {
+      f32x16 S = mfma32(K[rr][0], Q[rr][qq][0], Bt[qq]);
+      S = mfma32(K[rr][1], Q[rr][qq][1], S);
+      return mfma32(KM[rr], QA[rr][qq], S);
+    };
+    bool keyed[RW];
 #pragma unroll
-    for (int rr = 0; rr < RW; ++rr) {
-      bool keyed = false;   // this block holds a kept key of row rr (wave-uniform)
-#pragma unroll
-      for (int qq = 0; qq < QB; ++qq) {
-        f32x16 S = mfma32(K[rr][0], Q[rr][qq][0], Bt[qq]);
-        S = mfma32(K[rr][1], Q[rr][qq][1], S);
-        S = mfma32(KM[rr], QA[rr][qq], S);
+    for (int rr = 0; rr < RW; ++rr) keyed[rr] = false;   // block holds a kept key of row rr
 
-        float p[16];
-        float psum = 0.0f;
-        bool slow = !mset[rr];
-        if (!slow) {
+    // software pipeline: the logits of unit u+1 are on the matrix cores
+    // while the softmax of unit u runs on the VALU
+    f32x16 Scur = qk(0, 0);
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            p[j] = fast_exp2(S[j]);
-            psum += p[j];
-          }
-          slow = __ballot(!(psum <= 256.0f)) != 0;
-        }
-        if (slow) {
-          float bmax = S[0];
+    for (int u = 0; u < NU; ++u) {
+      const int rr = u / QB, qq = u % QB;
+      f32x16 Snext;
+      if (u + 1 < NU) Snext = qk((u + 1) / QB, (u + 1) % QB);
+      const f32x16 S = Scur;
+
+      float p[16];
+      float psum;
+      bool slow = !mset[rr];
+      if (!slow) {
 #pragma unroll
-          for (int j = 1; j < 16; ++j) bmax = fmaxf(bmax, S[j]);
-          bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-          const bool any_key = __ballot(bmax > -__builtin_inff()) != 0;
-          keyed = keyed || any_key;
-          float d_use = 0.0f;
-          if (any_key) {
-            const float delta = mset[rr] ? fmaxf(bmax, 0.0f) : bmax;
-            const float m_new = m_rep[rr][qq] + delta;
-            const f16 hi = f2h(m_new);
-            const f16 lo = f2h(m_new - (float)hi);
-            const float m_new_rep = (float)hi + (float)lo;
-            d_use = m_new_rep - m_rep[rr][qq];
-            const float alpha = mset[rr] ? fast_exp2(-d_use) : 0.0f;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) O[rr][qq][j] *= alpha;
-            l_run[rr][qq] *= alpha;
-            m_rep[rr][qq] = m_new_rep;
-            if (g == 0) {
-              QA[rr][qq][0] = -hi;
-              QA[rr][qq][1] = -lo;
-            }
-          }
-          psum = 0.0f;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            p[j] = fast_exp2(S[j] - d_use);
-            psum += p[j];
-          }
-        }
-        l_run[rr][qq] += psum;
-        f16x8 P0, P1;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          P0[j] = f2h(p[j]);
-          P1[j] = f2h(p[8 + j]);
-        }
-        O[rr][qq] = mfma32(V[rr][0], P0, O[rr][qq]);
-        O[rr][qq] = mfma32(V[rr][1], P1, O[rr][qq]);
+        for (int j = 0; j < 16; ++j) p[j] = fast_exp2(S[j]);
+        float a0 = (p[0] + p[1]) + (p[2] + p[3]), a1 = (p[4] + p[5]) + (p[6] + p[7]);
+        float a2 = (p[8] + p[9]) + (p[10] + p[11]), a3 = (p[12] + p[13]) + (p[14] + p[15]);
+        psum = (a0 + a1) + (a2 + a3);
+        slow = __ballot(!(psum <= 256.0f)) != 0;
       }
-      // the first block with a kept key sets the reference maximum of the row
-      mset[rr] = mset[rr] || keyed;
+      if (slow) {
+        float bmax = S[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) bmax = fmaxf(bmax, S[j]);
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+        const bool any_key = __ballot(bmax > -__builtin_inff()) != 0;
+        keyed[rr] = keyed[rr] || any_key;
+        float d_use = 0.0f;
+        if (any_key) {
+          const float delta = mset[rr] ? fmaxf(bmax, 0.0f) : bmax;
+          const float m_new = m_rep[rr][qq] + delta;
+          const f16 hi = f2h(m_new);
+          const f16 lo = f2h(m_new - (float)hi);
+          const float m_new_rep = (float)hi + (float)lo;
+          d_use = m_new_rep - m_rep[rr][qq];
+          const float alpha = mset[rr] ? fast_exp2(-d_use) : 0.0f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) O[rr][qq][j] *= alpha;
+          l_run[rr][qq] *= alpha;
+          m_rep[rr][qq] = m_new_rep;
+          if (g == 0) {
+            QA[rr][qq][0] = -hi;
+            QA[rr][qq][1] = -lo;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) p[j] = fast_exp2(S[j] - d_use);
+        float a0 = (p[0] + p[1]) + (p[2] + p[3]), a1 = (p[4] + p[5]) + (p[6] + p[7]);
+        float a2 = (p[8] + p[9]) + (p[10] + p[11]), a3 = (p[12] + p[13]) + (p[14] + p[15]);
+        psum = (a0 + a1) + (a2 + a3);
+      }
+      l_run[rr][qq] += psum;
+      f16x8 P0, P1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        P0[j] = f2h(p[j]);
+        P1[j] = f2h(p[8 + j]);
+      }
+      O[rr][qq] = mfma32(V[rr][0], P0, O[rr][qq]);
+      O[rr][qq] = mfma32(V[rr][1], P1, O[rr][qq]);
+      if (u + 1 < NU) Scur = Snext;
     }
+    // the first block with a kept key sets the reference maximum of the row
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) mset[rr] = mset[rr] || keyed[rr];
   }
 
   // ---- epilogue: normalise, gate, output projection ----
@@ -324,6 +340,38 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
   }
 }
 
+// keep bits per (row, 32-key block): bit b of word (r, kb) = key kb*32+b is
+// kept (key < P and mask[r*ms_r + key*ms_k] != 0, or no mask).  One wave
+// per word group: lane = key within the block, ballot packs the bits.
+__global__ void mask_bits_kernel(const uint8_t* __restrict__ mask, int64_t ms_r, int64_t ms_k,
+                                 uint32_t* __restrict__ bits, int nrows, int P, int nkb) {
+  const int64_t nwords = (int64_t)nrows * nkb;
+  const int lane = threadIdx.x % kWave;
+  const int64_t wave0 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
+  for (int64_t w = wave0 * 2; w < nwords; w += nwaves * 2) {   // two words per wave (lane halves)
+    const int64_t word = w + (lane >> 5);
+    bool keep = false;
+    if (word < nwords) {
+      const int r = (int)(word / nkb), kb = (int)(word % nkb);
+      const int key = kb * 32 + (lane & 31);
+      keep = key < P && (mask == nullptr || mask[(int64_t)r * ms_r + (int64_t)key * ms_k] != 0);
+    }
+    const uint64_t b = __ballot(keep);
+    if (lane == 0) bits[w] = (uint32_t)b;
+    if (lane == 32 && word < nwords) bits[word] = (uint32_t)(b >> 32);
+  }
+}
+
+hipError_t launch_mask_bits(const uint8_t* mask, int64_t ms_r, int64_t ms_k, uint32_t* bits, int nrows, int P,
+                            int nkb, hipStream_t s) {
+  const int64_t nwords = (int64_t)nrows * nkb;
+  const int64_t waves = (nwords + 1) / 2;
+  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((waves + 3) / 4, 4096));
+  hipLaunchKernelGGL(mask_bits_kernel, dim3(blocks), dim3(256), 0, s, mask, ms_r, ms_k, bits, nrows, P, nkb);
+  return hipGetLastError();
+}
+
 template <int H, int C_OUT>
 static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
   constexpr int QB = H == 4 ? 2 : 1;
@@ -332,7 +380,7 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
   const int n_rg = (a.nrows + RWG - 1) / RWG;
   const int64_t n = (int64_t)n_qp * n_rg;
   hipLaunchKernelGGL((attn_kernel<H, C_OUT>), dim3((unsigned)n), dim3(512), 0, s, (const f16*)a.q_ws,
-                     (const f16*)a.k_ws, (const f16*)a.v_ws, (const f16*)a.g_ws, a.bias, a.mask, a.ms_r, a.ms_k,
+                     (const f16*)a.k_ws, (const f16*)a.v_ws, (const f16*)a.g_ws, a.bias, a.mask_bits,
                      (const f16*)a.woT, (const bf16*)a.b_o, (bf16*)a.out, a.os_r, a.os_p, a.nrows, a.P, a.Pp, n_qp,
                      n_rg);
   return hipGetLastError();

@@ -33,8 +33,9 @@ struct ProjArgs {
 struct AttnArgs {
   const void *q_ws, *k_ws, *v_ws, *g_ws;
   const float* bias;             // bf16 path: attention layout, log2 units; fp32 path: [H][P][P] natural
-  const uint8_t* mask;           // key kept iff mask[r*ms_r + k*ms_k] != 0 (NULL = all)
+  const uint8_t* mask;           // fp32 path: key kept iff mask[r*ms_r + k*ms_k] != 0 (NULL = all)
   int64_t ms_r, ms_k;
+  const uint32_t* mask_bits;     // bf16 path: keep bits per (row, 32-key block), see launch_mask_bits
   const void *woT, *wo, *b_o;    // woT for bf16, wo (natural) for fp32
   void* out;                     // element (r, p, c) at out[r*os_r + p*os_p + c]
   int64_t os_r, os_p;
@@ -46,6 +47,9 @@ hipError_t launch_bias_to_attn_layout(const float* src, float* dst, int H, int P
 // mode 0: q,k,v,g   1: q,k,v,g + bias   2: bias only
 hipError_t launch_proj_bf16(const ProjArgs& a, int mode, int num_cu, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+// keep bits [nrows][nkb] for the bf16 attention (mask may be NULL: all keys < P kept)
+hipError_t launch_mask_bits(const uint8_t* mask, int64_t ms_r, int64_t ms_k, uint32_t* bits, int nrows, int P,
+                            int nkb, hipStream_t s);
 
 hipError_t launch_proj_f32(const ProjArgs& a, int mode, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);

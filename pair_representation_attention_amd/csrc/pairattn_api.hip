@@ -41,7 +41,7 @@ constexpr int64_t kMaxPositions = 1LL << 20;
 
 // ---- workspace layout -----------------------------------------------------
 struct Layout {
-  size_t wT = 0, woT = 0, q = 0, k = 0, v = 0, g = 0, bias = 0, total = 0;
+  size_t wT = 0, woT = 0, q = 0, k = 0, v = 0, g = 0, bias = 0, bits = 0, total = 0;
 };
 
 // nrows x P positions, c_in input channels, c_out output channels.
@@ -66,6 +66,7 @@ Layout make_layout(int64_t nrows, int64_t P, int64_t c_in, int64_t c_out, int64_
     // the attention reads the bias in operand order, Pp x Pp, log2 units; a
     // caller-provided bias (row block) is converted into this buffer as well
     L.bias = take((size_t)H * Pp * Pp * 4);
+    L.bits = take((size_t)nrows * (Pp / 32) * 4);
   } else {
     L.q = take((size_t)nrows * P * hd * 4);
     L.k = take((size_t)nrows * P * hd * 4);
@@ -451,6 +452,7 @@ static int run_row_attention(const pairattn_params* p, const Layout& L, hipStrea
   at.g_ws = pj.g_ws;
   at.bias = bias;
   at.mask = mask;
+  at.mask_bits = bf ? reinterpret_cast<const uint32_t*>(ws_at(p, L.bits)) : nullptr;
   at.ms_r = ms_r;
   at.ms_k = ms_k;
   at.woT = bf ? ws_at(p, L.woT) : nullptr;
@@ -464,6 +466,12 @@ static int run_row_attention(const pairattn_params* p, const Layout& L, hipStrea
   at.nrows = (int)nrows;
   at.P = (int)P;
   at.Pp = Pp;
+  if (bf) {
+    PA_TRY(hip_status(pa::launch_mask_bits(mask, ms_r, ms_k, reinterpret_cast<uint32_t*>(ws_at(p, L.bits)),
+                                           (int)nrows, (int)P, Pp / 32, s),
+                      "mask bits launch"));
+    tm_mark(s, "mask_bits");
+  }
   if (bf) PA_TRY(hip_status(pa::launch_attn_bf16(at, s), "attention launch"));
   else PA_TRY(hip_status(pa::launch_attn_f32(at, s), "attention launch"));
   tm_mark(s, "attention");
