@@ -56,8 +56,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 //   k: same with lane pi(pos%32), pi = swap of bits 2 and 3 (the key order
 //      that makes the S^T accumulator the K-slot order of the P operand)
 //   v: chunk (rh, pos/32, (pos/16)%2): lane d + 32*((pos/8)%2), half pos%8
-//   bias: chunk (h, q/32, k/32, c): lane (q%32) + 32*g, float e, where for
-//      kk = k%32: g = (kk/8)%2, j = (kk/16)*8 + kk%8, c = j/4, e = j%4
+//   bias (fp16, the S^T accumulator image): chunk (h, q/32, k/32, u):
+//      lane (q%32) + 32*g, half s, where for kk = k%32: u = kk/16,
+//      g = (kk/8)%2, s = kk%8 -- accumulator register u*8+s of that lane
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ constexpr int kperm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
@@ -70,14 +71,15 @@ __device__ __forceinline__ int64_t k_off(int64_t rh, int nb, int pos, int d) {
 __device__ __forceinline__ int64_t v_off(int64_t rh, int nb, int pos, int d) {
   return ((((rh * nb + (pos >> 5)) * 2 + ((pos >> 4) & 1)) * 64 + d + 32 * ((pos >> 3) & 1)) << 3) + (pos & 7);
 }
-__device__ __forceinline__ int64_t b_off(int h, int nb, int q, int k) {
-  const int kk = k & 31, g = (kk >> 3) & 1, j = ((kk >> 4) << 3) + (kk & 7);
-  return (((((int64_t)h * nb + (q >> 5)) * nb + (k >> 5)) * 4 + (j >> 2)) * 64 + (q & 31) + 32 * g) * 4 + (j & 3);
+__device__ __forceinline__ int64_t b16_off(int h, int nb, int q, int k) {
+  const int kk = k & 31;
+  return (((((int64_t)h * nb + (q >> 5)) * nb + (k >> 5)) * 2 + (kk >> 4)) * 64 + (q & 31) + 32 * ((kk >> 3) & 1)) * 8 +
+         (kk & 7);
 }
 // start of chunk `c` of block (a, b): element offsets for the 16-byte-per-lane reads
 __device__ __forceinline__ int64_t qkv_chunk(int64_t rh, int nb, int blk, int c) { return ((rh * nb + blk) * 2 + c) * 512; }
-__device__ __forceinline__ int64_t b_chunk(int h, int nb, int qb, int kb, int c) {
-  return ((((int64_t)h * nb + qb) * nb + kb) * 4 + c) * 256;
+__device__ __forceinline__ int64_t b16_chunk(int h, int nb, int qb, int kb, int c) {
+  return ((((int64_t)h * nb + qb) * nb + kb) * 2 + c) * 512;
 }
 
 // Sum over an aligned group of `width` lanes (width a power of two <= 64).

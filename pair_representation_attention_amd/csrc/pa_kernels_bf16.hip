@@ -19,7 +19,7 @@
 // and the bias use the operand-ordered layouts of pa_device.h:
 //   q, k, v  nrows*H*Pp*32 fp16 (q scaled by log2(e)/sqrt(d))
 //   g        [nrows][P][H*32] fp16, sigmoid already applied
-//   bias     H*Pp*Pp float, log2 units (natural bias * log2(e)), zero padding
+//   bias     H*Pp*Pp fp16, log2 units (natural bias * log2(e)), zero padding
 #include "pa_device.h"
 
 namespace pa {
@@ -212,18 +212,19 @@ __global__ __launch_bounds__(512) void proj_kernel(
 #pragma unroll
       for (int t = 0; t < KS; ++t) acc = mfma32(WB[t], ld16(xs + lq * (C_IN + 8) + t * 16 + g * 8), acc);
       const int p = p0 + lq;
-      if (bias_swizzled) {   // attention layout: log2 units, padded to Pp x Pp with zeros
+      if (bias_swizzled) {   // attention layout: fp16, log2 units, padded to Pp x Pp with zeros
         const int nb = Pp / 32;
+        f16* b16 = reinterpret_cast<f16*>(bias);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int hh = acc_row(j, g);
           if (hh < H) {
-            bias[b_off(hh, nb, r, p)] = p < P ? acc[j] * bias_scale : 0.0f;
+            b16[b16_off(hh, nb, r, p)] = p < P ? f2h_sat(acc[j] * bias_scale) : f2h(0.0f);
             if (r == P - 1)   // the padded query rows get zeros at the same keys
-              for (int rp = P; rp < Pp; ++rp) bias[b_off(hh, nb, rp, p)] = 0.0f;
+              for (int rp = P; rp < Pp; ++rp) b16[b16_off(hh, nb, rp, p)] = f2h(0.0f);
           }
         }
-      } else if (p < P) {    // caller layout [H][P][P]
+      } else if (p < P) {    // caller layout [H][P][P] float
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int hh = acc_row(j, g);
@@ -234,9 +235,9 @@ __global__ __launch_bounds__(512) void proj_kernel(
   }
 }
 
-// Copy of a caller-provided bias [H][P][P] (natural-log units) into the
-// attention layout (operand order, log2 units, zero padding to Pp x Pp).
-__global__ void bias_to_attn_layout_kernel(const float* __restrict__ src, float* __restrict__ dst, int H, int P,
+// Copy of a caller-provided bias [H][P][P] (float, natural-log units) into
+// the attention layout (fp16 operand order, log2 units, zero padding).
+__global__ void bias_to_attn_layout_kernel(const float* __restrict__ src, f16* __restrict__ dst, int H, int P,
                                            int Pp) {
   const int64_t total = (int64_t)H * Pp * Pp;
   const int nb = Pp / 32;
@@ -244,7 +245,7 @@ __global__ void bias_to_attn_layout_kernel(const float* __restrict__ src, float*
     const int h = (int)(i / ((int64_t)Pp * Pp));
     const int64_t rem = i % ((int64_t)Pp * Pp);
     const int q = (int)(rem / Pp), k = (int)(rem % Pp);
-    dst[b_off(h, nb, q, k)] = (q < P && k < P) ? src[((int64_t)h * P + q) * P + k] * kLog2e : 0.0f;
+    dst[b16_off(h, nb, q, k)] = (q < P && k < P) ? f2h_sat(src[((int64_t)h * P + q) * P + k] * kLog2e) : f2h(0.0f);
   }
 }
 
@@ -257,10 +258,10 @@ __global__ void bias_to_attn_layout_kernel(const float* __restrict__ src, float*
 
 namespace pa {
 
-hipError_t launch_bias_to_attn_layout(const float* src, float* dst, int H, int P, int Pp, hipStream_t s) {
+hipError_t launch_bias_to_attn_layout(const float* src, void* dst, int H, int P, int Pp, hipStream_t s) {
   const int64_t total = (int64_t)H * Pp * Pp;
   const int blocks = (int)std::min<int64_t>((total + 255) / 256, 8192);
-  hipLaunchKernelGGL(bias_to_attn_layout_kernel, dim3(blocks), dim3(256), 0, s, src, dst, H, P, Pp);
+  hipLaunchKernelGGL(bias_to_attn_layout_kernel, dim3(blocks), dim3(256), 0, s, src, (f16*)dst, H, P, Pp);
   return hipGetLastError();
 }
 

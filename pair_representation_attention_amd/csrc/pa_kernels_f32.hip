@@ -136,7 +136,7 @@ hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.P + 31) / 32, a.nrows);
   const size_t lds = sizeof(float) * 32 * (a.H * 32 + 1);
   hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(32 * a.H), lds, s, (const float*)a.q_ws, (const float*)a.k_ws,
-                     (const float*)a.v_ws, (const float*)a.g_ws, a.bias, a.mask, a.ms_r, a.ms_k, (const float*)a.wo,
+                     (const float*)a.v_ws, (const float*)a.g_ws, (const float*)a.bias, a.mask, a.ms_r, a.ms_k, (const float*)a.wo,
                      (const float*)a.b_o, (float*)a.out, a.os_r, a.os_p, a.H, a.c_out, a.nrows, a.P);
   return hipGetLastError();
 }

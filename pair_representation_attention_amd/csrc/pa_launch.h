@@ -24,15 +24,15 @@ struct ProjArgs {
   const void *wb, *b_g;          // both paths: w_b [c_in][H], gate bias [H*32]
   float q_scale;
   void *q_ws, *k_ws, *v_ws, *g_ws;
-  float* bias;                   // pair bias output (rows = the projected rows r)
-  int bias_swizzled;             // 1: attention layout (operand order, Pp x Pp, zero padded); 0: [H][P][P]
+  float* bias;                   // pair bias output (rows = the projected rows r); fp16 when swizzled
+  int bias_swizzled;             // 1: attention layout (fp16 operand order, Pp x Pp, zero padded); 0: [H][P][P] float
   float bias_scale;              // multiplies the stored bias (log2(e) for the attention layout)
   int c_in, hd, H, nrows, P, Pp;
 };
 
 struct AttnArgs {
   const void *q_ws, *k_ws, *v_ws, *g_ws;
-  const float* bias;             // bf16 path: attention layout, log2 units; fp32 path: [H][P][P] natural
+  const void* bias;              // bf16 path: attention layout (fp16, log2 units); fp32 path: [H][P][P] float natural
   const uint8_t* mask;           // fp32 path: key kept iff mask[r*ms_r + k*ms_k] != 0 (NULL = all)
   int64_t ms_r, ms_k;
   const uint32_t* mask_bits;     // bf16 path: keep bits per (row, 32-key block), see launch_mask_bits
@@ -43,7 +43,7 @@ struct AttnArgs {
 };
 
 hipError_t launch_pack_bf16(const PackArgs& a, hipStream_t s);
-hipError_t launch_bias_to_attn_layout(const float* src, float* dst, int H, int P, int Pp, hipStream_t s);
+hipError_t launch_bias_to_attn_layout(const float* src, void* dst, int H, int P, int Pp, hipStream_t s);
 // mode 0: q,k,v,g   1: q,k,v,g + bias   2: bias only
 hipError_t launch_proj_bf16(const ProjArgs& a, int mode, int num_cu, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);

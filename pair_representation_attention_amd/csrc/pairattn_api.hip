@@ -63,9 +63,9 @@ Layout make_layout(int64_t nrows, int64_t P, int64_t c_in, int64_t c_out, int64_
     L.k = take((size_t)nrows * H * Pp * 32 * 2);
     L.v = take((size_t)nrows * H * 32 * Pp * 2);
     L.g = take((size_t)nrows * P * hd * 2);
-    // the attention reads the bias in operand order, Pp x Pp, log2 units; a
-    // caller-provided bias (row block) is converted into this buffer as well
-    L.bias = take((size_t)H * Pp * Pp * 4);
+    // the attention reads the bias as fp16 in operand order, Pp x Pp, log2
+    // units; a caller-provided bias (row block) is converted into it as well
+    L.bias = take((size_t)H * Pp * Pp * 2);
     L.bits = take((size_t)nrows * (Pp / 32) * 4);
   } else {
     L.q = take((size_t)nrows * P * hd * 4);
@@ -372,7 +372,7 @@ static int run_row_attention(const pairattn_params* p, const Layout& L, hipStrea
   // bf16 path: the attention reads the workspace bias ([H][P][Pp], log2 units);
   // fp32 path: [H][P][P] natural units, the caller's own array for row blocks
   float* bias_ws = (bf || bias_given == nullptr) ? reinterpret_cast<float*>(ws_at(p, L.bias)) : nullptr;
-  const float* bias = (bf || bias_given == nullptr) ? bias_ws : bias_given;
+  const void* bias = (bf || bias_given == nullptr) ? (const void*)bias_ws : (const void*)bias_given;
   const int bias_swz = bf ? 1 : 0;
   const float bias_scale = bf ? 1.4426950408889634f : 1.0f;
 

@@ -52,7 +52,7 @@ def test_version_and_status_strings(L):
 def test_workspace_sizes():
     w = lib.pairattn_tri_workspace_bytes(384, 128, 4, 32, lib.PAIRATTN_BF16)
     # q, k, v (padded to 384) + g + bias + packed weights, each 256-aligned
-    assert w >= 3 * 384 * 4 * 384 * 32 * 2 + 384 * 384 * 128 * 2 + 4 * 384 * 384 * 4
+    assert w >= 3 * 384 * 4 * 384 * 32 * 2 + 384 * 384 * 128 * 2 + 4 * 384 * 384 * 2
     assert lib.pairattn_tri_workspace_bytes(384, 128, 4, 32, lib.PAIRATTN_F32) >= 4 * 384 * 384 * 128 * 4
     assert lib.pairattn_tri_workspace_bytes(384, 128, 4, 64, lib.PAIRATTN_BF16) == 0
     assert lib.pairattn_tri_workspace_bytes(384, 128, 3, 32, lib.PAIRATTN_BF16) == 0
