@@ -17,6 +17,12 @@ Prints one JSON line (the last line of stdout):
              workload on this host's cores
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--extra]
+       python bench.py --copy-probe MIB ...   (adds a plain device copy of
+           MIB MiB after the timed region: the reference kernel for scaling
+           the FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 --pmc run)
+       python bench.py --traffic-from FETCH_CSV WRITE_CSV --copy-mib MIB
+           (no GPU: turns the counter CSVs of two such runs into the HBM
+           traffic summary that later bench lines report)
 """
 from __future__ import annotations
 
@@ -34,7 +40,14 @@ if ROOT not in sys.path:
 METRIC = "triangle-attn bf16 TFLOP/s + pair-rows/s at I=1536; % of MFMA peak"
 PEAK_MFMA_16BIT_TFLOPS = 2516.6          # 256 CU x 4096 flop/clk x 2.4 GHz (bf16 = fp16 dense)
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_tri_bf16_i1536_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_tri_bf16_i1536.json")
+CSRC = os.path.join(ROOT, "pair_representation_attention_amd", "csrc")
+# source files each kernel is compiled from (a counter summary is valid for one source state)
+KERNEL_SOURCES = {
+    "attention": ("pa_attn.hip", "pa_device.h"),
+    "projection": ("pa_kernels_bf16.hip", "pa_device.h"),
+}
+KERNEL_SYMBOLS = {"attention": "attn_kernel", "projection": "proj_kernel"}
 
 
 def log(msg: str) -> None:
@@ -74,25 +87,75 @@ def attn_kernel_flops(R: int, I: int, c: int, H: int, d: int) -> float:
     return 4.0 * R * I * I * H * d + 2.0 * R * I * H * d * c
 
 
-def kernel_source_hash() -> str:
+def proj_kernel_bytes(R: int, I: int, c: int, H: int, d: int, with_bias: bool = True) -> float:
+    """Algorithmic HBM bytes of one projection launch (bf16 in, fp16 out):
+    read the R x I positions of x once, write q, k, v, g and the pair bias."""
+    hd = H * d
+    return 2.0 * R * I * c + 4 * 2.0 * R * I * hd + (2.0 * H * I * I if with_bias else 0.0)
+
+
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for name in ("pa_kernels_bf16.hip", "pa_device.h"):
-        with open(os.path.join(ROOT, "pair_representation_attention_amd", "csrc", name), "rb") as f:
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_entry(per_launch_flops_bytes=None):
-    """HBM bytes per attention launch from the committed counter summary, if
-    it was taken on the current kernel source; else None."""
+def traffic_entry(kernel: str):
+    """Measured HBM bytes per launch of `kernel` from the committed counter
+    summary, if it was taken on the kernel's current source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    k = t.get("kernels", {}).get(kernel)
+    if not k or k.get("source_hash") != kernel_source_hash(kernel):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return k.get("hbm_bytes_per_launch")
+
+
+def _read_counter_csv(path: str, counter: str) -> dict:
+    """{kernel name: [value per dispatch]} for one counter of a rocprofv3 CSV."""
+    import csv
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def traffic_from(fetch_csv: str, write_csv: str, copy_mib: float, commands) -> dict:
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the same
+    counters read for the plain copy of copy_mib MiB, per kernel."""
+    fetch = _read_counter_csv(fetch_csv, "FETCH_SIZE")
+    write = _read_counter_csv(write_csv, "WRITE_SIZE")
+
+    def copy_value(tab):
+        vals = [v for name, vs in tab.items() if "copyBuffer" in name for v in vs]
+        if not vals:
+            raise SystemExit("no copy dispatch in the counter file (run bench.py with --copy-probe)")
+        return max(vals)
+
+    known_kib = copy_mib * 1024.0
+    f_fetch = known_kib / copy_value(fetch)
+    f_write = known_kib / copy_value(write)
+    res = {"copy_mib": copy_mib, "fetch_scale": f_fetch, "write_scale": f_write, "commands": commands,
+           "kernels": {}}
+    for kernel, sym in KERNEL_SYMBOLS.items():
+        fv = [v for name, vs in fetch.items() if sym in name for v in vs]
+        wv = [v for name, vs in write.items() if sym in name for v in vs]
+        if not fv or not wv:
+            continue
+        fb = sum(fv) / len(fv) * 1024.0 * f_fetch
+        wb = sum(wv) / len(wv) * 1024.0 * f_write
+        res["kernels"][kernel] = {"source_hash": kernel_source_hash(kernel), "dispatches": len(fv),
+                                  "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                                  "hbm_bytes_per_launch": fb + wb}
+    return res
 
 
 # ----------------------------------------------------------------------------
@@ -131,9 +194,23 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=3, help="oracle sample size (rows)")
+    ap.add_argument("--cpu-rows", type=int, default=12, help="oracle sample size (rows, about 1.4 s each)")
     ap.add_argument("--extra", action="store_true", help="also time MSA row attention and the row block")
+    ap.add_argument("--copy-probe", type=float, default=0.0, metavar="MIB",
+                    help="after timing, run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary from two rocprofv3 --pmc counter CSVs and exit")
+    ap.add_argument("--copy-mib", type=float, default=1024.0, help="copy size used in the --pmc runs")
+    ap.add_argument("--command", action="append", default=[], help="command lines recorded with --traffic-from")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        res = traffic_from(args.traffic_from[0], args.traffic_from[1], args.copy_mib, args.command)
+        os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(res, f, indent=1)
+        print(json.dumps(res, indent=1))
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -199,17 +276,30 @@ def main() -> int:
     attn_ms = float(np.mean(stage_ms["start_attention"] + stage_ms["end_attention"]))
     attn_flops = attn_kernel_flops(I, I, c, H, d)
     achieved = attn_flops / (attn_ms * 1e-3) / 1e12
-    traffic = traffic_entry()
     roof = {
-        "kernel": "attn_kernel<4,128,4> (tri, bf16 I/O, fp16 MFMA operands)",
+        "kernel": "attn_kernel<4,128> (tri, bf16 I/O, fp16 MFMA operands)",
         "bound": "mfma",
         "achieved": achieved,
         "peak": PEAK_MFMA_16BIT_TFLOPS,
         "unit": "TFLOP/s",
         "frac": achieved / PEAK_MFMA_16BIT_TFLOPS,
-        "traffic": traffic,
+        "traffic": traffic_entry("attention"),
         "flops_per_launch": attn_flops,
         "mean_launch_ms": attn_ms,
+    }
+    proj_ms = float(np.mean(stage_ms["start_projection"] + stage_ms["end_projection"]))
+    proj_bytes = proj_kernel_bytes(I, I, c, H, d)
+    proj_gbs = proj_bytes / (proj_ms * 1e-3) / 1e9
+    roof_proj = {
+        "kernel": "proj_kernel<128,128,512,1> (LayerNorm + q|k|v|g + pair bias)",
+        "bound": "hbm",
+        "achieved": proj_gbs,
+        "peak": PEAK_HBM_GBS,
+        "unit": "GB/s",
+        "frac": proj_gbs / PEAK_HBM_GBS,
+        "traffic": traffic_entry("projection"),
+        "bytes_per_launch": proj_bytes,
+        "mean_launch_ms": proj_ms,
     }
     kernels = {k: float(np.mean(v)) for k, v in sorted(stage_ms.items())}
 
@@ -233,10 +323,21 @@ def main() -> int:
         "step_flops": step_flops,
         "kernels_ms": kernels,
         "roofline": roof,
+        "roofline_projection": roof_proj,
     }
 
     if args.extra:
         result["extra"] = extra_workloads(args, device, inputs, lib, torch, np)
+
+    if args.copy_probe > 0:   # plain device copy of a known size, outside the timed region
+        n = int(args.copy_probe * 1024 * 1024)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe} MiB x 2")
+        del src, dst
 
     del start, end
     torch.cuda.empty_cache()

@@ -263,7 +263,7 @@ def tri_points(z, mask, p: Mapping, H: int, orientation: int, points) -> np.ndar
 
 
 def tri_rows(z_rows, bias_hqk, mask_rows, p: Mapping, H: int,
-             queries: Optional[Sequence[int]] = None) -> np.ndarray:
+             queries: Optional[Sequence[int]] = None, bias_restricted: bool = False) -> np.ndarray:
     """Starting-node attention for a block of rows with a given bias.
 
     z_rows [R, I, c] are rows of Z; bias_hqk [H, I, I] is the full-length
@@ -271,11 +271,15 @@ def tri_rows(z_rows, bias_hqk, mask_rows, p: Mapping, H: int,
     or None.  This is one device's share when the query rows are split
     across devices while keys/values stay whole (self-attention recast as
     cross-attention: Design-CP, Metodologia 1).  Returns [R, Q, c].
+    With ``bias_restricted`` the bias holds only the rows of ``queries``
+    ([H, Q, I], e.g. from attention_bias over those rows of Z).
     """
     z_rows = np.asarray(z_rows)
     R, I = z_rows.shape[0], z_rows.shape[1]
     q_i = _as_index(queries, I)
-    bias = _f64(bias_hqk)[:, q_i, :]
+    bias = _f64(bias_hqk) if bias_restricted else _f64(bias_hqk)[:, q_i, :]
+    if bias.shape[1] != len(q_i):
+        raise ValueError("bias rows do not match the selected queries")
     keep = np.ones((R, I), bool) if mask_rows is None else np.asarray(mask_rows) != 0
     out = np.empty((R, len(q_i), z_rows.shape[-1]))
     for r in range(R):

@@ -54,181 +54,254 @@ __global__ void pack_weights_kernel(const bf16* __restrict__ wq, const bf16* __r
 }
 
 // --------------------------------------------------------------------------
-// LayerNorm of a tile of 32 positions of one row into LDS (fp16, row pitch
-// C_IN + 8 elements).  Positions >= P are written as zeros.
-// --------------------------------------------------------------------------
-template <int C_IN, int NT>
-__device__ __forceinline__ void ln_tile_to_lds(const bf16* __restrict__ x, int64_t xs_r, int64_t xs_p,
-                                               int r, int p0, int P, const bf16* __restrict__ gamma,
-                                               const bf16* __restrict__ beta, float eps, f16* xs) {
-  constexpr int TPP = C_IN / 8;           // threads per position (8 channels each)
-  constexpr int PPP = NT / TPP;           // positions per pass
-  static_assert(TPP <= 64 && (64 % TPP) == 0, "channel groups must tile a wave");
-  const int tid = threadIdx.x;
-  const int sub = tid % TPP;
-#pragma unroll
-  for (int base = 0; base < 32; base += PPP) {
-    const int pl = base + tid / TPP;
-    if (PPP <= 32 || pl < 32) {
-      const int p = p0 + pl;
-      float v[8];
-      if (p < P) {
-        const bf16x8 raw = ld16(x + (int64_t)r * xs_r + (int64_t)p * xs_p + sub * 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = bf2f(raw[e]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
-      }
-      float s = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s += v[e];
-      const float mean = group_sum<TPP>(s) * (1.0f / C_IN);
-      float s2 = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float t = v[e] - mean;
-        s2 += t * t;
-      }
-      const float var = group_sum<TPP>(s2) * (1.0f / C_IN);
-      const float rstd = 1.0f / __builtin_sqrtf(var + eps);
-      const bf16x8 gm = ld16(gamma + sub * 8);
-      const bf16x8 bt = ld16(beta + sub * 8);
-      f16x8 y;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        y[e] = (p < P) ? f2h_sat((v[e] - mean) * rstd * bf2f(gm[e]) + bf2f(bt[e])) : f2h(0.0f);
-      *reinterpret_cast<f16x8*>(xs + pl * (C_IN + 8) + sub * 8) = y;
-    }
-  }
-}
-
-// --------------------------------------------------------------------------
-// Fused LayerNorm + projections.  One workgroup of 8 waves loops over tiles
-// of 32 positions of one row; each wave keeps its 64 (or 96) weight columns
-// in registers for the whole kernel.
+// Fused LayerNorm + projections.
+//
+// Every wave works on its own tiles of 32 positions of one row; there is no
+// barrier in the tile loop.  A lane holds one position (lane % 32) and half
+// of its channels, exactly the register image of the activation operand of
+// a 32x32x16 MFMA: in K-step t the lane of half g holds channels
+// t*16 + g*8 .. +7.  LayerNorm therefore runs in registers (one cross-half
+// exchange per statistic), and the same registers serve as the A operand
+// (v = X W, rows = positions) or the B operand (q, k, g: out^T = W^T X^T,
+// columns = positions).  The raw rows of the next PF tiles are loaded
+// before the current tile is computed.
+//
+// The weight operands of this workgroup's NCOL projection columns sit in
+// LDS in operand order ([column block][K-step][lane][8]), loaded once; so
+// do LayerNorm's gamma and beta, the gate bias and, when the pair bias is
+// produced, the w_b operand (rows = heads, zero beyond H).
 //   MODE 0: q, k, v, g          MODE 1: q, k, v, g and the pair bias
-//   MODE 2: pair bias only (wave 0 computes, the other waves only normalise)
-// Column group blockIdx.y selects 512 of the 4*HD projection columns.
+//   MODE 2: pair bias only (NCOL = 0)
+// Column group blockIdx.y covers columns [y*NCOL, (y+1)*NCOL) of q|k|v|g;
+// the pair bias is produced by group 0.
 // --------------------------------------------------------------------------
-template <int C_IN, int HD, int MODE>
-__global__ __launch_bounds__(512) void proj_kernel(
-    const bf16* __restrict__ x, int64_t xs_r, int64_t xs_p, const bf16* __restrict__ gamma,
+template <int C_IN, int HD, int NCOL, int MODE>
+struct ProjShape {
+  static constexpr int KS = C_IN / 16;                 // MFMA K-steps
+  static constexpr int NBLK = NCOL / 32;               // 32-column blocks
+  static constexpr bool HAS_BIAS = MODE != 0;
+  static constexpr int W_BYTES = NCOL * C_IN * 2;
+  static constexpr int WB_BYTES = HAS_BIAS ? KS * 1024 : 0;
+  static constexpr int LDS = W_BYTES + WB_BYTES + NCOL * 4 + 8 * 4;
+  static constexpr int PF = C_IN <= 128 ? 2 : 1;       // tiles prefetched ahead
+  static_assert(LDS <= 160 * 1024, "projection operands exceed LDS");
+};
+
+constexpr int kProjThreads = 512;
+
+template <int C_IN, int HD, int NCOL, int MODE>
+__global__ __launch_bounds__(kProjThreads) void proj_kernel(
+    const bf16* __restrict__ x, int64_t xs_r, int64_t xs_p, int tile_rmajor, const bf16* __restrict__ gamma,
     const bf16* __restrict__ beta, float eps, const f16* __restrict__ wT, const bf16* __restrict__ wb,
     const bf16* __restrict__ b_g, float q_scale, f16* __restrict__ q_ws, f16* __restrict__ k_ws,
     f16* __restrict__ v_ws, f16* __restrict__ g_ws, float* __restrict__ bias, int bias_swizzled, float bias_scale,
     int nrows, int P, int Pp, int H) {
-  constexpr int NT = 512;
-  constexpr int KS = C_IN / 16;          // MFMA K-steps
-  constexpr bool HAS_QKVG = MODE != 2;
-  constexpr bool HAS_BIAS = MODE != 0;
-  __shared__ __attribute__((aligned(16))) f16 xs[32 * (C_IN + 8)];
+  using SH = ProjShape<C_IN, HD, NCOL, MODE>;
+  constexpr int KS = SH::KS;
+  constexpr int NW = kProjThreads / kWave;
+  __shared__ __attribute__((aligned(1024))) char smem[SH::LDS];
+  f16* w_lds = reinterpret_cast<f16*>(smem);
+  f16* wb_lds = reinterpret_cast<f16*>(smem + SH::W_BYTES);
+  float* cb = reinterpret_cast<float*>(smem + SH::W_BYTES + SH::WB_BYTES);   // [NCOL] column constants
+  float* cbb = cb + NCOL;                                                      // [8] pair-bias constants
 
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
   const int lq = lane & 31, g = lane >> 5;
-  const int colbase = blockIdx.y * 512 + wave * 64;    // first of this wave's 64 columns
-  const int tensor = colbase / HD;                     // 0 q, 1 k, 2 v, 3 g
-  const bool bias_wave = HAS_BIAS && blockIdx.y == 0 && wave == 0;
+  const int col0 = blockIdx.y * NCOL;
+  const bool do_bias = SH::HAS_BIAS && blockIdx.y == 0;
 
-  f16x8 W[2][KS];
-  f16x8 WB[KS];
-  if (HAS_QKVG) {
+  // ---- operands into LDS (once per workgroup) ----
+  // LayerNorm's affine map is folded into the projection:
+  //   ((x-mu)*rstd*gamma + beta) . W = ((x-mu)*rstd) . (gamma o W) + beta . W
+  // so the operands hold gamma o W and the per-column constants beta . W
+  // (plus the gate bias for g columns) are added to the accumulators.
+  for (int i = tid; i < SH::NBLK * KS * 64; i += kProjThreads) {
+    const int l = i & 63, t = (i >> 6) % KS, b = (i >> 6) / KS;
+    const int k0 = t * 16 + (l >> 5) * 8;
+    const f16x8 w = ld16(wT + (int64_t)(col0 + b * 32 + (l & 31)) * C_IN + k0);
+    f16x8 o;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int t = 0; t < KS; ++t) W[mb][t] = ld16(wT + (int64_t)(colbase + mb * 32 + lq) * C_IN + t * 16 + g * 8);
+    for (int e = 0; e < 8; ++e) o[e] = f2h_sat((float)w[e] * bf2f(gamma[k0 + e]));
+    *reinterpret_cast<f16x8*>(w_lds + i * 8) = o;
   }
-  if (bias_wave) {   // w_b is [C_IN][H]; rows >= H of the operand are zero
+  for (int n = tid; n < NCOL; n += kProjThreads) {
+    const f16* wr = wT + (int64_t)(col0 + n) * C_IN;
+    float acc = 0.0f;
+    for (int k = 0; k < C_IN; ++k) acc += bf2f(beta[k]) * (float)wr[k];
+    const int col = col0 + n;
+    if (col >= 3 * HD && b_g != nullptr) acc += bf2f(b_g[col - 3 * HD]);
+    cb[n] = acc;
+  }
+  if (SH::HAS_BIAS) {
+    for (int i = tid; i < KS * 64; i += kProjThreads) {
+      const int l = i & 63, t = i >> 6, hh = l & 31;
+      const int k0 = t * 16 + (l >> 5) * 8;
+      f16x8 w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        w[e] = hh < H ? f2h_sat(bf2f(wb[(int64_t)(k0 + e) * H + hh]) * bf2f(gamma[k0 + e])) : f2h(0.0f);
+      *reinterpret_cast<f16x8*>(wb_lds + i * 8) = w;
+    }
+    if (tid < 8) {
+      float acc = 0.0f;
+      if (tid < H)
+        for (int k = 0; k < C_IN; ++k) acc += bf2f(beta[k]) * bf2f(wb[(int64_t)k * H + tid]);
+      cbb[tid] = acc;
+    }
+  }
+  __syncthreads();
+
+  const int nb = Pp / 32;
+  const int64_t ntiles = (int64_t)nb * nrows;
+  const int64_t stride = (int64_t)gridDim.x * NW;
+  // tile -> (row, first position): row-major when positions are contiguous
+  // in memory, else position-block-major, so that the waves running at the
+  // same time read neighbouring bytes of x.
+  auto tile_rp = [&](int64_t tile, int& r, int& p0) {
+    if (tile_rmajor) {
+      r = (int)(tile / nb);
+      p0 = (int)(tile % nb) * 32;
+    } else {
+      r = (int)(tile % nrows);
+      p0 = (int)(tile / nrows) * 32;
+    }
+  };
+  auto load_tile = [&](int64_t tile, bf16x8* raw) {
+    if (tile < ntiles) {
+      int r, p0;
+      tile_rp(tile, r, p0);
+      const int p = p0 + lq;
+      if (p < P) {
+        const bf16* src = x + (int64_t)r * xs_r + (int64_t)p * xs_p + g * 8;
+#pragma unroll
+        for (int t = 0; t < KS; ++t) raw[t] = ld16(src + t * 16);
+        return;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < KS; ++t) raw[t] = bf16x8{};
+  };
+
+  constexpr int PF = SH::PF;
+  bf16x8 pre[PF][KS];
+  int64_t tile = (int64_t)blockIdx.x * NW + wave;
+#pragma unroll
+  for (int f = 0; f < PF; ++f) load_tile(tile + f * stride, pre[f]);
+
+  for (; tile < ntiles; tile += stride) {
+    bf16x8 raw[KS];
+#pragma unroll
+    for (int t = 0; t < KS; ++t) raw[t] = pre[0][t];
+#pragma unroll
+    for (int f = 0; f + 1 < PF; ++f)
+#pragma unroll
+      for (int t = 0; t < KS; ++t) pre[f][t] = pre[f + 1][t];
+    load_tile(tile + PF * stride, pre[PF - 1]);
+
+    int r, p0;
+    tile_rp(tile, r, p0);
+    const int p = p0 + lq;
+    const bool valid = p < P;
+
+    // ---- LayerNorm in registers (two passes, fp32); affine map folded into W ----
+    float s = 0.0f;
 #pragma unroll
     for (int t = 0; t < KS; ++t)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) WB[t][e] = lq < H ? f2h_sat(bf2f(wb[(int64_t)(t * 16 + g * 8 + e) * H + lq])) : f2h(0.0f);
-  }
+      for (int e = 0; e < 8; ++e) s += bf2f(raw[t][e]);
+    s += __shfl_xor(s, 32, 64);
+    const float mean = s * (1.0f / C_IN);
+    float s2 = 0.0f;
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = bf2f(raw[t][e]) - mean;
+        s2 += d * d;
+      }
+    s2 += __shfl_xor(s2, 32, 64);
+    const float rstd = 1.0f / __builtin_sqrtf(s2 * (1.0f / C_IN) + eps);
+    f16x8 X[KS];
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) X[t][e] = f2h_sat((bf2f(raw[t][e]) - mean) * rstd);
 
-  const int tiles_per_row = Pp / 32;
-  const int64_t ntiles = (int64_t)tiles_per_row * nrows;
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int r = (int)(tile / tiles_per_row);
-    const int p0 = (int)(tile % tiles_per_row) * 32;
-    __syncthreads();   // previous tile's LDS reads are done
-    ln_tile_to_lds<C_IN, NT>(x, xs_r, xs_p, r, p0, P, gamma, beta, eps, xs);
-    __syncthreads();
-
-    if (HAS_QKVG) {
+    // ---- q | k | v | g column blocks ----
+#pragma unroll 2
+    for (int b = 0; b < SH::NBLK; ++b) {
+      const int col = col0 + b * 32;
+      const int tensor = col / HD;            // 0 q, 1 k, 2 v, 3 g
+      const int hcol = col - tensor * HD;     // first column within the tensor
+      const int64_t rh = (int64_t)r * H + hcol / 32;
+      const f16* wop = w_lds + (b * KS) * 512 + lane * 8;
+      const float* cbk = cb + b * 32;
+      f32x16 acc = {};
+      if (tensor == 2) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        f32x16 acc = {};
-        if (tensor == 2) {   // v: out = X W, rows = positions, columns = channels
+        for (int t = 0; t < KS; ++t) acc = mfma32(X[t], *reinterpret_cast<const f16x8*>(wop + t * 512), acc);
+        const float c = cbk[lq];
 #pragma unroll
-          for (int t = 0; t < KS; ++t) acc = mfma32(ld16(xs + lq * (C_IN + 8) + t * 16 + g * 8), W[mb][t], acc);
-        } else {             // q, k, g: out^T = W^T X^T, rows = channels, columns = positions
+        for (int jj = 0; jj < 4; ++jj) {      // lane = channel lq; registers = 4 runs of 4 positions
+          const int pp = p0 + jj * 8 + g * 4;
+          f16x4 o;
 #pragma unroll
-          for (int t = 0; t < KS; ++t) acc = mfma32(W[mb][t], ld16(xs + lq * (C_IN + 8) + t * 16 + g * 8), acc);
+          for (int e = 0; e < 4; ++e) o[e] = pp + e < P ? f2h_sat(acc[jj * 4 + e] + c) : f2h(0.0f);
+          st8(v_ws + v_off(rh, nb, pp, lq), o);
         }
-        const int col = colbase + mb * 32 - tensor * HD;   // first column within the tensor
-        const int h = col / 32;
-        const int64_t rh = (int64_t)r * H + h;
-        const int nb = Pp / 32;
-        if (tensor == 0 || tensor == 1) {   // lane = position p0+lq; registers = 4 runs of 4 channels
-          const float sc = tensor == 0 ? q_scale : 1.0f;
+      } else {
+#pragma unroll
+        for (int t = 0; t < KS; ++t) acc = mfma32(*reinterpret_cast<const f16x8*>(wop + t * 512), X[t], acc);
+        if (tensor <= 1) {                    // lane = position; registers = 4 runs of 4 channels
+          const float sc = valid ? (tensor == 0 ? q_scale : 1.0f) : 0.0f;
+          f16* base = tensor == 0 ? q_ws : k_ws;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            f16x4 o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = f2h_sat(acc[jj * 4 + e] * sc);
             const int d0 = jj * 8 + g * 4;
-            st8((tensor == 0 ? q_ws + q_off(rh, nb, p0 + lq, d0) : k_ws + k_off(rh, nb, p0 + lq, d0)), o);
-          }
-        } else if (tensor == 2) {           // lane = channel lq; registers = 4 runs of 4 positions
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 c = *reinterpret_cast<const f32x4*>(cbk + d0);
             f16x4 o;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = f2h_sat(acc[jj * 4 + e]);
-            st8(v_ws + v_off(rh, nb, p0 + jj * 8 + g * 4, lq), o);
+            for (int e = 0; e < 4; ++e) o[e] = f2h_sat((acc[jj * 4 + e] + c[e]) * sc);
+            st8(base + (tensor == 0 ? q_off(rh, nb, p, d0) : k_off(rh, nb, p, d0)), o);
           }
-        } else {
-          const int p = p0 + lq;
-          if (p < P) {
-            f16* dst = g_ws + ((int64_t)r * P + p) * HD + col;
+        } else if (valid) {                   // gate: sigmoid, natural layout [row][position][HD]
+          f16* dst = g_ws + ((int64_t)r * P + p) * HD + hcol;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              f16x4 o;
+          for (int jj = 0; jj < 4; ++jj) {
+            const int d0 = jj * 8 + g * 4;
+            const f32x4 c = *reinterpret_cast<const f32x4*>(cbk + d0);
+            f16x4 o;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int d = jj * 8 + g * 4 + e;
-                const float bg = b_g != nullptr ? bf2f(b_g[col + d]) : 0.0f;
-                const float t = acc[jj * 4 + e] + bg;
-                o[e] = f2h(1.0f / (1.0f + __expf(-t)));
-              }
-              st8(dst + jj * 8 + g * 4, o);
-            }
+            for (int e = 0; e < 4; ++e) o[e] = f2h(1.0f / (1.0f + __expf(-(acc[jj * 4 + e] + c[e]))));
+            st8(dst + d0, o);
           }
         }
       }
     }
-    if (bias_wave) {
+
+    // ---- pair bias: rows = heads (zero beyond H), columns = positions ----
+    if (do_bias) {
       f32x16 acc = {};
 #pragma unroll
-      for (int t = 0; t < KS; ++t) acc = mfma32(WB[t], ld16(xs + lq * (C_IN + 8) + t * 16 + g * 8), acc);
-      const int p = p0 + lq;
+      for (int t = 0; t < KS; ++t)
+        acc = mfma32(*reinterpret_cast<const f16x8*>(wb_lds + t * 512 + lane * 8), X[t], acc);
       if (bias_swizzled) {   // attention layout: fp16, log2 units, padded to Pp x Pp with zeros
-        const int nb = Pp / 32;
         f16* b16 = reinterpret_cast<f16*>(bias);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 4; ++j) {          // heads (< 8) are rows g*4 + j of registers 0..3
           const int hh = acc_row(j, g);
           if (hh < H) {
-            b16[b16_off(hh, nb, r, p)] = p < P ? f2h_sat(acc[j] * bias_scale) : f2h(0.0f);
+            b16[b16_off(hh, nb, r, p)] = valid ? f2h_sat((acc[j] + cbb[hh]) * bias_scale) : f2h(0.0f);
             if (r == P - 1)   // the padded query rows get zeros at the same keys
               for (int rp = P; rp < Pp; ++rp) b16[b16_off(hh, nb, rp, p)] = f2h(0.0f);
           }
         }
-      } else if (p < P) {    // caller layout [H][P][P] float
+      } else if (valid) {    // caller layout [H][P][P] float
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 4; ++j) {
           const int hh = acc_row(j, g);
-          if (hh < H) bias[((int64_t)hh * P + r) * P + p] = acc[j] * bias_scale;
+          if (hh < H) bias[((int64_t)hh * P + r) * P + p] = (acc[j] + cbb[hh]) * bias_scale;
         }
       }
     }
@@ -276,40 +349,54 @@ hipError_t launch_pack_bf16(const PackArgs& a, hipStream_t s) {
 }
 
 template <int C_IN, int HD, int MODE>
-static hipError_t proj_dispatch(const ProjArgs& a, int grid_x, int grid_y, hipStream_t s) {
-  hipLaunchKernelGGL((proj_kernel<C_IN, HD, MODE>), dim3(grid_x, grid_y), dim3(512), 0, s, (const bf16*)a.x, a.xs_r,
-                     a.xs_p, (const bf16*)a.gamma, (const bf16*)a.beta, a.eps, (const f16*)a.wT,
-                     (const bf16*)a.wb, (const bf16*)a.b_g, a.q_scale, (f16*)a.q_ws, (f16*)a.k_ws,
-                     (f16*)a.v_ws, (f16*)a.g_ws, a.bias, a.bias_swizzled, a.bias_scale, a.nrows, a.P, a.Pp, a.H);
+static hipError_t proj_dispatch(const ProjArgs& a, int num_cu, hipStream_t s) {
+  // columns per group: all of q|k|v|g when their operands fit in 128 KB of LDS
+  constexpr int NCOL = MODE == 2 ? 0 : std::min(4 * HD, 65536 / C_IN);
+  constexpr int groups = MODE == 2 ? 1 : 4 * HD / NCOL;
+  const int64_t ntiles = (int64_t)(a.Pp / 32) * a.nrows;
+  static int wg_per_cu = 0;   // resident workgroups per CU (registers and LDS), asked once per instance
+  if (wg_per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, proj_kernel<C_IN, HD, NCOL, MODE>, kProjThreads, 0) !=
+            hipSuccess ||
+        n < 1)
+      n = 1;
+    wg_per_cu = n;
+  }
+  const int64_t want = (ntiles + kProjThreads / kWave - 1) / (kProjThreads / kWave);
+  const int grid_x = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)num_cu * wg_per_cu));
+  const int rmajor = a.xs_p <= a.xs_r ? 1 : 0;
+  hipLaunchKernelGGL((proj_kernel<C_IN, HD, NCOL, MODE>), dim3(grid_x, groups), dim3(kProjThreads), 0, s,
+                     (const bf16*)a.x, a.xs_r, a.xs_p, rmajor, (const bf16*)a.gamma, (const bf16*)a.beta, a.eps,
+                     (const f16*)a.wT, (const bf16*)a.wb, (const bf16*)a.b_g, a.q_scale, (f16*)a.q_ws,
+                     (f16*)a.k_ws, (f16*)a.v_ws, (f16*)a.g_ws, a.bias, a.bias_swizzled, a.bias_scale, a.nrows, a.P,
+                     a.Pp, a.H);
   return hipGetLastError();
 }
 
 template <int C_IN, int MODE>
-static hipError_t proj_dispatch_hd(const ProjArgs& a, int grid_x, int grid_y, hipStream_t s) {
-  if (MODE == 2) return proj_dispatch<C_IN, 128, 2>(a, grid_x, 1, s);
-  if (a.hd == 128) return proj_dispatch<C_IN, 128, MODE>(a, grid_x, grid_y, s);
-  if (a.hd == 256) return proj_dispatch<C_IN, 256, MODE>(a, grid_x, grid_y, s);
+static hipError_t proj_dispatch_hd(const ProjArgs& a, int num_cu, hipStream_t s) {
+  if (MODE == 2) return proj_dispatch<C_IN, 128, 2>(a, num_cu, s);
+  if (a.hd == 128) return proj_dispatch<C_IN, 128, MODE>(a, num_cu, s);
+  if (a.hd == 256) return proj_dispatch<C_IN, 256, MODE>(a, num_cu, s);
   return hipErrorInvalidValue;
 }
 
 template <int MODE>
-static hipError_t proj_dispatch_c(const ProjArgs& a, int grid_x, int grid_y, hipStream_t s) {
+static hipError_t proj_dispatch_c(const ProjArgs& a, int num_cu, hipStream_t s) {
   switch (a.c_in) {
-    case 64: return proj_dispatch_hd<64, MODE>(a, grid_x, grid_y, s);
-    case 128: return proj_dispatch_hd<128, MODE>(a, grid_x, grid_y, s);
-    case 256: return proj_dispatch_hd<256, MODE>(a, grid_x, grid_y, s);
+    case 64: return proj_dispatch_hd<64, MODE>(a, num_cu, s);
+    case 128: return proj_dispatch_hd<128, MODE>(a, num_cu, s);
+    case 256: return proj_dispatch_hd<256, MODE>(a, num_cu, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_proj_bf16(const ProjArgs& a, int mode, int num_cu, hipStream_t s) {
-  const int64_t ntiles = (int64_t)(a.Pp / 32) * a.nrows;
-  const int grid_y = mode == 2 ? 1 : (4 * a.hd) / 512;
-  const int grid_x = (int)std::max<int64_t>(1, std::min<int64_t>(ntiles, (int64_t)num_cu * 2));
   switch (mode) {
-    case 0: return proj_dispatch_c<0>(a, grid_x, grid_y, s);
-    case 1: return proj_dispatch_c<1>(a, grid_x, grid_y, s);
-    case 2: return proj_dispatch_c<2>(a, grid_x, grid_y, s);
+    case 0: return proj_dispatch_c<0>(a, num_cu, s);
+    case 1: return proj_dispatch_c<1>(a, num_cu, s);
+    case 2: return proj_dispatch_c<2>(a, num_cu, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -284,26 +284,65 @@ def make_msa_case(S: int, I: int, c_m: int = 256, c_z: int = 128, H: int = 8, d:
 
 
 def make_assembly_z_bits(I: int, c: int, asu: int, noise_std: float, seed: int,
-                         rows: Optional[slice] = None) -> np.ndarray:
+                         rows: Optional[slice] = None, workers: Optional[int] = None) -> np.ndarray:
     """bf16 bits of a repeated-block pair tensor, generated row by row.
 
     Z[a,b] = A[a mod asu, b mod asu] + noise_std * eps, A ~ N(0,1)^[asu,asu,c],
     eps ~ N(0,1) drawn per row from a per-row child stream, so any row can be
-    regenerated on its own.  Returns uint16 [n_rows, I, c].
+    regenerated on its own (and rows are filled in parallel threads without
+    changing a bit).  Returns uint16 [n_rows, I, c].
     """
+    import concurrent.futures as cf
+    import os
+
     seq = np.random.SeedSequence(seed)
     s_asu, s_rows = seq.spawn(2)
     A = np.random.Generator(np.random.PCG64(s_asu)).standard_normal((asu, asu, c), dtype=np.float32)
     rows = rows or slice(0, I)
-    idx = range(*rows.indices(I))
+    idx = list(range(*rows.indices(I)))
     out = np.empty((len(idx), I, c), np.uint16)
     reps = -(-I // asu)
-    for n, a in enumerate(idx):
+
+    def fill(n: int) -> None:
+        a = idx[n]
         rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 1, a])))
         base = np.tile(A[a % asu], (reps, 1))[:I]
         noise = rng.standard_normal((I, c), dtype=np.float32) * np.float32(noise_std)
         out[n] = f32_to_bf16_bits(base + noise)
+
+    workers = workers or min(16, os.cpu_count() or 1)
+    if workers <= 1 or len(idx) < 8:
+        for n in range(len(idx)):
+            fill(n)
+    else:
+        with cf.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fill, range(len(idx))))
     return out
+
+
+@dataclasses.dataclass
+class RowsCase:
+    I: int
+    R: int
+    c: int
+    H: int
+    d: int
+    zbits: np.ndarray                   # [I, I, c] bf16 bits of the whole pair tensor
+    r0: int                             # the block holds rows r0 .. r0+R-1
+    params: Params
+    seed: int
+
+
+def make_rows_case(I: int, R: int, c: int = 128, H: int = 4, d: int = 32, asu: int = 171,
+                   noise: float = 0.1, seed: int = 0, r0: Optional[int] = None) -> RowsCase:
+    """A block of R starting-node rows of a large repeated-block pair tensor
+    (bf16), with random LayerNorm affine terms and biases.  The block holds
+    rows r0 .. r0+R-1 (rows 0 .. R-1 by default)."""
+    zbits = make_assembly_z_bits(I, c, asu, noise, seed)
+    r_w = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 2])))
+    params = make_params(r_w, c, H, d, BF16, affine=True, biases=True)
+    r0 = 0 if r0 is None else r0
+    return RowsCase(I=I, R=R, c=c, H=H, d=d, zbits=zbits, r0=r0, params=params, seed=seed)
 
 
 # ----------------------------------------------------------------------------

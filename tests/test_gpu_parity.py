@@ -147,6 +147,36 @@ def test_cfg_tri_bf16_i1536_sampled():
         del out
 
 
+def test_cfg_rows_bf16_i4096_r512():
+    """A block of 512 starting-node rows of Z[4096, 4096, 128] (repeated
+    171-residue blocks plus noise): the bias comes from the whole Z through
+    pairattn_tri_bias, the rows through pairattn_tri_rows_fwd.  The oracle
+    evaluates sampled (row, query) outputs from the rows of Z they need."""
+    cfg = inputs.CONFIGS["rows_bf16_i4096_r512"]
+    I, R, c, H, d = cfg["I"], cfg["R"], cfg["c"], cfg["H"], cfg["d"]
+    print(f"[cfg rows] generating Z[{I},{I},{c}]", flush=True)
+    case = inputs.make_rows_case(I=I, R=R, c=c, H=H, d=d, asu=cfg["asu"], noise=cfg["noise"], seed=cfg["seed"])
+    dev = _dev()
+    zf = torch.from_numpy(case.zbits.view(np.int16)).to("cuda").view(torch.bfloat16)
+    r0 = case.r0
+    rr = dev.RowsRunner(zf, zf[r0:r0 + R], None, case.params, H, "bf16")
+    got = rr()
+    torch.cuda.synchronize()
+    p = case.params.as_dict()
+    rows = np.array([0, 217, R - 1])
+    queries = np.array([0, 5, 170, 171, 2047, r0 + 217, I - 1])
+    zq = inputs.bf16_bits_to_f32(case.zbits[queries])
+    bias_q = oracle.attention_bias(zq, p, H, oracle.START)            # [H, Q, I] for these query rows
+    got_bias = rr.bias[:, torch.as_tensor(queries, device="cuda")].cpu().numpy()
+    assert np.max(np.abs(got_bias - bias_q)) < 3e-2
+    zr = inputs.bf16_bits_to_f32(case.zbits[r0 + rows])
+    ref = oracle.tri_rows(zr, bias_q, None, p, H, queries=queries, bias_restricted=True)
+    g = gpu_to_f64(got[torch.as_tensor(rows, device="cuda")][:, torch.as_tensor(queries, device="cuda")])
+    check(g, ref, "bf16", f"cfg rows_bf16_i4096_r512 rows={(r0 + rows).tolist()} queries={queries.tolist()}")
+    del rr, zf
+    torch.cuda.empty_cache()
+
+
 # ----------------------------------------------------------------------------
 # properties of the GPU path
 # ----------------------------------------------------------------------------
