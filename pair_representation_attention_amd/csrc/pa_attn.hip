@@ -54,6 +54,31 @@ __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" :
 
 __device__ __forceinline__ f16x8 lds_f16x8(const char* p) { return *reinterpret_cast<const f16x8*>(p); }
 
+// s where bit `lane` of the wave-uniform mask is set, else -inf.  Volatile so
+// that it is not speculated out of the (rare) masked-block branch.
+__device__ __forceinline__ float keep_or_neg_inf(float s, uint64_t lanes) {
+  float r;
+  asm volatile("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(-__builtin_inff()), "v"(s), "s"(lanes));
+  return r;
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Sum of the 16 fp16 softmax weights of a lane (the values the P.V product
+// uses), accumulated in fp32 by dot products with (1, 1).
+__device__ __forceinline__ float sum16_f16(const f16x8& a, const f16x8& b) {
+  const f16x2 one = {(f16)1.0f, (f16)1.0f};
+  float s0 = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 0, 1), one, 0.0f, false);
+  float s1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(b, b, 0, 1), one, 0.0f, false);
+  s0 = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 2, 3), one, s0, false);
+  s1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(b, b, 2, 3), one, s1, false);
+  s0 = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 4, 5), one, s0, false);
+  s1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(b, b, 4, 5), one, s1, false);
+  s0 = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 6, 7), one, s0, false);
+  s1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(b, b, 6, 7), one, s1, false);
+  return s0 + s1;
+}
+
 // Scheduling hint for the unit loop: alternate single MFMAs with groups of
 // VALU instructions, so that dependent MFMAs (each waits for the previous
 // one's result) are separated by softmax work instead of stalling issue.
@@ -153,24 +178,33 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
   }
 
   // ---- staging of key block kb into stage buffer `buf` ----
+  // Every 1 KB copy of this wave advances by 2 KB (one key block) per kb in
+  // its source, so the sources of key block 0 and the LDS offsets are
+  // computed once.
+  constexpr int NCW = SH::N_CH / 8;          // copies per wave and stage
+  const f16* src0[NCW];
+  int dst_off[NCW];
+#pragma unroll
+  for (int j = 0; j < NCW; ++j) {
+    const int i = wave + 8 * j;
+    if (i < SH::N_KV_CH) {
+      const int t = i >> 2, c = i & 3;          // tile (row, head), chunk K0 K1 V0 V1
+      const int rr = t / H, hh = t % H;
+      const int64_t rh = (int64_t)rows_c[rr] * H + hh;
+      src0[j] = (c < 2 ? k_ws : v_ws) + qkv_chunk(rh, nkb, 0, c & 1);
+      dst_off[j] = t * SH::KV_TILE + c * 1024;
+    } else {
+      const int ib = i - SH::N_KV_CH;
+      const int t = ib >> 1, c = ib & 1;        // tile (query block, head), chunk
+      const int qb = min(qb0_wg + t / H, nkb - 1), hh = t % H;
+      src0[j] = bias + b16_chunk(hh, nkb, qb, 0, c);
+      dst_off[j] = SH::KV_BYTES + t * SH::B_TILE + c * 1024;
+    }
+  }
   auto stage = [&](int kb, int buf) {
     char* base = smem + buf * SH::STAGE;
 #pragma unroll
-    for (int j = 0; j < SH::N_CH / 8; ++j) {
-      const int i = wave + 8 * j;
-      if (i < SH::N_KV_CH) {
-        const int t = i >> 2, c = i & 3;          // tile (row, head), chunk K0 K1 V0 V1
-        const int rr = t / H, hh = t % H;
-        const int64_t rh = (int64_t)rows_c[rr] * H + hh;
-        const f16* src = (c < 2 ? k_ws : v_ws) + qkv_chunk(rh, nkb, kb, c & 1) + lane * 8;
-        g2lds16(src, base + t * SH::KV_TILE + c * 1024);
-      } else {
-        const int ib = i - SH::N_KV_CH;
-        const int t = ib >> 1, c = ib & 1;        // tile (query block, head), chunk
-        const int qb = min(qb0_wg + t / H, nkb - 1), hh = t % H;
-        g2lds16(bias + b16_chunk(hh, nkb, qb, kb, c) + lane * 8, base + SH::KV_BYTES + t * SH::B_TILE + c * 1024);
-      }
-    }
+    for (int j = 0; j < NCW; ++j) g2lds16(src0[j] + (int64_t)kb * 1024 + lane * 8, base + dst_off[j]);
   };
   // keep bits: word (row, kb) of mask_bits holds bit b = key kb*32+b kept
   auto load_bits = [&](int rr, int kb) -> uint32_t { return mask_bits[(int64_t)rows_c[rr] * nkb + kb]; };
@@ -237,10 +271,17 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
       }
       f32x16 S = Scur;
       if (!full[rr]) {   // masked keys (or keys past P) get -inf
-        const uint32_t kb_bits = bits_cur[rr] >> (g * 8);
+        // Register j holds key (j/8)*16 + g*8 + j%8: its keep bit depends only
+        // on the lane half g, so the select's lane mask is built on the
+        // scalar unit (no per-lane bit tests).
+        const uint32_t b = bits_cur[rr];
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (!((kb_bits >> ((j >> 3) * 16 + (j & 7))) & 1u)) S[j] = -__builtin_inff();
+        for (int j = 0; j < 16; ++j) {
+          const int k0 = (j >> 3) * 16 + (j & 7);
+          const uint64_t lanes = (((b >> k0) & 1u) ? 0x00000000ffffffffull : 0ull) |
+                                 (((b >> (k0 + 8)) & 1u) ? 0xffffffff00000000ull : 0ull);
+          S[j] = keep_or_neg_inf(S[j], lanes);
+        }
       }
       if (shifted[rr]) {
 #pragma unroll
@@ -249,15 +290,13 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
 
       // fast path, unconditional so that it shares a basic block (and the
       // scheduler's interleaving) with the MFMAs issued around it
-      float p[16];
+      f16x8 P0, P1;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) p[j] = fast_exp2(S[j]);
-      float psum;
-      {
-        const float a0 = (p[0] + p[1]) + (p[2] + p[3]), a1 = (p[4] + p[5]) + (p[6] + p[7]);
-        const float a2 = (p[8] + p[9]) + (p[10] + p[11]), a3 = (p[12] + p[13]) + (p[14] + p[15]);
-        psum = (a0 + a1) + (a2 + a3);
+      for (int j = 0; j < 8; ++j) {
+        P0[j] = f2h(fast_exp2(S[j]));
+        P1[j] = f2h(fast_exp2(S[8 + j]));
       }
+      float psum = sum16_f16(P0, P1);
       SCHED_INTERLEAVE();
       if (!mset[rr] || __ballot(!(psum <= 32768.0f)) != 0) {
         // S is relative to the current shift; choose / raise the shift
@@ -281,19 +320,14 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
           m_sh[rr][qq] += d;
         }
 #pragma unroll
-        for (int j = 0; j < 16; ++j) p[j] = fast_exp2(S[j] - d);
-        const float a0 = (p[0] + p[1]) + (p[2] + p[3]), a1 = (p[4] + p[5]) + (p[6] + p[7]);
-        const float a2 = (p[8] + p[9]) + (p[10] + p[11]), a3 = (p[12] + p[13]) + (p[14] + p[15]);
-        psum = (a0 + a1) + (a2 + a3);
+        for (int j = 0; j < 8; ++j) {
+          P0[j] = f2h(fast_exp2(S[j] - d));
+          P1[j] = f2h(fast_exp2(S[8 + j] - d));
+        }
+        psum = sum16_f16(P0, P1);
         shifted[rr] = shifted[rr] || __ballot(m_sh[rr][qq] != 0.0f) != 0;
       }
       l_run[rr][qq] += psum;
-      f16x8 P0, P1;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        P0[j] = f2h(p[j]);
-        P1[j] = f2h(p[8 + j]);
-      }
       O[rr][qq] = mfma32(V[rr][0], P0, O[rr][qq]);
       O[rr][qq] = mfma32(V[rr][1], P1, O[rr][qq]);
       if (u + 1 < NU) Scur = Snext;
