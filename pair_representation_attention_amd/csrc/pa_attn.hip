@@ -52,14 +52,39 @@ __device__ __forceinline__ void g2lds16(const void* gsrc, char* lds_base) {
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// The same copy issued from inline asm, for the staging rings.  The
+// compiler tracks every LDS-DMA copy in one slot and would drain all copies
+// in flight before each LDS read; the rings keep their order explicitly
+// instead (a counted wait before the barrier of each key block, a full
+// drain before the LDS is reused).  The copy has no register result and its
+// address operands are read at issue; one wait state separates the M0 write
+// from the copy that reads it.
+__device__ __forceinline__ void g2lds16_ring(const void* gsrc, char* lds_base) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_void_t*)lds_base;
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off" ::"v"(gsrc),
+      "s"(lds_addr)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(N) through the builtin (gfx9 immediate layout: vmcnt in
+// bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] at their no-wait
+// maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 __device__ __forceinline__ f16x8 lds_f16x8(const char* p) { return *reinterpret_cast<const f16x8*>(p); }
 
-// s where bit `lane` of the wave-uniform mask is set, else -inf.  Volatile so
-// that it is not speculated out of the (rare) masked-block branch.
+// s where bit `lane` of the wave-uniform mask is set, else -inf: one
+// v_cndmask with the mask as its scalar condition.  (A compiler builtin, not
+// inline asm, so that the wait states after the MFMA producing s are known.)
 __device__ __forceinline__ float keep_or_neg_inf(float s, uint64_t lanes) {
-  float r;
-  asm volatile("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(-__builtin_inff()), "v"(s), "s"(lanes));
-  return r;
+  return __builtin_amdgcn_inverse_ballot_w64(lanes) ? s : -__builtin_inff();
 }
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -101,17 +126,26 @@ struct AttnShape {
   static constexpr int RWG = 2;                    // rows per workgroup (every wave does both)
   static constexpr int KV_TILE = 4096;             // K (2 chunks) + V (2 chunks) of one (row, head)
   static constexpr int B_TILE = 2048;              // fp16 bias tile (2 chunks) of one (query block, head)
-  static constexpr int KV_BYTES = RWG * H * KV_TILE;
-  static constexpr int B_BYTES = QWG * H * B_TILE;
-  static constexpr int STAGE = KV_BYTES + B_BYTES;  // 64 KB (H=4) or 80 KB (H=8)
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int KV_STAGE = RWG * H * KV_TILE;   // 32 KB (H=4) or 64 KB (H=8)
+  static constexpr int B_STAGE = QWG * H * B_TILE;     // 32 KB (H=4) or 16 KB (H=8)
+  // K/V ring of NKV stages (NKV-1 key blocks ahead), bias ring of 2 (one
+  // block ahead): 3 x 32 + 2 x 32 KB (H=4) or 2 x 64 + 2 x 16 KB (H=8)
+  static constexpr int NKV = 3 * KV_STAGE + 2 * B_STAGE <= 160 * 1024 ? 3 : 2;
+  static constexpr int LDS_KV = NKV * KV_STAGE;
+  static constexpr int LDS_B = 2 * B_STAGE;
   static constexpr int N_KV_CH = RWG * H * 4;      // 1 KB copies per stage
   static constexpr int N_B_CH = QWG * H * 2;
-  static constexpr int N_CH = N_KV_CH + N_B_CH;
-  static_assert(N_CH % 8 == 0, "copies split evenly over the 8 waves");
+  static constexpr int NCW = N_KV_CH / 8;          // K/V copies per wave and stage
+  static constexpr int NCB = N_B_CH / 8;           // bias copies per wave and stage
+  static_assert(N_KV_CH % 8 == 0 && N_B_CH % 8 == 0, "copies split evenly over the 8 waves");
+  static_assert(LDS_KV + LDS_B <= 160 * 1024, "LDS");
+  // Block kb needs bias stage kb (issued at the top of kb-1, before that
+  // block's K/V copies) and K/V stage kb (issued NKV-1 blocks ago): the K/V
+  // copies of block kb-1 may stay in flight when the ring is 3 deep.
+  static constexpr int WAIT = NKV == 3 ? NCW : 0;
 };
 
-template <int H, int C_OUT>
+template <int H, int C_OUT, bool HAS_MASK>
 __global__ __launch_bounds__(512, 1) void attn_kernel(
     const f16* __restrict__ q_ws, const f16* __restrict__ k_ws, const f16* __restrict__ v_ws,
     const f16* __restrict__ g_ws, const f16* __restrict__ bias, const uint32_t* __restrict__ mask_bits,
@@ -122,8 +156,9 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
   constexpr int HD = H * 32;
   constexpr int QW = SH::QW, RW = SH::RWG;
   constexpr int OP = HD + 8;                 // epilogue o tile pitch (fp16 elements)
-  static_assert(SH::QWG * 32 * OP * 2 <= SH::LDS, "epilogue tile fits");
-  __shared__ __attribute__((aligned(1024))) char smem[SH::LDS];
+  static_assert(SH::QWG * 32 * OP * 2 <= SH::LDS_KV, "epilogue tile fits");
+  __shared__ __attribute__((aligned(1024))) char kv_lds[SH::LDS_KV];
+  __shared__ __attribute__((aligned(1024))) char b_lds[SH::LDS_B];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
@@ -177,56 +212,89 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
     }
   }
 
-  // ---- staging of key block kb into stage buffer `buf` ----
+  // ---- staging: K/V ring (NKV stages) and bias ring (2 stages) ----
   // Every 1 KB copy of this wave advances by 2 KB (one key block) per kb in
   // its source, so the sources of key block 0 and the LDS offsets are
-  // computed once.
-  constexpr int NCW = SH::N_CH / 8;          // copies per wave and stage
-  const f16* src0[NCW];
-  int dst_off[NCW];
+  // computed once.  Blocks past the end are clamped to the last one
+  // (in-bounds copies into a free stage), so that every block issues the
+  // same number of copies and the counted wait holds.
+  constexpr int NCW = SH::NCW, NCB = SH::NCB;
+  const f16* kv_src[NCW];
+  int kv_off[NCW];
+  const f16* b_src[NCB];
+  int b_off[NCB];
 #pragma unroll
   for (int j = 0; j < NCW; ++j) {
     const int i = wave + 8 * j;
-    if (i < SH::N_KV_CH) {
-      const int t = i >> 2, c = i & 3;          // tile (row, head), chunk K0 K1 V0 V1
-      const int rr = t / H, hh = t % H;
-      const int64_t rh = (int64_t)rows_c[rr] * H + hh;
-      src0[j] = (c < 2 ? k_ws : v_ws) + qkv_chunk(rh, nkb, 0, c & 1);
-      dst_off[j] = t * SH::KV_TILE + c * 1024;
-    } else {
-      const int ib = i - SH::N_KV_CH;
-      const int t = ib >> 1, c = ib & 1;        // tile (query block, head), chunk
-      const int qb = min(qb0_wg + t / H, nkb - 1), hh = t % H;
-      src0[j] = bias + b16_chunk(hh, nkb, qb, 0, c);
-      dst_off[j] = SH::KV_BYTES + t * SH::B_TILE + c * 1024;
-    }
+    const int t = i >> 2, c = i & 3;          // tile (row, head), chunk K0 K1 V0 V1
+    const int rr = t / H, hh = t % H;
+    const int64_t rh = (int64_t)rows_c[rr] * H + hh;
+    kv_src[j] = (c < 2 ? k_ws : v_ws) + qkv_chunk(rh, nkb, 0, c & 1);
+    kv_off[j] = t * SH::KV_TILE + c * 1024;
   }
-  auto stage = [&](int kb, int buf) {
-    char* base = smem + buf * SH::STAGE;
 #pragma unroll
-    for (int j = 0; j < NCW; ++j) g2lds16(src0[j] + (int64_t)kb * 1024 + lane * 8, base + dst_off[j]);
+  for (int j = 0; j < NCB; ++j) {
+    const int ib = wave + 8 * j;
+    const int t = ib >> 1, c = ib & 1;        // tile (query block, head), chunk
+    const int qb = min(qb0_wg + t / H, nkb - 1), hh = t % H;
+    b_src[j] = bias + b16_chunk(hh, nkb, qb, 0, c);
+    b_off[j] = t * SH::B_TILE + c * 1024;
+  }
+  auto stage_kv = [&](int kb) {
+    const int kbc = min(kb, nkb - 1);
+    char* base = kv_lds + (kb % SH::NKV) * SH::KV_STAGE;
+#pragma unroll
+    for (int j = 0; j < NCW; ++j) g2lds16_ring(kv_src[j] + (int64_t)kbc * 1024 + lane * 8, base + kv_off[j]);
   };
-  // keep bits: word (row, kb) of mask_bits holds bit b = key kb*32+b kept
-  auto load_bits = [&](int rr, int kb) -> uint32_t { return mask_bits[(int64_t)rows_c[rr] * nkb + kb]; };
-
-  stage(0, 0);
-  uint32_t bits_cur[RW];
+  auto stage_b = [&](int kb) {
+    const int kbc = min(kb, nkb - 1);
+    char* base = b_lds + (kb & 1) * SH::B_STAGE;
 #pragma unroll
-  for (int rr = 0; rr < RW; ++rr) bits_cur[rr] = load_bits(rr, 0);
+    for (int j = 0; j < NCB; ++j) g2lds16_ring(b_src[j] + (int64_t)kbc * 1024 + lane * 8, base + b_off[j]);
+  };
+  // keep bits: word (row, kb) of mask_bits holds bit b = key kb*32+b kept.
+  // Without a mask only keys past P are dropped, which is computed; with
+  // one the word is a scalar load (scalar loads do not count against the
+  // copies' vector-memory counter).
+  auto keep_bits = [&](int rr, int kb) -> uint32_t {
+    if constexpr (HAS_MASK) {
+      return mask_bits[(int64_t)rows_c[rr] * nkb + kb];
+    } else {
+      const int n = P - kb * 32;
+      return n >= 32 ? 0xffffffffu : (n <= 0 ? 0u : ((1u << n) - 1u));
+    }
+  };
+
+  // Q has landed before any copy is in flight: the compiler's waits for it
+  // would otherwise sit inside the loop and drain the copies too.  (The
+  // empty asm statements consume Q here, so its loads cannot sink below.)
+#pragma unroll
+  for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+    for (int qq = 0; qq < QW; ++qq) asm volatile("" ::"v"(Q[rr][qq][0]), "v"(Q[rr][qq][1]));
+  wait_vmcnt<0>();
+  stage_b(0);
+#pragma unroll
+  for (int j = 0; j < SH::NKV - 1; ++j) stage_kv(j);
 
   constexpr int NU = RW * QW;   // units per wave and key block, query-block major
   for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    wait_vm0();
-    __syncthreads();   // stage kb visible to all waves; stage kb-1 fully read
-    uint32_t bits_next[RW];
-    if (kb + 1 < nkb) {
-      stage(kb + 1, buf ^ 1);
+    // Bias stage kb and K/V stage kb landed for all waves, stages kb-1 fully
+    // read.  A bare barrier: __syncthreads' release fence would also wait
+    // for the copies in flight for later blocks.  The empty asm statements
+    // keep the compiler from moving LDS accesses across it.
+    wait_vmcnt<SH::WAIT>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    stage_b(kb + 1);
+    stage_kv(kb + SH::NKV - 1);
+    uint32_t bits_cur[RW];
 #pragma unroll
-      for (int rr = 0; rr < RW; ++rr) bits_next[rr] = load_bits(rr, kb + 1);
-    }
+    for (int rr = 0; rr < RW; ++rr) bits_cur[rr] = keep_bits(rr, kb);
 
-    const char* st = smem + buf * SH::STAGE;
+    const char* st = kv_lds + (kb % SH::NKV) * SH::KV_STAGE;
+    const char* bst = b_lds + (kb & 1) * SH::B_STAGE;
     f16x8 K[RW][2], V[RW][2];
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
@@ -237,7 +305,7 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
       V[rr][1] = lds_f16x8(kv + 3072);
     }
     auto bias_c = [&](int qq) -> f32x16 {
-      const char* bt = st + SH::KV_BYTES + ((qgrp * QW + qq) * H + h) * SH::B_TILE + lane * 16;
+      const char* bt = bst + ((qgrp * QW + qq) * H + h) * SH::B_TILE + lane * 16;
       const f16x8 b0 = lds_f16x8(bt), b1 = lds_f16x8(bt + 1024);
       f32x16 c;
 #pragma unroll
@@ -334,10 +402,7 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
     }
     // the first block with a kept key sets the reference maximum of the row
 #pragma unroll
-    for (int rr = 0; rr < RW; ++rr) {
-      mset[rr] = mset[rr] || keyed[rr];
-      if (kb + 1 < nkb) bits_cur[rr] = bits_next[rr];
-    }
+    for (int rr = 0; rr < RW; ++rr) mset[rr] = mset[rr] || keyed[rr];
   }
 
   // ---- epilogue: normalise, gate, output projection ----
@@ -351,7 +416,7 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
   f16x8 Wo[KO];
 #pragma unroll
   for (int t = 0; t < KO; ++t) Wo[t] = ld16(woT + (int64_t)(cb_w * 32 + lq) * HD + t * 16 + g * 8);
-  f16* o_lds = reinterpret_cast<f16*>(smem);
+  f16* o_lds = reinterpret_cast<f16*>(kv_lds);
 
 #pragma unroll
   for (int rr = 0; rr < RW; ++rr) {
@@ -431,29 +496,34 @@ hipError_t launch_mask_bits(const uint8_t* mask, int64_t ms_r, int64_t ms_k, uin
   return hipGetLastError();
 }
 
-template <int H, int C_OUT>
+template <int H, int C_OUT, bool HAS_MASK>
 static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
   using SH = AttnShape<H>;
   const int nkb = a.Pp / 32;
   const int n_qg = (nkb + SH::QWG - 1) / SH::QWG;
   const int n_rg = (a.nrows + SH::RWG - 1) / SH::RWG;
   const int64_t n = (int64_t)n_qg * n_rg;
-  hipLaunchKernelGGL((attn_kernel<H, C_OUT>), dim3((unsigned)n), dim3(512), 0, s, (const f16*)a.q_ws,
+  hipLaunchKernelGGL((attn_kernel<H, C_OUT, HAS_MASK>), dim3((unsigned)n), dim3(512), 0, s, (const f16*)a.q_ws,
                      (const f16*)a.k_ws, (const f16*)a.v_ws, (const f16*)a.g_ws, (const f16*)a.bias, a.mask_bits,
                      (const f16*)a.woT, (const bf16*)a.b_o, (bf16*)a.out, a.os_r, a.os_p, a.nrows, a.P, a.Pp, n_qg,
                      n_rg);
   return hipGetLastError();
 }
 
+template <int H, int C_OUT>
+static hipError_t attn_dispatch_m(const AttnArgs& a, hipStream_t s) {
+  return a.mask_bits != nullptr ? attn_dispatch<H, C_OUT, true>(a, s) : attn_dispatch<H, C_OUT, false>(a, s);
+}
+
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.H == 4) {
-    if (a.c_out == 64) return attn_dispatch<4, 64>(a, s);
-    if (a.c_out == 128) return attn_dispatch<4, 128>(a, s);
-    if (a.c_out == 256) return attn_dispatch<4, 256>(a, s);
+    if (a.c_out == 64) return attn_dispatch_m<4, 64>(a, s);
+    if (a.c_out == 128) return attn_dispatch_m<4, 128>(a, s);
+    if (a.c_out == 256) return attn_dispatch_m<4, 256>(a, s);
   } else if (a.H == 8) {
-    if (a.c_out == 64) return attn_dispatch<8, 64>(a, s);
-    if (a.c_out == 128) return attn_dispatch<8, 128>(a, s);
-    if (a.c_out == 256) return attn_dispatch<8, 256>(a, s);
+    if (a.c_out == 64) return attn_dispatch_m<8, 64>(a, s);
+    if (a.c_out == 128) return attn_dispatch_m<8, 128>(a, s);
+    if (a.c_out == 256) return attn_dispatch_m<8, 256>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -452,7 +452,9 @@ static int run_row_attention(const pairattn_params* p, const Layout& L, hipStrea
   at.g_ws = pj.g_ws;
   at.bias = bias;
   at.mask = mask;
-  at.mask_bits = bf ? reinterpret_cast<const uint32_t*>(ws_at(p, L.bits)) : nullptr;
+  // bf16 path: keep bits only when there is a mask (without one the kernel
+  // drops just the keys past P, which it computes)
+  at.mask_bits = (bf && mask != nullptr) ? reinterpret_cast<const uint32_t*>(ws_at(p, L.bits)) : nullptr;
   at.ms_r = ms_r;
   at.ms_k = ms_k;
   at.woT = bf ? ws_at(p, L.woT) : nullptr;
@@ -466,7 +468,7 @@ static int run_row_attention(const pairattn_params* p, const Layout& L, hipStrea
   at.nrows = (int)nrows;
   at.P = (int)P;
   at.Pp = Pp;
-  if (bf) {
+  if (bf && mask != nullptr) {
     PA_TRY(hip_status(pa::launch_mask_bits(mask, ms_r, ms_k, reinterpret_cast<uint32_t*>(ws_at(p, L.bits)),
                                            (int)nrows, (int)P, Pp / 32, s),
                       "mask bits launch"));
