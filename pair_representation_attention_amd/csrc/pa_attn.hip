@@ -240,17 +240,30 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
     b_src[j] = bias + b16_chunk(hh, nkb, qb, 0, c);
     b_off[j] = t * SH::B_TILE + c * 1024;
   }
-  auto stage_kv = [&](int kb) {
+  constexpr int NU = RW * QW;   // units per wave and key block, query-block major
+  // copies [j0, j1) of one stage
+  auto stage_kv = [&](int kb, int j0, int j1) {
     const int kbc = min(kb, nkb - 1);
     char* base = kv_lds + (kb % SH::NKV) * SH::KV_STAGE;
 #pragma unroll
-    for (int j = 0; j < NCW; ++j) g2lds16_ring(kv_src[j] + (int64_t)kbc * 1024 + lane * 8, base + kv_off[j]);
+    for (int j = 0; j < NCW; ++j)
+      if (j >= j0 && j < j1) g2lds16_ring(kv_src[j] + (int64_t)kbc * 1024 + lane * 8, base + kv_off[j]);
   };
-  auto stage_b = [&](int kb) {
+  auto stage_b = [&](int kb, int j0, int j1) {
     const int kbc = min(kb, nkb - 1);
     char* base = b_lds + (kb & 1) * SH::B_STAGE;
 #pragma unroll
-    for (int j = 0; j < NCB; ++j) g2lds16_ring(b_src[j] + (int64_t)kbc * 1024 + lane * 8, base + b_off[j]);
+    for (int j = 0; j < NCB; ++j)
+      if (j >= j0 && j < j1) g2lds16_ring(b_src[j] + (int64_t)kbc * 1024 + lane * 8, base + b_off[j]);
+  };
+  // The copies of one block (bias stage kb+1, then K/V stage kb+NKV-1) are
+  // spread over its units, so that the address unit works through them while
+  // the waves compute instead of stalling the issue of every wave at once.
+  constexpr int NCP = NCB + NCW;                 // copies per wave and block
+  auto copies_for_unit = [&](int kb, int u) {
+    const int c0 = u * NCP / NU, c1 = (u + 1) * NCP / NU;
+    stage_b(kb + 1, c0, min(c1, NCB));
+    stage_kv(kb + SH::NKV - 1, max(c0 - NCB, 0), c1 - NCB);
   };
   // keep bits: word (row, kb) of mask_bits holds bit b = key kb*32+b kept.
   // Without a mask only keys past P are dropped, which is computed; with
@@ -273,11 +286,10 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
 #pragma unroll
     for (int qq = 0; qq < QW; ++qq) asm volatile("" ::"v"(Q[rr][qq][0]), "v"(Q[rr][qq][1]));
   wait_vmcnt<0>();
-  stage_b(0);
+  stage_b(0, 0, NCB);
 #pragma unroll
-  for (int j = 0; j < SH::NKV - 1; ++j) stage_kv(j);
+  for (int j = 0; j < SH::NKV - 1; ++j) stage_kv(j, 0, NCW);
 
-  constexpr int NU = RW * QW;   // units per wave and key block, query-block major
   for (int kb = 0; kb < nkb; ++kb) {
     // Bias stage kb and K/V stage kb landed for all waves, stages kb-1 fully
     // read.  A bare barrier: __syncthreads' release fence would also wait
@@ -287,8 +299,6 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    stage_b(kb + 1);
-    stage_kv(kb + SH::NKV - 1);
     uint32_t bits_cur[RW];
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) bits_cur[rr] = keep_bits(rr, kb);
@@ -331,6 +341,7 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int qq = u / RW, rr = u % RW;
+      copies_for_unit(kb, u);
       f32x16 Snext;
       if (u + 1 < NU) {
         const int nq = (u + 1) / RW, nr = (u + 1) % RW;
