@@ -146,7 +146,7 @@ struct AttnShape {
 };
 
 template <int H, int C_OUT, bool HAS_MASK>
-__global__ __launch_bounds__(512, 1) void attn_kernel(
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(
     const f16* __restrict__ q_ws, const f16* __restrict__ k_ws, const f16* __restrict__ v_ws,
     const f16* __restrict__ g_ws, const f16* __restrict__ bias, const uint32_t* __restrict__ mask_bits,
     const f16* __restrict__ woT, const bf16* __restrict__ b_o, bf16* __restrict__ out, int64_t os_r,
@@ -286,134 +286,192 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(
 #pragma unroll
     for (int qq = 0; qq < QW; ++qq) asm volatile("" ::"v"(Q[rr][qq][0]), "v"(Q[rr][qq][1]));
   wait_vmcnt<0>();
-  stage_b(0, 0, NCB);
-#pragma unroll
-  for (int j = 0; j < SH::NKV - 1; ++j) stage_kv(j, 0, NCW);
+  bool row_has_key[RW];   // wave-uniform: some block of the row keeps a key
 
-  for (int kb = 0; kb < nkb; ++kb) {
-    // Bias stage kb and K/V stage kb landed for all waves, stages kb-1 fully
-    // read.  A bare barrier: __syncthreads' release fence would also wait
-    // for the copies in flight for later blocks.  The empty asm statements
-    // keep the compiler from moving LDS accesses across it.
-    wait_vmcnt<SH::WAIT>();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    uint32_t bits_cur[RW];
-#pragma unroll
-    for (int rr = 0; rr < RW; ++rr) bits_cur[rr] = keep_bits(rr, kb);
-
-    const char* st = kv_lds + (kb % SH::NKV) * SH::KV_STAGE;
-    const char* bst = b_lds + (kb & 1) * SH::B_STAGE;
-    f16x8 K[RW][2], V[RW][2];
+  // One sweep over all key blocks.
+  //   FAST: p = exp2(S) with no shift and no per-unit test, so the units of
+  //         a block form one basic block.  Valid when every sum l stays finite
+  //         (no fp16 weight overflowed) and is at least 1 for rows with a kept
+  //         key (the largest weights are normal fp16 numbers); checked after
+  //         the sweep, and the workgroup sweeps again with SAFE otherwise.
+  //   SAFE: a per-(row, query) shift chosen on the row's first block with a
+  //         kept key and raised whenever a block sum passes 2^15.
+  auto sweep = [&](auto fastc) {
+    constexpr bool FAST = decltype(fastc)::value;
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
-      const char* kv = st + (rr * H + h) * SH::KV_TILE + lane * 16;
-      K[rr][0] = lds_f16x8(kv);
-      K[rr][1] = lds_f16x8(kv + 1024);
-      V[rr][0] = lds_f16x8(kv + 2048);
-      V[rr][1] = lds_f16x8(kv + 3072);
-    }
-    auto bias_c = [&](int qq) -> f32x16 {
-      const char* bt = bst + ((qgrp * QW + qq) * H + h) * SH::B_TILE + lane * 16;
-      const f16x8 b0 = lds_f16x8(bt), b1 = lds_f16x8(bt + 1024);
-      f32x16 c;
+      mset[rr] = FAST;
+      shifted[rr] = false;
+      row_has_key[rr] = false;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        c[e] = (float)b0[e];
-        c[8 + e] = (float)b1[e];
+      for (int qq = 0; qq < QW; ++qq) {
+        O[rr][qq] = f32x16{};
+        m_sh[rr][qq] = 0.0f;
+        l_run[rr][qq] = 0.0f;
       }
-      return c;
-    };
-    auto qk = [&](int rr, int qq, const f32x16& C) -> f32x16 {
-      const f32x16 S = mfma32(K[rr][0], Q[rr][qq][0], C);
-      return mfma32(K[rr][1], Q[rr][qq][1], S);
-    };
-    bool keyed[RW], full[RW];
-#pragma unroll
-    for (int rr = 0; rr < RW; ++rr) {
-      keyed[rr] = false;                           // block holds a kept key of row rr
-      full[rr] = bits_cur[rr] == 0xffffffffu;      // no masked key in this block
     }
+    stage_b(0, 0, NCB);
+  #pragma unroll
+    for (int j = 0; j < SH::NKV - 1; ++j) stage_kv(j, 0, NCW);
 
-    f32x16 Cb = bias_c(0);
-    f32x16 Scur = qk(0, 0, Cb);
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int qq = u / RW, rr = u % RW;
-      copies_for_unit(kb, u);
-      f32x16 Snext;
-      if (u + 1 < NU) {
-        const int nq = (u + 1) / RW, nr = (u + 1) % RW;
-        if (nr == 0) Cb = bias_c(nq);
-        Snext = qk(nr, nq, Cb);
+
+    for (int kb = 0; kb < nkb; ++kb) {
+      // Bias stage kb and K/V stage kb landed for all waves, stages kb-1 fully
+      // read.  A bare barrier: __syncthreads' release fence would also wait
+      // for the copies in flight for later blocks.  The empty asm statements
+      // keep the compiler from moving LDS accesses across it.
+      wait_vmcnt<SH::WAIT>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      uint32_t bits_cur[RW];
+  #pragma unroll
+      for (int rr = 0; rr < RW; ++rr) bits_cur[rr] = keep_bits(rr, kb);
+
+      const char* st = kv_lds + (kb % SH::NKV) * SH::KV_STAGE;
+      const char* bst = b_lds + (kb & 1) * SH::B_STAGE;
+      f16x8 K[RW][2], V[RW][2];
+  #pragma unroll
+      for (int rr = 0; rr < RW; ++rr) {
+        const char* kv = st + (rr * H + h) * SH::KV_TILE + lane * 16;
+        K[rr][0] = lds_f16x8(kv);
+        K[rr][1] = lds_f16x8(kv + 1024);
+        V[rr][0] = lds_f16x8(kv + 2048);
+        V[rr][1] = lds_f16x8(kv + 3072);
       }
-      f32x16 S = Scur;
-      if (!full[rr]) {   // masked keys (or keys past P) get -inf
-        // Register j holds key (j/8)*16 + g*8 + j%8: its keep bit depends only
-        // on the lane half g, so the select's lane mask is built on the
-        // scalar unit (no per-lane bit tests).
-        const uint32_t b = bits_cur[rr];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int k0 = (j >> 3) * 16 + (j & 7);
-          const uint64_t lanes = (((b >> k0) & 1u) ? 0x00000000ffffffffull : 0ull) |
-                                 (((b >> (k0 + 8)) & 1u) ? 0xffffffff00000000ull : 0ull);
-          S[j] = keep_or_neg_inf(S[j], lanes);
+      auto bias_c = [&](int qq) -> f32x16 {
+        const char* bt = bst + ((qgrp * QW + qq) * H + h) * SH::B_TILE + lane * 16;
+        const f16x8 b0 = lds_f16x8(bt), b1 = lds_f16x8(bt + 1024);
+        f32x16 c;
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          c[e] = (float)b0[e];
+          c[8 + e] = (float)b1[e];
         }
-      }
-      if (shifted[rr]) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) S[j] -= m_sh[rr][qq];
+        return c;
+      };
+      auto qk = [&](int rr, int qq, const f32x16& C) -> f32x16 {
+        const f32x16 S = mfma32(K[rr][0], Q[rr][qq][0], C);
+        return mfma32(K[rr][1], Q[rr][qq][1], S);
+      };
+      bool keyed[RW], full[RW];
+  #pragma unroll
+      for (int rr = 0; rr < RW; ++rr) {
+        keyed[rr] = false;                           // block holds a kept key of row rr
+        full[rr] = bits_cur[rr] == 0xffffffffu;      // no masked key in this block
       }
 
-      // fast path, unconditional so that it shares a basic block (and the
-      // scheduler's interleaving) with the MFMAs issued around it
-      f16x8 P0, P1;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        P0[j] = f2h(fast_exp2(S[j]));
-        P1[j] = f2h(fast_exp2(S[8 + j]));
-      }
-      float psum = sum16_f16(P0, P1);
-      SCHED_INTERLEAVE();
-      if (!mset[rr] || __ballot(!(psum <= 32768.0f)) != 0) {
-        // S is relative to the current shift; choose / raise the shift
-        float bmax = S[0];
-#pragma unroll
-        for (int j = 1; j < 16; ++j) bmax = fmaxf(bmax, S[j]);
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-        const bool any_key = __ballot(bmax > -__builtin_inff()) != 0;
-        keyed[rr] = keyed[rr] || any_key;
-        float d = 0.0f;
-        if (any_key) {
-          if (mset[rr]) {
-            d = fmaxf(bmax, 0.0f);
-            const float alpha = fast_exp2(-d);
-#pragma unroll
-            for (int j = 0; j < 16; ++j) O[rr][qq][j] *= alpha;
-            l_run[rr][qq] *= alpha;
-          } else {
-            d = (bmax >= -8.0f && bmax <= 8.0f) ? 0.0f : bmax;
+      // The units of the block (MASKED: the keep bits are consulted).
+      auto units = [&](auto maskedc) {
+        constexpr bool MASKED = decltype(maskedc)::value;
+        f32x16 Cb = bias_c(0);
+        f32x16 Scur = qk(0, 0, Cb);
+    #pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int qq = u / RW, rr = u % RW;
+          copies_for_unit(kb, u);
+          f32x16 Snext;
+          if (u + 1 < NU) {
+            const int nq = (u + 1) / RW, nr = (u + 1) % RW;
+            if (nr == 0) Cb = bias_c(nq);
+            Snext = qk(nr, nq, Cb);
           }
-          m_sh[rr][qq] += d;
+          f32x16 S = Scur;
+          if (MASKED && !full[rr]) {   // masked keys (or keys past P) get -inf
+            // Register j holds key (j/8)*16 + g*8 + j%8: its keep bit depends only
+            // on the lane half g, so the select's lane mask is built on the
+            // scalar unit (no per-lane bit tests).
+            const uint32_t b = bits_cur[rr];
+    #pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int k0 = (j >> 3) * 16 + (j & 7);
+              const uint64_t lanes = (((b >> k0) & 1u) ? 0x00000000ffffffffull : 0ull) |
+                                     (((b >> (k0 + 8)) & 1u) ? 0xffffffff00000000ull : 0ull);
+              S[j] = keep_or_neg_inf(S[j], lanes);
+            }
+          }
+          if (!FAST && shifted[rr]) {
+    #pragma unroll
+            for (int j = 0; j < 16; ++j) S[j] -= m_sh[rr][qq];
+          }
+
+          // fast path, unconditional so that it shares a basic block (and the
+          // scheduler's interleaving) with the MFMAs issued around it
+          f16x8 P0, P1;
+    #pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            P0[j] = f2h(fast_exp2(S[j]));
+            P1[j] = f2h(fast_exp2(S[8 + j]));
+          }
+          float psum = sum16_f16(P0, P1);
+          if (!FAST && (!mset[rr] || __ballot(!(psum <= 32768.0f)) != 0)) {
+            // S is relative to the current shift; choose / raise the shift
+            float bmax = S[0];
+    #pragma unroll
+            for (int j = 1; j < 16; ++j) bmax = fmaxf(bmax, S[j]);
+            bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+            const bool any_key = __ballot(bmax > -__builtin_inff()) != 0;
+            keyed[rr] = keyed[rr] || any_key;
+            float d = 0.0f;
+            if (any_key) {
+              if (mset[rr]) {
+                d = fmaxf(bmax, 0.0f);
+                const float alpha = fast_exp2(-d);
+    #pragma unroll
+                for (int j = 0; j < 16; ++j) O[rr][qq][j] *= alpha;
+                l_run[rr][qq] *= alpha;
+              } else {
+                d = (bmax >= -8.0f && bmax <= 8.0f) ? 0.0f : bmax;
+              }
+              m_sh[rr][qq] += d;
+            }
+    #pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              P0[j] = f2h(fast_exp2(S[j] - d));
+              P1[j] = f2h(fast_exp2(S[8 + j] - d));
+            }
+            psum = sum16_f16(P0, P1);
+            shifted[rr] = shifted[rr] || __ballot(m_sh[rr][qq] != 0.0f) != 0;
+          }
+          l_run[rr][qq] += psum;
+          O[rr][qq] = mfma32(V[rr][0], P0, O[rr][qq]);
+          O[rr][qq] = mfma32(V[rr][1], P1, O[rr][qq]);
+          if (u + 1 < NU) Scur = Snext;
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          P0[j] = f2h(fast_exp2(S[j] - d));
-          P1[j] = f2h(fast_exp2(S[8 + j] - d));
-        }
-        psum = sum16_f16(P0, P1);
-        shifted[rr] = shifted[rr] || __ballot(m_sh[rr][qq] != 0.0f) != 0;
+      };
+      units(std::integral_constant<bool, true>{});
+      // the first block with a kept key sets the reference maximum of the row
+  #pragma unroll
+      for (int rr = 0; rr < RW; ++rr) {
+        mset[rr] = mset[rr] || keyed[rr];
+        row_has_key[rr] = row_has_key[rr] || bits_cur[rr] != 0u;
       }
-      l_run[rr][qq] += psum;
-      O[rr][qq] = mfma32(V[rr][0], P0, O[rr][qq]);
-      O[rr][qq] = mfma32(V[rr][1], P1, O[rr][qq]);
-      if (u + 1 < NU) Scur = Snext;
     }
-    // the first block with a kept key sets the reference maximum of the row
+
+  };
+
+  sweep(std::integral_constant<bool, true>{});
+  wait_vm0();   // copies past the end have landed before the LDS is reused
+  bool bad = false;
 #pragma unroll
-    for (int rr = 0; rr < RW; ++rr) mset[rr] = mset[rr] || keyed[rr];
+  for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+    for (int qq = 0; qq < QW; ++qq) {
+      const float lt = l_run[rr][qq] + __shfl_xor(l_run[rr][qq], 32, 64);
+      bad = bad || !(lt < __builtin_inff()) || (row_has_key[rr] && lt < 1.0f);
+    }
+  // workgroup-wide "any wave bad", through the (now idle) K/V stage memory
+  {
+    int* flag = reinterpret_cast<int*>(kv_lds);
+    const bool wbad = __ballot(bad) != 0;
+    __syncthreads();   // every wave is done with the ring
+    if (lane == 0) flag[wave] = wbad ? 1 : 0;
+    __syncthreads();
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) any |= flag[w];
+    __syncthreads();   // flags read before the LDS is written again
+    if (any) sweep(std::integral_constant<bool, false>{});
   }
 
   // ---- epilogue: normalise, gate, output projection ----

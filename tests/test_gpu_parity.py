@@ -58,6 +58,40 @@ def test_tri_other_widths(c, H):
 
 
 # ----------------------------------------------------------------------------
+# logits far from zero: the kernel's zero-shift sweep cannot represent the
+# softmax weights there (fp16 overflow above 2^16, too little mass below), so
+# the workgroup sweeps again with per-query shifts.  The pair-bias offset is
+# set through the LayerNorm beta: beta = t * w_b (w_b^T w_b)^-1 1 gives
+# beta . w_b[:, h] = t for every head h.
+# ----------------------------------------------------------------------------
+def _offset_case(t: float, keep_per_row: int, seed: int):
+    case = inputs.make_tri_case(I=64, c=128, H=4, d=32, dtype="bf16", mask="none", seed=seed, affine=True,
+                                biases=True)
+    p = case.params_start
+    wb = p.w_b.astype(np.float64)
+    beta = wb @ np.linalg.solve(wb.T @ wb, np.full(4, t))
+    p.ln_beta = inputs.round_to_bf16(beta.astype(np.float32))
+    p.ln_gamma = inputs.round_to_bf16((0.25 * p.ln_gamma).astype(np.float32))
+    mask = None
+    if keep_per_row:
+        rng = np.random.default_rng(seed)
+        mask = np.zeros((64, 64), np.uint8)
+        for i in range(64):
+            mask[i, rng.choice(64, size=keep_per_row, replace=False)] = 1
+    return case.z, mask, p
+
+
+@pytest.mark.parametrize("t,keep", [(-4.0, 3), (12.0, 0), (-8.0, 0)])
+def test_far_logits_take_the_shifted_sweep(t, keep):
+    z, mask, p = _offset_case(t, keep, seed=31)
+    got = gpu_to_f64(_dev().TriRunner(z, mask, p, 4, "bf16")(0))
+    ref = oracle.tri_fwd(z, mask, p.as_dict(), 4, 0)
+    b = oracle.attention_bias(z, p.as_dict(), 4, oracle.START)
+    assert np.abs(b.mean() - t) < 1.0    # the offset is in place
+    check(got, ref, "bf16", f"far logits t={t} keep={keep}")
+
+
+# ----------------------------------------------------------------------------
 # workload configurations
 # ----------------------------------------------------------------------------
 def test_cfg_tri_fp32_i64():
