@@ -339,9 +339,15 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         V[rr][0] = lds_f16x8(kv + 2048);
         V[rr][1] = lds_f16x8(kv + 3072);
       }
-      auto bias_c = [&](int qq) -> f32x16 {
+      f16x8 Bt[QW][2];
+  #pragma unroll
+      for (int qq = 0; qq < QW; ++qq) {
         const char* bt = bst + ((qgrp * QW + qq) * H + h) * SH::B_TILE + lane * 16;
-        const f16x8 b0 = lds_f16x8(bt), b1 = lds_f16x8(bt + 1024);
+        Bt[qq][0] = lds_f16x8(bt);
+        Bt[qq][1] = lds_f16x8(bt + 1024);
+      }
+      auto bias_c = [&](int qq) -> f32x16 {
+        const f16x8 b0 = Bt[qq][0], b1 = Bt[qq][1];
         f32x16 c;
   #pragma unroll
         for (int e = 0; e < 8; ++e) {
