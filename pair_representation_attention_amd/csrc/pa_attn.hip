@@ -384,15 +384,15 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
           }
           f32x16 S = Scur;
           if (MASKED && !full[rr]) {   // masked keys (or keys past P) get -inf
-            // Register j holds key (j/8)*16 + g*8 + j%8: its keep bit depends only
+            // Register j holds key (j/4)*8 + g*4 + j%4: its keep bit depends only
             // on the lane half g, so the select's lane mask is built on the
             // scalar unit (no per-lane bit tests).
             const uint32_t b = bits_cur[rr];
     #pragma unroll
             for (int j = 0; j < 16; ++j) {
-              const int k0 = (j >> 3) * 16 + (j & 7);
+              const int k0 = (j >> 2) * 8 + (j & 3);
               const uint64_t lanes = (((b >> k0) & 1u) ? 0x00000000ffffffffull : 0ull) |
-                                     (((b >> (k0 + 8)) & 1u) ? 0xffffffff00000000ull : 0ull);
+                                     (((b >> (k0 + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
               S[j] = keep_or_neg_inf(S[j], lanes);
             }
           }
@@ -499,15 +499,21 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     for (int qq = 0; qq < QW; ++qq) {
       const float ltot = l_run[rr][qq] + __shfl_xor(l_run[rr][qq], 32, 64);
       const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-      const int qpos = min((qb0 + qq) * 32 + lq, P - 1);
-      const f16* gp = g_ws + ((int64_t)rows_c[rr] * P + qpos) * HD + h * 32;
+      // gate in the layout of q: its chunk t holds the gates of O registers
+      // 8t..8t+7 (channels slot_x(t, g, 0..7)) of this lane
+      const int64_t rh = (int64_t)rows_c[rr] * H + h;
+      const f16* gp = g_ws + qkv_chunk(rh, nkb, min(qb0 + qq, nkb - 1), 0) + lane * 8;
+      const f16x8 g0 = ld16(gp), g1 = ld16(gp + 512);
       f16* dst = o_lds + ((qgrp * QW + qq) * 32 + lq) * OP + h * 32;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const f16x4 gv = *reinterpret_cast<const f16x4*>(gp + jj * 8 + g * 4);
+      for (int jj = 0; jj < 4; ++jj) {   // O register jj*4+e holds channel jj*8 + g*4 + e
         f16x4 ov;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = f2h_sat(O[rr][qq][jj * 4 + e] * inv * (float)gv[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int j = jj * 4 + e;
+          const float gv = (float)(j < 8 ? g0[j] : g1[j - 8]);
+          ov[e] = f2h_sat(O[rr][qq][j] * inv * gv);
+        }
         st8(dst + jj * 8 + g * 4, ov);
       }
     }

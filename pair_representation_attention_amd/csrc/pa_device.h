@@ -38,6 +38,7 @@ __device__ __forceinline__ bf16x8 ld16(const bf16* p) { return *reinterpret_cast
 __device__ __forceinline__ f16x8 ld16(const f16* p) { return *reinterpret_cast<const f16x8*>(p); }
 __device__ __forceinline__ void st8(bf16* p, const bf16x4& v) { *reinterpret_cast<bf16x4*>(p) = v; }
 __device__ __forceinline__ void st8(f16* p, const f16x4& v) { *reinterpret_cast<f16x4*>(p) = v; }
+__device__ __forceinline__ void st16(f16* p, const f16x8& v) { *reinterpret_cast<f16x8*>(p) = v; }
 
 __device__ __forceinline__ float bf2f(bf16 v) { return (float)v; }
 __device__ __forceinline__ bf16 f2bf(float v) { return (bf16)v; }   // round to nearest even
@@ -52,29 +53,38 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // register image of one MFMA operand for a wave (lane l owns bytes l*16..+16),
 // so a wave copies a chunk with one contiguous 1 KB load.
 //   rh = row * H + head;  nb = padded positions / 32
-//   q: chunk (rh, pos/32, d/16): lane (pos%32) + 32*((d/8)%2), half d%8
-//   k: same with lane pi(pos%32), pi = swap of bits 2 and 3 (the key order
-//      that makes the S^T accumulator the K-slot order of the P operand)
-//   v: chunk (rh, pos/32, (pos/16)%2): lane d + 32*((pos/8)%2), half pos%8
-//   bias (fp16, the S^T accumulator image): chunk (h, q/32, k/32, u):
-//      lane (q%32) + 32*g, half s, where for kk = k%32: u = kk/16,
-//      g = (kk/8)%2, s = kk%8 -- accumulator register u*8+s of that lane
+// Along the contraction index x of an operand (head channel d for q, k and
+// the gate; key for v and the bias), x = 16t + 8*(e/4) + 4*hg + e%4 sits in
+// chunk t, lane half hg, half-word e.  This is the order in which a 32x32
+// accumulator holds its rows (register 8t+e of lane half hg is row
+// (2t + e/4)*8 + 4*hg + e%4), so
+//   * the projection's accumulators, read in register order, are whole
+//     16-byte lane slots (each chunk is written as one contiguous 1 KB), and
+//   * with keys in natural order in K, the S^T accumulator of Q.K^T is
+//     already the K-slot order of the P operand of P.V.
+//   q, k, gate: chunk (rh, pos/32, t(d)):   lane (pos%32) + 32*hg(d),  half e(d)
+//   v:          chunk (rh, pos/32, t(pos%32)): lane d + 32*hg(pos%32), half e(pos%32)
+//   bias (fp16, the S^T accumulator image): chunk (h, q/32, k/32, t(k%32)):
+//               lane (q%32) + 32*hg(k%32), half e(k%32)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ constexpr int kperm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+__device__ __forceinline__ constexpr int slot_t(int x) { return (x >> 4) & 1; }
+__device__ __forceinline__ constexpr int slot_hg(int x) { return (x >> 2) & 1; }
+__device__ __forceinline__ constexpr int slot_e(int x) { return (((x >> 3) & 1) << 2) | (x & 3); }
+// the index x held by half-word e of lane half hg in chunk t
+__device__ __forceinline__ constexpr int slot_x(int t, int hg, int e) { return 16 * t + 8 * (e >> 2) + 4 * hg + (e & 3); }
 
 __device__ __forceinline__ int64_t q_off(int64_t rh, int nb, int pos, int d) {
-  return ((((rh * nb + (pos >> 5)) * 2 + (d >> 4)) * 64 + (pos & 31) + 32 * ((d >> 3) & 1)) << 3) + (d & 7);
+  return ((((rh * nb + (pos >> 5)) * 2 + slot_t(d)) * 64 + (pos & 31) + 32 * slot_hg(d)) << 3) + slot_e(d);
 }
-__device__ __forceinline__ int64_t k_off(int64_t rh, int nb, int pos, int d) {
-  return ((((rh * nb + (pos >> 5)) * 2 + (d >> 4)) * 64 + kperm(pos & 31) + 32 * ((d >> 3) & 1)) << 3) + (d & 7);
-}
+__device__ __forceinline__ int64_t k_off(int64_t rh, int nb, int pos, int d) { return q_off(rh, nb, pos, d); }
 __device__ __forceinline__ int64_t v_off(int64_t rh, int nb, int pos, int d) {
-  return ((((rh * nb + (pos >> 5)) * 2 + ((pos >> 4) & 1)) * 64 + d + 32 * ((pos >> 3) & 1)) << 3) + (pos & 7);
+  const int x = pos & 31;
+  return ((((rh * nb + (pos >> 5)) * 2 + slot_t(x)) * 64 + d + 32 * slot_hg(x)) << 3) + slot_e(x);
 }
 __device__ __forceinline__ int64_t b16_off(int h, int nb, int q, int k) {
-  const int kk = k & 31;
-  return (((((int64_t)h * nb + (q >> 5)) * nb + (k >> 5)) * 2 + (kk >> 4)) * 64 + (q & 31) + 32 * ((kk >> 3) & 1)) * 8 +
-         (kk & 7);
+  const int x = k & 31;
+  return (((((int64_t)h * nb + (q >> 5)) * nb + (k >> 5)) * 2 + slot_t(x)) * 64 + (q & 31) + 32 * slot_hg(x)) * 8 +
+         slot_e(x);
 }
 // start of chunk `c` of block (a, b): element offsets for the 16-byte-per-lane reads
 __device__ __forceinline__ int64_t qkv_chunk(int64_t rh, int nb, int blk, int c) { return ((rh * nb + blk) * 2 + c) * 512; }

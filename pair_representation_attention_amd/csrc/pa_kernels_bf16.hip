@@ -18,7 +18,7 @@
 // Workspace (Pp = P rounded up to 32; padded positions hold zeros); q, k, v
 // and the bias use the operand-ordered layouts of pa_device.h:
 //   q, k, v  nrows*H*Pp*32 fp16 (q scaled by log2(e)/sqrt(d))
-//   g        [nrows][P][H*32] fp16, sigmoid already applied
+//   g        nrows*H*Pp*32 fp16 in the layout of q, sigmoid already applied
 //   bias     H*Pp*Pp fp16, log2 units (natural bias * log2(e)), zero padding
 #include "pa_device.h"
 
@@ -229,52 +229,55 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
       for (int e = 0; e < 8; ++e) X[t][e] = f2h_sat((bf2f(raw[t][e]) - mean) * rstd);
 
     // ---- q | k | v | g column blocks ----
+    // Register 8t+e of lane half g holds accumulator row slot_x(t, g, e), so
+    // registers 8t..8t+7 are exactly this lane's 16-byte slot of chunk t of
+    // the operand image: every chunk is written as one contiguous 1 KB store.
 #pragma unroll 2
     for (int b = 0; b < SH::NBLK; ++b) {
       const int col = col0 + b * 32;
       const int tensor = col / HD;            // 0 q, 1 k, 2 v, 3 g
       const int hcol = col - tensor * HD;     // first column within the tensor
       const int64_t rh = (int64_t)r * H + hcol / 32;
+      const int64_t chunk0 = (rh * nb + (p0 >> 5)) * 2;   // chunk of (rh, position block), t = 0
       const f16* wop = w_lds + (b * KS) * 512 + lane * 8;
       const float* cbk = cb + b * 32;
       f32x16 acc = {};
-      if (tensor == 2) {
+      if (tensor == 2) {                      // v = X W: rows = positions, lane = channel lq
 #pragma unroll
         for (int t = 0; t < KS; ++t) acc = mfma32(X[t], *reinterpret_cast<const f16x8*>(wop + t * 512), acc);
         const float c = cbk[lq];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {      // lane = channel lq; registers = 4 runs of 4 positions
-          const int pp = p0 + jj * 8 + g * 4;
-          f16x4 o;
+        for (int t = 0; t < 2; ++t) {
+          f16x8 o;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = pp + e < P ? f2h_sat(acc[jj * 4 + e] + c) : f2h(0.0f);
-          st8(v_ws + v_off(rh, nb, pp, lq), o);
+          for (int e = 0; e < 8; ++e)
+            o[e] = p0 + slot_x(t, g, e) < P ? f2h_sat(acc[8 * t + e] + c) : f2h(0.0f);
+          st16(v_ws + (chunk0 + t) * 512 + lane * 8, o);
         }
-      } else {
+      } else {                                // out^T = W^T X^T: rows = channels, lane = position
 #pragma unroll
         for (int t = 0; t < KS; ++t) acc = mfma32(*reinterpret_cast<const f16x8*>(wop + t * 512), X[t], acc);
-        if (tensor <= 1) {                    // lane = position; registers = 4 runs of 4 channels
-          const float sc = valid ? (tensor == 0 ? q_scale : 1.0f) : 0.0f;
-          f16* base = tensor == 0 ? q_ws : k_ws;
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int d0 = jj * 8 + g * 4;
-            const f32x4 c = *reinterpret_cast<const f32x4*>(cbk + d0);
-            f16x4 o;
+        for (int t = 0; t < 2; ++t) {
+          // channels slot_x(t, g, 0..7): two runs of four
+          const f32x4 c0 = *reinterpret_cast<const f32x4*>(cbk + 16 * t + 4 * g);
+          const f32x4 c1 = *reinterpret_cast<const f32x4*>(cbk + 16 * t + 8 + 4 * g);
+          f16x8 o;
+          if (tensor <= 1) {
+            const float sc = valid ? (tensor == 0 ? q_scale : 1.0f) : 0.0f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = f2h_sat((acc[jj * 4 + e] + c[e]) * sc);
-            st8(base + (tensor == 0 ? q_off(rh, nb, p, d0) : k_off(rh, nb, p, d0)), o);
-          }
-        } else if (valid) {                   // gate: sigmoid, natural layout [row][position][HD]
-          f16* dst = g_ws + ((int64_t)r * P + p) * HD + hcol;
+            for (int e = 0; e < 4; ++e) {
+              o[e] = f2h_sat((acc[8 * t + e] + c0[e]) * sc);
+              o[4 + e] = f2h_sat((acc[8 * t + 4 + e] + c1[e]) * sc);
+            }
+            st16((tensor == 0 ? q_ws : k_ws) + (chunk0 + t) * 512 + lane * 8, o);
+          } else {                            // gate: sigmoid, same layout as q
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int d0 = jj * 8 + g * 4;
-            const f32x4 c = *reinterpret_cast<const f32x4*>(cbk + d0);
-            f16x4 o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = f2h(1.0f / (1.0f + __expf(-(acc[jj * 4 + e] + c[e]))));
-            st8(dst + d0, o);
+            for (int e = 0; e < 4; ++e) {
+              o[e] = f2h(1.0f / (1.0f + __expf(-(acc[8 * t + e] + c0[e]))));
+              o[4 + e] = f2h(1.0f / (1.0f + __expf(-(acc[8 * t + 4 + e] + c1[e]))));
+            }
+            st16(g_ws + (chunk0 + t) * 512 + lane * 8, o);
           }
         }
       }

@@ -62,7 +62,7 @@ Layout make_layout(int64_t nrows, int64_t P, int64_t c_in, int64_t c_out, int64_
     L.q = take((size_t)nrows * H * Pp * 32 * 2);
     L.k = take((size_t)nrows * H * Pp * 32 * 2);
     L.v = take((size_t)nrows * H * 32 * Pp * 2);
-    L.g = take((size_t)nrows * P * hd * 2);
+    L.g = take((size_t)nrows * H * Pp * 32 * 2);   // gate in the layout of q
     // the attention reads the bias as fp16 in operand order, Pp x Pp, log2
     // units; a caller-provided bias (row block) is converted into it as well
     L.bias = take((size_t)H * Pp * Pp * 2);
