@@ -15,28 +15,23 @@
 //   per key block and unit (S^T is keys x queries, log2 units):
 //     S^T = K Q^T + C      two MFMAs; C = the fp16 bias tile widened to fp32
 //                          by VALU converts (shared by both rows)
+//     p = exp2(S - m)      rounded to fp16 (the P operand); l += sum of p
 //     O^T += V^T P^T       two MFMAs
-//   Softmax without a per-block maximum: each (row, query) keeps a shift m
-//   chosen on its first key block with a kept key (m = 0 while that block's
-//   maximum lies in [-8, 8], else the maximum), and p = exp2(S - m).  With
-//   m = 0 for the whole row -- the common case -- the fast path is just
-//   exp2, sum and convert; the subtract runs only for shifted rows, the
-//   select only for blocks holding masked keys.  A lane whose block sum
-//   exceeds 2^15 raises m to the block maximum (O and l rescaled), which keeps
-//   every p below the fp16 limit.  Exact in real arithmetic for any shift.
-//   The logits of the next unit are issued to the matrix cores before the
-//   softmax of the current one runs on the VALU.
-// Memory path: K/V tiles of the workgroup's rows (each shared by the waves of
-// that head) and the bias tiles of its query blocks are copied per key block
-// with global_load_lds_dwordx4 into a double-buffered LDS stage.  The
-// workspace is stored in MFMA operand order (pa_device.h), so every copy is a
-// contiguous 1 KB read and every LDS read a conflict-free ds_read_b128.
+//   Softmax shift m per (row, query): a first sweep uses m = 0 with no
+//   per-unit test; afterwards every l must be finite (no fp16 weight
+//   overflowed) and at least 1 on rows with a kept key (the largest weights
+//   are normal fp16 numbers).  Where that fails anywhere in the workgroup,
+//   it sweeps again choosing m on the row's first block with a kept key and
+//   raising it (O and l rescaled) whenever a block sum passes 2^15.  Exact in
+//   real arithmetic for any shift.
+// Memory path: K/V tiles of the workgroup's rows (each shared by the two
+// waves of a head) and the bias tiles of its query blocks are copied per key
+// block with global_load_lds_dwordx4 into LDS rings (K/V three stages deep,
+// bias two).  The workspace is stored in MFMA operand order (pa_device.h):
+// every copy is a contiguous 1 KB read, every LDS read a conflict-free
+// ds_read_b128, and the S^T accumulator (rows = keys in natural order) is
+// already the K-slot order of the P operand.
 // Bytes moved per unit: 4 KB K/V / 4 query blocks + 2 KB bias / 2 rows.
-// Register maps (32x32 accumulator: column = lane % 32, register j of half g
-// = row (j/4)*8 + g*4 + j%4): keys enter the S^T MFMA in the order pi(m)
-// (bits 2 and 3 of m swapped), which makes S^T register j hold key
-// (j/8)*16 + g*8 + j%8 -- exactly the K-slot order of the P operand, and the
-// order in which the bias tile is stored.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -66,6 +61,17 @@ __device__ __forceinline__ void g2lds16_ring(const void* gsrc, char* lds_base) {
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %0, off" ::"v"(gsrc),
       "s"(lds_addr)
+      : "memory");
+}
+
+// The same copy from a wave-uniform 64-bit base in scalar registers plus a
+// 32-bit per-lane byte offset (no vector address arithmetic per copy).
+__device__ __forceinline__ void g2lds16_sbase(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1" ::"v"(voff),
+      "s"(sbase), "s"(lds_addr)
       : "memory");
 }
 
@@ -155,8 +161,6 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   using SH = AttnShape<H>;
   constexpr int HD = H * 32;
   constexpr int QW = SH::QW, RW = SH::RWG;
-  constexpr int OP = HD + 8;                 // epilogue o tile pitch (fp16 elements)
-  static_assert(SH::QWG * 32 * OP * 2 <= SH::LDS_KV, "epilogue tile fits");
   __shared__ __attribute__((aligned(1024))) char kv_lds[SH::LDS_KV];
   __shared__ __attribute__((aligned(1024))) char b_lds[SH::LDS_B];
 
@@ -278,15 +282,42 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
   };
 
-  // Q has landed before any copy is in flight: the compiler's waits for it
-  // would otherwise sit inside the loop and drain the copies too.  (The
-  // empty asm statements consume Q here, so its loads cannot sink below.)
+  // Q has landed before the generic sweep issues any copy: the compiler's
+  // waits for it would otherwise sit inside the loop and drain the copies
+  // too.  (The empty asm statements consume Q, so its loads cannot sink
+  // below.)
+  auto wait_q = [&]() {
 #pragma unroll
-  for (int rr = 0; rr < RW; ++rr)
+    for (int rr = 0; rr < RW; ++rr)
 #pragma unroll
-    for (int qq = 0; qq < QW; ++qq) asm volatile("" ::"v"(Q[rr][qq][0]), "v"(Q[rr][qq][1]));
-  wait_vmcnt<0>();
+      for (int qq = 0; qq < QW; ++qq) asm volatile("" ::"v"(Q[rr][qq][0]), "v"(Q[rr][qq][1]));
+    wait_vmcnt<0>();
+  };
   bool row_has_key[RW];   // wave-uniform: some block of the row keeps a key
+
+  // Epilogue operands: the gate tiles (layout of q; loaded during the last
+  // key block of the pipelined sweep, so that their latency hides behind it)
+  // and the W_o^T rows of this wave's output channel block (loaded before
+  // the gated o tiles are formed).
+  constexpr int CBN = C_OUT / 32;
+  constexpr int KO = HD / 16;
+  const int cb_w = wave % CBN;
+  f16x8 Gt[RW][QW][2], Wo[KO];
+  auto load_wo = [&]() {
+#pragma unroll
+    for (int t = 0; t < KO; ++t) Wo[t] = ld16(woT + (int64_t)(cb_w * 32 + lq) * HD + t * 16 + g * 8);
+  };
+  auto load_epi = [&]() {
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+      for (int qq = 0; qq < QW; ++qq) {
+        const int64_t rh = (int64_t)rows_c[rr] * H + h;
+        const f16* gp = g_ws + qkv_chunk(rh, nkb, min(qb0 + qq, nkb - 1), 0) + lane * 8;
+        Gt[rr][qq][0] = ld16(gp);
+        Gt[rr][qq][1] = ld16(gp + 512);
+      }
+  };
 
   // One sweep over all key blocks.
   //   FAST: p = exp2(S) with no shift and no per-unit test, so the units of
@@ -298,6 +329,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   //         kept key and raised whenever a block sum passes 2^15.
   auto sweep = [&](auto fastc) {
     constexpr bool FAST = decltype(fastc)::value;
+    wait_q();
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
       mset[rr] = FAST;
@@ -456,8 +488,241 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
   };
 
-  sweep(std::integral_constant<bool, true>{});
-  wait_vm0();   // copies past the end have landed before the LDS is reused
+  // Software-pipelined form of the fast sweep for blocks without masked
+  // keys (no mask, P a multiple of 32; H = 4, four units per wave and key
+  // block).  Unit order within a block: (row 0, qb 0), (1, 0), (0, 1),
+  // (1, 1).  Stream s of a block runs the softmax of unit s on the VALU and
+  // issues, between its groups of exp2, the logits of unit s+1 and the P.V
+  // product of unit s, so that the matrix cores work while the softmax runs
+  // and no exp2 waits for the logits it reads.  The barrier that publishes
+  // key block kb+1 sits at the start of stream 2 of block kb: the LDS reads
+  // of the next K and bias tiles run under the softmax of units 2 and 3, and
+  // the logits of the next block's first unit are issued in stream 3.
+  //
+  // Staging (per wave; NCW K/V and NCB bias copies per block):
+  //   stream 0 of kb: K/V copies 2..3 of block kb+2
+  //   stream 2 of kb: wait until at most NCW copies are in flight (bias
+  //                   kb+1 and K/V kb+1 landed), barrier, bias copies of
+  //                   block kb+2 (its stage held block kb, read before it)
+  //   stream 3 of kb: K/V copies 0..1 of block kb+3 (stage of block kb,
+  //                   already in registers)
+  // Copies for blocks past the end are clamped dummies, so that every
+  // counted wait sees the same number of copies behind it; the last block
+  // issues none.  Each copy is addressed as a wave-uniform base (advanced
+  // per block on the scalar unit) plus a fixed per-lane offset.
+  //
+  // Wave priority falls from 3 to 0 over the four streams of a block.  The
+  // two waves sharing a SIMD are otherwise issued oldest first: the older
+  // one finishes its block early and idles at the barrier while the younger
+  // one runs the rest alone; with the ladder the wave that is behind in the
+  // block wins the issue arbitration, and both reach the barrier together.
+  auto sweep_pipe = [&]() {
+   if constexpr (QW == 2 && RW == 2 && NCW == 4) {
+    using T = std::integral_constant<bool, true>;
+    using F = std::integral_constant<bool, false>;
+    float l2[RW][QW];   // second partial row sum (keys 16..31 of each unit's lane half)
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) {
+      row_has_key[rr] = true;
+#pragma unroll
+      for (int qq = 0; qq < QW; ++qq) {
+        O[rr][qq] = f32x16{};
+        m_sh[rr][qq] = 0.0f;
+        l_run[rr][qq] = 0.0f;
+        l2[rr][qq] = 0.0f;
+      }
+    }
+    // copy sources: one wave-uniform base per ring, per-lane byte offsets
+    const f16* kv_base = kv_src[0];
+    const f16* b_base = b_src[0];
+    uint32_t kv_voff[NCW], b_voff[NCB];
+#pragma unroll
+    for (int j = 0; j < NCW; ++j) kv_voff[j] = (uint32_t)((kv_src[j] - kv_base) * 2) + lane * 16;
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) b_voff[j] = (uint32_t)((b_src[j] - b_base) * 2) + lane * 16;
+    auto copy_kv = [&](int kb, int j0, int j1) {
+      const int kbc = min(kb, nkb - 1);
+      const f16* src = kv_base + (int64_t)kbc * 1024;
+      const uint32_t base = (uint32_t)(uintptr_t)(lds_void_t*)(kv_lds + (kb % SH::NKV) * SH::KV_STAGE);
+#pragma unroll
+      for (int j = j0; j < j1; ++j) g2lds16_sbase(src, kv_voff[j], base + kv_off[j]);
+    };
+    auto copy_b = [&](int kb) {
+      const int kbc = min(kb, nkb - 1);
+      const f16* src = b_base + (int64_t)kbc * 1024;
+      const uint32_t base = (uint32_t)(uintptr_t)(lds_void_t*)(b_lds + (kb & 1) * SH::B_STAGE);
+#pragma unroll
+      for (int j = 0; j < NCB; ++j) g2lds16_sbase(src, b_voff[j], base + b_off[j]);
+    };
+    auto kv_tile = [&](int kb, int rr) -> const char* {
+      return kv_lds + (kb % SH::NKV) * SH::KV_STAGE + (rr * H + h) * SH::KV_TILE + lane * 16;
+    };
+    auto b_tile = [&](int kb, int qq) -> const char* {
+      return b_lds + (kb & 1) * SH::B_STAGE + ((qgrp * QW + qq) * H + h) * SH::B_TILE + lane * 16;
+    };
+    auto cvt_bias = [&](const f16x8* b) -> f32x16 {
+      f32x16 c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        c[e] = (float)b[0][e];
+        c[8 + e] = (float)b[1][e];
+      }
+      return c;
+    };
+    auto barrier = [&]() {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    // softmax of S (one unit) with the next unit's logits (NEXT) and this
+    // unit's P.V product issued between its exp2 groups; the row sums
+    // accumulate in la (keys of chunk 0) and lb (chunk 1)
+    auto stream = [&](auto nextc, const f32x16& S, f32x16& Sn, const f16x8* kn, const f16x8* qn, const f32x16& cn,
+                      const f16x8* v, f32x16& o, float& la, float& lb) {
+      constexpr bool NEXT = decltype(nextc)::value;
+      const f16x2 one = {(f16)1.0f, (f16)1.0f};
+      float e[16];
+      f16x8 p0, p1;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) e[j] = fast_exp2(S[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NEXT) Sn = mfma32(kn[0], qn[0], cn);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 4; j < 8; ++j) e[j] = fast_exp2(S[j]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p0[j] = f2h(e[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NEXT) Sn = mfma32(kn[1], qn[1], Sn);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 8; j < 12; ++j) e[j] = fast_exp2(S[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      o = mfma32(v[0], p0, o);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 12; j < 16; ++j) e[j] = fast_exp2(S[j]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p1[j] = f2h(e[8 + j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) la = __builtin_amdgcn_fdot2(f16x2{p0[2 * j], p0[2 * j + 1]}, one, la, false);
+      __builtin_amdgcn_sched_barrier(0);
+      o = mfma32(v[1], p1, o);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lb = __builtin_amdgcn_fdot2(f16x2{p1[2 * j], p1[2 * j + 1]}, one, lb, false);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    struct Regs {
+      f16x8 K[RW][2], V[RW][2], B1[2];   // K and V tiles of both rows, bias tile of query block 1
+    };
+    Regs ra, rb;
+    f32x16 S_pipe, C_pipe;   // logits of the unit the next stream runs; bias accumulator of its query block
+
+    // prologue: stages of blocks 0 and 1 and Q land together (one latency
+    // instead of two), barrier, block 0 in registers
+    copy_b(0);
+    copy_kv(0, 0, NCW);
+    copy_kv(1, 0, NCW);
+    wait_q();
+    barrier();
+    {
+      f16x8 B0[2];
+#pragma unroll
+      for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) ra.K[rr][c] = lds_f16x8(kv_tile(0, rr) + c * 1024);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) B0[c] = lds_f16x8(b_tile(0, 0) + c * 1024);
+      copy_b(1);
+      copy_kv(2, 0, 2);
+#pragma unroll
+      for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) ra.V[rr][c] = lds_f16x8(kv_tile(0, rr) + 2048 + c * 1024);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) ra.B1[c] = lds_f16x8(b_tile(0, 1) + c * 1024);
+      C_pipe = cvt_bias(B0);
+      S_pipe = mfma32(ra.K[0][1], Q[0][0][1], mfma32(ra.K[0][0], Q[0][0][0], C_pipe));
+    }
+    // block kb from the registers in `cur`; the next block's land in `nx`
+    auto block = [&](int kb, auto morec, Regs& cur, Regs& nx) {
+      constexpr bool MORE = decltype(morec)::value;
+      f32x16 Sn;
+      // stream 0: unit (0, 0); next (1, 0)
+      __builtin_amdgcn_s_setprio(3);
+      if constexpr (MORE) copy_kv(kb + 2, 2, 4);
+      else load_epi();
+      stream(T{}, S_pipe, Sn, cur.K[1], Q[1][0], C_pipe, cur.V[0], O[0][0], l_run[0][0], l2[0][0]);
+      S_pipe = Sn;
+      C_pipe = cvt_bias(cur.B1);
+      // stream 1: unit (1, 0); next (0, 1)
+      __builtin_amdgcn_s_setprio(2);
+      stream(T{}, S_pipe, Sn, cur.K[0], Q[0][1], C_pipe, cur.V[1], O[1][0], l_run[1][0], l2[1][0]);
+      S_pipe = Sn;
+      // stream 2: unit (0, 1); next (1, 1); block kb+1 published
+      __builtin_amdgcn_s_setprio(1);
+      f16x8 Bn0[2];
+      f32x16 Cn;
+      if constexpr (MORE) {
+        wait_vmcnt<NCW>();
+        barrier();
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) nx.K[rr][c] = lds_f16x8(kv_tile(kb + 1, rr) + c * 1024);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) Bn0[c] = lds_f16x8(b_tile(kb + 1, 0) + c * 1024);
+        copy_b(kb + 2);
+      }
+      stream(T{}, S_pipe, Sn, cur.K[1], Q[1][1], C_pipe, cur.V[0], O[0][1], l_run[0][1], l2[0][1]);
+      S_pipe = Sn;
+      if constexpr (MORE) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) nx.V[0][c] = lds_f16x8(kv_tile(kb + 1, 0) + 2048 + c * 1024);
+        Cn = cvt_bias(Bn0);
+      }
+      // stream 3: unit (1, 1); next = unit (0, 0) of block kb+1
+      __builtin_amdgcn_s_setprio(0);
+      stream(morec, S_pipe, Sn, nx.K[0], Q[0][0], Cn, cur.V[1], O[1][1], l_run[1][1], l2[1][1]);
+      if constexpr (MORE) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          nx.V[1][c] = lds_f16x8(kv_tile(kb + 1, 1) + 2048 + c * 1024);
+          nx.B1[c] = lds_f16x8(b_tile(kb + 1, 1) + c * 1024);
+        }
+        copy_kv(kb + 3, 0, 2);
+        C_pipe = Cn;
+        S_pipe = Sn;
+      }
+    };
+    for (int kb = 0; kb + 1 < nkb; ++kb) {
+      block(kb, T{}, ra, rb);
+      ra = rb;
+    }
+    block(nkb - 1, F{}, ra, rb);
+    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+      for (int qq = 0; qq < QW; ++qq) l_run[rr][qq] += l2[rr][qq];
+   }
+  };
+
+  bool epi_loaded = false;
+  if constexpr (H == 4 && !HAS_MASK) {
+    if (P == Pp) {
+      sweep_pipe();
+      epi_loaded = true;
+    } else {
+      sweep(std::integral_constant<bool, true>{});
+    }
+  } else {
+    sweep(std::integral_constant<bool, true>{});
+  }
+  if (!epi_loaded) load_epi();
+  wait_vm0();   // this wave's copies (dummies past the end included) have landed
   bool bad = false;
 #pragma unroll
   for (int rr = 0; rr < RW; ++rr)
@@ -466,61 +731,62 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       const float lt = l_run[rr][qq] + __shfl_xor(l_run[rr][qq], 32, 64);
       bad = bad || !(lt < __builtin_inff()) || (row_has_key[rr] && lt < 1.0f);
     }
-  // workgroup-wide "any wave bad", through the (now idle) K/V stage memory
+  // Workgroup-wide "any wave bad", through the last words of the bias ring.
+  // After the first barrier every copy of every wave has landed and no wave
+  // reads the rings any more; a rerun writes that stage only after the first
+  // barrier of its own loop, which every wave reaches after reading the flags.
   {
-    int* flag = reinterpret_cast<int*>(kv_lds);
+    int* flag = reinterpret_cast<int*>(b_lds + SH::LDS_B - 8 * sizeof(int));
     const bool wbad = __ballot(bad) != 0;
-    __syncthreads();   // every wave is done with the ring
+    __syncthreads();
     if (lane == 0) flag[wave] = wbad ? 1 : 0;
     __syncthreads();
     int any = 0;
 #pragma unroll
     for (int w = 0; w < 8; ++w) any |= flag[w];
-    __syncthreads();   // flags read before the LDS is written again
-    if (any) sweep(std::integral_constant<bool, false>{});
+    if (any) {
+      sweep(std::integral_constant<bool, false>{});
+      wait_vm0();
+      __syncthreads();   // the rings are idle before the o tiles overwrite them
+      load_epi();   // (reloaded, so that the gate tiles are not live across the rerun)
+    }
   }
+  load_wo();
 
-  // ---- epilogue: normalise, gate, output projection ----
-  wait_vm0();
-  __syncthreads();   // LDS is reused for the gated o tiles
-  constexpr int CBN = C_OUT / 32;
+  // ---- epilogue: normalise, gate, output projection (both rows at once) ----
+  constexpr int OP = HD + 8;                 // o tile pitch (fp16 elements)
   constexpr int NBLK = SH::QWG * CBN;        // 32x32 output blocks per row
   static_assert(8 % CBN == 0, "a wave keeps one output channel block");
-  constexpr int KO = HD / 16;
-  const int cb_w = wave % CBN;
-  f16x8 Wo[KO];
-#pragma unroll
-  for (int t = 0; t < KO; ++t) Wo[t] = ld16(woT + (int64_t)(cb_w * 32 + lq) * HD + t * 16 + g * 8);
+  static_assert(RW * SH::QWG * 32 * OP * 2 <= SH::LDS_KV, "o tiles of both rows fit the K/V ring");
   f16* o_lds = reinterpret_cast<f16*>(kv_lds);
-
 #pragma unroll
   for (int rr = 0; rr < RW; ++rr) {
 #pragma unroll
     for (int qq = 0; qq < QW; ++qq) {
       const float ltot = l_run[rr][qq] + __shfl_xor(l_run[rr][qq], 32, 64);
       const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-      // gate in the layout of q: its chunk t holds the gates of O registers
-      // 8t..8t+7 (channels slot_x(t, g, 0..7)) of this lane
-      const int64_t rh = (int64_t)rows_c[rr] * H + h;
-      const f16* gp = g_ws + qkv_chunk(rh, nkb, min(qb0 + qq, nkb - 1), 0) + lane * 8;
-      const f16x8 g0 = ld16(gp), g1 = ld16(gp + 512);
-      f16* dst = o_lds + ((qgrp * QW + qq) * 32 + lq) * OP + h * 32;
+      // gate chunk t holds the gates of O registers 8t..8t+7 (channels
+      // slot_x(t, g, 0..7)) of this lane
+      f16* dst = o_lds + ((rr * SH::QWG + qgrp * QW + qq) * 32 + lq) * OP + h * 32;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {   // O register jj*4+e holds channel jj*8 + g*4 + e
         f16x4 ov;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = jj * 4 + e;
-          const float gv = (float)(j < 8 ? g0[j] : g1[j - 8]);
+          const float gv = (float)(j < 8 ? Gt[rr][qq][0][j] : Gt[rr][qq][1][j - 8]);
           ov[e] = f2h_sat(O[rr][qq][j] * inv * gv);
         }
         st8(dst + jj * 8 + g * 4, ov);
       }
     }
-    __syncthreads();
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rr = 0; rr < RW; ++rr) {
     for (int blk = wave; blk < NBLK; blk += 8) {
       const int qbl = blk / CBN;             // query block within the workgroup
-      const f16* src = o_lds + (qbl * 32 + lq) * OP + g * 8;
+      const f16* src = o_lds + ((rr * SH::QWG + qbl) * 32 + lq) * OP + g * 8;
       f32x16 acc = {};
 #pragma unroll
       for (int t = 0; t < KO; ++t) acc = mfma32(Wo[t], lds_f16x8((const char*)(src + t * 16)), acc);
@@ -541,7 +807,6 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         }
       }
     }
-    __syncthreads();
   }
 }
 
