@@ -782,29 +782,55 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
   }
   __syncthreads();
+  // bf16 store of one 32x32 output block (+ b_o) at the caller's strides
+  auto store_block = [&](int rr, int qbl, const f32x16& acc) {
+    const int r = r0 + rr;
+    const int q = (qb0_wg + qbl) * 32 + lq;
+    if (r < nrows && q < P) {
+      bf16* o = out + (int64_t)r * os_r + (int64_t)q * os_p + cb_w * 32;
 #pragma unroll
-  for (int rr = 0; rr < RW; ++rr) {
-    for (int blk = wave; blk < NBLK; blk += 8) {
-      const int qbl = blk / CBN;             // query block within the workgroup
-      const f16* src = o_lds + ((rr * SH::QWG + qbl) * 32 + lq) * OP + g * 8;
-      f32x16 acc = {};
+      for (int jj = 0; jj < 4; ++jj) {
+        bf16x4 ov;
 #pragma unroll
-      for (int t = 0; t < KO; ++t) acc = mfma32(Wo[t], lds_f16x8((const char*)(src + t * 16)), acc);
-      const int r = r0 + rr;
-      const int q = (qb0_wg + qbl) * 32 + lq;
-      if (r < nrows && q < P) {
-        bf16* o = out + (int64_t)r * os_r + (int64_t)q * os_p + cb_w * 32;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          bf16x4 ov;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int c = jj * 8 + g * 4 + e;
-            const float bo = b_o != nullptr ? bf2f(b_o[cb_w * 32 + c]) : 0.0f;
-            ov[e] = f2bf(acc[jj * 4 + e] + bo);
-          }
-          st8(o + jj * 8 + g * 4, ov);
+        for (int e = 0; e < 4; ++e) {
+          const int c = jj * 8 + g * 4 + e;
+          const float bo = b_o != nullptr ? bf2f(b_o[cb_w * 32 + c]) : 0.0f;
+          ov[e] = f2bf(acc[jj * 4 + e] + bo);
         }
+        st8(o + jj * 8 + g * 4, ov);
+      }
+    }
+  };
+  if constexpr (NBLK % 8 == 0) {
+    // every wave owns NBLK/8 output blocks of each row: their MFMA chains
+    // are interleaved, so that no MFMA waits for the one before it
+    constexpr int NB = NBLK / 8 * RW;
+    f32x16 acc[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) acc[i] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < KO; ++t)
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int rr = i / (NBLK / 8), qbl = (wave + 8 * (i % (NBLK / 8))) / CBN;
+        const f16* src = o_lds + ((rr * SH::QWG + qbl) * 32 + lq) * OP + g * 8;
+        acc[i] = mfma32(Wo[t], lds_f16x8((const char*)(src + t * 16)), acc[i]);
+      }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int rr = i / (NBLK / 8), qbl = (wave + 8 * (i % (NBLK / 8))) / CBN;
+      store_block(rr, qbl, acc[i]);
+    }
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) {
+      for (int blk = wave; blk < NBLK; blk += 8) {
+        const int qbl = blk / CBN;             // query block within the workgroup
+        const f16* src = o_lds + ((rr * SH::QWG + qbl) * 32 + lq) * OP + g * 8;
+        f32x16 acc = {};
+#pragma unroll
+        for (int t = 0; t < KO; ++t) acc = mfma32(Wo[t], lds_f16x8((const char*)(src + t * 16)), acc);
+        store_block(rr, qbl, acc);
       }
     }
   }
