@@ -31,8 +31,12 @@ def _dev():
 # ----------------------------------------------------------------------------
 # small shapes: full output against the oracle, tails and masks
 # ----------------------------------------------------------------------------
+# I a multiple of 32 without a mask takes the software-pipelined sweep of the
+# bf16 kernel: 32, 64, 96 and 160 give 1, 2, 3 and 5 key blocks (a single
+# final block, one pipelined block, an odd count, several), the others the
+# generic sweep with its tail block.
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("I", [1, 7, 33, 64, 100])
+@pytest.mark.parametrize("I", [1, 7, 32, 33, 64, 96, 100, 160])
 @pytest.mark.parametrize("mask", ["none", "random"])
 def test_tri_small_shapes(dtype, I, mask):
     case = inputs.make_tri_case(I=I, c=128, H=4, d=32, dtype=dtype, mask=mask, seed=100 + I,
