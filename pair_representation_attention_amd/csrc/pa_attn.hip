@@ -38,22 +38,17 @@
 namespace pa {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
-
-// 16 bytes per lane, global -> LDS at lds_base + lane*16 (lds_base wave-uniform)
-__device__ __forceinline__ void g2lds16(const void* gsrc, char* lds_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t*)gsrc, (lds_void_t*)lds_base, 16, 0, 0);
-}
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// The same copy issued from inline asm, for the staging rings.  The
-// compiler tracks every LDS-DMA copy in one slot and would drain all copies
-// in flight before each LDS read; the rings keep their order explicitly
-// instead (a counted wait before the barrier of each key block, a full
-// drain before the LDS is reused).  The copy has no register result and its
-// address operands are read at issue; one wait state separates the M0 write
-// from the copy that reads it.
+// 16 bytes per lane, global -> LDS at lds_base + lane*16 (lds_base
+// wave-uniform), issued from inline asm for the staging rings.  (The
+// compiler tracks every LDS-DMA copy of its own builtin in one slot and would
+// drain all copies in flight before each LDS read; the rings keep their
+// order explicitly instead: a counted wait before the barrier of each key
+// block, a full drain before the LDS is reused.)  The copy has no register
+// result and its address operands are read at issue; one wait state
+// separates the M0 write from the copy that reads it.
 __device__ __forceinline__ void g2lds16_ring(const void* gsrc, char* lds_base) {
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_void_t*)lds_base;
   asm volatile(
@@ -109,20 +104,6 @@ __device__ __forceinline__ float sum16_f16(const f16x8& a, const f16x8& b) {
   s1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(b, b, 6, 7), one, s1, false);
   return s0 + s1;
 }
-
-// Scheduling hint for the unit loop: alternate single MFMAs with groups of
-// VALU instructions, so that dependent MFMAs (each waits for the previous
-// one's result) are separated by softmax work instead of stalling issue.
-#ifndef PA_SCHED_VALU_PER_MFMA
-#define PA_SCHED_VALU_PER_MFMA 6
-#endif
-#define SCHED_INTERLEAVE()                                                  \
-  do {                                                                      \
-    _Pragma("unroll") for (int _i = 0; _i < 7; ++_i) {                      \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    \
-      __builtin_amdgcn_sched_group_barrier(0x002, PA_SCHED_VALU_PER_MFMA, 0); \
-    }                                                                       \
-  } while (0)
 
 template <int H>
 struct AttnShape {
