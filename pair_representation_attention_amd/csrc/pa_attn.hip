@@ -853,6 +853,8 @@ template <int H, int C_OUT, bool HAS_MASK>
 static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
   using SH = AttnShape<H>;
   const int nkb = a.Pp / 32;
+  // the sweeps assume at least one key block and rows to work on
+  if (nkb < 1 || a.Pp != nkb * 32 || a.P < 1 || a.P > a.Pp || a.nrows < 1) return hipErrorInvalidValue;
   const int n_qg = (nkb + SH::QWG - 1) / SH::QWG;
   const int n_rg = (a.nrows + SH::RWG - 1) / SH::RWG;
   const int64_t n = (int64_t)n_qg * n_rg;
