@@ -194,7 +194,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=12, help="oracle sample size (rows, about 1.4 s each)")
+    ap.add_argument("--cpu-rows", type=int, default=24, help="oracle sample size (rows, about 0.35-1.4 s each by host)")
     ap.add_argument("--extra", action="store_true", help="also time MSA row attention and the row block")
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="MIB",
                     help="after timing, run a plain device copy of MIB MiB (counter calibration)")
