@@ -598,7 +598,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     struct Regs {
       f16x8 K[RW][2], V[RW][2], B1[2];   // K and V tiles of both rows, bias tile of query block 1
     };
-    Regs ra, rb;
+    Regs ra;
     f32x16 S_pipe, C_pipe;   // logits of the unit the next stream runs; bias accumulator of its query block
 
     // prologue: stages of blocks 0 and 1 and Q land together (one latency
@@ -628,19 +628,24 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       S_pipe = mfma32(ra.K[0][1], Q[0][0][1], mfma32(ra.K[0][0], Q[0][0][0], C_pipe));
     }
     // block kb from the registers in `cur`; the next block's land in `nx`
-    auto block = [&](int kb, auto morec, Regs& cur, Regs& nx) {
+    // block kb from the registers in r; the next block's tiles are read into
+    // r in place, each once its current value has had its last use (K of
+    // row 0 after the logits of unit 2, K of row 1 after those of unit 3, V
+    // of row 0 after the P.V of unit 2, V of row 1 and the bias tile of
+    // query block 1 after that of unit 3)
+    auto block = [&](int kb, auto morec, Regs& r) {
       constexpr bool MORE = decltype(morec)::value;
       f32x16 Sn;
       // stream 0: unit (0, 0); next (1, 0)
       __builtin_amdgcn_s_setprio(3);
       if constexpr (MORE) copy_kv(kb + 2, 2, 4);
       else load_epi();
-      stream(T{}, S_pipe, Sn, cur.K[1], Q[1][0], C_pipe, cur.V[0], O[0][0], l_run[0][0], l2[0][0]);
+      stream(T{}, S_pipe, Sn, r.K[1], Q[1][0], C_pipe, r.V[0], O[0][0], l_run[0][0], l2[0][0]);
       S_pipe = Sn;
-      C_pipe = cvt_bias(cur.B1);
+      C_pipe = cvt_bias(r.B1);
       // stream 1: unit (1, 0); next (0, 1)
       __builtin_amdgcn_s_setprio(2);
-      stream(T{}, S_pipe, Sn, cur.K[0], Q[0][1], C_pipe, cur.V[1], O[1][0], l_run[1][0], l2[1][0]);
+      stream(T{}, S_pipe, Sn, r.K[0], Q[0][1], C_pipe, r.V[1], O[1][0], l_run[1][0], l2[1][0]);
       S_pipe = Sn;
       // stream 2: unit (0, 1); next (1, 1); block kb+1 published
       __builtin_amdgcn_s_setprio(1);
@@ -650,39 +655,37 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         wait_vmcnt<NCW>();
         barrier();
 #pragma unroll
-        for (int rr = 0; rr < RW; ++rr)
-#pragma unroll
-          for (int c = 0; c < 2; ++c) nx.K[rr][c] = lds_f16x8(kv_tile(kb + 1, rr) + c * 1024);
+        for (int c = 0; c < 2; ++c) r.K[0][c] = lds_f16x8(kv_tile(kb + 1, 0) + c * 1024);
 #pragma unroll
         for (int c = 0; c < 2; ++c) Bn0[c] = lds_f16x8(b_tile(kb + 1, 0) + c * 1024);
         copy_b(kb + 2);
       }
-      stream(T{}, S_pipe, Sn, cur.K[1], Q[1][1], C_pipe, cur.V[0], O[0][1], l_run[0][1], l2[0][1]);
+      stream(T{}, S_pipe, Sn, r.K[1], Q[1][1], C_pipe, r.V[0], O[0][1], l_run[0][1], l2[0][1]);
       S_pipe = Sn;
       if constexpr (MORE) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) nx.V[0][c] = lds_f16x8(kv_tile(kb + 1, 0) + 2048 + c * 1024);
+        for (int c = 0; c < 2; ++c) {
+          r.K[1][c] = lds_f16x8(kv_tile(kb + 1, 1) + c * 1024);
+          r.V[0][c] = lds_f16x8(kv_tile(kb + 1, 0) + 2048 + c * 1024);
+        }
         Cn = cvt_bias(Bn0);
       }
       // stream 3: unit (1, 1); next = unit (0, 0) of block kb+1
       __builtin_amdgcn_s_setprio(0);
-      stream(morec, S_pipe, Sn, nx.K[0], Q[0][0], Cn, cur.V[1], O[1][1], l_run[1][1], l2[1][1]);
+      stream(morec, S_pipe, Sn, r.K[0], Q[0][0], Cn, r.V[1], O[1][1], l_run[1][1], l2[1][1]);
       if constexpr (MORE) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          nx.V[1][c] = lds_f16x8(kv_tile(kb + 1, 1) + 2048 + c * 1024);
-          nx.B1[c] = lds_f16x8(b_tile(kb + 1, 1) + c * 1024);
+          r.V[1][c] = lds_f16x8(kv_tile(kb + 1, 1) + 2048 + c * 1024);
+          r.B1[c] = lds_f16x8(b_tile(kb + 1, 1) + c * 1024);
         }
         copy_kv(kb + 3, 0, 2);
         C_pipe = Cn;
         S_pipe = Sn;
       }
     };
-    for (int kb = 0; kb + 1 < nkb; ++kb) {
-      block(kb, T{}, ra, rb);
-      ra = rb;
-    }
-    block(nkb - 1, F{}, ra, rb);
+    for (int kb = 0; kb + 1 < nkb; ++kb) block(kb, T{}, ra);
+    block(nkb - 1, F{}, ra);
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr)
