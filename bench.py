@@ -376,6 +376,24 @@ def extra_workloads(args, device, inputs, lib, torch, np) -> dict:
     out["msa_bf16_s512_i384"] = {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12, "rows_per_s": cfg["S"] / (ms * 1e-3)}
     del run
     torch.cuda.empty_cache()
+
+    # row block: 512 starting-node rows of Z[4096,4096,128], bias from the whole Z
+    cfg = inputs.CONFIGS["rows_bf16_i4096_r512"]
+    I, R, c, H, d = cfg["I"], cfg["R"], cfg["c"], cfg["H"], cfg["d"]
+    log(f"extra: row block, {R} rows of Z[{I},{I},{c}]")
+    case = inputs.make_rows_case(I=I, R=R, c=c, H=H, d=d, asu=cfg["asu"], noise=cfg["noise"], seed=cfg["seed"])
+    zf = torch.from_numpy(case.zbits.view(np.int16)).to("cuda").view(torch.bfloat16)
+    rr = device.RowsRunner(zf, zf[case.r0:case.r0 + R], None, case.params, H, "bf16")
+    del case
+    steps = max(3, args.steps)
+    ms_bias = _time(rr.compute_bias, steps, 2, torch)
+    ms_rows = _time(rr.rows, steps, 2, torch)
+    ms = _time(rr, steps, 2, torch)
+    f = tri_module_flops(R, I, c, H, d, with_bias=True)["total"]
+    out["rows_bf16_i4096_r512"] = {"ms": ms, "ms_bias": ms_bias, "ms_rows": ms_rows,
+                                   "tflops": f / (ms * 1e-3) / 1e12, "rows_per_s": R / (ms * 1e-3)}
+    del rr, zf
+    torch.cuda.empty_cache()
     return out
 
 
