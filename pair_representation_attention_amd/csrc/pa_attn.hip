@@ -497,14 +497,16 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // one finishes its block early and idles at the barrier while the younger
   // one runs the rest alone; with the ladder the wave that is behind in the
   // block wins the issue arbitration, and both reach the barrier together.
-  auto sweep_pipe = [&]() {
+  auto sweep_pipe = [&](auto anyc) {
+   // ANY: P is not a multiple of 32, so the last block holds keys past P
+   constexpr bool ANY = decltype(anyc)::value;
    if constexpr (QW == 2 && RW == 2 && NCW == 4) {
     using T = std::integral_constant<bool, true>;
     using F = std::integral_constant<bool, false>;
     float l2[RW][QW];   // second partial row sum (keys 16..31 of each unit's lane half)
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
-      row_has_key[rr] = true;
+      row_has_key[rr] = true;   // P >= 1: every row has a kept key
 #pragma unroll
       for (int qq = 0; qq < QW; ++qq) {
         O[rr][qq] = f32x16{};
@@ -557,13 +559,27 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     };
     // softmax of S (one unit) with the next unit's logits (NEXT) and this
     // unit's P.V product issued between its exp2 groups; the row sums
-    // accumulate in la (keys of chunk 0) and lb (chunk 1)
-    auto stream = [&](auto nextc, const f32x16& S, f32x16& Sn, const f16x8* kn, const f16x8* qn, const f32x16& cn,
-                      const f16x8* v, f32x16& o, float& la, float& lb) {
+    // accumulate in la (keys of chunk 0) and lb (chunk 1).  MASKED: keys
+    // whose bit in `bits` is clear get -inf first (register j holds key
+    // (j/4)*8 + g*4 + j%4, so the select's lane mask is built on the scalar
+    // unit).
+    auto stream = [&](auto nextc, auto maskc, const f32x16& S_in, f32x16& Sn, const f16x8* kn, const f16x8* qn,
+                      const f32x16& cn, const f16x8* v, f32x16& o, float& la, float& lb, uint32_t bits) {
       constexpr bool NEXT = decltype(nextc)::value;
+      constexpr bool MASKED = decltype(maskc)::value;
       const f16x2 one = {(f16)1.0f, (f16)1.0f};
       float e[16];
       f16x8 p0, p1;
+      f32x16 S = S_in;
+      if constexpr (MASKED) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int k0 = (j >> 2) * 8 + (j & 3);
+          const uint64_t lanes = (((bits >> k0) & 1u) ? 0x00000000ffffffffull : 0ull) |
+                                 (((bits >> (k0 + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
+          S[j] = keep_or_neg_inf(S[j], lanes);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) e[j] = fast_exp2(S[j]);
@@ -627,25 +643,25 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       C_pipe = cvt_bias(B0);
       S_pipe = mfma32(ra.K[0][1], Q[0][0][1], mfma32(ra.K[0][0], Q[0][0][0], C_pipe));
     }
-    // block kb from the registers in `cur`; the next block's land in `nx`
     // block kb from the registers in r; the next block's tiles are read into
     // r in place, each once its current value has had its last use (K of
     // row 0 after the logits of unit 2, K of row 1 after those of unit 3, V
     // of row 0 after the P.V of unit 2, V of row 1 and the bias tile of
     // query block 1 after that of unit 3)
-    auto block = [&](int kb, auto morec, Regs& r) {
+    // bits0, bits1: keep bits of block kb for rows 0 and 1 (MASKED blocks)
+    auto block = [&](int kb, auto morec, auto maskc, Regs& r, uint32_t bits0, uint32_t bits1) {
       constexpr bool MORE = decltype(morec)::value;
       f32x16 Sn;
       // stream 0: unit (0, 0); next (1, 0)
       __builtin_amdgcn_s_setprio(3);
       if constexpr (MORE) copy_kv(kb + 2, 2, 4);
       else load_epi();
-      stream(T{}, S_pipe, Sn, r.K[1], Q[1][0], C_pipe, r.V[0], O[0][0], l_run[0][0], l2[0][0]);
+      stream(T{}, maskc, S_pipe, Sn, r.K[1], Q[1][0], C_pipe, r.V[0], O[0][0], l_run[0][0], l2[0][0], bits0);
       S_pipe = Sn;
       C_pipe = cvt_bias(r.B1);
       // stream 1: unit (1, 0); next (0, 1)
       __builtin_amdgcn_s_setprio(2);
-      stream(T{}, S_pipe, Sn, r.K[0], Q[0][1], C_pipe, r.V[1], O[1][0], l_run[1][0], l2[1][0]);
+      stream(T{}, maskc, S_pipe, Sn, r.K[0], Q[0][1], C_pipe, r.V[1], O[1][0], l_run[1][0], l2[1][0], bits1);
       S_pipe = Sn;
       // stream 2: unit (0, 1); next (1, 1); block kb+1 published
       __builtin_amdgcn_s_setprio(1);
@@ -660,7 +676,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         for (int c = 0; c < 2; ++c) Bn0[c] = lds_f16x8(b_tile(kb + 1, 0) + c * 1024);
         copy_b(kb + 2);
       }
-      stream(T{}, S_pipe, Sn, r.K[1], Q[1][1], C_pipe, r.V[0], O[0][1], l_run[0][1], l2[0][1]);
+      stream(T{}, maskc, S_pipe, Sn, r.K[1], Q[1][1], C_pipe, r.V[0], O[0][1], l_run[0][1], l2[0][1], bits0);
       S_pipe = Sn;
       if constexpr (MORE) {
 #pragma unroll
@@ -672,7 +688,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       }
       // stream 3: unit (1, 1); next = unit (0, 0) of block kb+1
       __builtin_amdgcn_s_setprio(0);
-      stream(morec, S_pipe, Sn, r.K[0], Q[0][0], Cn, r.V[1], O[1][1], l_run[1][1], l2[1][1]);
+      stream(morec, maskc, S_pipe, Sn, r.K[0], Q[0][0], Cn, r.V[1], O[1][1], l_run[1][1], l2[1][1], bits1);
       if constexpr (MORE) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -684,8 +700,16 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         S_pipe = Sn;
       }
     };
-    for (int kb = 0; kb + 1 < nkb; ++kb) block(kb, T{}, ra);
-    block(nkb - 1, F{}, ra);
+    if constexpr (!ANY) {
+      for (int kb = 0; kb + 1 < nkb; ++kb) block(kb, T{}, F{}, ra, ~0u, ~0u);
+      block(nkb - 1, F{}, F{}, ra, ~0u, ~0u);
+    } else {
+      // only the last block holds keys past P (no mask here)
+      static_assert(!HAS_MASK, "masked inputs take the generic sweep");
+      for (int kb = 0; kb + 1 < nkb; ++kb) block(kb, T{}, F{}, ra, ~0u, ~0u);
+      const uint32_t bl = keep_bits(0, nkb - 1);
+      block(nkb - 1, F{}, T{}, ra, bl, bl);
+    }
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr)
@@ -696,12 +720,9 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
   bool epi_loaded = false;
   if constexpr (H == 4 && !HAS_MASK) {
-    if (P == Pp) {
-      sweep_pipe();
-      epi_loaded = true;
-    } else {
-      sweep(std::integral_constant<bool, true>{});
-    }
+    if (P == Pp) sweep_pipe(std::integral_constant<bool, false>{});
+    else sweep_pipe(std::integral_constant<bool, true>{});
+    epi_loaded = true;
   } else {
     sweep(std::integral_constant<bool, true>{});
   }

@@ -83,7 +83,9 @@ struct ProjShape {
   static constexpr int W_BYTES = NCOL * C_IN * 2;
   static constexpr int WB_BYTES = HAS_BIAS ? KS * 1024 : 0;
   static constexpr int LDS = W_BYTES + WB_BYTES + NCOL * 4 + 8 * 4;
-  static constexpr int PF = C_IN <= 128 ? 2 : 1;       // tiles prefetched ahead
+  // tiles prefetched ahead (the bias-only form has registers to spare for a
+  // deeper prefetch, which its pure read stream needs to cover HBM latency)
+  static constexpr int PF = MODE == 2 ? (C_IN <= 128 ? 4 : 1) : (C_IN <= 128 ? 2 : 1);
   static_assert(LDS <= 160 * 1024, "projection operands exceed LDS");
 };
 
