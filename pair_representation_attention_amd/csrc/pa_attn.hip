@@ -388,6 +388,13 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     #pragma unroll
         for (int u = 0; u < NU; ++u) {
           const int qq = u / RW, rr = u % RW;
+          // priority ladder over the units of a block, falling from 3 (as in
+          // the pipelined sweep: the wave that is behind in the block wins
+          // the issue arbitration)
+          if (u == 0) __builtin_amdgcn_s_setprio(3);
+          else if (u == 1) __builtin_amdgcn_s_setprio(NU == 4 ? 2 : 0);
+          else if (u == 2) __builtin_amdgcn_s_setprio(1);
+          else __builtin_amdgcn_s_setprio(0);
           copies_for_unit(kb, u);
           f32x16 Snext;
           if (u + 1 < NU) {
@@ -727,6 +734,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     sweep(std::integral_constant<bool, true>{});
   }
   if (!epi_loaded) load_epi();
+  __builtin_amdgcn_s_setprio(0);
   wait_vm0();   // this wave's copies (dummies past the end included) have landed
   bool bad = false;
 #pragma unroll
