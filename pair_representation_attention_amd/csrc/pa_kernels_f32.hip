@@ -1,144 +1,628 @@
-// fp32 kernels for gated pair-biased attention on gfx950 (plain fp32 VALU
-// arithmetic: no reduced-precision matrix mode anywhere on this path).
+// fp32 kernels for gated pair-biased attention on gfx950.
 //
-// Same row-attention formulation as the bf16 path.  Workspace layouts:
-//   q, k, v, g [nrows][P][H*32] float (q scaled by 1/sqrt(d), g after sigmoid)
-//   bias [H][P][P] float
+// fp32 in, fp32 out, fp32-accurate, on the matrix cores.  Every product of
+// the path (projections, logits, P.V, output projection) takes its operands
+// as fp16 pairs: an fp32 value x is held as hi + lo, where hi is x with its
+// significand cut to fp16's 11 bits (exact in fp16 for |x| in [2^-14, 65504])
+// and lo = x - hi (exact in fp32) rounded to fp16.  A product a.b is formed
+// from the three fp16 products hi.hi + hi.lo + lo.hi, each a 32x32x16 f16
+// MFMA accumulating in fp32.  What is dropped (lo.lo and the rounding of
+// lo) is below 2^-19 of |a||b|, against 2^-24 for fp32 itself, at three fp16
+// MFMAs per product instead of the sixteen-fold cost of fp32 MFMAs.
+// Operands must stay below 65504 in magnitude; below 2^-14 they keep an
+// absolute error under 2^-24.  The softmax, LayerNorm, sigmoid, bias and all
+// accumulation run in fp32.
+//
+// Row-attention formulation as in the bf16 path: nrows rows of P positions
+// (queries = keys), H heads of width 32, bias[h][query][key] shared by all
+// rows.  Workspace (Pp = P rounded up to 32, nb = Pp / 32, rh = row*H + h;
+// padded positions hold zeros):
+//   q, k, v  hi and lo planes, nrows*H*Pp*32 fp16 each, in the operand-ordered
+//            layouts of pa_device.h (q scaled by log2(e)/sqrt(d))
+//   g        nrows*H*Pp*32 float, sigmoid applied, one 4 KB tile per (rh,
+//            query block) holding the O^T accumulator image: lane = query %
+//            32 + 32*half, register j = channel acc_row(j, half)
+//   bias     H*Pp*Pp float in log2 units, one 4 KB tile per (h, query block,
+//            key block) holding the S^T accumulator image (lane = query % 32
+//            + 32*half, register j = key acc_row(j, half)); keys >= P hold
+//            -inf, so padded keys get weight 0 without a mask
+//   packed weights: gamma-folded q|k|v|g (+ pair bias) operands, hi and lo
+//            planes, [block of 32 columns][K-step][64 lanes][8]; W_o as the
+//            B operand of out = og.W_o, [c block][head][chunk][64 lanes][8]
 #include "pa_device.h"
 #include "pa_launch.h"
 
+#include <type_traits>
+
 namespace pa {
 
-// LayerNorm of 32 positions into LDS (fp32, pitch c_in + 1), then every
-// requested output column as a plain dot product in channel order.
-// mode 0: q,k,v,g   1: q,k,v,g + bias   2: bias only
-__global__ __launch_bounds__(256) void proj_f32_kernel(
-    const float* __restrict__ x, int64_t xs_r, int64_t xs_p, const float* __restrict__ gamma,
-    const float* __restrict__ beta, float eps, const float* __restrict__ wq, const float* __restrict__ wk,
-    const float* __restrict__ wv, const float* __restrict__ wg, const float* __restrict__ wb,
-    const float* __restrict__ b_g, float q_scale, float* __restrict__ q_ws, float* __restrict__ k_ws,
-    float* __restrict__ v_ws, float* __restrict__ g_ws, float* __restrict__ bias, float bias_scale, int c_in, int hd,
-    int H, int nrows, int P, int mode) {
-  extern __shared__ float xs[];   // [32][c_in + 1]
-  const int pitch = c_in + 1;
-  const int r = blockIdx.y;
-  const int p0 = blockIdx.x * 32;
-  const int tid = threadIdx.x;
-  {
-    const int pl = tid / 8, sub = tid % 8;   // 8 threads per position
-    const int p = p0 + pl;
-    const bool valid = p < P;
-    const float* xp = x + (int64_t)r * xs_r + (int64_t)(valid ? p : 0) * xs_p;
-    float s = 0.0f;
-    for (int c = sub; c < c_in; c += 8) s += valid ? xp[c] : 0.0f;
-    const float mean = group_sum<8>(s) / (float)c_in;
-    float s2 = 0.0f;
-    for (int c = sub; c < c_in; c += 8) {
-      const float t = (valid ? xp[c] : 0.0f) - mean;
-      s2 += t * t;
-    }
-    const float var = group_sum<8>(s2) / (float)c_in;
-    const float rstd = 1.0f / sqrtf(var + eps);
-    for (int c = sub; c < c_in; c += 8)
-      xs[pl * pitch + c] = valid ? (xp[c] - mean) * rstd * gamma[c] + beta[c] : 0.0f;
+// ---------------------------------------------------------------------------
+// fp16 pairs
+// ---------------------------------------------------------------------------
+// hi: significand cut to 11 bits; lo: the exact remainder rounded to fp16
+__device__ __forceinline__ void split8(const float* x, f16x8& hi, f16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float t = __uint_as_float(__float_as_uint(x[e]) & 0xffffe000u);
+    hi[e] = (f16)t;
+    lo[e] = (f16)(x[e] - t);
   }
-  __syncthreads();
-  const int nq = mode == 2 ? 0 : 4 * hd;
-  const int nb = mode == 0 ? 0 : H;
-  const int ncol = nq + nb;
-  for (int idx = tid; idx < 32 * ncol; idx += blockDim.x) {
-    const int pl = idx / ncol, col = idx % ncol;
-    const int p = p0 + pl;
-    if (p >= P) continue;
-    const float* xr = xs + pl * pitch;
-    if (col < nq) {
-      const int t = col / hd, cc = col % hd;
-      const float* w = t == 0 ? wq : t == 1 ? wk : t == 2 ? wv : wg;
+}
+// D = A.B + C with A = ah + al, B = bh + bl (the small terms first)
+__device__ __forceinline__ f32x16 mfma3(const f16x8& ah, const f16x8& al, const f16x8& bh, const f16x8& bl,
+                                        f32x16 c) {
+  c = mfma32(al, bh, c);
+  c = mfma32(ah, bl, c);
+  return mfma32(ah, bh, c);
+}
+
+// ---------------------------------------------------------------------------
+// Weight packing.  LayerNorm's affine map is folded into the projection:
+//   ((x-mu)*rstd*gamma + beta) . W = ((x-mu)*rstd) . (gamma o W) + beta . W
+// Block b of the packed list is columns b*32..+31 of q|k|v|g (each H*32
+// wide).  Lane l of K-step t holds column l%32 and channels t*16 + (l/32)*8
+// .. +7 (the activation operand uses the same slots).
+// cst[n] = beta . W[:, n] (+ b_g for gate columns).
+// W_o is packed as the B operand of out = og . W_o: lane l of (c block cb,
+// head hh, chunk t) holds output column cb*32 + l%32 and, in element e, the
+// head channel slot_x(t, l/32, e), the order in which an O^T accumulator
+// holds its rows.
+// ---------------------------------------------------------------------------
+__global__ void pack_f32_kernel(const float* __restrict__ wq, const float* __restrict__ wk,
+                                const float* __restrict__ wv, const float* __restrict__ wg,
+                                const float* __restrict__ gamma, const float* __restrict__ beta,
+                                const float* __restrict__ b_g, int c_in, int hd, int H, int nqkvg,
+                                f16* __restrict__ w_hi, f16* __restrict__ w_lo,
+                                float* __restrict__ cst, const float* __restrict__ wo, f16* __restrict__ wo_hi,
+                                f16* __restrict__ wo_lo, int c_out) {
+  const int ks = c_in / 16;
+  const int64_t n_w = (int64_t)nqkvg * ks * 64;    // 8-element slots of the projection operands
+  const int64_t n_c = (int64_t)nqkvg * 32;          // column constants
+  const int64_t n_o = wo != nullptr ? (int64_t)(c_out / 32) * H * 2 * 64 : 0;
+  const int64_t total = n_w + n_c + n_o;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    if (i < n_w) {
+      const int l = (int)(i & 63), t = (int)((i >> 6) % ks), b = (int)((i >> 6) / ks);
+      const int k0 = t * 16 + (l >> 5) * 8;
+      const int col = b * 32 + (l & 31);
+      const int tsr = col / hd, cc = col % hd;
+      const float* src = tsr == 0 ? wq : tsr == 1 ? wk : tsr == 2 ? wv : wg;
+      float w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = src[(int64_t)(k0 + e) * hd + cc] * gamma[k0 + e];
+      f16x8 hi, lo;
+      split8(w, hi, lo);
+      *reinterpret_cast<f16x8*>(w_hi + i * 8) = hi;
+      *reinterpret_cast<f16x8*>(w_lo + i * 8) = lo;
+    } else if (i < n_w + n_c) {
+      const int n = (int)(i - n_w);
+      const int tsr = n / hd, cc = n % hd;
+      const float* src = tsr == 0 ? wq : tsr == 1 ? wk : tsr == 2 ? wv : wg;
       float acc = 0.0f;
-      for (int k = 0; k < c_in; ++k) acc = fmaf(xr[k], w[(int64_t)k * hd + cc], acc);
-      const int64_t o = ((int64_t)r * P + p) * hd + cc;
-      if (t == 0) q_ws[o] = acc * q_scale;
-      else if (t == 1) k_ws[o] = acc;
-      else if (t == 2) v_ws[o] = acc;
-      else g_ws[o] = 1.0f / (1.0f + expf(-(acc + (b_g != nullptr ? b_g[cc] : 0.0f))));
+      for (int k = 0; k < c_in; ++k) acc = __builtin_fmaf(beta[k], src[(int64_t)k * hd + cc], acc);
+      if (tsr == 3 && b_g != nullptr) acc += b_g[cc];
+      cst[n] = acc;
     } else {
-      const int hh = col - nq;
-      float acc = 0.0f;
-      for (int k = 0; k < c_in; ++k) acc = fmaf(xr[k], wb[(int64_t)k * H + hh], acc);
-      bias[((int64_t)hh * P + r) * P + p] = acc * bias_scale;
+      const int64_t j = i - n_w - n_c;
+      const int l = (int)(j & 63), t = (int)((j >> 6) & 1), hh = (int)((j >> 7) % H), cb = (int)((j >> 7) / H);
+      const int col = cb * 32 + (l & 31);
+      float w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = wo[(int64_t)(hh * 32 + slot_x(t, l >> 5, e)) * c_out + col];
+      f16x8 hi, lo;
+      split8(w, hi, lo);
+      *reinterpret_cast<f16x8*>(wo_hi + j * 8) = hi;
+      *reinterpret_cast<f16x8*>(wo_lo + j * 8) = lo;
     }
   }
 }
 
-// One thread per (query, head): online softmax over all keys in fp32 with
-// expf, then the gated output projection from LDS.
-__global__ __launch_bounds__(256) void attn_f32_kernel(
-    const float* __restrict__ q_ws, const float* __restrict__ k_ws, const float* __restrict__ v_ws,
-    const float* __restrict__ g_ws, const float* __restrict__ bias, const uint8_t* __restrict__ mask,
-    int64_t ms_r, int64_t ms_k, const float* __restrict__ wo, const float* __restrict__ b_o,
-    float* __restrict__ out, int64_t os_r, int64_t os_p, int H, int c_out, int nrows, int P) {
-  extern __shared__ float o_s[];   // [32][hd + 1]
-  const int hd = H * 32;
-  const int pitch = hd + 1;
-  const int r = blockIdx.y;
-  const int q0 = blockIdx.x * 32;
-  const int qi = threadIdx.x % 32, h = threadIdx.x / 32;
-  const int q = q0 + qi;
-  const int qc = min(q, P - 1);
-  float qv[32], o[32];
-  const float* qp = q_ws + ((int64_t)r * P + qc) * hd + h * 32;
-  for (int e = 0; e < 32; ++e) {
-    qv[e] = qp[e];
-    o[e] = 0.0f;
+// offset (floats) of bias element (h, query, key) in the tiled S^T image
+__device__ __forceinline__ int64_t bias_c_off(int h, int nb, int q, int k) {
+  const int x = k & 31;
+  const int lane = (q & 31) + 32 * slot_hg(x);
+  const int j = (x >> 3) * 4 + (x & 3);
+  return ((((int64_t)h * nb + (q >> 5)) * nb + (k >> 5)) * 64 + lane) * 16 + j;
+}
+
+// ---------------------------------------------------------------------------
+// Fused LayerNorm + projections.  Each wave works on its own tiles of 32
+// positions of one row; a lane holds one position (lane % 32) and, in K-step
+// t, channels t*16 + half*8 .. +7, which is the register image of both MFMA
+// operand kinds.  LayerNorm runs in registers; the normalised activations
+// are split into fp16 pairs.  The workgroup's NB column blocks sit in LDS
+// (hi and lo planes): packed q|k|v|g blocks are copied, the pair-bias block
+// (rows = heads, zero beyond H; the last block when with_bias) is built here
+// from w_b and gamma, with its constants beta . w_b.  Block kinds: q and k (out^T = W^T X^T, rows =
+// channels, lane = position) are written as operand chunks; v (X W, rows =
+// positions, lane = channel) likewise in its own order; the gate as its
+// fp32 O^T image; the pair bias (rows = heads) into the tiled S^T image
+// (log2 units) or, with bias_natural, as [H][P][P] float.
+// ---------------------------------------------------------------------------
+constexpr int kProjF32Threads = 256;
+
+template <int C_IN>
+struct ProjF32Shape {
+  static constexpr int KS = C_IN / 16;
+  static constexpr int NB = 32 / KS;                // column blocks per workgroup: 64 KB of operands
+  static constexpr int LDS = NB * KS * 2 * 1024;
+};
+
+template <int C_IN>
+__global__ __launch_bounds__(kProjF32Threads) void proj_f32_kernel(
+    const float* __restrict__ x, int64_t xs_r, int64_t xs_p, int tile_rmajor, float eps, const f16* __restrict__ w_hi,
+    const f16* __restrict__ w_lo, const float* __restrict__ cst, int nqkvg, int with_bias,
+    const float* __restrict__ wb, const float* __restrict__ gamma, const float* __restrict__ beta, int hd,
+    float q_scale,
+    f16* __restrict__ q_hi, f16* __restrict__ q_lo, f16* __restrict__ k_hi, f16* __restrict__ k_lo,
+    f16* __restrict__ v_hi, f16* __restrict__ v_lo, float* __restrict__ g_ws, float* __restrict__ bias,
+    int bias_natural, float bias_scale, int nrows, int P, int Pp, int H) {
+  using SH = ProjF32Shape<C_IN>;
+  constexpr int KS = SH::KS;
+  constexpr int NW = kProjF32Threads / kWave;
+  __shared__ __attribute__((aligned(1024))) char smem[SH::LDS];
+  __shared__ float cstb[8];
+  f16* wl_hi = reinterpret_cast<f16*>(smem);
+  f16* wl_lo = wl_hi + SH::NB * KS * 512;
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int lq = lane & 31, g = lane >> 5;
+  const int nblk = nqkvg + with_bias;
+  const int b0 = blockIdx.y * SH::NB;
+  const int nbl = min(SH::NB, nblk - b0);   // blocks of this workgroup
+
+  for (int i = tid; i < nbl * KS * 64; i += kProjF32Threads) {
+    const int b = b0 + i / (KS * 64);
+    if (b < nqkvg) {
+      const int64_t src = (int64_t)b0 * KS * 64 + i;
+      *reinterpret_cast<f16x8*>(wl_hi + i * 8) = *reinterpret_cast<const f16x8*>(w_hi + src * 8);
+      *reinterpret_cast<f16x8*>(wl_lo + i * 8) = *reinterpret_cast<const f16x8*>(w_lo + src * 8);
+    } else {
+      const int l = i & 63, t = (i >> 6) % KS, hh = l & 31;
+      const int k0 = t * 16 + (l >> 5) * 8;
+      float w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = hh < H ? wb[(int64_t)(k0 + e) * H + hh] * gamma[k0 + e] : 0.0f;
+      f16x8 hi, lo;
+      split8(w, hi, lo);
+      *reinterpret_cast<f16x8*>(wl_hi + i * 8) = hi;
+      *reinterpret_cast<f16x8*>(wl_lo + i * 8) = lo;
+    }
   }
-  float m = -__builtin_inff(), l = 0.0f;
-  const float* brow = bias + ((int64_t)h * P + qc) * P;
-  for (int k = 0; k < P; ++k) {
-    if (mask != nullptr && mask[(int64_t)r * ms_r + (int64_t)k * ms_k] == 0) continue;
-    const float* kp = k_ws + ((int64_t)r * P + k) * hd + h * 32;
-    float s = 0.0f;
-    for (int e = 0; e < 32; ++e) s = fmaf(qv[e], kp[e], s);
-    s += brow[k];
-    const float m_new = fmaxf(m, s);
-    const float alpha = expf(m - m_new);
-    const float pw = expf(s - m_new);
-    l = l * alpha + pw;
-    const float* vp = v_ws + ((int64_t)r * P + k) * hd + h * 32;
-    for (int e = 0; e < 32; ++e) o[e] = fmaf(pw, vp[e], o[e] * alpha);
-    m = m_new;
-  }
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  const float* gp = g_ws + ((int64_t)r * P + qc) * hd + h * 32;
-  for (int e = 0; e < 32; ++e) o_s[qi * pitch + h * 32 + e] = o[e] * inv * gp[e];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < 32 * c_out; idx += blockDim.x) {
-    const int qq = idx / c_out, c = idx % c_out;
-    const int p = q0 + qq;
-    if (p >= P) continue;
+  if (with_bias && tid < 8) {
     float acc = 0.0f;
-    for (int k = 0; k < hd; ++k) acc = fmaf(o_s[qq * pitch + k], wo[(int64_t)k * c_out + c], acc);
-    out[(int64_t)r * os_r + (int64_t)p * os_p + c] = acc + (b_o != nullptr ? b_o[c] : 0.0f);
+    if (tid < H)
+      for (int k = 0; k < C_IN; ++k) acc = __builtin_fmaf(beta[k], wb[(int64_t)k * H + tid], acc);
+    cstb[tid] = acc;
+  }
+  __syncthreads();
+
+  const int nb = Pp / 32;
+  const int64_t ntiles = (int64_t)nb * nrows;
+  const int64_t stride = (int64_t)gridDim.x * NW;
+  for (int64_t tile = (int64_t)blockIdx.x * NW + wave; tile < ntiles; tile += stride) {
+    int r, p0;
+    if (tile_rmajor) {
+      r = (int)(tile / nb);
+      p0 = (int)(tile % nb) * 32;
+    } else {
+      r = (int)(tile % nrows);
+      p0 = (int)(tile / nrows) * 32;
+    }
+    const int p = p0 + lq;
+    const bool valid = p < P;
+
+    // ---- LayerNorm (two passes, fp32) and fp16 pairs ----
+    float raw[KS][8];
+    if (valid) {
+      const float* src = x + (int64_t)r * xs_r + (int64_t)p * xs_p + g * 8;
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(src + t * 16);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(src + t * 16 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          raw[t][e] = a[e];
+          raw[t][4 + e] = b[e];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < KS; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) raw[t][e] = 0.0f;
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += raw[t][e];
+    s += __shfl_xor(s, 32, 64);
+    const float mean = s * (1.0f / C_IN);
+    float s2 = 0.0f;
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = raw[t][e] - mean;
+        s2 = __builtin_fmaf(d, d, s2);
+      }
+    s2 += __shfl_xor(s2, 32, 64);
+    const float rstd = 1.0f / __builtin_sqrtf(s2 * (1.0f / C_IN) + eps);
+    f16x8 Xh[KS], Xl[KS];
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      float xn[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xn[e] = valid ? (raw[t][e] - mean) * rstd : 0.0f;
+      split8(xn, Xh[t], Xl[t]);
+    }
+
+    for (int bl = 0; bl < nbl; ++bl) {
+      const int b = b0 + bl;
+      const f16* oph = wl_hi + bl * KS * 512 + lane * 8;
+      const f16* opl = wl_lo + bl * KS * 512 + lane * 8;
+      f32x16 acc = {};
+      if (b < nqkvg) {
+        const int col = b * 32;
+        const int tsr = col / hd;                 // 0 q, 1 k, 2 v, 3 g
+        const int64_t rh = (int64_t)r * H + (col - tsr * hd) / 32;
+        const int64_t chunk0 = (rh * nb + (p0 >> 5)) * 2;
+        const float* cb = cst + col;
+        if (tsr == 2) {                           // v = X W: rows = positions, lane = channel
+#pragma unroll
+          for (int t = 0; t < KS; ++t)
+            acc = mfma3(Xh[t], Xl[t], *reinterpret_cast<const f16x8*>(oph + t * 512),
+                        *reinterpret_cast<const f16x8*>(opl + t * 512), acc);
+          const float c = cb[lq];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = p0 + slot_x(t, g, e) < P ? acc[8 * t + e] + c : 0.0f;
+            f16x8 hi, lo;
+            split8(o, hi, lo);
+            st16(v_hi + (chunk0 + t) * 512 + lane * 8, hi);
+            st16(v_lo + (chunk0 + t) * 512 + lane * 8, lo);
+          }
+        } else {                                  // out^T = W^T X^T: rows = channels, lane = position
+#pragma unroll
+          for (int t = 0; t < KS; ++t)
+            acc = mfma3(*reinterpret_cast<const f16x8*>(oph + t * 512),
+                        *reinterpret_cast<const f16x8*>(opl + t * 512), Xh[t], Xl[t], acc);
+          if (tsr <= 1) {
+            const float sc = valid ? (tsr == 0 ? q_scale : 1.0f) : 0.0f;
+            f16* dh = tsr == 0 ? q_hi : k_hi;
+            f16* dl = tsr == 0 ? q_lo : k_lo;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              float o[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) o[e] = (acc[8 * t + e] + cb[slot_x(t, g, e)]) * sc;
+              f16x8 hi, lo;
+              split8(o, hi, lo);
+              st16(dh + (chunk0 + t) * 512 + lane * 8, hi);
+              st16(dl + (chunk0 + t) * 512 + lane * 8, lo);
+            }
+          } else {                                // gate: sigmoid, O^T image in fp32
+            f32x16 o;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[j] = 1.0f / (1.0f + __expf(-(acc[j] + cb[acc_row(j, g)])));
+            float* dst = g_ws + ((rh * nb + (p0 >> 5)) * 64 + lane) * 16;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+              *reinterpret_cast<f32x4*>(dst + 4 * q4) = f32x4{o[4 * q4], o[4 * q4 + 1], o[4 * q4 + 2], o[4 * q4 + 3]};
+          }
+        }
+      } else {                                    // pair bias: rows = heads, lane = position (key)
+#pragma unroll
+        for (int t = 0; t < KS; ++t)
+          acc = mfma3(*reinterpret_cast<const f16x8*>(oph + t * 512),
+                      *reinterpret_cast<const f16x8*>(opl + t * 512), Xh[t], Xl[t], acc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {            // heads (< 8) are rows g*4 + j of registers 0..3
+          const int hh = acc_row(j, g);
+          if (hh >= H) continue;
+          const float val = (acc[j] + cstb[hh]) * bias_scale;
+          if (bias_natural) {
+            if (valid) bias[((int64_t)hh * P + r) * P + p] = val;
+          } else {
+            bias[bias_c_off(hh, nb, r, p)] = valid ? val : -__builtin_inff();
+            if (r == P - 1)   // padded query rows: finite at real keys, -inf at padded ones
+              for (int rp = P; rp < Pp; ++rp) bias[bias_c_off(hh, nb, rp, p)] = valid ? 0.0f : -__builtin_inff();
+          }
+        }
+      }
+    }
   }
 }
 
-hipError_t launch_proj_f32(const ProjArgs& a, int mode, hipStream_t s) {
-  dim3 grid((a.P + 31) / 32, a.nrows);
-  const size_t lds = sizeof(float) * 32 * (a.c_in + 1);
-  hipLaunchKernelGGL(proj_f32_kernel, grid, dim3(256), lds, s, (const float*)a.x, a.xs_r, a.xs_p,
-                     (const float*)a.gamma, (const float*)a.beta, a.eps, (const float*)a.wq, (const float*)a.wk,
-                     (const float*)a.wv, (const float*)a.wg, (const float*)a.wb, (const float*)a.b_g, a.q_scale,
-                     (float*)a.q_ws, (float*)a.k_ws, (float*)a.v_ws, (float*)a.g_ws, a.bias, a.bias_scale, a.c_in,
-                     a.hd, a.H, a.nrows, a.P, mode);
+// Caller-provided bias [H][P][P] float (natural-log units) -> tiled S^T image
+// in log2 units, -inf at padded keys.
+__global__ void bias_to_f32_layout_kernel(const float* __restrict__ src, float* __restrict__ dst, int H, int P,
+                                          int Pp) {
+  const int64_t total = (int64_t)H * Pp * Pp;
+  const int nb = Pp / 32;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int h = (int)(i / ((int64_t)Pp * Pp));
+    const int64_t rem = i % ((int64_t)Pp * Pp);
+    const int q = (int)(rem / Pp), k = (int)(rem % Pp);
+    float v = -__builtin_inff();
+    if (k < P) v = q < P ? src[((int64_t)h * P + q) * P + k] * kLog2e : 0.0f;
+    dst[bias_c_off(h, nb, q, k)] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Attention.  A workgroup is H waves (wave = head) over one row and two query
+// blocks (64 queries); a unit is 32 queries x 32 keys of one head.  Per unit:
+//   S^T = K.Q^T + C      six MFMAs (two K-steps of three), C = bias tile
+//   online softmax per query (lane): running maximum m raised only when a
+//   block's maximum passes it by more than 8 (log2 units), so p = exp2(s - m)
+//   <= 256; l accumulates p in fp32
+//   O^T += V^T.P^T       six MFMAs, P split into fp16 pairs
+// The K/V chunks of the next key block and the bias tile of the next unit
+// are loaded while the current one computes (two named register sets).
+// Epilogue: o = O/l times the gate, as fp16 pairs into LDS; then the waves
+// share the output tiles (query block x 32 columns), each a K = H*32
+// contraction of og with W_o, + b_o, fp32 stores.
+// ---------------------------------------------------------------------------
+template <int H, bool HAS_MASK>
+__global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_f32_kernel(
+    const f16* __restrict__ q_hi, const f16* __restrict__ q_lo, const f16* __restrict__ k_hi,
+    const f16* __restrict__ k_lo, const f16* __restrict__ v_hi, const f16* __restrict__ v_lo,
+    const float* __restrict__ g_ws, const float* __restrict__ bias, const uint32_t* __restrict__ mask_bits,
+    const f16* __restrict__ wo_hi, const f16* __restrict__ wo_lo, const float* __restrict__ b_o,
+    float* __restrict__ out, int64_t os_r, int64_t os_p, int c_out, int nrows, int P, int nb, int ngroups) {
+  // og tiles: [query block u][head][chunk t][plane][64 lanes][8] fp16
+  __shared__ __attribute__((aligned(1024))) f16 og_lds[2 * H * 2 * 2 * 512];
+
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int g = lane >> 5;
+  const int h = wave;
+
+  // XCD-aware order: consecutive ids go round-robin over the 8 XCDs; give
+  // each XCD a contiguous range of tiles so that the query groups of a row
+  // (which share K and V) meet in one L2
+  const int64_t ntile = (int64_t)ngroups * nrows;
+  int64_t tile = blockIdx.x;
+  if ((ntile & 7) == 0) tile = (tile & 7) * (ntile >> 3) + (tile >> 3);
+  const int r = (int)(tile / ngroups);
+  const int grp = (int)(tile % ngroups);
+  const int qb0 = 2 * grp, qb1 = min(2 * grp + 1, nb - 1);   // an odd last group repeats its block
+  const int64_t rh = (int64_t)r * H + h;
+
+  f16x8 Qh[2][2], Ql[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    Qh[0][t] = ld16(q_hi + qkv_chunk(rh, nb, qb0, t) + lane * 8);
+    Ql[0][t] = ld16(q_lo + qkv_chunk(rh, nb, qb0, t) + lane * 8);
+    Qh[1][t] = ld16(q_hi + qkv_chunk(rh, nb, qb1, t) + lane * 8);
+    Ql[1][t] = ld16(q_lo + qkv_chunk(rh, nb, qb1, t) + lane * 8);
+  }
+
+  struct KV {
+    f16x8 kh[2], kl[2], vh[2], vl[2];
+  };
+  auto load_kv = [&](KV& d, int kb) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t o = qkv_chunk(rh, nb, kb, t) + lane * 8;
+      d.kh[t] = ld16(k_hi + o);
+      d.kl[t] = ld16(k_lo + o);
+      d.vh[t] = ld16(v_hi + o);
+      d.vl[t] = ld16(v_lo + o);
+    }
+  };
+  auto load_bias = [&](f32x16& d, int qb, int kb) {
+    const float* src = bias + ((((int64_t)h * nb + qb) * nb + kb) * 64 + lane) * 16;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * q4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[4 * q4 + e] = v[e];
+    }
+  };
+
+  f32x16 O[2] = {};
+  float m[2] = {-__builtin_inff(), -__builtin_inff()};
+  float l[2] = {0.0f, 0.0f};
+
+  // one unit: logits, softmax update, P.V
+  auto unit = [&](auto uc, const KV& kv, const f32x16& C, uint32_t bits) {
+    constexpr int u = decltype(uc)::value;
+    f32x16 S = C;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) S = mfma3(kv.kh[t], kv.kl[t], Qh[u][t], Ql[u][t], S);
+    if constexpr (HAS_MASK) {
+      // register j holds key (j/4)*8 + 4*half + j%4
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int k0 = (j >> 2) * 8 + (j & 3);
+        const uint64_t lanes = (((bits >> k0) & 1u) ? 0x00000000ffffffffull : 0ull) |
+                               (((bits >> (k0 + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
+        S[j] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? S[j] : -__builtin_inff();
+      }
+    }
+    float bm = S[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) bm = __builtin_fmaxf(bm, S[j]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+      bm = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float mn = bm > m[u] + 8.0f ? bm : m[u];
+    if (__builtin_amdgcn_ballot_w64(mn != m[u]) != 0) {
+      const float alpha = fast_exp2(m[u] - mn);   // 0 while m is -inf
+#pragma unroll
+      for (int j = 0; j < 16; ++j) O[u][j] *= alpha;
+      l[u] *= alpha;
+      m[u] = mn;
+    }
+    const float ms = m[u] == -__builtin_inff() ? 0.0f : m[u];
+    float p[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) p[j] = fast_exp2(S[j] - ms);
+    float ls = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ls += p[j];
+    l[u] += ls;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f16x8 ph, pl;
+      split8(p + 8 * t, ph, pl);
+      O[u] = mfma3(kv.vh[t], kv.vl[t], ph, pl, O[u]);
+    }
+  };
+
+  const uint32_t* brow = HAS_MASK ? mask_bits + (int64_t)r * nb : nullptr;
+  KV A, B;
+  f32x16 C0, C1;
+  load_kv(A, 0);
+  load_bias(C0, qb0, 0);
+  // key block kb from `cur` (bias of its first unit in C0); loads the next
+  // block into `nxt` and the next units' bias tiles
+  auto step = [&](int kb, const KV& cur, KV& nxt) {
+    const bool more = kb + 1 < nb;
+    if (more) load_kv(nxt, kb + 1);
+    load_bias(C1, qb1, kb);
+    const uint32_t bits = HAS_MASK ? brow[kb] : 0u;
+    unit(std::integral_constant<int, 0>{}, cur, C0, bits);
+    if (more) load_bias(C0, qb0, kb + 1);
+    unit(std::integral_constant<int, 1>{}, cur, C1, bits);
+  };
+  int kb = 0;
+  for (; kb + 1 < nb; kb += 2) {
+    step(kb, A, B);
+    step(kb + 1, B, A);
+  }
+  if (kb < nb) step(kb, A, B);
+
+  // ---- epilogue ----
+  const int ncb = c_out / 32;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    float lt = l[u];
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lt), __float_as_uint(lt), false, false);
+      lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    f32x16 G;
+    {
+      const float* src = g_ws + ((rh * nb + (u == 0 ? qb0 : qb1)) * 64 + lane) * 16;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * q4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) G[4 * q4 + e] = v[e];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = O[u][8 * t + e] * inv * G[8 * t + e];
+      f16x8 hi, lo;
+      split8(o, hi, lo);
+      f16* dst = og_lds + ((((u * H + h) * 2 + t) * 2) * 64 + lane) * 8;
+      *reinterpret_cast<f16x8*>(dst) = hi;
+      *reinterpret_cast<f16x8*>(dst + 512) = lo;
+    }
+  }
+  __syncthreads();
+  for (int ti = wave; ti < 2 * ncb; ti += H) {
+    const int u = ti / ncb, cb = ti % ncb;
+    if (u == 1 && qb1 == qb0) continue;   // repeated block of an odd last group
+    f32x16 acc = {};
+#pragma unroll
+    for (int hh = 0; hh < H; ++hh)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const f16* a = og_lds + ((((u * H + hh) * 2 + t) * 2) * 64 + lane) * 8;
+        const int64_t wo = (((int64_t)cb * H + hh) * 2 + t) * 512 + lane * 8;
+        acc = mfma3(*reinterpret_cast<const f16x8*>(a), *reinterpret_cast<const f16x8*>(a + 512), ld16(wo_hi + wo),
+                    ld16(wo_lo + wo), acc);
+      }
+    // rows = queries, lane = output column
+    const int c = cb * 32 + (lane & 31);
+    const float bo = b_o != nullptr ? b_o[c] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int q = (u == 0 ? qb0 : qb1) * 32 + acc_row(j, g);
+      if (q < P) out[(int64_t)r * os_r + (int64_t)q * os_p + c] = acc[j] + bo;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_pack_f32(const PackF32Args& a, hipStream_t s) {
+  const int64_t n_w = (int64_t)a.nqkvg * (a.c_in / 16) * 64;
+  const int64_t n_c = (int64_t)a.nqkvg * 32;
+  const int64_t n_o = a.wo != nullptr ? (int64_t)(a.c_out / 32) * a.H * 2 * 64 : 0;
+  const int64_t total = n_w + n_c + n_o;
+  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 4096));
+  hipLaunchKernelGGL(pack_f32_kernel, dim3(blocks), dim3(256), 0, s, (const float*)a.wq, (const float*)a.wk,
+                     (const float*)a.wv, (const float*)a.wg, (const float*)a.gamma, (const float*)a.beta,
+                     (const float*)a.b_g, a.c_in, a.hd, a.H, a.nqkvg, (f16*)a.w_hi, (f16*)a.w_lo, a.cst, (const float*)a.wo, (f16*)a.wo_hi, (f16*)a.wo_lo, a.c_out);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {
-  dim3 grid((a.P + 31) / 32, a.nrows);
-  const size_t lds = sizeof(float) * 32 * (a.H * 32 + 1);
-  hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(32 * a.H), lds, s, (const float*)a.q_ws, (const float*)a.k_ws,
-                     (const float*)a.v_ws, (const float*)a.g_ws, (const float*)a.bias, a.mask, a.ms_r, a.ms_k, (const float*)a.wo,
-                     (const float*)a.b_o, (float*)a.out, a.os_r, a.os_p, a.H, a.c_out, a.nrows, a.P);
+template <int C_IN>
+static hipError_t proj_f32_dispatch(const ProjF32Args& a, int num_cu, hipStream_t s) {
+  using SH = ProjF32Shape<C_IN>;
+  const int groups = (a.nqkvg + a.with_bias + SH::NB - 1) / SH::NB;
+  const int64_t ntiles = (int64_t)(a.Pp / 32) * a.nrows;
+  const int64_t want = (ntiles + kProjF32Threads / kWave - 1) / (kProjF32Threads / kWave);
+  const int grid_x = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)num_cu * 4));
+  const int rmajor = a.xs_p <= a.xs_r ? 1 : 0;
+  hipLaunchKernelGGL((proj_f32_kernel<C_IN>), dim3(grid_x, groups), dim3(kProjF32Threads), 0, s, (const float*)a.x,
+                     a.xs_r, a.xs_p, rmajor, a.eps, (const f16*)a.w_hi, (const f16*)a.w_lo, a.cst, a.nqkvg,
+                     a.with_bias, (const float*)a.wb, (const float*)a.gamma, (const float*)a.beta, a.hd, a.q_scale, (f16*)a.q_hi, (f16*)a.q_lo, (f16*)a.k_hi, (f16*)a.k_lo, (f16*)a.v_hi,
+                     (f16*)a.v_lo, a.g_ws, a.bias, a.bias_natural, a.bias_scale, a.nrows, a.P, a.Pp, a.H);
   return hipGetLastError();
+}
+
+hipError_t launch_proj_f32(const ProjF32Args& a, int num_cu, hipStream_t s) {
+  if (a.nqkvg + a.with_bias < 1 || a.Pp % 32 != 0 || a.P < 1 || a.P > a.Pp || a.nrows < 1) return hipErrorInvalidValue;
+  switch (a.c_in) {
+    case 64: return proj_f32_dispatch<64>(a, num_cu, s);
+    case 128: return proj_f32_dispatch<128>(a, num_cu, s);
+    case 256: return proj_f32_dispatch<256>(a, num_cu, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bias_to_f32_layout(const float* src, float* dst, int H, int P, int Pp, hipStream_t s) {
+  const int64_t total = (int64_t)H * Pp * Pp;
+  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 8192));
+  hipLaunchKernelGGL(bias_to_f32_layout_kernel, dim3(blocks), dim3(256), 0, s, src, dst, H, P, Pp);
+  return hipGetLastError();
+}
+
+template <int H, bool HAS_MASK>
+static hipError_t attn_f32_dispatch(const AttnF32Args& a, hipStream_t s) {
+  const int nb = a.Pp / 32;
+  const int ngroups = (nb + 1) / 2;
+  const int64_t n = (int64_t)ngroups * a.nrows;
+  if (n > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_f32_kernel<H, HAS_MASK>), dim3((unsigned)n), dim3(H * 64), 0, s, (const f16*)a.q_hi,
+                     (const f16*)a.q_lo, (const f16*)a.k_hi, (const f16*)a.k_lo, (const f16*)a.v_hi,
+                     (const f16*)a.v_lo, a.g_ws, a.bias, a.mask_bits, (const f16*)a.wo_hi, (const f16*)a.wo_lo,
+                     (const float*)a.b_o, (float*)a.out, a.os_r, a.os_p, a.c_out, a.nrows, a.P, nb, ngroups);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_f32(const AttnF32Args& a, hipStream_t s) {
+  if (a.Pp < 32 || a.Pp % 32 != 0 || a.P < 1 || a.P > a.Pp || a.nrows < 1 || a.c_out % 32 != 0)
+    return hipErrorInvalidValue;
+  const bool m = a.mask_bits != nullptr;
+  if (a.H == 4) return m ? attn_f32_dispatch<4, true>(a, s) : attn_f32_dispatch<4, false>(a, s);
+  if (a.H == 8) return m ? attn_f32_dispatch<8, true>(a, s) : attn_f32_dispatch<8, false>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

@@ -19,9 +19,8 @@ struct ProjArgs {
   int64_t xs_r, xs_p;
   const void *gamma, *beta;
   float eps;
-  const void* wT;                // bf16 path: packed q|k|v|g weights
-  const void *wq, *wk, *wv, *wg; // fp32 path: natural layouts
-  const void *wb, *b_g;          // both paths: w_b [c_in][H], gate bias [H*32]
+  const void* wT;                // packed q|k|v|g weights
+  const void *wb, *b_g;          // w_b [c_in][H], gate bias [H*32]
   float q_scale;
   void *q_ws, *k_ws, *v_ws, *g_ws;
   float* bias;                   // pair bias output (rows = the projected rows r); fp16 when swizzled
@@ -32,11 +31,9 @@ struct ProjArgs {
 
 struct AttnArgs {
   const void *q_ws, *k_ws, *v_ws, *g_ws;
-  const void* bias;              // bf16 path: attention layout (fp16, log2 units); fp32 path: [H][P][P] float natural
-  const uint8_t* mask;           // fp32 path: key kept iff mask[r*ms_r + k*ms_k] != 0 (NULL = all)
-  int64_t ms_r, ms_k;
-  const uint32_t* mask_bits;     // bf16 path: keep bits per (row, 32-key block), see launch_mask_bits
-  const void *woT, *wo, *b_o;    // woT for bf16, wo (natural) for fp32
+  const void* bias;              // attention layout (fp16, log2 units)
+  const uint32_t* mask_bits;     // keep bits per (row, 32-key block), see launch_mask_bits; NULL = no mask
+  const void *woT, *b_o;
   void* out;                     // element (r, p, c) at out[r*os_r + p*os_p + c]
   int64_t os_r, os_p;
   int H, c_out, nrows, P, Pp;
@@ -51,7 +48,48 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_mask_bits(const uint8_t* mask, int64_t ms_r, int64_t ms_k, uint32_t* bits, int nrows, int P,
                             int nkb, hipStream_t s);
 
-hipError_t launch_proj_f32(const ProjArgs& a, int mode, hipStream_t s);
-hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
+// ---- fp32 path (fp16-pair operands on the matrix cores) ----
+// Packs the gamma-folded q|k|v|g projection operands (nqkvg blocks of 32
+// columns) and, when wo != NULL, the W_o operand.
+struct PackF32Args {
+  const void *wq, *wk, *wv, *wg, *gamma, *beta, *b_g, *wo;
+  void *w_hi, *w_lo;             // [nqkvg][c_in/16][64][8] fp16 each
+  float* cst;                    // [nqkvg * 32]
+  void *wo_hi, *wo_lo;           // [c_out/32][H][2][64][8] fp16 each
+  int c_in, hd, H, nqkvg, c_out;
+};
+struct ProjF32Args {
+  const void* x;
+  int64_t xs_r, xs_p;
+  float eps;
+  const void *w_hi, *w_lo;       // packed q|k|v|g operands (launch_pack_f32)
+  const float* cst;
+  int nqkvg;                     // q|k|v|g blocks to compute (0 or 4*hd/32)
+  int with_bias;                 // 1: also the pair bias, from wb with LayerNorm gamma and beta
+  const void *wb, *gamma, *beta;
+  int hd;
+  float q_scale;
+  void *q_hi, *q_lo, *k_hi, *k_lo, *v_hi, *v_lo;
+  float* g_ws;
+  float* bias;                   // tiled S^T image (log2 units via bias_scale) or, with bias_natural, [H][P][P]
+  int bias_natural;
+  float bias_scale;
+  int c_in, H, nrows, P, Pp;
+};
+struct AttnF32Args {
+  const void *q_hi, *q_lo, *k_hi, *k_lo, *v_hi, *v_lo;
+  const float* g_ws;
+  const float* bias;             // tiled S^T image, log2 units, -inf at padded keys
+  const uint32_t* mask_bits;     // NULL = no mask
+  const void *wo_hi, *wo_lo;
+  const void* b_o;
+  void* out;
+  int64_t os_r, os_p;
+  int H, c_out, nrows, P, Pp;
+};
+hipError_t launch_pack_f32(const PackF32Args& a, hipStream_t s);
+hipError_t launch_proj_f32(const ProjF32Args& a, int num_cu, hipStream_t s);
+hipError_t launch_bias_to_f32_layout(const float* src, float* dst, int H, int P, int Pp, hipStream_t s);
+hipError_t launch_attn_f32(const AttnF32Args& a, hipStream_t s);
 
 }  // namespace pa

@@ -33,47 +33,59 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool supported_c(int64_t c) { return c == 64 || c == 128 || c == 256; }
 bool supported_h(int64_t H) { return H == 4 || H == 8; }
 
-// Largest attention-row count a launch grid can address (grid.y <= 65535
-// with 4 rows per workgroup on the bf16 path, 1 row on the fp32 path).
-constexpr int64_t kMaxRowsBf16 = 65535LL * 4;
-constexpr int64_t kMaxRowsF32 = 65535LL;
+// Largest attention-row count the launches address (the projection grid
+// and the bf16 attention grid count rows in 4-row groups below 65536).
+constexpr int64_t kMaxRows = 65535LL * 4;
 constexpr int64_t kMaxPositions = 1LL << 20;
 
 // ---- workspace layout -----------------------------------------------------
 struct Layout {
-  size_t wT = 0, woT = 0, q = 0, k = 0, v = 0, g = 0, bias = 0, bits = 0, total = 0;
+  // bf16 path
+  size_t wT = 0, woT = 0, q = 0, k = 0, v = 0, g = 0, bias = 0, bits = 0;
+  // fp32 path: hi/lo planes of q, k, v and of the packed weights
+  size_t q_lo = 0, k_lo = 0, v_lo = 0, w_hi = 0, w_lo = 0, cst = 0, wo_hi = 0, wo_lo = 0;
+  size_t total = 0;
 };
 
 // nrows x P positions, c_in input channels, c_out output channels.
-Layout make_layout(int64_t nrows, int64_t P, int64_t c_in, int64_t c_out, int64_t H, int32_t dtype,
-                   bool with_bias) {
+Layout make_layout(int64_t nrows, int64_t P, int64_t c_in, int64_t c_out, int64_t H, int32_t dtype) {
   Layout L;
   const int64_t hd = H * 32;
+  const int64_t Pp = pad32(P);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
     off += align_up(bytes);
     return at;
   };
+  const size_t plane = (size_t)nrows * H * Pp * 32 * 2;   // one fp16 q/k/v plane
   if (dtype == PAIRATTN_BF16) {
-    const int64_t Pp = pad32(P);
     L.wT = take((size_t)4 * hd * c_in * 2);
     L.woT = take((size_t)c_out * hd * 2);
-    L.q = take((size_t)nrows * H * Pp * 32 * 2);
-    L.k = take((size_t)nrows * H * Pp * 32 * 2);
-    L.v = take((size_t)nrows * H * 32 * Pp * 2);
-    L.g = take((size_t)nrows * H * Pp * 32 * 2);   // gate in the layout of q
+    L.q = take(plane);
+    L.k = take(plane);
+    L.v = take(plane);
+    L.g = take(plane);   // gate in the layout of q
     // the attention reads the bias as fp16 in operand order, Pp x Pp, log2
     // units; a caller-provided bias (row block) is converted into it as well
     L.bias = take((size_t)H * Pp * Pp * 2);
-    L.bits = take((size_t)nrows * (Pp / 32) * 4);
   } else {
-    L.q = take((size_t)nrows * P * hd * 4);
-    L.k = take((size_t)nrows * P * hd * 4);
-    L.v = take((size_t)nrows * P * hd * 4);
-    L.g = take((size_t)nrows * P * hd * 4);
-    if (with_bias) L.bias = take((size_t)H * P * P * 4);
+    const int64_t nblk = 4 * hd / 32;        // q|k|v|g column blocks
+    L.w_hi = take((size_t)nblk * c_in * 64);   // (c_in/16) K-steps x 64 lanes x 8 fp16 per block
+    L.w_lo = take((size_t)nblk * c_in * 64);
+    L.cst = take((size_t)nblk * 32 * 4);
+    L.wo_hi = take((size_t)c_out * hd * 2);
+    L.wo_lo = take((size_t)c_out * hd * 2);
+    L.q = take(plane);
+    L.q_lo = take(plane);
+    L.k = take(plane);
+    L.k_lo = take(plane);
+    L.v = take(plane);
+    L.v_lo = take(plane);
+    L.g = take(2 * plane);                     // float, O^T tile images
+    L.bias = take((size_t)H * Pp * Pp * 4);    // float, S^T tile images
   }
+  L.bits = take((size_t)nrows * (Pp / 32) * 4);
   L.total = off;
   return L;
 }
@@ -168,10 +180,10 @@ int check_shape_common(int64_t I, int64_t c, int64_t H, int64_t d, int32_t dtype
 }
 
 int check_rows_limit(int64_t nrows, int32_t dtype) {
-  const int64_t lim = dtype == PAIRATTN_BF16 ? kMaxRowsBf16 : kMaxRowsF32;
-  if (nrows > lim)
+  (void)dtype;
+  if (nrows > kMaxRows)
     return fail(PAIRATTN_ERR_UNSUPPORTED, "%lld attention rows exceed the launch limit %lld", (long long)nrows,
-                (long long)lim);
+                (long long)kMaxRows);
   return PAIRATTN_OK;
 }
 
@@ -271,7 +283,7 @@ size_t pairattn_tri_workspace_bytes(int64_t I, int64_t c_z, int64_t H, int64_t d
   if ((dtype != PAIRATTN_F32 && dtype != PAIRATTN_BF16) || I < 1 || d != 32 || !supported_h(H) ||
       !supported_c(c_z) || I > kMaxPositions)
     return 0;
-  return make_layout(I, I, c_z, c_z, H, dtype, true).total;
+  return make_layout(I, I, c_z, c_z, H, dtype).total;
 }
 
 size_t pairattn_msa_workspace_bytes(int64_t S, int64_t I, int64_t c_m, int64_t c_z, int64_t H, int64_t d,
@@ -279,14 +291,14 @@ size_t pairattn_msa_workspace_bytes(int64_t S, int64_t I, int64_t c_m, int64_t c
   if ((dtype != PAIRATTN_F32 && dtype != PAIRATTN_BF16) || S < 1 || I < 1 || d != 32 || !supported_h(H) ||
       !supported_c(c_m) || !supported_c(c_z) || I > kMaxPositions)
     return 0;
-  return make_layout(S, I, c_m, c_m, H, dtype, true).total;
+  return make_layout(S, I, c_m, c_m, H, dtype).total;
 }
 
 size_t pairattn_rows_workspace_bytes(int64_t R, int64_t I, int64_t c_z, int64_t H, int64_t d, int32_t dtype) {
   if ((dtype != PAIRATTN_F32 && dtype != PAIRATTN_BF16) || R < 1 || I < 1 || d != 32 || !supported_h(H) ||
       !supported_c(c_z) || I > kMaxPositions)
     return 0;
-  return make_layout(R, I, c_z, c_z, H, dtype, false).total;
+  return make_layout(R, I, c_z, c_z, H, dtype).total;
 }
 
 int pairattn_validate_tri(const void* z, const uint8_t* mask, const pairattn_params* p, const void* out,
@@ -359,34 +371,36 @@ int pairattn_validate_rows(const void* z_rows, const float* bias, const uint8_t*
 // One launch sequence for all three operations: (pack) -> projections of
 // the attended tensor -> (pair bias of a separate tensor) -> attention.
 // ---------------------------------------------------------------------------
-static int run_row_attention(const pairattn_params* p, const Layout& L, hipStream_t s, int num_cu,
-                             // attended tensor
-                             const void* x, int64_t xs_r, int64_t xs_p, int64_t c, int64_t nrows, int64_t P, int64_t H,
-                             // bias: computed in the projection (bias_in_proj), from a separate tensor (zb != NULL), or given
-                             bool bias_in_proj, const void* zb, int64_t zb_c, const float* bias_given,
-                             // mask and output addressing
-                             const uint8_t* mask, int64_t ms_r, int64_t ms_k, void* out, int64_t os_r, int64_t os_p) {
-  const int64_t hd = H * 32;
-  const bool bf = p->dtype == PAIRATTN_BF16;
-  const int Pp = (int)pad32(P);
-  // bf16 path: the attention reads the workspace bias ([H][P][Pp], log2 units);
-  // fp32 path: [H][P][P] natural units, the caller's own array for row blocks
-  float* bias_ws = (bf || bias_given == nullptr) ? reinterpret_cast<float*>(ws_at(p, L.bias)) : nullptr;
-  const void* bias = (bf || bias_given == nullptr) ? (const void*)bias_ws : (const void*)bias_given;
-  const int bias_swz = bf ? 1 : 0;
-  const float bias_scale = bf ? 1.4426950408889634f : 1.0f;
+struct RowAttn {
+  // attended tensor: element (row, position, channel) at x[row*xs_r + pos*xs_p + ch]
+  const void* x;
+  int64_t xs_r, xs_p, c, nrows, P, H;
+  // bias: computed in the projection (bias_in_proj), from a separate tensor (zb != NULL), or given
+  bool bias_in_proj;
+  const void* zb;
+  int64_t zb_c;
+  const float* bias_given;
+  // mask and output addressing
+  const uint8_t* mask;
+  int64_t ms_r, ms_k;
+  void* out;
+  int64_t os_r, os_p;
+};
+
+static int run_row_attention_bf16(const pairattn_params* p, const Layout& L, hipStream_t s, int num_cu,
+                                  const RowAttn& ra) {
+  const int64_t hd = ra.H * 32;
+  const int Pp = (int)pad32(ra.P);
+  // the attention reads the workspace bias (fp16 operand order, log2 units)
+  float* bias_ws = reinterpret_cast<float*>(ws_at(p, L.bias));
 
   pa::ProjArgs pj{};
-  pj.x = x;
-  pj.xs_r = xs_r;
-  pj.xs_p = xs_p;
+  pj.x = ra.x;
+  pj.xs_r = ra.xs_r;
+  pj.xs_p = ra.xs_p;
   pj.gamma = p->ln_gamma;
   pj.beta = p->ln_beta;
   pj.eps = p->ln_eps;
-  pj.wq = p->w_q;
-  pj.wk = p->w_k;
-  pj.wv = p->w_v;
-  pj.wg = p->w_g;
   pj.wb = p->w_b;
   pj.b_g = p->b_g;
   pj.q_ws = ws_at(p, L.q);
@@ -394,54 +408,49 @@ static int run_row_attention(const pairattn_params* p, const Layout& L, hipStrea
   pj.v_ws = ws_at(p, L.v);
   pj.g_ws = ws_at(p, L.g);
   pj.bias = bias_ws;
-  pj.bias_swizzled = bias_swz;
-  pj.bias_scale = bias_scale;
-  pj.c_in = (int)c;
+  pj.bias_swizzled = 1;
+  pj.bias_scale = 1.4426950408889634f;
+  pj.c_in = (int)ra.c;
   pj.hd = (int)hd;
-  pj.H = (int)H;
-  pj.nrows = (int)nrows;
-  pj.P = (int)P;
+  pj.H = (int)ra.H;
+  pj.nrows = (int)ra.nrows;
+  pj.P = (int)ra.P;
   pj.Pp = Pp;
-  const int mode = bias_in_proj ? 1 : 0;
 
   tm_begin(s);
-  if (bf) {
-    pa::PackArgs pk{p->w_q, p->w_k, p->w_v, p->w_g, p->w_o, ws_at(p, L.wT), ws_at(p, L.woT), (int)c, (int)hd, (int)c};
-    PA_TRY(hip_status(pa::launch_pack_bf16(pk, s), "weight packing launch"));
-    tm_mark(s, "pack");
-    pj.wT = ws_at(p, L.wT);
-    pj.q_scale = 1.4426950408889634f / std::sqrt(32.0f);
-    PA_TRY(hip_status(pa::launch_proj_bf16(pj, mode, num_cu, s), "projection launch"));
-  } else {
-    pj.q_scale = 1.0f / std::sqrt(32.0f);
-    PA_TRY(hip_status(pa::launch_proj_f32(pj, mode, s), "projection launch"));
-  }
+  pa::PackArgs pk{p->w_q, p->w_k, p->w_v, p->w_g, p->w_o, ws_at(p, L.wT), ws_at(p, L.woT), (int)ra.c, (int)hd,
+                  (int)ra.c};
+  PA_TRY(hip_status(pa::launch_pack_bf16(pk, s), "weight packing launch"));
+  tm_mark(s, "pack");
+  pj.wT = ws_at(p, L.wT);
+  pj.q_scale = 1.4426950408889634f / std::sqrt(32.0f);
+  PA_TRY(hip_status(pa::launch_proj_bf16(pj, ra.bias_in_proj ? 1 : 0, num_cu, s), "projection launch"));
   tm_mark(s, "projection");
 
-  if (zb != nullptr) {   // MSA: bias from the pair tensor with its own LayerNorm
+  if (ra.zb != nullptr) {   // MSA: bias from the pair tensor with its own LayerNorm
     pa::ProjArgs pb{};
-    pb.x = zb;
-    pb.xs_r = P * zb_c;
-    pb.xs_p = zb_c;
+    pb.x = ra.zb;
+    pb.xs_r = ra.P * ra.zb_c;
+    pb.xs_p = ra.zb_c;
     pb.gamma = p->lnz_gamma;
     pb.beta = p->lnz_beta;
     pb.eps = p->ln_eps;
     pb.wb = p->w_b;
     pb.bias = bias_ws;
-    pb.bias_swizzled = bias_swz;
-    pb.bias_scale = bias_scale;
-    pb.c_in = (int)zb_c;
+    pb.bias_swizzled = 1;
+    pb.bias_scale = 1.4426950408889634f;
+    pb.c_in = (int)ra.zb_c;
     pb.hd = (int)hd;
-    pb.H = (int)H;
-    pb.nrows = (int)P;
-    pb.P = (int)P;
+    pb.H = (int)ra.H;
+    pb.nrows = (int)ra.P;
+    pb.P = (int)ra.P;
     pb.Pp = Pp;
-    if (bf) PA_TRY(hip_status(pa::launch_proj_bf16(pb, 2, num_cu, s), "pair-bias launch"));
-    else PA_TRY(hip_status(pa::launch_proj_f32(pb, 2, s), "pair-bias launch"));
+    PA_TRY(hip_status(pa::launch_proj_bf16(pb, 2, num_cu, s), "pair-bias launch"));
     tm_mark(s, "pair_bias");
   }
-  if (bf && bias_given != nullptr) {   // row block: caller's bias -> attention layout
-    PA_TRY(hip_status(pa::launch_bias_to_attn_layout(bias_given, bias_ws, (int)H, (int)P, Pp, s), "bias copy launch"));
+  if (ra.bias_given != nullptr) {   // row block: caller's bias -> attention layout
+    PA_TRY(hip_status(pa::launch_bias_to_attn_layout(ra.bias_given, bias_ws, (int)ra.H, (int)ra.P, Pp, s),
+                      "bias copy launch"));
     tm_mark(s, "bias_copy");
   }
 
@@ -450,34 +459,158 @@ static int run_row_attention(const pairattn_params* p, const Layout& L, hipStrea
   at.k_ws = pj.k_ws;
   at.v_ws = pj.v_ws;
   at.g_ws = pj.g_ws;
-  at.bias = bias;
-  at.mask = mask;
-  // bf16 path: keep bits only when there is a mask (without one the kernel
-  // drops just the keys past P, which it computes)
-  at.mask_bits = (bf && mask != nullptr) ? reinterpret_cast<const uint32_t*>(ws_at(p, L.bits)) : nullptr;
-  at.ms_r = ms_r;
-  at.ms_k = ms_k;
-  at.woT = bf ? ws_at(p, L.woT) : nullptr;
-  at.wo = p->w_o;
+  at.bias = bias_ws;
+  // keep bits only when there is a mask (without one the kernel drops just
+  // the keys past P, which it computes)
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws_at(p, L.bits));
+  at.mask_bits = ra.mask != nullptr ? bits : nullptr;
+  at.woT = ws_at(p, L.woT);
   at.b_o = p->b_o;
-  at.out = out;
-  at.os_r = os_r;
-  at.os_p = os_p;
-  at.H = (int)H;
-  at.c_out = (int)c;
-  at.nrows = (int)nrows;
-  at.P = (int)P;
+  at.out = ra.out;
+  at.os_r = ra.os_r;
+  at.os_p = ra.os_p;
+  at.H = (int)ra.H;
+  at.c_out = (int)ra.c;
+  at.nrows = (int)ra.nrows;
+  at.P = (int)ra.P;
   at.Pp = Pp;
-  if (bf && mask != nullptr) {
-    PA_TRY(hip_status(pa::launch_mask_bits(mask, ms_r, ms_k, reinterpret_cast<uint32_t*>(ws_at(p, L.bits)),
-                                           (int)nrows, (int)P, Pp / 32, s),
+  if (ra.mask != nullptr) {
+    PA_TRY(hip_status(pa::launch_mask_bits(ra.mask, ra.ms_r, ra.ms_k, bits, (int)ra.nrows, (int)ra.P, Pp / 32, s),
                       "mask bits launch"));
     tm_mark(s, "mask_bits");
   }
-  if (bf) PA_TRY(hip_status(pa::launch_attn_bf16(at, s), "attention launch"));
-  else PA_TRY(hip_status(pa::launch_attn_f32(at, s), "attention launch"));
+  PA_TRY(hip_status(pa::launch_attn_bf16(at, s), "attention launch"));
   tm_mark(s, "attention");
   return PAIRATTN_OK;
+}
+
+static int run_row_attention_f32(const pairattn_params* p, const Layout& L, hipStream_t s, int num_cu,
+                                 const RowAttn& ra) {
+  const int64_t hd = ra.H * 32;
+  const int Pp = (int)pad32(ra.P);
+  const int nqkvg = (int)(4 * hd / 32);
+  float* bias_ws = reinterpret_cast<float*>(ws_at(p, L.bias));
+
+  tm_begin(s);
+  pa::PackF32Args pk{};
+  pk.wq = p->w_q;
+  pk.wk = p->w_k;
+  pk.wv = p->w_v;
+  pk.wg = p->w_g;
+  pk.gamma = p->ln_gamma;
+  pk.beta = p->ln_beta;
+  pk.b_g = p->b_g;
+  pk.wo = p->w_o;
+  pk.w_hi = ws_at(p, L.w_hi);
+  pk.w_lo = ws_at(p, L.w_lo);
+  pk.cst = reinterpret_cast<float*>(ws_at(p, L.cst));
+  pk.wo_hi = ws_at(p, L.wo_hi);
+  pk.wo_lo = ws_at(p, L.wo_lo);
+  pk.c_in = (int)ra.c;
+  pk.hd = (int)hd;
+  pk.H = (int)ra.H;
+  pk.nqkvg = nqkvg;
+  pk.c_out = (int)ra.c;
+  PA_TRY(hip_status(pa::launch_pack_f32(pk, s), "weight packing launch"));
+  tm_mark(s, "pack");
+
+  pa::ProjF32Args pj{};
+  pj.x = ra.x;
+  pj.xs_r = ra.xs_r;
+  pj.xs_p = ra.xs_p;
+  pj.eps = p->ln_eps;
+  pj.w_hi = pk.w_hi;
+  pj.w_lo = pk.w_lo;
+  pj.cst = pk.cst;
+  pj.nqkvg = nqkvg;
+  pj.with_bias = ra.bias_in_proj ? 1 : 0;
+  pj.wb = p->w_b;
+  pj.gamma = p->ln_gamma;
+  pj.beta = p->ln_beta;
+  pj.hd = (int)hd;
+  pj.q_scale = 1.4426950408889634f / std::sqrt(32.0f);
+  pj.q_hi = ws_at(p, L.q);
+  pj.q_lo = ws_at(p, L.q_lo);
+  pj.k_hi = ws_at(p, L.k);
+  pj.k_lo = ws_at(p, L.k_lo);
+  pj.v_hi = ws_at(p, L.v);
+  pj.v_lo = ws_at(p, L.v_lo);
+  pj.g_ws = reinterpret_cast<float*>(ws_at(p, L.g));
+  pj.bias = bias_ws;
+  pj.bias_natural = 0;
+  pj.bias_scale = 1.4426950408889634f;
+  pj.c_in = (int)ra.c;
+  pj.H = (int)ra.H;
+  pj.nrows = (int)ra.nrows;
+  pj.P = (int)ra.P;
+  pj.Pp = Pp;
+  PA_TRY(hip_status(pa::launch_proj_f32(pj, num_cu, s), "projection launch"));
+  tm_mark(s, "projection");
+
+  if (ra.zb != nullptr) {
+    pa::ProjF32Args pb{};
+    pb.x = ra.zb;
+    pb.xs_r = ra.P * ra.zb_c;
+    pb.xs_p = ra.zb_c;
+    pb.eps = p->ln_eps;
+    pb.nqkvg = 0;
+    pb.with_bias = 1;
+    pb.wb = p->w_b;
+    pb.gamma = p->lnz_gamma;
+    pb.beta = p->lnz_beta;
+    pb.hd = (int)hd;
+    pb.bias = bias_ws;
+    pb.bias_natural = 0;
+    pb.bias_scale = 1.4426950408889634f;
+    pb.c_in = (int)ra.zb_c;
+    pb.H = (int)ra.H;
+    pb.nrows = (int)ra.P;
+    pb.P = (int)ra.P;
+    pb.Pp = Pp;
+    PA_TRY(hip_status(pa::launch_proj_f32(pb, num_cu, s), "pair-bias launch"));
+    tm_mark(s, "pair_bias");
+  }
+  if (ra.bias_given != nullptr) {
+    PA_TRY(hip_status(pa::launch_bias_to_f32_layout(ra.bias_given, bias_ws, (int)ra.H, (int)ra.P, Pp, s),
+                      "bias copy launch"));
+    tm_mark(s, "bias_copy");
+  }
+
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws_at(p, L.bits));
+  if (ra.mask != nullptr) {
+    PA_TRY(hip_status(pa::launch_mask_bits(ra.mask, ra.ms_r, ra.ms_k, bits, (int)ra.nrows, (int)ra.P, Pp / 32, s),
+                      "mask bits launch"));
+    tm_mark(s, "mask_bits");
+  }
+  pa::AttnF32Args at{};
+  at.q_hi = pj.q_hi;
+  at.q_lo = pj.q_lo;
+  at.k_hi = pj.k_hi;
+  at.k_lo = pj.k_lo;
+  at.v_hi = pj.v_hi;
+  at.v_lo = pj.v_lo;
+  at.g_ws = pj.g_ws;
+  at.bias = bias_ws;
+  at.mask_bits = ra.mask != nullptr ? bits : nullptr;
+  at.wo_hi = pk.wo_hi;
+  at.wo_lo = pk.wo_lo;
+  at.b_o = p->b_o;
+  at.out = ra.out;
+  at.os_r = ra.os_r;
+  at.os_p = ra.os_p;
+  at.H = (int)ra.H;
+  at.c_out = (int)ra.c;
+  at.nrows = (int)ra.nrows;
+  at.P = (int)ra.P;
+  at.Pp = Pp;
+  PA_TRY(hip_status(pa::launch_attn_f32(at, s), "attention launch"));
+  tm_mark(s, "attention");
+  return PAIRATTN_OK;
+}
+
+static int run_row_attention(const pairattn_params* p, const Layout& L, hipStream_t s, int num_cu, const RowAttn& ra) {
+  return p->dtype == PAIRATTN_BF16 ? run_row_attention_bf16(p, L, s, num_cu, ra)
+                                   : run_row_attention_f32(p, L, s, num_cu, ra);
 }
 
 int pairattn_tri_fwd(const void* z, const uint8_t* mask, const pairattn_params* p, void* out, int64_t I, int64_t c_z,
@@ -485,15 +618,15 @@ int pairattn_tri_fwd(const void* z, const uint8_t* mask, const pairattn_params* 
   PA_TRY(pairattn_validate_tri(z, mask, p, out, I, c_z, H, d, orientation));
   int num_cu = 0;
   PA_TRY(check_device(&num_cu));
-  const Layout L = make_layout(I, I, c_z, c_z, H, p->dtype, true);
+  const Layout L = make_layout(I, I, c_z, c_z, H, p->dtype);
   const bool start = orientation == PAIRATTN_START;
   // START: row i, position j -> pair (i, j); END: row j, position i -> pair (i, j)
   const int64_t xs_r = start ? I * c_z : c_z;
   const int64_t xs_p = start ? c_z : I * c_z;
   const int64_t ms_r = start ? I : 1;
   const int64_t ms_k = start ? 1 : I;
-  return run_row_attention(p, L, static_cast<hipStream_t>(stream), num_cu, z, xs_r, xs_p, c_z, I, I, H, true,
-                           nullptr, 0, nullptr, mask, ms_r, ms_k, out, xs_r, xs_p);
+  const RowAttn ra{z, xs_r, xs_p, c_z, I, I, H, true, nullptr, 0, nullptr, mask, ms_r, ms_k, out, xs_r, xs_p};
+  return run_row_attention(p, L, static_cast<hipStream_t>(stream), num_cu, ra);
 }
 
 int pairattn_msa_row_fwd(const void* m, const void* z, const uint8_t* mask, const pairattn_params* p, void* out,
@@ -501,9 +634,9 @@ int pairattn_msa_row_fwd(const void* m, const void* z, const uint8_t* mask, cons
   PA_TRY(pairattn_validate_msa(m, z, mask, p, out, S, I, c_m, c_z, H, d));
   int num_cu = 0;
   PA_TRY(check_device(&num_cu));
-  const Layout L = make_layout(S, I, c_m, c_m, H, p->dtype, true);
-  return run_row_attention(p, L, static_cast<hipStream_t>(stream), num_cu, m, I * c_m, c_m, c_m, S, I, H, false, z,
-                           c_z, nullptr, mask, I, 1, out, I * c_m, c_m);
+  const Layout L = make_layout(S, I, c_m, c_m, H, p->dtype);
+  const RowAttn ra{m, I * c_m, c_m, c_m, S, I, H, false, z, c_z, nullptr, mask, I, 1, out, I * c_m, c_m};
+  return run_row_attention(p, L, static_cast<hipStream_t>(stream), num_cu, ra);
 }
 
 int pairattn_tri_bias(const void* z, const pairattn_params* p, float* bias, int64_t I, int64_t c_z, int64_t H,
@@ -528,27 +661,52 @@ int pairattn_tri_bias(const void* z, const pairattn_params* p, float* bias, int6
   int num_cu = 0;
   PA_TRY(check_device(&num_cu));
   const bool start = orientation == PAIRATTN_START;
-  pa::ProjArgs pb{};
-  pb.x = z;
-  pb.xs_r = start ? I * c_z : c_z;
-  pb.xs_p = start ? c_z : I * c_z;
-  pb.gamma = p->ln_gamma;
-  pb.beta = p->ln_beta;
-  pb.eps = p->ln_eps;
-  pb.wb = p->w_b;
-  pb.bias = bias;
-  pb.bias_swizzled = 0;
-  pb.bias_scale = 1.0f;
-  pb.c_in = (int)c_z;
-  pb.hd = (int)(H * 32);
-  pb.H = (int)H;
-  pb.nrows = (int)I;
-  pb.P = (int)I;
-  pb.Pp = (int)pad32(I);
+  const int64_t xs_r = start ? I * c_z : c_z;
+  const int64_t xs_p = start ? c_z : I * c_z;
   hipStream_t s = static_cast<hipStream_t>(stream);
   tm_begin(s);
-  const int st = p->dtype == PAIRATTN_BF16 ? hip_status(pa::launch_proj_bf16(pb, 2, num_cu, s), "pair-bias launch")
-                                           : hip_status(pa::launch_proj_f32(pb, 2, s), "pair-bias launch");
+  int st;
+  if (p->dtype == PAIRATTN_BF16) {
+    pa::ProjArgs pb{};
+    pb.x = z;
+    pb.xs_r = xs_r;
+    pb.xs_p = xs_p;
+    pb.gamma = p->ln_gamma;
+    pb.beta = p->ln_beta;
+    pb.eps = p->ln_eps;
+    pb.wb = p->w_b;
+    pb.bias = bias;
+    pb.bias_swizzled = 0;
+    pb.bias_scale = 1.0f;
+    pb.c_in = (int)c_z;
+    pb.hd = (int)(H * 32);
+    pb.H = (int)H;
+    pb.nrows = (int)I;
+    pb.P = (int)I;
+    pb.Pp = (int)pad32(I);
+    st = hip_status(pa::launch_proj_bf16(pb, 2, num_cu, s), "pair-bias launch");
+  } else {
+    pa::ProjF32Args pb{};
+    pb.x = z;
+    pb.xs_r = xs_r;
+    pb.xs_p = xs_p;
+    pb.eps = p->ln_eps;
+    pb.nqkvg = 0;
+    pb.with_bias = 1;
+    pb.wb = p->w_b;
+    pb.gamma = p->ln_gamma;
+    pb.beta = p->ln_beta;
+    pb.hd = (int)(H * 32);
+    pb.bias = bias;
+    pb.bias_natural = 1;
+    pb.bias_scale = 1.0f;
+    pb.c_in = (int)c_z;
+    pb.H = (int)H;
+    pb.nrows = (int)I;
+    pb.P = (int)I;
+    pb.Pp = (int)pad32(I);
+    st = hip_status(pa::launch_proj_f32(pb, num_cu, s), "pair-bias launch");
+  }
   tm_mark(s, "pair_bias");
   return st;
 }
@@ -558,9 +716,9 @@ int pairattn_tri_rows_fwd(const void* z_rows, const float* bias, const uint8_t* 
   PA_TRY(pairattn_validate_rows(z_rows, bias, mask_rows, p, out_rows, R, I, c_z, H, d));
   int num_cu = 0;
   PA_TRY(check_device(&num_cu));
-  const Layout L = make_layout(R, I, c_z, c_z, H, p->dtype, false);
-  return run_row_attention(p, L, static_cast<hipStream_t>(stream), num_cu, z_rows, I * c_z, c_z, c_z, R, I, H, false,
-                           nullptr, 0, bias, mask_rows, I, 1, out_rows, I * c_z, c_z);
+  const Layout L = make_layout(R, I, c_z, c_z, H, p->dtype);
+  const RowAttn ra{z_rows, I * c_z, c_z, c_z, R, I, H, false, nullptr, 0, bias, mask_rows, I, 1, out_rows, I * c_z, c_z};
+  return run_row_attention(p, L, static_cast<hipStream_t>(stream), num_cu, ra);
 }
 
 }  // extern "C"

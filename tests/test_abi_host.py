@@ -64,9 +64,13 @@ def test_workspace_sizes():
     # a block of 16 rows needs less than all 64 rows
     assert lib.pairattn_rows_workspace_bytes(16, 64, 128, 4, 32, lib.PAIRATTN_BF16) < \
         lib.pairattn_tri_workspace_bytes(64, 128, 4, 32, lib.PAIRATTN_BF16)
-    # the fp32 row block reads the caller's bias in place
-    assert lib.pairattn_rows_workspace_bytes(64, 64, 128, 4, 32, lib.PAIRATTN_F32) < \
+    assert lib.pairattn_rows_workspace_bytes(16, 64, 128, 4, 32, lib.PAIRATTN_F32) < \
         lib.pairattn_tri_workspace_bytes(64, 128, 4, 32, lib.PAIRATTN_F32)
+    # both paths copy the caller's bias into the attention's own layout: a
+    # block of all rows needs the same workspace as the whole call
+    for dt in (lib.PAIRATTN_BF16, lib.PAIRATTN_F32):
+        assert lib.pairattn_rows_workspace_bytes(64, 64, 128, 4, 32, dt) == \
+            lib.pairattn_tri_workspace_bytes(64, 128, 4, 32, dt)
 
 
 def _tri_ok_params(I=64, c=128, H=4, dtype=lib.PAIRATTN_BF16):
