@@ -356,4 +356,7 @@ CONFIGS = {
     "tri_bf16_i1536": dict(kind="tri", I=1536, c=128, H=4, d=32, dtype=BF16, mask="none", seed=4),
     "rows_bf16_i4096_r512": dict(kind="rows", I=4096, R=512, c=128, H=4, d=32, dtype=BF16,
                                  asu=171, noise=0.1, seed=5),
+    # extra-MSA row attention: 5120 sequences of 64 channels, fp32 end to end
+    "msa_fp32_s5120_i384": dict(kind="msa", S=5120, I=384, c_m=64, c_z=128, H=8, d=32, dtype=F32,
+                                mask="bernoulli", seed=6),
 }
