@@ -2,13 +2,13 @@
 //
 // fp32 in, fp32 out, fp32-accurate, on the matrix cores.  Every product of
 // the path (projections, logits, P.V, output projection) takes its operands
-// as fp16 pairs: an fp32 value x is held as hi + lo, where hi is x with its
-// significand cut to fp16's 11 bits (exact in fp16 for |x| in [2^-14, 65504])
-// and lo = x - hi (exact in fp32) rounded to fp16.  A product a.b is formed
-// from the three fp16 products hi.hi + hi.lo + lo.hi, each a 32x32x16 f16
-// MFMA accumulating in fp32.  What is dropped (lo.lo and the rounding of
-// lo) is below 2^-19 of |a||b|, against 2^-24 for fp32 itself, at three fp16
-// MFMAs per product instead of the sixteen-fold cost of fp32 MFMAs.
+// as fp16 pairs: an fp32 value x is held as hi + lo, where hi is x rounded to
+// fp16 and lo = x - hi (exact in fp32) rounded to fp16.  A product a.b is
+// formed from the three fp16 products hi.hi + hi.lo + lo.hi, each a
+// 32x32x16 f16 MFMA accumulating in fp32.  For |a|, |b| in [2^-14, 65504]
+// what is dropped (lo.lo and the rounding of lo) is below 2^-21 of |a||b|,
+// against 2^-24 for fp32 itself, at three fp16 MFMAs per product instead of
+// the sixteen-fold cost of fp32 MFMAs.
 // Operands must stay below 65504 in magnitude; below 2^-14 they keep an
 // absolute error under 2^-24.  The softmax, LayerNorm, sigmoid, bias and all
 // accumulation run in fp32.
@@ -39,13 +39,29 @@ namespace pa {
 // ---------------------------------------------------------------------------
 // fp16 pairs
 // ---------------------------------------------------------------------------
-// hi: significand cut to 11 bits; lo: the exact remainder rounded to fp16
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// x - h exactly, h the low (or high) fp16 half of a packed register: one
+// mixed-precision FMA (h * -1 + x) instead of a convert and a subtract
+__device__ __forceinline__ float minus_lo_half(f16x2 h, float x) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
+  return r;
+}
+__device__ __forceinline__ float minus_hi_half(f16x2 h, float x) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
+  return r;
+}
+// hi = fp16(x) (round to nearest even), lo = fp16(x - hi): two VALU
+// operations per value (a packed convert per pair for each plane, one FMA)
 __device__ __forceinline__ void split8(const float* x, f16x8& hi, f16x8& lo) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float t = __uint_as_float(__float_as_uint(x[e]) & 0xffffe000u);
-    hi[e] = (f16)t;
-    lo[e] = (f16)(x[e] - t);
+  for (int e = 0; e < 8; e += 2) {
+    const f16x2 h = {(f16)x[e], (f16)x[e + 1]};
+    hi[e] = h[0];
+    hi[e + 1] = h[1];
+    lo[e] = (f16)minus_lo_half(h, x[e]);
+    lo[e + 1] = (f16)minus_hi_half(h, x[e + 1]);
   }
 }
 // D = A.B + C with A = ah + al, B = bh + bl (the small terms first)
@@ -362,8 +378,8 @@ __global__ void bias_to_f32_layout_kernel(const float* __restrict__ src, float* 
 //   block's maximum passes it by more than 8 (log2 units), so p = exp2(s - m)
 //   <= 256; l accumulates p in fp32
 //   O^T += V^T.P^T       six MFMAs, P split into fp16 pairs
-// The K/V chunks of the next key block and the bias tile of the next unit
-// are loaded while the current one computes (two named register sets).
+// The units are software-pipelined: each unit's softmax VALU runs with the
+// next unit's logit MFMAs and its own P.V MFMAs issued in between.
 // Epilogue: o = O/l times the gate, as fp16 pairs into LDS; then the waves
 // share the output tiles (query block x 32 columns), each a K = H*32
 // contraction of og with W_o, + b_o, fp32 stores.
@@ -378,9 +394,14 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
   // og tiles: [query block u][head][chunk t][plane][64 lanes][8] fp16
   __shared__ __attribute__((aligned(1024))) f16 og_lds[2 * H * 2 * 2 * 512];
 
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  // the wave index (= head) as a scalar, so that every load is a uniform
+  // base plus a 32-bit lane offset
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
   const int g = lane >> 5;
   const int h = wave;
+  // lane's 16-byte slot of a 1 KB operand chunk
+  auto ld_chunk = [&](const f16* base) { return reinterpret_cast<const f16x8*>(base)[lane]; };
 
   // XCD-aware order: consecutive ids go round-robin over the 8 XCDs; give
   // each XCD a contiguous range of tiles so that the query groups of a row
@@ -396,108 +417,209 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
   f16x8 Qh[2][2], Ql[2][2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    Qh[0][t] = ld16(q_hi + qkv_chunk(rh, nb, qb0, t) + lane * 8);
-    Ql[0][t] = ld16(q_lo + qkv_chunk(rh, nb, qb0, t) + lane * 8);
-    Qh[1][t] = ld16(q_hi + qkv_chunk(rh, nb, qb1, t) + lane * 8);
-    Ql[1][t] = ld16(q_lo + qkv_chunk(rh, nb, qb1, t) + lane * 8);
+    Qh[0][t] = ld_chunk(q_hi + qkv_chunk(rh, nb, qb0, t));
+    Ql[0][t] = ld_chunk(q_lo + qkv_chunk(rh, nb, qb0, t));
+    Qh[1][t] = ld_chunk(q_hi + qkv_chunk(rh, nb, qb1, t));
+    Ql[1][t] = ld_chunk(q_lo + qkv_chunk(rh, nb, qb1, t));
   }
 
   struct KV {
     f16x8 kh[2], kl[2], vh[2], vl[2];
   };
-  auto load_kv = [&](KV& d, int kb) {
+  auto load_k = [&](KV& d, int kb) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int64_t o = qkv_chunk(rh, nb, kb, t) + lane * 8;
-      d.kh[t] = ld16(k_hi + o);
-      d.kl[t] = ld16(k_lo + o);
-      d.vh[t] = ld16(v_hi + o);
-      d.vl[t] = ld16(v_lo + o);
+      const int64_t o = qkv_chunk(rh, nb, kb, t);
+      d.kh[t] = ld_chunk(k_hi + o);
+      d.kl[t] = ld_chunk(k_lo + o);
     }
   };
-  auto load_bias = [&](f32x16& d, int qb, int kb) {
-    const float* src = bias + ((((int64_t)h * nb + qb) * nb + kb) * 64 + lane) * 16;
+  auto load_v = [&](KV& d, int kb) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t o = qkv_chunk(rh, nb, kb, t);
+      d.vh[t] = ld_chunk(v_hi + o);
+      d.vl[t] = ld_chunk(v_lo + o);
+    }
+  };
+  // a lane's 16 floats of a 4 KB accumulator-image tile
+  auto load_bias_like = [&](f32x16& d, const float* tile) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(tile) + lane * 4;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * q4);
+      const f32x4 v = src[q4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) d[4 * q4 + e] = v[e];
     }
+  };
+  auto load_bias = [&](f32x16& d, int qb, int kb) {
+    load_bias_like(d, bias + (((int64_t)h * nb + qb) * nb + kb) * 1024);
   };
 
   f32x16 O[2] = {};
   float m[2] = {-__builtin_inff(), -__builtin_inff()};
   float l[2] = {0.0f, 0.0f};
+  // logits of the units of query block 0 in SA, of query block 1 in SB; the
+  // bias tiles prefetched for them in CA and CB
+  f32x16 SA, SB, CA, CB;
+  const uint32_t* brow = HAS_MASK ? mask_bits + (int64_t)r * nb : nullptr;
+  uint32_t bits_cur = 0, bits_nxt = 0;
 
-  // one unit: logits, softmax update, P.V
-  auto unit = [&](auto uc, const KV& kv, const f32x16& C, uint32_t bits) {
-    constexpr int u = decltype(uc)::value;
-    f32x16 S = C;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) S = mfma3(kv.kh[t], kv.kl[t], Qh[u][t], Ql[u][t], S);
+  // Unit u (key block kb, query block J) as one instruction stream: the
+  // softmax of u on the VALU, with the six logit MFMAs of unit u+1 (bias of
+  // u+1 in its C buffer, K of u+1's key block in `kn`) and the six P.V MFMAs
+  // of u issued between its groups, so that the matrix cores run while the
+  // softmax does.  Loads: K (J = 0) or V (J = 1) of block kb+1 first, one
+  // stream before their first use, into registers whose last reader has
+  // been issued (at most three of the four K/V tiles of two blocks are
+  // live); the bias tile of unit u+3 at the end, into the C buffer that u+1
+  // has just consumed.
+  auto stream = [&](auto jc, auto nextc, int kb, KV& cur, KV& oth) {
+    constexpr int J = decltype(jc)::value;
+    constexpr int JN = 1 - J;
+    constexpr bool NEXT = decltype(nextc)::value;
+    f32x16& Sc = J ? SB : SA;
+    f32x16& Sn = J ? SA : SB;
+    f32x16& Cn = J ? CA : CB;
+    const KV& kn = J ? oth : cur;
+    // every path issues the same loads (past the last block they repeat it,
+    // into registers nobody reads), so the compiler's counted waits are exact
+    const int kb1 = min(kb + 1, nb - 1);
+    if constexpr (J == 0) {
+      load_k(oth, kb1);
+    } else {
+      load_v(oth, kb1);
+      if (HAS_MASK) bits_nxt = brow[kb1];
+    }
+    // ---- running maximum and rescale (uniform branch, rarely taken) ----
     if constexpr (HAS_MASK) {
       // register j holds key (j/4)*8 + 4*half + j%4
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int k0 = (j >> 2) * 8 + (j & 3);
-        const uint64_t lanes = (((bits >> k0) & 1u) ? 0x00000000ffffffffull : 0ull) |
-                               (((bits >> (k0 + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
-        S[j] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? S[j] : -__builtin_inff();
+        const uint64_t lanes = (((bits_cur >> k0) & 1u) ? 0x00000000ffffffffull : 0ull) |
+                               (((bits_cur >> (k0 + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
+        Sc[j] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? Sc[j] : -__builtin_inff();
       }
     }
-    float bm = S[0];
+    float bm = Sc[0];
 #pragma unroll
-    for (int j = 1; j < 16; ++j) bm = __builtin_fmaxf(bm, S[j]);
+    for (int j = 1; j < 16; ++j) bm = __builtin_fmaxf(bm, Sc[j]);
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
       bm = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    const float mn = bm > m[u] + 8.0f ? bm : m[u];
-    if (__builtin_amdgcn_ballot_w64(mn != m[u]) != 0) {
-      const float alpha = fast_exp2(m[u] - mn);   // 0 while m is -inf
+    const float mn = bm > m[J] + 8.0f ? bm : m[J];
+    if (__builtin_amdgcn_ballot_w64(mn != m[J]) != 0) {
+      const float alpha = fast_exp2(m[J] - mn);   // 0 while m is -inf
 #pragma unroll
-      for (int j = 0; j < 16; ++j) O[u][j] *= alpha;
-      l[u] *= alpha;
-      m[u] = mn;
+      for (int j = 0; j < 16; ++j) O[J][j] *= alpha;
+      l[J] *= alpha;
+      m[J] = mn;
     }
-    const float ms = m[u] == -__builtin_inff() ? 0.0f : m[u];
+    const float ms = m[J] == -__builtin_inff() ? 0.0f : m[J];
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- softmax weights and fp16 pairs, with the MFMAs in between ----
     float p[16];
+    f16x8 ph0, pl0, ph1, pl1;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) p[j] = fast_exp2(S[j] - ms);
-    float ls = 0.0f;
+    for (int j = 0; j < 4; ++j) p[j] = fast_exp2(Sc[j] - ms);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) Sn = mfma32(kn.kl[0], Qh[JN][0], Cn);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) ls += p[j];
-    l[u] += ls;
+    for (int j = 4; j < 8; ++j) p[j] = fast_exp2(Sc[j] - ms);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) Sn = mfma32(kn.kh[0], Ql[JN][0], Sn);
+    __builtin_amdgcn_sched_barrier(0);
+    split8(p, ph0, pl0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) Sn = mfma32(kn.kh[0], Qh[JN][0], Sn);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      float ls = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f16x8 ph, pl;
-      split8(p + 8 * t, ph, pl);
-      O[u] = mfma3(kv.vh[t], kv.vl[t], ph, pl, O[u]);
+      for (int j = 0; j < 8; ++j) ls += p[j];
+      l[J] += ls;
     }
+#pragma unroll
+    for (int j = 8; j < 10; ++j) p[j] = fast_exp2(Sc[j] - ms);
+    __builtin_amdgcn_sched_barrier(0);
+    O[J] = mfma32(cur.vl[0], ph0, O[J]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 10; j < 13; ++j) p[j] = fast_exp2(Sc[j] - ms);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) Sn = mfma32(kn.kl[1], Qh[JN][1], Sn);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 13; j < 16; ++j) p[j] = fast_exp2(Sc[j] - ms);
+    __builtin_amdgcn_sched_barrier(0);
+    O[J] = mfma32(cur.vh[0], pl0, O[J]);
+    __builtin_amdgcn_sched_barrier(0);
+    split8(p + 8, ph1, pl1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) Sn = mfma32(kn.kh[1], Ql[JN][1], Sn);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      float ls = 0.0f;
+#pragma unroll
+      for (int j = 8; j < 16; ++j) ls += p[j];
+      l[J] += ls;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    O[J] = mfma32(cur.vh[0], ph0, O[J]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) Sn = mfma32(kn.kh[1], Qh[JN][1], Sn);
+    __builtin_amdgcn_sched_barrier(0);
+    O[J] = mfma32(cur.vl[1], ph1, O[J]);
+    O[J] = mfma32(cur.vh[1], pl1, O[J]);
+    O[J] = mfma32(cur.vh[1], ph1, O[J]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) load_bias(Cn, JN ? qb1 : qb0, min(kb + (J + 3) / 2, nb - 1));   // unit u+3
+    if constexpr (J == 1 && HAS_MASK) bits_cur = bits_nxt;
   };
 
-  const uint32_t* brow = HAS_MASK ? mask_bits + (int64_t)r * nb : nullptr;
-  KV A, B;
-  f32x16 C0, C1;
-  load_kv(A, 0);
-  load_bias(C0, qb0, 0);
-  // key block kb from `cur` (bias of its first unit in C0); loads the next
-  // block into `nxt` and the next units' bias tiles
-  auto step = [&](int kb, const KV& cur, KV& nxt) {
-    const bool more = kb + 1 < nb;
-    if (more) load_kv(nxt, kb + 1);
-    load_bias(C1, qb1, kb);
-    const uint32_t bits = HAS_MASK ? brow[kb] : 0u;
-    unit(std::integral_constant<int, 0>{}, cur, C0, bits);
-    if (more) load_bias(C0, qb0, kb + 1);
-    unit(std::integral_constant<int, 1>{}, cur, C1, bits);
-  };
+  // prologue: K, V of block 0, the first bias tiles, the logits of unit 0
+  KV X, Y;   // key blocks of even / odd index
+  load_k(X, 0);
+  load_v(X, 0);
+  load_bias(CA, qb0, 0);
+  load_bias(CB, qb1, 0);
+  if (HAS_MASK) bits_cur = brow[0];
+  SA = mfma3(X.kh[0], X.kl[0], Qh[0][0], Ql[0][0], CA);
+  SA = mfma3(X.kh[1], X.kl[1], Qh[0][1], Ql[0][1], SA);
+  load_bias(CA, qb0, min(1, nb - 1));
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using BT = std::true_type;
+  using BF = std::false_type;
   int kb = 0;
-  for (; kb + 1 < nb; kb += 2) {
-    step(kb, A, B);
-    step(kb + 1, B, A);
+  for (; kb + 2 < nb; kb += 2) {
+    stream(I0{}, BT{}, kb, X, Y);
+    stream(I1{}, BT{}, kb, X, Y);
+    stream(I0{}, BT{}, kb + 1, Y, X);
+    stream(I1{}, BT{}, kb + 1, Y, X);
   }
-  if (kb < nb) step(kb, A, B);
+  // the gate tiles (read once, from HBM) are loaded two streams before the
+  // sweep ends, so their latency hides under the last key block
+  f32x16 G0, G1;
+  auto load_gate = [&]() {
+    load_bias_like(G0, g_ws + (rh * nb + qb0) * 1024);
+    load_bias_like(G1, g_ws + (rh * nb + qb1) * 1024);
+  };
+  if (nb - kb == 2) {
+    stream(I0{}, BT{}, kb, X, Y);
+    stream(I1{}, BT{}, kb, X, Y);
+    load_gate();
+    stream(I0{}, BT{}, kb + 1, Y, X);
+    stream(I1{}, BF{}, kb + 1, Y, X);
+  } else {
+    load_gate();
+    stream(I0{}, BT{}, kb, X, Y);
+    stream(I1{}, BF{}, kb, X, Y);
+  }
 
   // ---- epilogue ----
   const int ncb = c_out / 32;
@@ -509,16 +631,7 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
       lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    f32x16 G;
-    {
-      const float* src = g_ws + ((rh * nb + (u == 0 ? qb0 : qb1)) * 64 + lane) * 16;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * q4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) G[4 * q4 + e] = v[e];
-      }
-    }
+    const f32x16& G = u == 0 ? G0 : G1;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       float o[8];
@@ -532,6 +645,8 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
   }
   __syncthreads();
+  // output tiles (query block u, 32 columns cb), each a K = H*32 contraction
+  // of og with W_o, + b_o, fp32 stores
   for (int ti = wave; ti < 2 * ncb; ti += H) {
     const int u = ti / ncb, cb = ti % ncb;
     if (u == 1 && qb1 == qb0) continue;   // repeated block of an odd last group
@@ -541,9 +656,9 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const f16* a = og_lds + ((((u * H + hh) * 2 + t) * 2) * 64 + lane) * 8;
-        const int64_t wo = (((int64_t)cb * H + hh) * 2 + t) * 512 + lane * 8;
-        acc = mfma3(*reinterpret_cast<const f16x8*>(a), *reinterpret_cast<const f16x8*>(a + 512), ld16(wo_hi + wo),
-                    ld16(wo_lo + wo), acc);
+        const int64_t wo = (((int64_t)cb * H + hh) * 2 + t) * 512;
+        acc = mfma3(*reinterpret_cast<const f16x8*>(a), *reinterpret_cast<const f16x8*>(a + 512),
+                    ld_chunk(wo_hi + wo), ld_chunk(wo_lo + wo), acc);
       }
     // rows = queries, lane = output column
     const int c = cb * 32 + (lane & 31);
