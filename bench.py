@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 METRIC = "triangle-attn bf16 TFLOP/s + pair-rows/s at I=1536; % of MFMA peak"
 PEAK_MFMA_16BIT_TFLOPS = 2516.6          # 256 CU x 4096 flop/clk x 2.4 GHz (bf16 = fp16 dense)
 PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_FP32_TFLOPS = 157.3           # dense fp32 matrix peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_tri_bf16_i1536.json")
 CSRC = os.path.join(ROOT, "pair_representation_attention_amd", "csrc")
 # source files each kernel is compiled from (a counter summary is valid for one source state)
@@ -393,6 +394,37 @@ def extra_workloads(args, device, inputs, lib, torch, np) -> dict:
     out["rows_bf16_i4096_r512"] = {"ms": ms, "ms_bias": ms_bias, "ms_rows": ms_rows,
                                    "tflops": f / (ms * 1e-3) / 1e12, "rows_per_s": R / (ms * 1e-3)}
     del rr, zf
+    torch.cuda.empty_cache()
+
+    # extra-MSA row attention, fp32 end to end (fp16-pair operands on the matrix cores)
+    cfg = inputs.CONFIGS["msa_fp32_s5120_i384"]
+    log(f"extra: fp32 extra-MSA row attention S={cfg['S']} I={cfg['I']} c_m={cfg['c_m']}")
+    case = inputs.make_msa_case(S=cfg["S"], I=cfg["I"], c_m=cfg["c_m"], c_z=cfg["c_z"], H=cfg["H"], d=cfg["d"],
+                                dtype=cfg["dtype"], mask=cfg["mask"], seed=cfg["seed"])
+    run = device.MsaRunner(case.m, case.z, case.mask, case.params, cfg["H"], "f32")
+    del case
+    steps = max(3, args.steps)
+    ms = _time(run, steps, 2, torch)
+    stages = {}
+    lib.pairattn_timing_enable(True)
+    for _ in range(steps):
+        run()
+        for name, t in lib.pairattn_timing_read():
+            stages[name] = stages.get(name, 0.0) + t / steps
+    lib.pairattn_timing_enable(False)
+    f = msa_module_flops(cfg["S"], cfg["I"], cfg["c_m"], cfg["c_z"], cfg["H"], cfg["d"])
+    fa = attn_kernel_flops(cfg["S"], cfg["I"], cfg["c_m"], cfg["H"], cfg["d"])
+    a_tf = fa / (stages["attention"] * 1e-3) / 1e12
+    out["msa_fp32_s5120_i384"] = {
+        "ms": ms, "tflops": f["total"] / (ms * 1e-3) / 1e12, "rows_per_s": cfg["S"] / (ms * 1e-3),
+        "kernels_ms": stages,
+        # every product is three f16 MFMA products: fp32 accuracy, measured
+        # against the fp32 matrix peak, with the f16 pipe's own load beside it
+        "attention_roofline": {"bound": "mfma", "achieved": a_tf, "peak": PEAK_MFMA_FP32_TFLOPS, "unit": "TFLOP/s",
+                               "frac": a_tf / PEAK_MFMA_FP32_TFLOPS,
+                               "f16_pipe_frac": 3.0 * a_tf / PEAK_MFMA_16BIT_TFLOPS},
+    }
+    del run
     torch.cuda.empty_cache()
     return out
 

@@ -155,17 +155,19 @@ __device__ __forceinline__ int64_t bias_c_off(int h, int nb, int q, int k) {
 // fp32 O^T image; the pair bias (rows = heads) into the tiled S^T image
 // (log2 units) or, with bias_natural, as [H][P][P] float.
 // ---------------------------------------------------------------------------
-constexpr int kProjF32Threads = 256;
-
 template <int C_IN>
 struct ProjF32Shape {
   static constexpr int KS = C_IN / 16;
-  static constexpr int NB = 32 / KS;                // column blocks per workgroup: 64 KB of operands
+  // 8 waves and 128 KB of operands (fewer column groups, so fewer passes
+  // over x) where the registers allow two waves per SIMD; 4 waves and 64 KB
+  // for 256 input channels
+  static constexpr int THREADS = C_IN <= 128 ? 512 : 256;
+  static constexpr int NB = (C_IN <= 128 ? 64 : 32) / KS;   // column blocks per workgroup
   static constexpr int LDS = NB * KS * 2 * 1024;
 };
 
 template <int C_IN>
-__global__ __launch_bounds__(kProjF32Threads) void proj_f32_kernel(
+__global__ __launch_bounds__(ProjF32Shape<C_IN>::THREADS) void proj_f32_kernel(
     const float* __restrict__ x, int64_t xs_r, int64_t xs_p, int tile_rmajor, float eps, const f16* __restrict__ w_hi,
     const f16* __restrict__ w_lo, const float* __restrict__ cst, int nqkvg, int with_bias,
     const float* __restrict__ wb, const float* __restrict__ gamma, const float* __restrict__ beta, int hd,
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(kProjF32Threads) void proj_f32_kernel(
     int bias_natural, float bias_scale, int nrows, int P, int Pp, int H) {
   using SH = ProjF32Shape<C_IN>;
   constexpr int KS = SH::KS;
-  constexpr int NW = kProjF32Threads / kWave;
+  constexpr int NW = SH::THREADS / kWave;
   __shared__ __attribute__((aligned(1024))) char smem[SH::LDS];
   __shared__ float cstb[8];
   f16* wl_hi = reinterpret_cast<f16*>(smem);
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(kProjF32Threads) void proj_f32_kernel(
   const int b0 = blockIdx.y * SH::NB;
   const int nbl = min(SH::NB, nblk - b0);   // blocks of this workgroup
 
-  for (int i = tid; i < nbl * KS * 64; i += kProjF32Threads) {
+  for (int i = tid; i < nbl * KS * 64; i += SH::THREADS) {
     const int b = b0 + i / (KS * 64);
     if (b < nqkvg) {
       const int64_t src = (int64_t)b0 * KS * 64 + i;
@@ -217,8 +219,7 @@ __global__ __launch_bounds__(kProjF32Threads) void proj_f32_kernel(
   const int nb = Pp / 32;
   const int64_t ntiles = (int64_t)nb * nrows;
   const int64_t stride = (int64_t)gridDim.x * NW;
-  for (int64_t tile = (int64_t)blockIdx.x * NW + wave; tile < ntiles; tile += stride) {
-    int r, p0;
+  auto tile_rp = [&](int64_t tile, int& r, int& p0) {
     if (tile_rmajor) {
       r = (int)(tile / nb);
       p0 = (int)(tile % nb) * 32;
@@ -226,28 +227,55 @@ __global__ __launch_bounds__(kProjF32Threads) void proj_f32_kernel(
       r = (int)(tile % nrows);
       p0 = (int)(tile / nrows) * 32;
     }
+  };
+  // this lane's raw channels of a tile (zeros past P or past the last tile)
+  auto load_raw = [&](int64_t tile, float (*raw)[8]) {
+    if (tile < ntiles) {
+      int r, p0;
+      tile_rp(tile, r, p0);
+      const int p = p0 + lq;
+      if (p < P) {
+        const float* src = x + (int64_t)r * xs_r + (int64_t)p * xs_p + g * 8;
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(src + t * 16);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(src + t * 16 + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            raw[t][e] = a[e];
+            raw[t][4 + e] = b[e];
+          }
+        }
+        return;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) raw[t][e] = 0.0f;
+  };
+  // the next tile's rows are loaded before this one is computed where the
+  // registers allow it (64 input channels)
+  constexpr bool PF = C_IN <= 64;
+  float nxt[KS][8];
+  int64_t tile = (int64_t)blockIdx.x * NW + wave;
+  if (PF) load_raw(tile, nxt);
+  for (; tile < ntiles; tile += stride) {
+    int r, p0;
+    tile_rp(tile, r, p0);
     const int p = p0 + lq;
     const bool valid = p < P;
 
     // ---- LayerNorm (two passes, fp32) and fp16 pairs ----
     float raw[KS][8];
-    if (valid) {
-      const float* src = x + (int64_t)r * xs_r + (int64_t)p * xs_p + g * 8;
-#pragma unroll
-      for (int t = 0; t < KS; ++t) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(src + t * 16);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(src + t * 16 + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          raw[t][e] = a[e];
-          raw[t][4 + e] = b[e];
-        }
-      }
-    } else {
+    if (PF) {
 #pragma unroll
       for (int t = 0; t < KS; ++t)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) raw[t][e] = 0.0f;
+        for (int e = 0; e < 8; ++e) raw[t][e] = nxt[t][e];
+      load_raw(tile + stride, nxt);
+    } else {
+      load_raw(tile, raw);
     }
     float s = 0.0f;
 #pragma unroll
@@ -691,10 +719,10 @@ static hipError_t proj_f32_dispatch(const ProjF32Args& a, int num_cu, hipStream_
   using SH = ProjF32Shape<C_IN>;
   const int groups = (a.nqkvg + a.with_bias + SH::NB - 1) / SH::NB;
   const int64_t ntiles = (int64_t)(a.Pp / 32) * a.nrows;
-  const int64_t want = (ntiles + kProjF32Threads / kWave - 1) / (kProjF32Threads / kWave);
-  const int grid_x = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)num_cu * 4));
+  const int64_t want = (ntiles + SH::THREADS / kWave - 1) / (SH::THREADS / kWave);
+  const int grid_x = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)num_cu * 2));
   const int rmajor = a.xs_p <= a.xs_r ? 1 : 0;
-  hipLaunchKernelGGL((proj_f32_kernel<C_IN>), dim3(grid_x, groups), dim3(kProjF32Threads), 0, s, (const float*)a.x,
+  hipLaunchKernelGGL((proj_f32_kernel<C_IN>), dim3(grid_x, groups), dim3(SH::THREADS), 0, s, (const float*)a.x,
                      a.xs_r, a.xs_p, rmajor, a.eps, (const f16*)a.w_hi, (const f16*)a.w_lo, a.cst, a.nqkvg,
                      a.with_bias, (const float*)a.wb, (const float*)a.gamma, (const float*)a.beta, a.hd, a.q_scale, (f16*)a.q_hi, (f16*)a.q_lo, (f16*)a.k_hi, (f16*)a.k_lo, (f16*)a.v_hi,
                      (f16*)a.v_lo, a.g_ws, a.bias, a.bias_natural, a.bias_scale, a.nrows, a.P, a.Pp, a.H);
