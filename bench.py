@@ -197,6 +197,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=24, help="oracle sample size (rows, about 0.35-1.4 s each by host)")
     ap.add_argument("--extra", action="store_true", help="also time MSA row attention and the row block")
+    ap.add_argument("--workload", choices=["tri_bf16_i1536", "msa_fp32_s5120_i384"], default="tri_bf16_i1536",
+                    help="msa_fp32_s5120_i384: time only the fp32 extra-MSA workload (one JSON line)")
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="MIB",
                     help="after timing, run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -229,6 +231,10 @@ def main() -> int:
         return 2
     lib.load()
     torch.cuda.set_device(0)
+    if args.workload == "msa_fp32_s5120_i384":
+        print(json.dumps({"workload": args.workload, **msa_fp32_workload(args, device, inputs, lib, torch)}),
+              flush=True)
+        return 0
     cfg = inputs.CONFIGS["tri_bf16_i1536"]
     I, c, H, d = cfg["I"], cfg["c"], cfg["H"], cfg["d"]
     log(f"generating Z[{I},{I},{c}] seed={cfg['seed']}")
@@ -396,7 +402,13 @@ def extra_workloads(args, device, inputs, lib, torch, np) -> dict:
     del rr, zf
     torch.cuda.empty_cache()
 
-    # extra-MSA row attention, fp32 end to end (fp16-pair operands on the matrix cores)
+    out["msa_fp32_s5120_i384"] = msa_fp32_workload(args, device, inputs, lib, torch)
+    return out
+
+
+def msa_fp32_workload(args, device, inputs, lib, torch) -> dict:
+    """Extra-MSA row attention, fp32 end to end (fp16-pair operands on the
+    matrix cores): whole-call time and the per-kernel split."""
     cfg = inputs.CONFIGS["msa_fp32_s5120_i384"]
     log(f"extra: fp32 extra-MSA row attention S={cfg['S']} I={cfg['I']} c_m={cfg['c_m']}")
     case = inputs.make_msa_case(S=cfg["S"], I=cfg["I"], c_m=cfg["c_m"], c_z=cfg["c_z"], H=cfg["H"], d=cfg["d"],
@@ -415,7 +427,7 @@ def extra_workloads(args, device, inputs, lib, torch, np) -> dict:
     f = msa_module_flops(cfg["S"], cfg["I"], cfg["c_m"], cfg["c_z"], cfg["H"], cfg["d"])
     fa = attn_kernel_flops(cfg["S"], cfg["I"], cfg["c_m"], cfg["H"], cfg["d"])
     a_tf = fa / (stages["attention"] * 1e-3) / 1e12
-    out["msa_fp32_s5120_i384"] = {
+    res = {
         "ms": ms, "tflops": f["total"] / (ms * 1e-3) / 1e12, "rows_per_s": cfg["S"] / (ms * 1e-3),
         "kernels_ms": stages,
         # every product is three f16 MFMA products: fp32 accuracy, measured
@@ -424,9 +436,14 @@ def extra_workloads(args, device, inputs, lib, torch, np) -> dict:
                                "frac": a_tf / PEAK_MFMA_FP32_TFLOPS,
                                "f16_pipe_frac": 3.0 * a_tf / PEAK_MFMA_16BIT_TFLOPS},
     }
+    # projection: read M once, write q, k, v as fp16 pairs and the gate as fp32
+    pb = 4.0 * cfg["S"] * cfg["I"] * cfg["c_m"] + 16.0 * cfg["S"] * cfg["I"] * cfg["H"] * cfg["d"]
+    p_gbs = pb / (stages["projection"] * 1e-3) / 1e9
+    res["projection_roofline"] = {"bound": "hbm", "achieved": p_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": p_gbs / PEAK_HBM_GBS, "bytes_per_launch": pb}
     del run
     torch.cuda.empty_cache()
-    return out
+    return res
 
 
 if __name__ == "__main__":

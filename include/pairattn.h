@@ -38,6 +38,15 @@
  *     NULL = the null stream).  The return value reports argument
  *     validation and launch errors; a device fault surfaces at the caller's
  *     next synchronisation.
+ *   - Arithmetic.  PAIRATTN_BF16: matrix products take fp16 operands (11
+ *     significant bits) with fp32 accumulation; LayerNorm, the softmax and
+ *     all sums run in fp32.  PAIRATTN_F32: fp32-accurate; every matrix
+ *     product is formed from fp16 pairs (hi = fp16(x), lo = fp16(x - hi);
+ *     hi.hi + hi.lo + lo.hi on the fp16 matrix cores, fp32 accumulation), so
+ *     each product carries a relative error below 2^-21.  On both paths
+ *     intermediate values (normalised activations, q, k, v, the softmax
+ *     weights, the gated o) must stay below 65504 in magnitude, the fp16
+ *     range; inputs in the usual ranges of these models do.
  *   - Supported shapes: d = 32; H in {4, 8}; c, c_m, c_z in {64, 128, 256};
  *     any I >= 1, S >= 1, R >= 1.  Anything else returns
  *     PAIRATTN_ERR_UNSUPPORTED; there is no fallback path.
