@@ -155,9 +155,31 @@ int pairattn_tri_rows_fwd(const void *z_rows, const float *bias, const uint8_t *
                           const pairattn_params *p, void *out_rows, int64_t R, int64_t I,
                           int64_t c_z, int64_t H, int64_t d, void *stream);
 
+/* Triangle attention of the whole Z in blocks: the low-memory form of
+ * pairattn_tri_fwd, for I far above what the one-pass workspace allows.
+ * The pair bias of the whole Z is computed once into the workspace; then
+ * `block` rows (START) or columns (END) at a time are projected and attend
+ * over all keys.  Same arguments and result as pairattn_tri_fwd (bit for bit
+ * when block is even: the attention kernels pair adjacent rows), with a
+ * workspace that grows with block * I instead of I * I (see
+ * pairattn_tri_chunked_workspace_bytes).  block >= 1; block >= I is one
+ * block.  Timing stages: "pair_bias", "blocks".
+ * Source: the memory wall of the pair representation and the remedy of
+ * evaluating attention in slices of rows with the bias computed once
+ * (Intel page, Step 4, tensor slicing of the attention module; Design-CP
+ * page, low-memory mode in its implementation details). */
+size_t pairattn_tri_chunked_workspace_bytes(int64_t I, int64_t c_z, int64_t H, int64_t d,
+                                            int32_t dtype, int64_t block);
+int pairattn_tri_chunked_fwd(const void *z, const uint8_t *mask, const pairattn_params *p,
+                             void *out, int64_t I, int64_t c_z, int64_t H, int64_t d,
+                             int32_t orientation, int64_t block, void *stream);
+
 /* Host-only argument checks with exactly the rules of the entry points
  * above (no HIP call, no device needed).  Return the status the entry point
  * would return before touching the device. */
+int pairattn_validate_tri_chunked(const void *z, const uint8_t *mask, const pairattn_params *p,
+                                  const void *out, int64_t I, int64_t c_z, int64_t H, int64_t d,
+                                  int32_t orientation, int64_t block);
 int pairattn_validate_tri(const void *z, const uint8_t *mask, const pairattn_params *p,
                           const void *out, int64_t I, int64_t c_z, int64_t H, int64_t d,
                           int32_t orientation);

@@ -3,6 +3,7 @@
 // include/pairattn.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -320,6 +321,35 @@ int pairattn_validate_tri(const void* z, const uint8_t* mask, const pairattn_par
   return PAIRATTN_OK;
 }
 
+size_t pairattn_tri_chunked_workspace_bytes(int64_t I, int64_t c_z, int64_t H, int64_t d, int32_t dtype,
+                                            int64_t block) {
+  if ((dtype != PAIRATTN_F32 && dtype != PAIRATTN_BF16) || I < 1 || block < 1 || d != 32 || !supported_h(H) ||
+      !supported_c(c_z) || I > kMaxPositions)
+    return 0;
+  // one block's projections and keep bits; the bias region covers the whole I x I
+  return make_layout(std::min(block, I), I, c_z, c_z, H, dtype).total;
+}
+
+int pairattn_validate_tri_chunked(const void* z, const uint8_t* mask, const pairattn_params* p, const void* out,
+                                  int64_t I, int64_t c_z, int64_t H, int64_t d, int32_t orientation, int64_t block) {
+  g_err[0] = '\0';
+  PA_TRY(check_params(p, true, false));
+  if (z == nullptr || out == nullptr) return fail(PAIRATTN_ERR_ARG, "z and out must not be NULL");
+  if (!aligned16(z) || !aligned16(out)) return fail(PAIRATTN_ERR_ARG, "z and out must be 16-byte aligned");
+  if (orientation != PAIRATTN_START && orientation != PAIRATTN_END)
+    return fail(PAIRATTN_ERR_ARG, "orientation %d is neither PAIRATTN_START nor PAIRATTN_END", orientation);
+  if (block < 1) return fail(PAIRATTN_ERR_ARG, "block must be >= 1 (got %lld)", (long long)block);
+  PA_TRY(check_shape_common(I, c_z, H, d, p->dtype));
+  PA_TRY(check_rows_limit(I, p->dtype));
+  const size_t zbytes = (size_t)I * I * c_z * elt_bytes(p->dtype);
+  if (overlaps(out, zbytes, z, zbytes)) return fail(PAIRATTN_ERR_ARG, "out overlaps z");
+  if (mask != nullptr && overlaps(out, zbytes, mask, (size_t)I * I)) return fail(PAIRATTN_ERR_ARG, "out overlaps mask");
+  const size_t need = pairattn_tri_chunked_workspace_bytes(I, c_z, H, d, p->dtype, block);
+  PA_TRY(check_workspace(p, need));
+  if (overlaps(out, zbytes, p->workspace, p->workspace_bytes)) return fail(PAIRATTN_ERR_ARG, "out overlaps the workspace");
+  return PAIRATTN_OK;
+}
+
 int pairattn_validate_msa(const void* m, const void* z, const uint8_t* mask, const pairattn_params* p,
                           const void* out, int64_t S, int64_t I, int64_t c_m, int64_t c_z, int64_t H, int64_t d) {
   g_err[0] = '\0';
@@ -375,7 +405,9 @@ struct RowAttn {
   // attended tensor: element (row, position, channel) at x[row*xs_r + pos*xs_p + ch]
   const void* x;
   int64_t xs_r, xs_p, c, nrows, P, H;
-  // bias: computed in the projection (bias_in_proj), from a separate tensor (zb != NULL), or given
+  // bias: computed in the projection (bias_in_proj), from a separate tensor
+  // (zb != NULL), given (bias_given), or none of these: already in the
+  // workspace in the attention's layout (chunked calls)
   bool bias_in_proj;
   const void* zb;
   int64_t zb_c;
@@ -385,6 +417,8 @@ struct RowAttn {
   int64_t ms_r, ms_k;
   void* out;
   int64_t os_r, os_p;
+  // part of a longer launch sequence whose caller records the timing marks
+  bool nested = false;
 };
 
 static int run_row_attention_bf16(const pairattn_params* p, const Layout& L, hipStream_t s, int num_cu,
@@ -417,15 +451,18 @@ static int run_row_attention_bf16(const pairattn_params* p, const Layout& L, hip
   pj.P = (int)ra.P;
   pj.Pp = Pp;
 
-  tm_begin(s);
+  auto mark = [&](const char* stage) {
+    if (!ra.nested) tm_mark(s, stage);
+  };
+  if (!ra.nested) tm_begin(s);
   pa::PackArgs pk{p->w_q, p->w_k, p->w_v, p->w_g, p->w_o, ws_at(p, L.wT), ws_at(p, L.woT), (int)ra.c, (int)hd,
                   (int)ra.c};
   PA_TRY(hip_status(pa::launch_pack_bf16(pk, s), "weight packing launch"));
-  tm_mark(s, "pack");
+  mark("pack");
   pj.wT = ws_at(p, L.wT);
   pj.q_scale = 1.4426950408889634f / std::sqrt(32.0f);
   PA_TRY(hip_status(pa::launch_proj_bf16(pj, ra.bias_in_proj ? 1 : 0, num_cu, s), "projection launch"));
-  tm_mark(s, "projection");
+  mark("projection");
 
   if (ra.zb != nullptr) {   // MSA: bias from the pair tensor with its own LayerNorm
     pa::ProjArgs pb{};
@@ -446,12 +483,12 @@ static int run_row_attention_bf16(const pairattn_params* p, const Layout& L, hip
     pb.P = (int)ra.P;
     pb.Pp = Pp;
     PA_TRY(hip_status(pa::launch_proj_bf16(pb, 2, num_cu, s), "pair-bias launch"));
-    tm_mark(s, "pair_bias");
+    mark("pair_bias");
   }
   if (ra.bias_given != nullptr) {   // row block: caller's bias -> attention layout
     PA_TRY(hip_status(pa::launch_bias_to_attn_layout(ra.bias_given, bias_ws, (int)ra.H, (int)ra.P, Pp, s),
                       "bias copy launch"));
-    tm_mark(s, "bias_copy");
+    mark("bias_copy");
   }
 
   pa::AttnArgs at{};
@@ -477,10 +514,10 @@ static int run_row_attention_bf16(const pairattn_params* p, const Layout& L, hip
   if (ra.mask != nullptr) {
     PA_TRY(hip_status(pa::launch_mask_bits(ra.mask, ra.ms_r, ra.ms_k, bits, (int)ra.nrows, (int)ra.P, Pp / 32, s),
                       "mask bits launch"));
-    tm_mark(s, "mask_bits");
+    mark("mask_bits");
   }
   PA_TRY(hip_status(pa::launch_attn_bf16(at, s), "attention launch"));
-  tm_mark(s, "attention");
+  mark("attention");
   return PAIRATTN_OK;
 }
 
@@ -491,7 +528,10 @@ static int run_row_attention_f32(const pairattn_params* p, const Layout& L, hipS
   const int nqkvg = (int)(4 * hd / 32);
   float* bias_ws = reinterpret_cast<float*>(ws_at(p, L.bias));
 
-  tm_begin(s);
+  auto mark = [&](const char* stage) {
+    if (!ra.nested) tm_mark(s, stage);
+  };
+  if (!ra.nested) tm_begin(s);
   pa::PackF32Args pk{};
   pk.wq = p->w_q;
   pk.wk = p->w_k;
@@ -512,7 +552,7 @@ static int run_row_attention_f32(const pairattn_params* p, const Layout& L, hipS
   pk.nqkvg = nqkvg;
   pk.c_out = (int)ra.c;
   PA_TRY(hip_status(pa::launch_pack_f32(pk, s), "weight packing launch"));
-  tm_mark(s, "pack");
+  mark("pack");
 
   pa::ProjF32Args pj{};
   pj.x = ra.x;
@@ -545,7 +585,7 @@ static int run_row_attention_f32(const pairattn_params* p, const Layout& L, hipS
   pj.P = (int)ra.P;
   pj.Pp = Pp;
   PA_TRY(hip_status(pa::launch_proj_f32(pj, num_cu, s), "projection launch"));
-  tm_mark(s, "projection");
+  mark("projection");
 
   if (ra.zb != nullptr) {
     pa::ProjF32Args pb{};
@@ -568,19 +608,19 @@ static int run_row_attention_f32(const pairattn_params* p, const Layout& L, hipS
     pb.P = (int)ra.P;
     pb.Pp = Pp;
     PA_TRY(hip_status(pa::launch_proj_f32(pb, num_cu, s), "pair-bias launch"));
-    tm_mark(s, "pair_bias");
+    mark("pair_bias");
   }
   if (ra.bias_given != nullptr) {
     PA_TRY(hip_status(pa::launch_bias_to_f32_layout(ra.bias_given, bias_ws, (int)ra.H, (int)ra.P, Pp, s),
                       "bias copy launch"));
-    tm_mark(s, "bias_copy");
+    mark("bias_copy");
   }
 
   uint32_t* bits = reinterpret_cast<uint32_t*>(ws_at(p, L.bits));
   if (ra.mask != nullptr) {
     PA_TRY(hip_status(pa::launch_mask_bits(ra.mask, ra.ms_r, ra.ms_k, bits, (int)ra.nrows, (int)ra.P, Pp / 32, s),
                       "mask bits launch"));
-    tm_mark(s, "mask_bits");
+    mark("mask_bits");
   }
   pa::AttnF32Args at{};
   at.q_hi = pj.q_hi;
@@ -604,7 +644,7 @@ static int run_row_attention_f32(const pairattn_params* p, const Layout& L, hipS
   at.P = (int)ra.P;
   at.Pp = Pp;
   PA_TRY(hip_status(pa::launch_attn_f32(at, s), "attention launch"));
-  tm_mark(s, "attention");
+  mark("attention");
   return PAIRATTN_OK;
 }
 
@@ -709,6 +749,83 @@ int pairattn_tri_bias(const void* z, const pairattn_params* p, float* bias, int6
   }
   tm_mark(s, "pair_bias");
   return st;
+}
+
+int pairattn_tri_chunked_fwd(const void* z, const uint8_t* mask, const pairattn_params* p, void* out, int64_t I,
+                             int64_t c_z, int64_t H, int64_t d, int32_t orientation, int64_t block, void* stream) {
+  PA_TRY(pairattn_validate_tri_chunked(z, mask, p, out, I, c_z, H, d, orientation, block));
+  int num_cu = 0;
+  PA_TRY(check_device(&num_cu));
+  block = std::min(block, I);
+  const Layout L = make_layout(block, I, c_z, c_z, H, p->dtype);
+  const bool start = orientation == PAIRATTN_START;
+  const bool bf = p->dtype == PAIRATTN_BF16;
+  const int Pp = (int)pad32(I);
+  const int64_t xs_r = start ? I * c_z : c_z;   // START: row i, position j; END: column j, position i
+  const int64_t xs_p = start ? c_z : I * c_z;
+  const int64_t ms_r = start ? I : 1;
+  const int64_t ms_k = start ? 1 : I;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  tm_begin(s);
+
+  // the pair bias of the whole Z, once, into the workspace in the attention's layout
+  if (bf) {
+    pa::ProjArgs pb{};
+    pb.x = z;
+    pb.xs_r = xs_r;
+    pb.xs_p = xs_p;
+    pb.gamma = p->ln_gamma;
+    pb.beta = p->ln_beta;
+    pb.eps = p->ln_eps;
+    pb.wb = p->w_b;
+    pb.bias = reinterpret_cast<float*>(ws_at(p, L.bias));
+    pb.bias_swizzled = 1;
+    pb.bias_scale = 1.4426950408889634f;
+    pb.c_in = (int)c_z;
+    pb.hd = (int)(H * 32);
+    pb.H = (int)H;
+    pb.nrows = (int)I;
+    pb.P = (int)I;
+    pb.Pp = Pp;
+    PA_TRY(hip_status(pa::launch_proj_bf16(pb, 2, num_cu, s), "pair-bias launch"));
+  } else {
+    pa::ProjF32Args pb{};
+    pb.x = z;
+    pb.xs_r = xs_r;
+    pb.xs_p = xs_p;
+    pb.eps = p->ln_eps;
+    pb.nqkvg = 0;
+    pb.with_bias = 1;
+    pb.wb = p->w_b;
+    pb.gamma = p->ln_gamma;
+    pb.beta = p->ln_beta;
+    pb.hd = (int)(H * 32);
+    pb.bias = reinterpret_cast<float*>(ws_at(p, L.bias));
+    pb.bias_natural = 0;
+    pb.bias_scale = 1.4426950408889634f;
+    pb.c_in = (int)c_z;
+    pb.H = (int)H;
+    pb.nrows = (int)I;
+    pb.P = (int)I;
+    pb.Pp = Pp;
+    PA_TRY(hip_status(pa::launch_proj_f32(pb, num_cu, s), "pair-bias launch"));
+  }
+  tm_mark(s, "pair_bias");
+
+  // then blocks of rows (START) or columns (END): projections and attention
+  // of `block` rows at a time against the bias above
+  const size_t eb = elt_bytes(p->dtype);
+  for (int64_t b0 = 0; b0 < I; b0 += block) {
+    const int64_t n = std::min(block, I - b0);
+    const int64_t xoff = start ? b0 * I * c_z : b0 * c_z;   // elements
+    RowAttn ra{static_cast<const char*>(z) + xoff * eb, xs_r, xs_p, c_z, n, I, H, false, nullptr, 0, nullptr,
+               mask != nullptr ? mask + (start ? b0 * I : b0) : nullptr, ms_r, ms_k,
+               static_cast<char*>(out) + xoff * eb, xs_r, xs_p};
+    ra.nested = true;
+    PA_TRY(run_row_attention(p, L, s, num_cu, ra));
+  }
+  tm_mark(s, "blocks");
+  return PAIRATTN_OK;
 }
 
 int pairattn_tri_rows_fwd(const void* z_rows, const float* bias, const uint8_t* mask_rows, const pairattn_params* p,

@@ -84,6 +84,26 @@ class TriRunner:
         return self.out
 
 
+class TriChunkedRunner:
+    """Triangle attention of a device-resident Z in blocks of rows (START)
+    or columns (END): pairattn_tri_chunked_fwd."""
+
+    def __init__(self, z_dev, mask_dev, params, H: int, dtype: str, block: int, d: int = 32, device="cuda"):
+        torch = _torch()
+        self.I, _, self.c = z_dev.shape
+        self.H, self.d, self.dtype, self.block = H, d, dtype, block
+        self.z = z_dev
+        self.mask = mask_dev
+        self.workspace_bytes = lib.pairattn_tri_chunked_workspace_bytes(self.I, self.c, H, d, dtype_code(dtype), block)
+        self.params = make_params(params, dtype, self.workspace_bytes, device)
+        self.out = torch.empty_like(self.z)
+
+    def __call__(self, orientation: int, stream=None):
+        lib.pairattn_tri_chunked_fwd(self.z, self.mask, self.params, self.out, self.I, self.c, self.H, self.d,
+                                     orientation, self.block, stream)
+        return self.out
+
+
 class MsaRunner:
     def __init__(self, m: np.ndarray, z: np.ndarray, mask: Optional[np.ndarray], params, H: int, dtype: str,
                  d: int = 32, device="cuda"):

@@ -345,6 +345,28 @@ def make_rows_case(I: int, R: int, c: int = 128, H: int = 4, d: int = 32, asu: i
     return RowsCase(I=I, R=R, c=c, H=H, d=d, zbits=zbits, r0=r0, params=params, seed=seed)
 
 
+def make_z_device(I: int, c: int, seed: int, dtype: str = BF16, device: str = "cuda"):
+    """Z[I, I, c] ~ N(0, 1) drawn on the device, for pair tensors too large
+    to generate on the host (I = 16384: 68.7 GB in bf16).  Row blocks are
+    drawn in order from one torch generator seeded with `seed`, so the tensor
+    depends only on (I, c, seed, dtype); the values are rounded to the dtype."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    z = torch.empty((I, I, c), dtype=torch.bfloat16 if dtype == BF16 else torch.float32, device=device)
+    step = max(1, (1 << 27) // (I * c))
+    for r0 in range(0, I, step):
+        r1 = min(I, r0 + step)
+        z[r0:r1] = torch.randn((r1 - r0, I, c), generator=g, device=device, dtype=torch.float32).to(z.dtype)
+    return z
+
+
+def make_chunked_params(c: int, H: int, d: int, seed: int, dtype: str = BF16) -> Params:
+    """Weights of the device-generated pair tensor workloads (host, seeded)."""
+    r_w = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 3])))
+    return make_params(r_w, c, H, d, dtype, affine=True, biases=True)
+
+
 # ----------------------------------------------------------------------------
 # the workload table
 # ----------------------------------------------------------------------------
@@ -356,6 +378,9 @@ CONFIGS = {
     "tri_bf16_i1536": dict(kind="tri", I=1536, c=128, H=4, d=32, dtype=BF16, mask="none", seed=4),
     "rows_bf16_i4096_r512": dict(kind="rows", I=4096, R=512, c=128, H=4, d=32, dtype=BF16,
                                  asu=171, noise=0.1, seed=5),
+    # I far beyond the one-pass workspace: Z drawn on the device, attention in blocks of 1024 rows
+    "tri_bf16_i16384_chunked": dict(kind="tri_chunked", I=16384, c=128, H=4, d=32, dtype=BF16, mask="none",
+                                    block=1024, seed=7),
     # extra-MSA row attention: 5120 sequences of 64 channels, fp32 end to end
     "msa_fp32_s5120_i384": dict(kind="msa", S=5120, I=384, c_m=64, c_z=128, H=8, d=32, dtype=F32,
                                 mask="bernoulli", seed=6),

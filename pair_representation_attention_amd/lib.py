@@ -78,6 +78,9 @@ _SIGNATURES = {
     "pairattn_msa_row_fwd": (ctypes.c_int, [_P, _P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
     "pairattn_tri_bias": (ctypes.c_int, [_P, _PP, _P, _I64, _I64, _I64, _I32, _P]),
     "pairattn_tri_rows_fwd": (ctypes.c_int, [_P, _P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I64, _P]),
+    "pairattn_tri_chunked_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64, _I32, _I64]),
+    "pairattn_tri_chunked_fwd": (ctypes.c_int, [_P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I32, _I64, _P]),
+    "pairattn_validate_tri_chunked": (ctypes.c_int, [_P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I32, _I64]),
     "pairattn_validate_tri": (ctypes.c_int, [_P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I32]),
     "pairattn_validate_msa": (ctypes.c_int, [_P, _P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I64, _I64]),
     "pairattn_validate_rows": (ctypes.c_int, [_P, _P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I64]),
@@ -192,6 +195,22 @@ def pairattn_tri_rows_fwd(z_rows, bias, mask_rows, params, out_rows, R, I, c_z, 
     st = load().pairattn_tri_rows_fwd(_ptr(z_rows), _ptr(bias), _ptr(mask_rows), ctypes.byref(params.struct()),
                                       _ptr(out_rows), R, I, c_z, H, d, _stream(stream))
     return _check(st, "pairattn_tri_rows_fwd") if check else st
+
+
+def pairattn_tri_chunked_workspace_bytes(I, c_z, H, d, dtype, block) -> int:
+    return load().pairattn_tri_chunked_workspace_bytes(I, c_z, H, d, dtype, block)
+
+
+def pairattn_tri_chunked_fwd(z, mask, params, out, I, c_z, H, d, orientation, block, stream=None,
+                             check=True) -> int:
+    st = load().pairattn_tri_chunked_fwd(_ptr(z), _ptr(mask), ctypes.byref(params.struct()), _ptr(out), I, c_z, H,
+                                         d, orientation, block, _stream(stream))
+    return _check(st, "pairattn_tri_chunked_fwd") if check else st
+
+
+def pairattn_validate_tri_chunked(z, mask, params, out, I, c_z, H, d, orientation, block) -> int:
+    return load().pairattn_validate_tri_chunked(_ptr(z), _ptr(mask), ctypes.byref(params.struct()), _ptr(out), I,
+                                                c_z, H, d, orientation, block)
 
 
 def pairattn_validate_tri(z, mask, params, out, I, c_z, H, d, orientation) -> int:

@@ -180,3 +180,61 @@ def test_python_binding_raises_on_error():
     with pytest.raises(lib.PairAttnError) as ei:
         lib.pairattn_tri_fwd(Z, None, _tri_ok_params(), OUT, 64, 128, 4, 48, 0, stream=0)
     assert ei.value.status == lib.PAIRATTN_ERR_UNSUPPORTED
+
+
+# ----------------------------------------------------------------------------
+# chunked triangle attention: workspace and argument rules
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", [lib.PAIRATTN_BF16, lib.PAIRATTN_F32])
+def test_chunked_workspace_sizes(dt):
+    full = lib.pairattn_tri_workspace_bytes(1024, 128, 4, 32, dt)
+    sizes = [lib.pairattn_tri_chunked_workspace_bytes(1024, 128, 4, 32, dt, b) for b in (1, 64, 256, 1024)]
+    assert all(x > 0 for x in sizes)
+    assert sizes == sorted(sizes) and sizes[0] < sizes[-1]
+    # one block of all rows is the one-pass layout; more never costs more
+    assert sizes[-1] == full
+    assert lib.pairattn_tri_chunked_workspace_bytes(1024, 128, 4, 32, dt, 4096) == full
+    # a block of 64 rows needs about 64/1024 of the projections plus the whole bias
+    assert sizes[1] < full / 8
+    assert lib.pairattn_tri_chunked_workspace_bytes(1024, 128, 4, 32, dt, 0) == 0
+    assert lib.pairattn_tri_chunked_workspace_bytes(1024, 96, 4, 32, dt, 64) == 0
+
+
+def test_chunked_at_i16384_fits_where_one_pass_does_not():
+    """I = 16384, c = 128, H = 4, bf16: Z and the update take 68.7 GB each.
+    The one-pass workspace (about 277 GB) cannot sit beside them on a 288 GB
+    device; blocks of 1024 rows need about 19 GB (17.2 GB of projections,
+    2.1 GB of bias)."""
+    one = lib.pairattn_tri_workspace_bytes(16384, 128, 4, 32, lib.PAIRATTN_BF16)
+    chunk = lib.pairattn_tri_chunked_workspace_bytes(16384, 128, 4, 32, lib.PAIRATTN_BF16, 1024)
+    zb = 16384 * 16384 * 128 * 2
+    assert one + 2 * zb > 288e9
+    assert chunk < 20e9 and chunk + 2 * zb < 160e9
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block=0), lib.PAIRATTN_ERR_ARG),
+    (dict(block=-3), lib.PAIRATTN_ERR_ARG),
+    (dict(z=None), lib.PAIRATTN_ERR_ARG),
+    (dict(orientation=7), lib.PAIRATTN_ERR_ARG),
+    (dict(H=5), lib.PAIRATTN_ERR_UNSUPPORTED),
+    (dict(out=Z + 4096), lib.PAIRATTN_ERR_ARG),
+    (dict(ws_bytes=-1), lib.PAIRATTN_ERR_WORKSPACE),      # one byte short
+])
+def test_validate_tri_chunked(kw, status):
+    args = dict(z=Z, mask=None, out=OUT, I=300, c=128, H=4, d=32, orientation=1, block=64)
+    args.update({k: v for k, v in kw.items() if k != "ws_bytes"})
+    need = lib.pairattn_tri_chunked_workspace_bytes(300, 128, 4, 32, lib.PAIRATTN_BF16, 64)
+    p = _params(lib.PAIRATTN_BF16, ws=WS, ws_bytes=need + kw.get("ws_bytes", 0))
+    st = lib.pairattn_validate_tri_chunked(args["z"], args["mask"], p, args["out"], args["I"], args["c"], args["H"],
+                                           args["d"], args["orientation"], args["block"])
+    assert st == status, lib.last_error()
+    st2 = lib.pairattn_tri_chunked_fwd(args["z"], args["mask"], p, args["out"], args["I"], args["c"], args["H"],
+                                       args["d"], args["orientation"], args["block"], stream=0, check=False)
+    assert st2 == status
+
+
+def test_validate_tri_chunked_ok():
+    need = lib.pairattn_tri_chunked_workspace_bytes(300, 128, 4, 32, lib.PAIRATTN_F32, 64)
+    p = _params(lib.PAIRATTN_F32, ws=WS, ws_bytes=need)
+    assert lib.pairattn_validate_tri_chunked(Z, None, p, OUT, 300, 128, 4, 32, 0, 64) == lib.PAIRATTN_OK
