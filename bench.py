@@ -197,8 +197,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=24, help="oracle sample size (rows, about 0.35-1.4 s each by host)")
     ap.add_argument("--extra", action="store_true", help="also time MSA row attention and the row block")
-    ap.add_argument("--workload", choices=["tri_bf16_i1536", "msa_fp32_s5120_i384"], default="tri_bf16_i1536",
-                    help="msa_fp32_s5120_i384: time only the fp32 extra-MSA workload (one JSON line)")
+    ap.add_argument("--workload", choices=["tri_bf16_i1536", "msa_fp32_s5120_i384", "tri_bf16_i16384_chunked"],
+                    default="tri_bf16_i1536",
+                    help="time only the fp32 extra-MSA workload, or chunked triangle attention at I = 16384 "
+                         "(one JSON line)")
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="MIB",
                     help="after timing, run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -231,9 +233,9 @@ def main() -> int:
         return 2
     lib.load()
     torch.cuda.set_device(0)
-    if args.workload == "msa_fp32_s5120_i384":
-        print(json.dumps({"workload": args.workload, **msa_fp32_workload(args, device, inputs, lib, torch)}),
-              flush=True)
+    if args.workload != "tri_bf16_i1536":
+        fn = msa_fp32_workload if args.workload == "msa_fp32_s5120_i384" else chunked_workload
+        print(json.dumps({"workload": args.workload, **fn(args, device, inputs, lib, torch)}), flush=True)
         return 0
     cfg = inputs.CONFIGS["tri_bf16_i1536"]
     I, c, H, d = cfg["I"], cfg["c"], cfg["H"], cfg["d"]
@@ -442,6 +444,34 @@ def msa_fp32_workload(args, device, inputs, lib, torch) -> dict:
     res["projection_roofline"] = {"bound": "hbm", "achieved": p_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                   "frac": p_gbs / PEAK_HBM_GBS, "bytes_per_launch": pb}
     del run
+    torch.cuda.empty_cache()
+    return res
+
+
+def chunked_workload(args, device, inputs, lib, torch) -> dict:
+    """Starting-node triangle attention of Z[16384, 16384, 128] bf16 in blocks
+    of 1024 rows (pairattn_tri_chunked_fwd): the one-pass workspace would not
+    fit beside Z and the update.  One call per step; Z drawn on the device."""
+    cfg = inputs.CONFIGS["tri_bf16_i16384_chunked"]
+    I, c, H, d, block = cfg["I"], cfg["c"], cfg["H"], cfg["d"], cfg["block"]
+    log(f"chunked: generating Z[{I},{I},{c}] on the device")
+    z = inputs.make_z_device(I, c, cfg["seed"])
+    p = inputs.make_chunked_params(c, H, d, cfg["seed"])
+    run = device.TriChunkedRunner(z, None, p, H, "bf16", block)
+    steps = max(1, min(args.steps, 3))
+    ms = _time(lambda: run(lib.PAIRATTN_START), steps, 1, torch)
+    stages = {}
+    lib.pairattn_timing_enable(True)
+    run(lib.PAIRATTN_START)
+    for name, t in lib.pairattn_timing_read():
+        stages[name] = t
+    lib.pairattn_timing_enable(False)
+    f = tri_module_flops(I, I, c, H, d, with_bias=True)["total"]
+    res = {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12, "rows_per_s": I / (ms * 1e-3), "block": block,
+           "stages_ms": stages, "workspace_bytes": run.workspace_bytes,
+           "one_pass_workspace_bytes": lib.pairattn_tri_workspace_bytes(I, c, H, d, lib.PAIRATTN_BF16),
+           "z_bytes": I * I * c * 2, "frac_of_peak": f / (ms * 1e-3) / 1e12 / PEAK_MFMA_16BIT_TFLOPS}
+    del run, z
     torch.cuda.empty_cache()
     return res
 
