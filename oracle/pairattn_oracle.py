@@ -311,6 +311,60 @@ def msa_row(m, z, mask, p: Mapping, H: int, seqs: Optional[Sequence[int]] = None
 
 
 # ----------------------------------------------------------------------------
+# one key shard at a time (2D grid sharding with ring attention)
+# ----------------------------------------------------------------------------
+def tri_partial(q_pairs, kv_pairs, bias_hqk, mask_rows, p: Mapping, H: int):
+    """Starting-node attention of R rows' query pairs against one shard of
+    key pairs of the same rows.
+
+    In the 2D grid of the Design-CP page (Metodologia 1, 2D grid sharding)
+    a device holds the pairs of its rows and columns: its queries.  Keys and
+    values arrive shard by shard around the ring, and the softmax is
+    assembled across shards without ever forming the I x I scores.
+    q_pairs [R, Jq, c] and kv_pairs [R, Kn, c]; bias_hqk [H, Jq, Kn]
+    (query, key) for these queries and keys; mask_rows [R, Kn] or None.
+
+    Returns (o, lse):
+      o   [R, Jq, H*d]  per head, the softmax-weighted sum of v over this
+                        shard's kept keys (0 when it has none);
+      lse [R, H, Jq]    ln sum_k exp(logit_k) over the same keys (-inf when
+                        none), so that shards combine by
+                        lse = ln sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) o_s.
+    """
+    qp, kp = _f64(q_pairs), _f64(kv_pairs)
+    R, Jq, Kn = qp.shape[0], qp.shape[1], kp.shape[1]
+    bias = _f64(bias_hqk)
+    keep = np.ones((R, Kn), bool) if mask_rows is None else np.asarray(mask_rows) != 0
+    hd = _param(p, "w_q").shape[1]
+    o = np.empty((R, Jq, hd))
+    lse = np.empty((R, H, Jq))
+    for r in range(R):
+        xq = layer_norm(qp[r], p["ln_gamma"], p["ln_beta"], _eps(p))
+        xk = layer_norm(kp[r], p["ln_gamma"], p["ln_beta"], _eps(p))
+        q = heads(xq @ _param(p, "w_q"), H)
+        k = heads(xk @ _param(p, "w_k"), H)
+        v = heads(xk @ _param(p, "w_v"), H)
+        logits = np.einsum("qhd,khd->hqk", q, k) / math.sqrt(q.shape[-1]) + bias
+        kept = keep[r][None, None, :]
+        w = masked_softmax_weights(logits, kept)
+        o[r] = np.einsum("hqk,khd->qhd", w, v).reshape(Jq, hd)
+        x = np.where(kept, logits, -np.inf)
+        mx = x.max(axis=-1)
+        safe = np.where(np.isfinite(mx), mx, 0.0)
+        tot = np.where(kept, np.exp(x - safe[..., None]), 0.0).sum(axis=-1)
+        lse[r] = np.where(tot > 0, safe + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)
+    return o, lse
+
+
+def tri_partial_finish(q_pairs, o, p: Mapping, H: int) -> np.ndarray:
+    """out [R, Jq, c] = (sigmoid(LN(q_pairs) W_g + b_g) * o) W_o + b_o, with o
+    the per-head outputs assembled over every key shard."""
+    qp = _f64(q_pairs)
+    xq = layer_norm(qp, p["ln_gamma"], p["ln_beta"], _eps(p))
+    return gated_output(_f64(o), xq @ _param(p, "w_g"), p)
+
+
+# ----------------------------------------------------------------------------
 # error metrics used by the parity bar
 # ----------------------------------------------------------------------------
 def max_abs_err(y, ref) -> float:

@@ -122,3 +122,40 @@ def msa(m, z, mask, p, H):
                                  [keepM[s][j] != 0 for j in range(I)], d)
             out[s][i] = _finish(o_cat, pr[i]["g"], P)
     return out
+
+
+def partial(q_pairs, kv_pairs, bias, mask, p, H):
+    """One key shard: per-head o = sum_k w_k v_k over the shard's kept keys
+    and lse = ln sum_k exp(logit_k) (explicit loops).  q_pairs [R][Jq][c],
+    kv_pairs [R][Kn][c], bias [H][Jq][Kn], mask [R][Kn] or None.  Returns
+    (o [R][Jq][H*d], lse [R][H][Jq]); a query with no kept key gets o = 0 and
+    lse = -inf."""
+    P, eps = _unpack(p)
+    P["_eps"] = eps
+    qp, kp, bias = _lst(q_pairs), _lst(kv_pairs), _lst(bias)
+    R, Jq, Kn = len(qp), len(qp[0]), len(kp[0])
+    hd = len(P["w_q"][0])
+    d = hd // H
+    keepM = [[1] * Kn for _ in range(R)] if mask is None else _lst(mask)
+    o = [[None] * Jq for _ in range(R)]
+    lse = [[[None] * Jq for _ in range(H)] for _ in range(R)]
+    for r in range(R):
+        pq = [_project_all(qp[r][j], P, H) for j in range(Jq)]
+        pk = [_project_all(kp[r][k], P, H) for k in range(Kn)]
+        for j in range(Jq):
+            o_cat = []
+            for h in range(H):
+                sl = slice(h * d, (h + 1) * d)
+                keep = [keepM[r][k] != 0 for k in range(Kn)]
+                o_cat += _attend(pq[j]["q"][sl], [pk[k]["k"][sl] for k in range(Kn)],
+                                 [pk[k]["v"][sl] for k in range(Kn)], bias[h][j], keep, d)
+                idx = [k for k in range(Kn) if keep[k]]
+                if idx:
+                    lg = [math.fsum(pq[j]["q"][sl][t] * pk[k]["k"][sl][t] for t in range(d)) / math.sqrt(d)
+                          + bias[h][j][k] for k in idx]
+                    mx = max(lg)
+                    lse[r][h][j] = mx + math.log(math.fsum(math.exp(t - mx) for t in lg))
+                else:
+                    lse[r][h][j] = -math.inf
+            o[r][j] = o_cat
+    return o, lse

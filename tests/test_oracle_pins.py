@@ -406,3 +406,68 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     attr, repl = MUTANTS[name]
     monkeypatch.setattr(O, attr, repl)
     assert _brute_gap() > 1e-6, f"mutant {name} was not detected"
+
+
+# ----------------------------------------------------------------------------
+# one key shard at a time (2D grid with ring attention): o and lse per shard
+# ----------------------------------------------------------------------------
+def _partial_case(R=2, Jq=5, Kn=7, c=8, H=2, d=4, seed=23, mask=True):
+    rng = np.random.default_rng(seed)
+    p = inputs.make_params(rng, c, H, d, "f32", affine=True, biases=True).as_dict()
+    qp = rng.standard_normal((R, Jq, c))
+    kp = rng.standard_normal((R, Kn, c))
+    bias = rng.standard_normal((H, Jq, Kn))
+    m = (rng.random((R, Kn)) < 0.7).astype(np.uint8) if mask else None
+    if mask:
+        m[1, :] = 0          # a row whose shard has no kept key
+    return p, qp, kp, bias, m
+
+
+def test_partial_matches_brute_force():
+    p, qp, kp, bias, m = _partial_case()
+    o, lse = oracle.tri_partial(qp, kp, bias, m, p, 2)
+    bo, blse = brute.partial(qp, kp, bias, m, p, 2)
+    assert np.allclose(o, np.array(bo), atol=1e-12, rtol=1e-12)
+    blse = np.array(blse)
+    assert np.array_equal(np.isinf(lse), np.isinf(blse))
+    fin = np.isfinite(blse)
+    assert np.allclose(lse[fin], blse[fin], atol=1e-12, rtol=1e-12)
+    assert np.all(o[1] == 0.0) and np.all(lse[1] == -np.inf)
+
+
+def test_partial_shards_merge_to_the_whole():
+    """lse = ln sum_s exp(lse_s) and o = sum_s exp(lse_s - lse) o_s over a
+    split of the keys give the unsplit o and lse (the softmax over a union of
+    key sets), including shards with no kept key."""
+    p, qp, kp, bias, m = _partial_case(Kn=11, mask=True)
+    o_all, lse_all = oracle.tri_partial(qp, kp, bias, m, p, 2)
+    parts = [slice(0, 4), slice(4, 5), slice(5, 11)]
+    res = [oracle.tri_partial(qp, kp[:, s], bias[:, :, s], m[:, s], p, 2) for s in parts]
+    lse_st = np.stack([r[1] for r in res])                     # [S, R, H, Jq]
+    mx = np.max(lse_st, axis=0)
+    safe = np.where(np.isfinite(mx), mx, 0.0)
+    tot = np.sum(np.exp(lse_st - safe), axis=0)
+    lse = np.where(tot > 0, safe + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)
+    w = np.where(np.isfinite(lse_st), np.exp(lse_st - np.where(np.isfinite(lse), lse, 0.0)), 0.0)   # [S, R, H, Jq]
+    R, Jq, H, d = 2, 5, 2, 4
+    o = np.zeros((R, Jq, H * d))
+    for sidx, (o_s, _) in enumerate(res):
+        ws = w[sidx].transpose(0, 2, 1)                        # [R, Jq, H]
+        o += (o_s.reshape(R, Jq, H, d) * ws[..., None]).reshape(R, Jq, H * d)
+    assert np.allclose(o, o_all, atol=1e-12)
+    assert np.array_equal(np.isinf(lse), np.isinf(lse_all))
+    assert np.allclose(lse[np.isfinite(lse)], lse_all[np.isfinite(lse_all)], atol=1e-12)
+
+
+def test_partial_finish_over_all_keys_is_the_row_form():
+    """Queries and keys from the same rows of Z, every key in one shard:
+    finish(partial) equals starting-node attention of those rows."""
+    case = _tri_case(I=6, c=8, H=2, d=4, mask="random", seed=29)
+    p = case.params_start.as_dict()
+    z = case.z.astype(np.float64)
+    bias = oracle.attention_bias(z, p, 2, oracle.START)
+    rows = np.array([0, 3, 5])
+    o, _ = oracle.tri_partial(z[rows], z[rows], bias, case.mask[rows], p, 2)
+    out = oracle.tri_partial_finish(z[rows], o, p, 2)
+    ref = oracle.tri_rows(z[rows], bias, case.mask[rows], p, 2)
+    assert np.allclose(out, ref, atol=1e-12)
