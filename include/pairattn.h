@@ -174,9 +174,52 @@ int pairattn_tri_chunked_fwd(const void *z, const uint8_t *mask, const pairattn_
                              void *out, int64_t I, int64_t c_z, int64_t H, int64_t d,
                              int32_t orientation, int64_t block, void *stream);
 
+/* One step of ring attention over a 2D device grid: starting-node attention
+ * of the query pairs a device holds against one shard of key pairs of the
+ * same rows, kept as a per-head output and its log-sum-exp so that shards
+ * combine exactly (Design-CP page, Metodologia 1, 2D grid sharding: queries
+ * split along rows, keys/values along columns and passed around a ring,
+ * attention never formed as an I x I matrix).  fp32 path only
+ * (params->dtype = PAIRATTN_F32; PAIRATTN_BF16 returns
+ * PAIRATTN_ERR_UNSUPPORTED).
+ *   q_pairs  [R][Jq][c_z]  the device's query pairs (rows r, their columns)
+ *   kv_pairs [R][Kn][c_z]  one shard of key pairs of the same rows
+ *   bias     [H][Jq][Kn]   float, natural-log units, for these queries/keys
+ *   mask     [R][Kn] uint8 or NULL (key kept iff nonzero)
+ *   o        [R][Jq][H*d]  float: per head, the softmax-weighted sum of v
+ *                          over the shard's kept keys (0 with none)
+ *   lse      [R][H][Jq]    float: ln sum_k exp(logit_k) over those keys
+ *                          (-inf with none)
+ * accumulate = 0 writes o and lse; accumulate != 0 merges this shard into
+ * the o and lse already there: lse' = ln(e^lse + e^lse_s),
+ * o' = e^(lse - lse') o + e^(lse_s - lse') o_s.  Workspace:
+ * pairattn_tri_partial_workspace_bytes. */
+size_t pairattn_tri_partial_workspace_bytes(int64_t R, int64_t Jq, int64_t Kn, int64_t c_z,
+                                            int64_t H, int64_t d, int32_t dtype);
+int pairattn_tri_partial_fwd(const void *q_pairs, const void *kv_pairs, const float *bias,
+                             const uint8_t *mask, const pairattn_params *p, float *o, float *lse,
+                             int32_t accumulate, int64_t R, int64_t Jq, int64_t Kn, int64_t c_z,
+                             int64_t H, int64_t d, void *stream);
+
+/* The end of the ring: out[r][j] = (sigmoid(LN(q_pairs) W_g + b_g) * o) W_o
+ * + b_o for the assembled o of pairattn_tri_partial_fwd.  out [R][Jq][c_z]
+ * float.  Workspace: pairattn_tri_partial_finish_workspace_bytes. */
+size_t pairattn_tri_partial_finish_workspace_bytes(int64_t R, int64_t Jq, int64_t c_z, int64_t H,
+                                                   int64_t d, int32_t dtype);
+int pairattn_tri_partial_finish(const void *q_pairs, const float *o, const pairattn_params *p,
+                                void *out, int64_t R, int64_t Jq, int64_t c_z, int64_t H, int64_t d,
+                                void *stream);
+
 /* Host-only argument checks with exactly the rules of the entry points
  * above (no HIP call, no device needed).  Return the status the entry point
  * would return before touching the device. */
+int pairattn_validate_tri_partial(const void *q_pairs, const void *kv_pairs, const float *bias,
+                                  const uint8_t *mask, const pairattn_params *p, const float *o,
+                                  const float *lse, int64_t R, int64_t Jq, int64_t Kn, int64_t c_z,
+                                  int64_t H, int64_t d);
+int pairattn_validate_tri_partial_finish(const void *q_pairs, const float *o,
+                                         const pairattn_params *p, const void *out, int64_t R,
+                                         int64_t Jq, int64_t c_z, int64_t H, int64_t d);
 int pairattn_validate_tri_chunked(const void *z, const uint8_t *mask, const pairattn_params *p,
                                   const void *out, int64_t I, int64_t c_z, int64_t H, int64_t d,
                                   int32_t orientation, int64_t block);

@@ -146,7 +146,9 @@ __device__ __forceinline__ int64_t bias_c_off(int h, int nb, int q, int k) {
 // positions of one row; a lane holds one position (lane % 32) and, in K-step
 // t, channels t*16 + half*8 .. +7, which is the register image of both MFMA
 // operand kinds.  LayerNorm runs in registers; the normalised activations
-// are split into fp16 pairs.  The workgroup's NB column blocks sit in LDS
+// are split into fp16 pairs.  The launch computes the q|k|v|g blocks
+// [b_first, b_first + nqkvg) of the packed list (q only, k and v only, ...).
+// The workgroup's NB column blocks sit in LDS
 // (hi and lo planes): packed q|k|v|g blocks are copied, the pair-bias block
 // (rows = heads, zero beyond H; the last block when with_bias) is built here
 // from w_b and gamma, with its constants beta . w_b.  Block kinds: q and k (out^T = W^T X^T, rows =
@@ -169,7 +171,7 @@ struct ProjF32Shape {
 template <int C_IN>
 __global__ __launch_bounds__(ProjF32Shape<C_IN>::THREADS) void proj_f32_kernel(
     const float* __restrict__ x, int64_t xs_r, int64_t xs_p, int tile_rmajor, float eps, const f16* __restrict__ w_hi,
-    const f16* __restrict__ w_lo, const float* __restrict__ cst, int nqkvg, int with_bias,
+    const f16* __restrict__ w_lo, const float* __restrict__ cst, int b_first, int nqkvg, int with_bias,
     const float* __restrict__ wb, const float* __restrict__ gamma, const float* __restrict__ beta, int hd,
     float q_scale,
     f16* __restrict__ q_hi, f16* __restrict__ q_lo, f16* __restrict__ k_hi, f16* __restrict__ k_lo,
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(ProjF32Shape<C_IN>::THREADS) void proj_f32_kernel(
   for (int i = tid; i < nbl * KS * 64; i += SH::THREADS) {
     const int b = b0 + i / (KS * 64);
     if (b < nqkvg) {
-      const int64_t src = (int64_t)b0 * KS * 64 + i;
+      const int64_t src = (int64_t)(b_first + b0) * KS * 64 + i;
       *reinterpret_cast<f16x8*>(wl_hi + i * 8) = *reinterpret_cast<const f16x8*>(w_hi + src * 8);
       *reinterpret_cast<f16x8*>(wl_lo + i * 8) = *reinterpret_cast<const f16x8*>(w_lo + src * 8);
     } else {
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(ProjF32Shape<C_IN>::THREADS) void proj_f32_kernel(
       const f16* opl = wl_lo + bl * KS * 512 + lane * 8;
       f32x16 acc = {};
       if (b < nqkvg) {
-        const int col = b * 32;
+        const int col = (b_first + b) * 32;
         const int tsr = col / hd;                 // 0 q, 1 k, 2 v, 3 g
         const int64_t rh = (int64_t)r * H + (col - tsr * hd) / 32;
         const int64_t chunk0 = (rh * nb + (p0 >> 5)) * 2;
@@ -382,19 +384,23 @@ __global__ __launch_bounds__(ProjF32Shape<C_IN>::THREADS) void proj_f32_kernel(
   }
 }
 
-// Caller-provided bias [H][P][P] float (natural-log units) -> tiled S^T image
-// in log2 units, -inf at padded keys.
-__global__ void bias_to_f32_layout_kernel(const float* __restrict__ src, float* __restrict__ dst, int H, int P,
-                                          int Pp) {
-  const int64_t total = (int64_t)H * Pp * Pp;
-  const int nb = Pp / 32;
+// Caller-provided bias [H][Pq][Pk] float (natural-log units) -> tiled S^T
+// image ([h][query block][key block] tiles) in log2 units, -inf at padded
+// keys, 0 at padded queries.
+__global__ void bias_to_f32_layout_kernel(const float* __restrict__ src, float* __restrict__ dst, int H, int Pq,
+                                          int Pk, int Ppq, int Ppk) {
+  const int64_t total = (int64_t)H * Ppq * Ppk;
+  const int nbk = Ppk / 32;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int h = (int)(i / ((int64_t)Pp * Pp));
-    const int64_t rem = i % ((int64_t)Pp * Pp);
-    const int q = (int)(rem / Pp), k = (int)(rem % Pp);
+    const int h = (int)(i / ((int64_t)Ppq * Ppk));
+    const int64_t rem = i % ((int64_t)Ppq * Ppk);
+    const int q = (int)(rem / Ppk), k = (int)(rem % Ppk);
     float v = -__builtin_inff();
-    if (k < P) v = q < P ? src[((int64_t)h * P + q) * P + k] * kLog2e : 0.0f;
-    dst[bias_c_off(h, nb, q, k)] = v;
+    if (k < Pk) v = q < Pq ? src[((int64_t)h * Pq + q) * Pk + k] * kLog2e : 0.0f;
+    const int x = k & 31;
+    const int ln = (q & 31) + 32 * slot_hg(x);
+    const int j = (x >> 3) * 4 + (x & 3);
+    dst[((((int64_t)h * (Ppq / 32) + (q >> 5)) * nbk + (k >> 5)) * 64 + ln) * 16 + j] = v;
   }
 }
 
@@ -412,13 +418,22 @@ __global__ void bias_to_f32_layout_kernel(const float* __restrict__ src, float* 
 // share the output tiles (query block x 32 columns), each a K = H*32
 // contraction of og with W_o, + b_o, fp32 stores.
 // ---------------------------------------------------------------------------
-template <int H, bool HAS_MASK>
+template <int H>
+__device__ __forceinline__ void gate_project_store(f16* og_lds, const f32x16 (&O)[2], const float (&inv)[2],
+                                                   const f32x16& G0, const f32x16& G1, int h, int wave, int lane,
+                                                   const f16* __restrict__ wo_hi, const f16* __restrict__ wo_lo,
+                                                   const float* __restrict__ b_o, float* __restrict__ out,
+                                                   int64_t os_r, int64_t os_p, int c_out, int r, int P, int qb0,
+                                                   int qb1);
+
+template <int H, bool HAS_MASK, int MODE>
 __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_f32_kernel(
     const f16* __restrict__ q_hi, const f16* __restrict__ q_lo, const f16* __restrict__ k_hi,
     const f16* __restrict__ k_lo, const f16* __restrict__ v_hi, const f16* __restrict__ v_lo,
     const float* __restrict__ g_ws, const float* __restrict__ bias, const uint32_t* __restrict__ mask_bits,
     const f16* __restrict__ wo_hi, const f16* __restrict__ wo_lo, const float* __restrict__ b_o,
-    float* __restrict__ out, int64_t os_r, int64_t os_p, int c_out, int nrows, int P, int nb, int ngroups) {
+    float* __restrict__ out, int64_t os_r, int64_t os_p, int c_out, int nrows, int P, int nbq, int nbk, int ngroups,
+    float* __restrict__ o_part, float* __restrict__ lse_part) {
   // og tiles: [query block u][head][chunk t][plane][64 lanes][8] fp16
   __shared__ __attribute__((aligned(1024))) f16 og_lds[2 * H * 2 * 2 * 512];
 
@@ -439,16 +454,16 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
   if ((ntile & 7) == 0) tile = (tile & 7) * (ntile >> 3) + (tile >> 3);
   const int r = (int)(tile / ngroups);
   const int grp = (int)(tile % ngroups);
-  const int qb0 = 2 * grp, qb1 = min(2 * grp + 1, nb - 1);   // an odd last group repeats its block
+  const int qb0 = 2 * grp, qb1 = min(2 * grp + 1, nbq - 1);   // an odd last group repeats its block
   const int64_t rh = (int64_t)r * H + h;
 
   f16x8 Qh[2][2], Ql[2][2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    Qh[0][t] = ld_chunk(q_hi + qkv_chunk(rh, nb, qb0, t));
-    Ql[0][t] = ld_chunk(q_lo + qkv_chunk(rh, nb, qb0, t));
-    Qh[1][t] = ld_chunk(q_hi + qkv_chunk(rh, nb, qb1, t));
-    Ql[1][t] = ld_chunk(q_lo + qkv_chunk(rh, nb, qb1, t));
+    Qh[0][t] = ld_chunk(q_hi + qkv_chunk(rh, nbq, qb0, t));
+    Ql[0][t] = ld_chunk(q_lo + qkv_chunk(rh, nbq, qb0, t));
+    Qh[1][t] = ld_chunk(q_hi + qkv_chunk(rh, nbq, qb1, t));
+    Ql[1][t] = ld_chunk(q_lo + qkv_chunk(rh, nbq, qb1, t));
   }
 
   struct KV {
@@ -457,7 +472,7 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
   auto load_k = [&](KV& d, int kb) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int64_t o = qkv_chunk(rh, nb, kb, t);
+      const int64_t o = qkv_chunk(rh, nbk, kb, t);
       d.kh[t] = ld_chunk(k_hi + o);
       d.kl[t] = ld_chunk(k_lo + o);
     }
@@ -465,7 +480,7 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
   auto load_v = [&](KV& d, int kb) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int64_t o = qkv_chunk(rh, nb, kb, t);
+      const int64_t o = qkv_chunk(rh, nbk, kb, t);
       d.vh[t] = ld_chunk(v_hi + o);
       d.vl[t] = ld_chunk(v_lo + o);
     }
@@ -481,7 +496,7 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
   };
   auto load_bias = [&](f32x16& d, int qb, int kb) {
-    load_bias_like(d, bias + (((int64_t)h * nb + qb) * nb + kb) * 1024);
+    load_bias_like(d, bias + (((int64_t)h * nbq + qb) * nbk + kb) * 1024);
   };
 
   f32x16 O[2] = {};
@@ -490,7 +505,7 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
   // logits of the units of query block 0 in SA, of query block 1 in SB; the
   // bias tiles prefetched for them in CA and CB
   f32x16 SA, SB, CA, CB;
-  const uint32_t* brow = HAS_MASK ? mask_bits + (int64_t)r * nb : nullptr;
+  const uint32_t* brow = HAS_MASK ? mask_bits + (int64_t)r * nbk : nullptr;
   uint32_t bits_cur = 0, bits_nxt = 0;
 
   // Unit u (key block kb, query block J) as one instruction stream: the
@@ -512,7 +527,7 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     const KV& kn = J ? oth : cur;
     // every path issues the same loads (past the last block they repeat it,
     // into registers nobody reads), so the compiler's counted waits are exact
-    const int kb1 = min(kb + 1, nb - 1);
+    const int kb1 = min(kb + 1, nbk - 1);
     if constexpr (J == 0) {
       load_k(oth, kb1);
     } else {
@@ -604,7 +619,7 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     O[J] = mfma32(cur.vh[1], pl1, O[J]);
     O[J] = mfma32(cur.vh[1], ph1, O[J]);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NEXT) load_bias(Cn, JN ? qb1 : qb0, min(kb + (J + 3) / 2, nb - 1));   // unit u+3
+    if constexpr (NEXT) load_bias(Cn, JN ? qb1 : qb0, min(kb + (J + 3) / 2, nbk - 1));   // unit u+3
     if constexpr (J == 1 && HAS_MASK) bits_cur = bits_nxt;
   };
 
@@ -617,14 +632,14 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
   if (HAS_MASK) bits_cur = brow[0];
   SA = mfma3(X.kh[0], X.kl[0], Qh[0][0], Ql[0][0], CA);
   SA = mfma3(X.kh[1], X.kl[1], Qh[0][1], Ql[0][1], SA);
-  load_bias(CA, qb0, min(1, nb - 1));
+  load_bias(CA, qb0, min(1, nbk - 1));
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using BT = std::true_type;
   using BF = std::false_type;
   int kb = 0;
-  for (; kb + 2 < nb; kb += 2) {
+  for (; kb + 2 < nbk; kb += 2) {
     stream(I0{}, BT{}, kb, X, Y);
     stream(I1{}, BT{}, kb, X, Y);
     stream(I0{}, BT{}, kb + 1, Y, X);
@@ -634,10 +649,12 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
   // sweep ends, so their latency hides under the last key block
   f32x16 G0, G1;
   auto load_gate = [&]() {
-    load_bias_like(G0, g_ws + (rh * nb + qb0) * 1024);
-    load_bias_like(G1, g_ws + (rh * nb + qb1) * 1024);
+    if constexpr (MODE == 0) {
+      load_bias_like(G0, g_ws + (rh * nbq + qb0) * 1024);
+      load_bias_like(G1, g_ws + (rh * nbq + qb1) * 1024);
+    }
   };
-  if (nb - kb == 2) {
+  if (nbk - kb == 2) {
     stream(I0{}, BT{}, kb, X, Y);
     stream(I1{}, BT{}, kb, X, Y);
     load_gate();
@@ -650,21 +667,87 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
   }
 
   // ---- epilogue ----
+  float lt[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l[u]), __float_as_uint(l[u]), false, false);
+    lt[u] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);   // the query's l over both lane halves
+  }
+  if constexpr (MODE == 0) {
+    const float inv[2] = {lt[0] > 0.0f ? 1.0f / lt[0] : 0.0f, lt[1] > 0.0f ? 1.0f / lt[1] : 0.0f};
+    gate_project_store<H>(og_lds, O, inv, G0, G1, h, wave, lane, wo_hi, wo_lo, b_o, out, os_r, os_p, c_out, r, P,
+                          qb0, qb1);
+  } else {
+    // one key shard: o = O/l per head ([row][query][h*32 + channel]) and
+    // lse = ln(l) + m ln 2 per (row, head, query); MODE 2 merges them into
+    // the values already there (log-sum-exp weights, fp32)
+    constexpr float kLn2 = 0.6931471805599453f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && qb1 == qb0) continue;   // repeated block of an odd last group
+      const int q = (u == 0 ? qb0 : qb1) * 32 + (lane & 31);
+      if (q >= P) continue;
+      const bool any = lt[u] > 0.0f;
+      const float ms = m[u] == -__builtin_inff() ? 0.0f : m[u];
+      const float lse_new = any ? (ms + __builtin_log2f(lt[u])) * kLn2 : -__builtin_inff();
+      const float inv = any ? 1.0f / lt[u] : 0.0f;
+      float wn = 1.0f, wo = 0.0f, lse = lse_new;
+      float* lse_at = lse_part + ((int64_t)r * H + h) * P + q;
+      if constexpr (MODE == 2) {
+        const float lse_old = *lse_at;
+        const float mx = __builtin_fmaxf(lse_old, lse_new);
+        if (mx == -__builtin_inff()) {
+          wn = 0.0f;   // no kept key in either part: o stays 0, lse -inf
+        } else {
+          wo = expf(lse_old - mx);
+          wn = expf(lse_new - mx);
+          const float den = wo + wn;
+          lse = mx + logf(den);
+          wo /= den;
+          wn /= den;
+        }
+      }
+      // registers 4i..4i+3 hold channels 8i + 4*half + 0..3
+      float* orow = o_part + ((int64_t)r * P + q) * (H * 32) + h * 32 + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4* dst = reinterpret_cast<f32x4*>(orow + 8 * i);
+        f32x4 v = {O[u][4 * i] * inv * wn, O[u][4 * i + 1] * inv * wn, O[u][4 * i + 2] * inv * wn,
+                   O[u][4 * i + 3] * inv * wn};
+        if constexpr (MODE == 2) {
+          const f32x4 old = *dst;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += old[e] * wo;
+        }
+        *dst = v;
+      }
+      if (g == 0) *lse_at = lse;
+    }
+  }
+}
+
+// Gate, output projection and store of one workgroup's two query blocks:
+// og = o * inv * G (o the O^T accumulator image of each head's wave, G the
+// gate tile) as fp16 pairs into LDS, one barrier, then the output tiles
+// (query block u, 32 columns cb) shared by the waves, each a K = H*32
+// contraction of og with W_o, + b_o, fp32 stores.
+template <int H>
+__device__ __forceinline__ void gate_project_store(f16* og_lds, const f32x16 (&O)[2], const float (&inv)[2],
+                                                   const f32x16& G0, const f32x16& G1, int h, int wave, int lane,
+                                                   const f16* __restrict__ wo_hi, const f16* __restrict__ wo_lo,
+                                                   const float* __restrict__ b_o, float* __restrict__ out,
+                                                   int64_t os_r, int64_t os_p, int c_out, int r, int P, int qb0,
+                                                   int qb1) {
+  const int g = lane >> 5;
   const int ncb = c_out / 32;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    float lt = l[u];
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lt), __float_as_uint(lt), false, false);
-      lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    }
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     const f32x16& G = u == 0 ? G0 : G1;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       float o[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = O[u][8 * t + e] * inv * G[8 * t + e];
+      for (int e = 0; e < 8; ++e) o[e] = O[u][8 * t + e] * inv[u] * G[8 * t + e];
       f16x8 hi, lo;
       split8(o, hi, lo);
       f16* dst = og_lds + ((((u * H + h) * 2 + t) * 2) * 64 + lane) * 8;
@@ -673,8 +756,6 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
   }
   __syncthreads();
-  // output tiles (query block u, 32 columns cb), each a K = H*32 contraction
-  // of og with W_o, + b_o, fp32 stores
   for (int ti = wave; ti < 2 * ncb; ti += H) {
     const int u = ti / ncb, cb = ti % ncb;
     if (u == 1 && qb1 == qb0) continue;   // repeated block of an odd last group
@@ -686,7 +767,8 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         const f16* a = og_lds + ((((u * H + hh) * 2 + t) * 2) * 64 + lane) * 8;
         const int64_t wo = (((int64_t)cb * H + hh) * 2 + t) * 512;
         acc = mfma3(*reinterpret_cast<const f16x8*>(a), *reinterpret_cast<const f16x8*>(a + 512),
-                    ld_chunk(wo_hi + wo), ld_chunk(wo_lo + wo), acc);
+                    reinterpret_cast<const f16x8*>(wo_hi + wo)[lane], reinterpret_cast<const f16x8*>(wo_lo + wo)[lane],
+                    acc);
       }
     // rows = queries, lane = output column
     const int c = cb * 32 + (lane & 31);
@@ -698,6 +780,53 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
   }
 }
+
+// Finish of a query block's partial attention over key shards: o from
+// o_part (per head, already merged), the gate from the projection of the
+// query pairs, then gate, output projection and store as in the one-pass
+// kernel.  Same workgroup shape and tile order as attn_f32_kernel.
+template <int H>
+__global__ __launch_bounds__(H * 64) void attn_f32_finish_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ g_ws, const f16* __restrict__ wo_hi,
+    const f16* __restrict__ wo_lo, const float* __restrict__ b_o, float* __restrict__ out, int64_t os_r,
+    int64_t os_p, int c_out, int nrows, int P, int nbq, int ngroups) {
+  __shared__ __attribute__((aligned(1024))) f16 og_lds[2 * H * 2 * 2 * 512];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int g = lane >> 5;
+  const int h = wave;
+  const int64_t ntile = (int64_t)ngroups * nrows;
+  int64_t tile = blockIdx.x;
+  if ((ntile & 7) == 0) tile = (tile & 7) * (ntile >> 3) + (tile >> 3);
+  const int r = (int)(tile / ngroups);
+  const int grp = (int)(tile % ngroups);
+  const int qb0 = 2 * grp, qb1 = min(2 * grp + 1, nbq - 1);
+  const int64_t rh = (int64_t)r * H + h;
+  f32x16 O[2], G[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int qb = u == 0 ? qb0 : qb1;
+    const int q = qb * 32 + (lane & 31);
+    const float* orow = o_part + ((int64_t)r * P + min(q, P - 1)) * (H * 32) + h * 32 + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(orow + 8 * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) O[u][4 * i + e] = q < P ? v[e] : 0.0f;
+    }
+    const f32x4* gt = reinterpret_cast<const f32x4*>(g_ws + (rh * nbq + qb) * 1024) + lane * 4;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 v = gt[q4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) G[u][4 * q4 + e] = v[e];
+    }
+  }
+  const float one[2] = {1.0f, 1.0f};
+  gate_project_store<H>(og_lds, O, one, G[0], G[1], h, wave, lane, wo_hi, wo_lo, b_o, out, os_r, os_p, c_out, r, P,
+                        qb0, qb1);
+}
+
 
 // ---------------------------------------------------------------------------
 // launchers
@@ -723,14 +852,17 @@ static hipError_t proj_f32_dispatch(const ProjF32Args& a, int num_cu, hipStream_
   const int grid_x = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)num_cu * 2));
   const int rmajor = a.xs_p <= a.xs_r ? 1 : 0;
   hipLaunchKernelGGL((proj_f32_kernel<C_IN>), dim3(grid_x, groups), dim3(SH::THREADS), 0, s, (const float*)a.x,
-                     a.xs_r, a.xs_p, rmajor, a.eps, (const f16*)a.w_hi, (const f16*)a.w_lo, a.cst, a.nqkvg,
-                     a.with_bias, (const float*)a.wb, (const float*)a.gamma, (const float*)a.beta, a.hd, a.q_scale, (f16*)a.q_hi, (f16*)a.q_lo, (f16*)a.k_hi, (f16*)a.k_lo, (f16*)a.v_hi,
-                     (f16*)a.v_lo, a.g_ws, a.bias, a.bias_natural, a.bias_scale, a.nrows, a.P, a.Pp, a.H);
+                     a.xs_r, a.xs_p, rmajor, a.eps, (const f16*)a.w_hi, (const f16*)a.w_lo, a.cst, a.b_first,
+                     a.nqkvg, a.with_bias, (const float*)a.wb, (const float*)a.gamma, (const float*)a.beta, a.hd,
+                     a.q_scale, (f16*)a.q_hi, (f16*)a.q_lo, (f16*)a.k_hi, (f16*)a.k_lo, (f16*)a.v_hi, (f16*)a.v_lo,
+                     a.g_ws, a.bias, a.bias_natural, a.bias_scale, a.nrows, a.P, a.Pp, a.H);
   return hipGetLastError();
 }
 
 hipError_t launch_proj_f32(const ProjF32Args& a, int num_cu, hipStream_t s) {
-  if (a.nqkvg + a.with_bias < 1 || a.Pp % 32 != 0 || a.P < 1 || a.P > a.Pp || a.nrows < 1) return hipErrorInvalidValue;
+  if (a.nqkvg + a.with_bias < 1 || a.b_first < 0 || a.b_first + a.nqkvg > 4 * a.hd / 32 || a.Pp % 32 != 0 ||
+      a.P < 1 || a.P > a.Pp || a.nrows < 1)
+    return hipErrorInvalidValue;
   switch (a.c_in) {
     case 64: return proj_f32_dispatch<64>(a, num_cu, s);
     case 128: return proj_f32_dispatch<128>(a, num_cu, s);
@@ -739,32 +871,66 @@ hipError_t launch_proj_f32(const ProjF32Args& a, int num_cu, hipStream_t s) {
   }
 }
 
-hipError_t launch_bias_to_f32_layout(const float* src, float* dst, int H, int P, int Pp, hipStream_t s) {
-  const int64_t total = (int64_t)H * Pp * Pp;
+hipError_t launch_bias_to_f32_layout(const float* src, float* dst, int H, int Pq, int Pk, int Ppq, int Ppk,
+                                     hipStream_t s) {
+  const int64_t total = (int64_t)H * Ppq * Ppk;
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 8192));
-  hipLaunchKernelGGL(bias_to_f32_layout_kernel, dim3(blocks), dim3(256), 0, s, src, dst, H, P, Pp);
+  hipLaunchKernelGGL(bias_to_f32_layout_kernel, dim3(blocks), dim3(256), 0, s, src, dst, H, Pq, Pk, Ppq, Ppk);
+  return hipGetLastError();
+}
+
+template <int H, bool HAS_MASK, int MODE>
+static hipError_t attn_f32_dispatch(const AttnF32Args& a, hipStream_t s) {
+  const int nbq = a.Pp / 32, nbk = a.Ppk / 32;
+  const int ngroups = (nbq + 1) / 2;
+  const int64_t n = (int64_t)ngroups * a.nrows;
+  if (n > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_f32_kernel<H, HAS_MASK, MODE>), dim3((unsigned)n), dim3(H * 64), 0, s,
+                     (const f16*)a.q_hi, (const f16*)a.q_lo, (const f16*)a.k_hi, (const f16*)a.k_lo,
+                     (const f16*)a.v_hi, (const f16*)a.v_lo, a.g_ws, a.bias, a.mask_bits, (const f16*)a.wo_hi,
+                     (const f16*)a.wo_lo, (const float*)a.b_o, (float*)a.out, a.os_r, a.os_p, a.c_out, a.nrows, a.P,
+                     nbq, nbk, ngroups, a.o_part, a.lse_part);
   return hipGetLastError();
 }
 
 template <int H, bool HAS_MASK>
-static hipError_t attn_f32_dispatch(const AttnF32Args& a, hipStream_t s) {
-  const int nb = a.Pp / 32;
-  const int ngroups = (nb + 1) / 2;
-  const int64_t n = (int64_t)ngroups * a.nrows;
-  if (n > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_f32_kernel<H, HAS_MASK>), dim3((unsigned)n), dim3(H * 64), 0, s, (const f16*)a.q_hi,
-                     (const f16*)a.q_lo, (const f16*)a.k_hi, (const f16*)a.k_lo, (const f16*)a.v_hi,
-                     (const f16*)a.v_lo, a.g_ws, a.bias, a.mask_bits, (const f16*)a.wo_hi, (const f16*)a.wo_lo,
-                     (const float*)a.b_o, (float*)a.out, a.os_r, a.os_p, a.c_out, a.nrows, a.P, nb, ngroups);
-  return hipGetLastError();
+static hipError_t attn_f32_dispatch_mode(const AttnF32Args& a, hipStream_t s) {
+  switch (a.mode) {
+    case 0: return attn_f32_dispatch<H, HAS_MASK, 0>(a, s);
+    case 1: return attn_f32_dispatch<H, HAS_MASK, 1>(a, s);
+    case 2: return attn_f32_dispatch<H, HAS_MASK, 2>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_attn_f32(const AttnF32Args& a, hipStream_t s) {
-  if (a.Pp < 32 || a.Pp % 32 != 0 || a.P < 1 || a.P > a.Pp || a.nrows < 1 || a.c_out % 32 != 0)
+  if (a.Pp < 32 || a.Pp % 32 != 0 || a.P < 1 || a.P > a.Pp || a.Ppk < 32 || a.Ppk % 32 != 0 || a.nrows < 1 ||
+      a.c_out % 32 != 0 || (a.mode != 0 && (a.o_part == nullptr || a.lse_part == nullptr)))
     return hipErrorInvalidValue;
   const bool m = a.mask_bits != nullptr;
-  if (a.H == 4) return m ? attn_f32_dispatch<4, true>(a, s) : attn_f32_dispatch<4, false>(a, s);
-  if (a.H == 8) return m ? attn_f32_dispatch<8, true>(a, s) : attn_f32_dispatch<8, false>(a, s);
+  if (a.H == 4) return m ? attn_f32_dispatch_mode<4, true>(a, s) : attn_f32_dispatch_mode<4, false>(a, s);
+  if (a.H == 8) return m ? attn_f32_dispatch_mode<8, true>(a, s) : attn_f32_dispatch_mode<8, false>(a, s);
+  return hipErrorInvalidValue;
+}
+
+template <int H>
+static hipError_t finish_f32_dispatch(const AttnF32Args& a, hipStream_t s) {
+  const int nbq = a.Pp / 32;
+  const int ngroups = (nbq + 1) / 2;
+  const int64_t n = (int64_t)ngroups * a.nrows;
+  if (n > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_f32_finish_kernel<H>), dim3((unsigned)n), dim3(H * 64), 0, s, a.o_part, a.g_ws,
+                     (const f16*)a.wo_hi, (const f16*)a.wo_lo, (const float*)a.b_o, (float*)a.out, a.os_r, a.os_p,
+                     a.c_out, a.nrows, a.P, nbq, ngroups);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish_f32(const AttnF32Args& a, hipStream_t s) {
+  if (a.Pp < 32 || a.Pp % 32 != 0 || a.P < 1 || a.P > a.Pp || a.nrows < 1 || a.c_out % 32 != 0 ||
+      a.o_part == nullptr)
+    return hipErrorInvalidValue;
+  if (a.H == 4) return finish_f32_dispatch<4>(a, s);
+  if (a.H == 8) return finish_f32_dispatch<8>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -64,7 +64,7 @@ struct ProjF32Args {
   float eps;
   const void *w_hi, *w_lo;       // packed q|k|v|g operands (launch_pack_f32)
   const float* cst;
-  int nqkvg;                     // q|k|v|g blocks to compute (0 or 4*hd/32)
+  int b_first, nqkvg;            // q|k|v|g blocks [b_first, b_first + nqkvg) of the packed list
   int with_bias;                 // 1: also the pair bias, from wb with LayerNorm gamma and beta
   const void *wb, *gamma, *beta;
   int hd;
@@ -85,11 +85,21 @@ struct AttnF32Args {
   const void* b_o;
   void* out;
   int64_t os_r, os_p;
-  int H, c_out, nrows, P, Pp;
+  int H, c_out, nrows;
+  int P, Pp;                     // queries (and keys when Pk = P)
+  int Pk, Ppk;                   // keys
+  // 0: one pass (gate, output projection, out); 1: this key shard's o and
+  // lse into o_part [nrows][P][H*32] / lse_part [nrows][H][P]; 2: merged
+  // into the o_part / lse_part already there
+  int mode;
+  float *o_part, *lse_part;
 };
 hipError_t launch_pack_f32(const PackF32Args& a, hipStream_t s);
 hipError_t launch_proj_f32(const ProjF32Args& a, int num_cu, hipStream_t s);
-hipError_t launch_bias_to_f32_layout(const float* src, float* dst, int H, int P, int Pp, hipStream_t s);
+hipError_t launch_bias_to_f32_layout(const float* src, float* dst, int H, int Pq, int Pk, int Ppq, int Ppk,
+                                     hipStream_t s);
 hipError_t launch_attn_f32(const AttnF32Args& a, hipStream_t s);
+// gate (g_ws), output projection and store of merged partial outputs o_part
+hipError_t launch_finish_f32(const AttnF32Args& a, hipStream_t s);
 
 }  // namespace pa

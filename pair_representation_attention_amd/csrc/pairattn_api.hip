@@ -91,6 +91,42 @@ Layout make_layout(int64_t nrows, int64_t P, int64_t c_in, int64_t c_out, int64_
   return L;
 }
 
+// Partial attention (fp32 path): R rows of Jq query pairs against Kn key
+// pairs.  Queries get q (and, for the finish, the gate); keys get k and v.
+struct PartialLayout {
+  size_t w_hi = 0, w_lo = 0, cst = 0, wo_hi = 0, wo_lo = 0, q = 0, q_lo = 0, k = 0, k_lo = 0, v = 0, v_lo = 0, g = 0,
+         bias = 0, bits = 0, total = 0;
+};
+PartialLayout make_partial_layout(int64_t R, int64_t Jq, int64_t Kn, int64_t c, int64_t H) {
+  PartialLayout L;
+  const int64_t hd = H * 32;
+  const int64_t Ppq = pad32(Jq), Ppk = pad32(Kn);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  const int64_t nblk = 4 * hd / 32;
+  L.w_hi = take((size_t)nblk * c * 64);
+  L.w_lo = take((size_t)nblk * c * 64);
+  L.cst = take((size_t)nblk * 32 * 4);
+  L.wo_hi = take((size_t)c * hd * 2);
+  L.wo_lo = take((size_t)c * hd * 2);
+  const size_t qplane = (size_t)R * H * Ppq * 32 * 2, kplane = (size_t)R * H * Ppk * 32 * 2;
+  L.q = take(qplane);
+  L.q_lo = take(qplane);
+  L.k = take(kplane);
+  L.k_lo = take(kplane);
+  L.v = take(kplane);
+  L.v_lo = take(kplane);
+  L.g = take(2 * qplane);
+  L.bias = take((size_t)H * Ppq * Ppk * 4);
+  L.bits = take((size_t)R * (Ppk / 32) * 4);
+  L.total = off;
+  return L;
+}
+
 // ---- device check -----------------------------------------------------------
 struct DevInfo {
   int state = 0;  // 0 unknown, 1 gfx950, -1 other
@@ -350,6 +386,43 @@ int pairattn_validate_tri_chunked(const void* z, const uint8_t* mask, const pair
   return PAIRATTN_OK;
 }
 
+size_t pairattn_tri_partial_workspace_bytes(int64_t R, int64_t Jq, int64_t Kn, int64_t c_z, int64_t H, int64_t d,
+                                            int32_t dtype) {
+  if (dtype != PAIRATTN_F32 || R < 1 || Jq < 1 || Kn < 1 || d != 32 || !supported_h(H) || !supported_c(c_z) ||
+      Jq > kMaxPositions || Kn > kMaxPositions)
+    return 0;
+  return make_partial_layout(R, Jq, Kn, c_z, H).total;
+}
+
+int pairattn_validate_tri_partial(const void* q_pairs, const void* kv_pairs, const float* bias, const uint8_t* mask,
+                                  const pairattn_params* p, const float* o, const float* lse, int64_t R, int64_t Jq,
+                                  int64_t Kn, int64_t c_z, int64_t H, int64_t d) {
+  g_err[0] = '\0';
+  PA_TRY(check_params(p, true, false));
+  if (p->dtype != PAIRATTN_F32)
+    return fail(PAIRATTN_ERR_UNSUPPORTED, "partial attention is built on the fp32 path only (dtype PAIRATTN_F32)");
+  if (q_pairs == nullptr || kv_pairs == nullptr || bias == nullptr || o == nullptr || lse == nullptr)
+    return fail(PAIRATTN_ERR_ARG, "q_pairs, kv_pairs, bias, o and lse must not be NULL");
+  if (!aligned16(q_pairs) || !aligned16(kv_pairs) || !aligned16(bias) || !aligned16(o) || !aligned16(lse))
+    return fail(PAIRATTN_ERR_ARG, "q_pairs, kv_pairs, bias, o and lse must be 16-byte aligned");
+  if (R < 1 || Jq < 1 || Kn < 1) return fail(PAIRATTN_ERR_ARG, "R, Jq and Kn must be >= 1");
+  PA_TRY(check_shape_common(std::max(Jq, Kn), c_z, H, d, p->dtype));
+  PA_TRY(check_rows_limit(R, p->dtype));
+  const size_t obytes = (size_t)R * Jq * H * d * 4, lbytes = (size_t)R * H * Jq * 4;
+  const size_t qbytes = (size_t)R * Jq * c_z * 4, kbytes = (size_t)R * Kn * c_z * 4;
+  if (overlaps(o, obytes, lse, lbytes)) return fail(PAIRATTN_ERR_ARG, "o overlaps lse");
+  for (const void* in : {q_pairs, kv_pairs, (const void*)bias}) {
+    const size_t nb = in == q_pairs ? qbytes : in == kv_pairs ? kbytes : (size_t)H * Jq * Kn * 4;
+    if (overlaps(o, obytes, in, nb) || overlaps(lse, lbytes, in, nb))
+      return fail(PAIRATTN_ERR_ARG, "o or lse overlaps an input");
+  }
+  const size_t need = pairattn_tri_partial_workspace_bytes(R, Jq, Kn, c_z, H, d, p->dtype);
+  PA_TRY(check_workspace(p, need));
+  if (overlaps(o, obytes, p->workspace, p->workspace_bytes) || overlaps(lse, lbytes, p->workspace, p->workspace_bytes))
+    return fail(PAIRATTN_ERR_ARG, "o or lse overlaps the workspace");
+  return PAIRATTN_OK;
+}
+
 int pairattn_validate_msa(const void* m, const void* z, const uint8_t* mask, const pairattn_params* p,
                           const void* out, int64_t S, int64_t I, int64_t c_m, int64_t c_z, int64_t H, int64_t d) {
   g_err[0] = '\0';
@@ -562,6 +635,7 @@ static int run_row_attention_f32(const pairattn_params* p, const Layout& L, hipS
   pj.w_hi = pk.w_hi;
   pj.w_lo = pk.w_lo;
   pj.cst = pk.cst;
+  pj.b_first = 0;
   pj.nqkvg = nqkvg;
   pj.with_bias = ra.bias_in_proj ? 1 : 0;
   pj.wb = p->w_b;
@@ -611,7 +685,8 @@ static int run_row_attention_f32(const pairattn_params* p, const Layout& L, hipS
     mark("pair_bias");
   }
   if (ra.bias_given != nullptr) {
-    PA_TRY(hip_status(pa::launch_bias_to_f32_layout(ra.bias_given, bias_ws, (int)ra.H, (int)ra.P, Pp, s),
+    PA_TRY(hip_status(pa::launch_bias_to_f32_layout(ra.bias_given, bias_ws, (int)ra.H, (int)ra.P, (int)ra.P, Pp,
+                                                    Pp, s),
                       "bias copy launch"));
     mark("bias_copy");
   }
@@ -643,6 +718,9 @@ static int run_row_attention_f32(const pairattn_params* p, const Layout& L, hipS
   at.nrows = (int)ra.nrows;
   at.P = (int)ra.P;
   at.Pp = Pp;
+  at.Pk = (int)ra.P;
+  at.Ppk = Pp;
+  at.mode = 0;
   PA_TRY(hip_status(pa::launch_attn_f32(at, s), "attention launch"));
   mark("attention");
   return PAIRATTN_OK;
@@ -825,6 +903,197 @@ int pairattn_tri_chunked_fwd(const void* z, const uint8_t* mask, const pairattn_
     PA_TRY(run_row_attention(p, L, s, num_cu, ra));
   }
   tm_mark(s, "blocks");
+  return PAIRATTN_OK;
+}
+
+int pairattn_tri_partial_fwd(const void* q_pairs, const void* kv_pairs, const float* bias, const uint8_t* mask,
+                             const pairattn_params* p, float* o, float* lse, int32_t accumulate, int64_t R, int64_t Jq,
+                             int64_t Kn, int64_t c_z, int64_t H, int64_t d, void* stream) {
+  PA_TRY(pairattn_validate_tri_partial(q_pairs, kv_pairs, bias, mask, p, o, lse, R, Jq, Kn, c_z, H, d));
+  int num_cu = 0;
+  PA_TRY(check_device(&num_cu));
+  const PartialLayout L = make_partial_layout(R, Jq, Kn, c_z, H);
+  const int64_t hd = H * 32;
+  const int Ppq = (int)pad32(Jq), Ppk = (int)pad32(Kn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  tm_begin(s);
+  pa::PackF32Args pk{};
+  pk.wq = p->w_q;
+  pk.wk = p->w_k;
+  pk.wv = p->w_v;
+  pk.wg = p->w_g;
+  pk.gamma = p->ln_gamma;
+  pk.beta = p->ln_beta;
+  pk.b_g = p->b_g;
+  pk.w_hi = ws_at(p, L.w_hi);
+  pk.w_lo = ws_at(p, L.w_lo);
+  pk.cst = reinterpret_cast<float*>(ws_at(p, L.cst));
+  pk.c_in = (int)c_z;
+  pk.hd = (int)hd;
+  pk.H = (int)H;
+  pk.nqkvg = (int)(4 * hd / 32);
+  PA_TRY(hip_status(pa::launch_pack_f32(pk, s), "weight packing launch"));
+  tm_mark(s, "pack");
+  // q of the query pairs (blocks [0, hd/32)), k and v of the key pairs (blocks [hd/32, 3*hd/32))
+  pa::ProjF32Args pj{};
+  pj.eps = p->ln_eps;
+  pj.w_hi = pk.w_hi;
+  pj.w_lo = pk.w_lo;
+  pj.cst = pk.cst;
+  pj.hd = (int)hd;
+  pj.q_scale = 1.4426950408889634f / std::sqrt(32.0f);
+  pj.q_hi = ws_at(p, L.q);
+  pj.q_lo = ws_at(p, L.q_lo);
+  pj.k_hi = ws_at(p, L.k);
+  pj.k_lo = ws_at(p, L.k_lo);
+  pj.v_hi = ws_at(p, L.v);
+  pj.v_lo = ws_at(p, L.v_lo);
+  pj.g_ws = reinterpret_cast<float*>(ws_at(p, L.g));
+  pj.c_in = (int)c_z;
+  pj.H = (int)H;
+  pj.nrows = (int)R;
+  pj.with_bias = 0;
+  pj.x = q_pairs;
+  pj.xs_r = Jq * c_z;
+  pj.xs_p = c_z;
+  pj.b_first = 0;
+  pj.nqkvg = (int)(hd / 32);
+  pj.P = (int)Jq;
+  pj.Pp = Ppq;
+  PA_TRY(hip_status(pa::launch_proj_f32(pj, num_cu, s), "query projection launch"));
+  pj.x = kv_pairs;
+  pj.xs_r = Kn * c_z;
+  pj.b_first = (int)(hd / 32);
+  pj.nqkvg = (int)(2 * hd / 32);
+  pj.P = (int)Kn;
+  pj.Pp = Ppk;
+  PA_TRY(hip_status(pa::launch_proj_f32(pj, num_cu, s), "key projection launch"));
+  tm_mark(s, "projection");
+  float* bias_ws = reinterpret_cast<float*>(ws_at(p, L.bias));
+  PA_TRY(hip_status(pa::launch_bias_to_f32_layout(bias, bias_ws, (int)H, (int)Jq, (int)Kn, Ppq, Ppk, s),
+                    "bias copy launch"));
+  tm_mark(s, "bias_copy");
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws_at(p, L.bits));
+  if (mask != nullptr) {
+    PA_TRY(hip_status(pa::launch_mask_bits(mask, Kn, 1, bits, (int)R, (int)Kn, Ppk / 32, s), "mask bits launch"));
+    tm_mark(s, "mask_bits");
+  }
+  pa::AttnF32Args at{};
+  at.q_hi = pj.q_hi;
+  at.q_lo = pj.q_lo;
+  at.k_hi = pj.k_hi;
+  at.k_lo = pj.k_lo;
+  at.v_hi = pj.v_hi;
+  at.v_lo = pj.v_lo;
+  at.bias = bias_ws;
+  at.mask_bits = mask != nullptr ? bits : nullptr;
+  at.H = (int)H;
+  at.c_out = (int)c_z;
+  at.nrows = (int)R;
+  at.P = (int)Jq;
+  at.Pp = Ppq;
+  at.Pk = (int)Kn;
+  at.Ppk = Ppk;
+  at.mode = accumulate ? 2 : 1;
+  at.o_part = o;
+  at.lse_part = lse;
+  PA_TRY(hip_status(pa::launch_attn_f32(at, s), "attention launch"));
+  tm_mark(s, "attention");
+  return PAIRATTN_OK;
+}
+
+size_t pairattn_tri_partial_finish_workspace_bytes(int64_t R, int64_t Jq, int64_t c_z, int64_t H, int64_t d,
+                                                   int32_t dtype) {
+  return pairattn_tri_partial_workspace_bytes(R, Jq, 1, c_z, H, d, dtype);
+}
+
+int pairattn_validate_tri_partial_finish(const void* q_pairs, const float* o, const pairattn_params* p,
+                                         const void* out, int64_t R, int64_t Jq, int64_t c_z, int64_t H, int64_t d) {
+  g_err[0] = '\0';
+  PA_TRY(check_params(p, true, false));
+  if (p->dtype != PAIRATTN_F32)
+    return fail(PAIRATTN_ERR_UNSUPPORTED, "partial attention is built on the fp32 path only (dtype PAIRATTN_F32)");
+  if (q_pairs == nullptr || o == nullptr || out == nullptr)
+    return fail(PAIRATTN_ERR_ARG, "q_pairs, o and out must not be NULL");
+  if (!aligned16(q_pairs) || !aligned16(o) || !aligned16(out))
+    return fail(PAIRATTN_ERR_ARG, "q_pairs, o and out must be 16-byte aligned");
+  if (R < 1 || Jq < 1) return fail(PAIRATTN_ERR_ARG, "R and Jq must be >= 1");
+  PA_TRY(check_shape_common(Jq, c_z, H, d, p->dtype));
+  PA_TRY(check_rows_limit(R, p->dtype));
+  const size_t obytes = (size_t)R * Jq * c_z * 4;
+  if (overlaps(out, obytes, q_pairs, obytes)) return fail(PAIRATTN_ERR_ARG, "out overlaps q_pairs");
+  if (overlaps(out, obytes, o, (size_t)R * Jq * H * d * 4)) return fail(PAIRATTN_ERR_ARG, "out overlaps o");
+  PA_TRY(check_workspace(p, pairattn_tri_partial_finish_workspace_bytes(R, Jq, c_z, H, d, p->dtype)));
+  if (overlaps(out, obytes, p->workspace, p->workspace_bytes)) return fail(PAIRATTN_ERR_ARG, "out overlaps the workspace");
+  return PAIRATTN_OK;
+}
+
+int pairattn_tri_partial_finish(const void* q_pairs, const float* o, const pairattn_params* p, void* out, int64_t R,
+                                int64_t Jq, int64_t c_z, int64_t H, int64_t d, void* stream) {
+  PA_TRY(pairattn_validate_tri_partial_finish(q_pairs, o, p, out, R, Jq, c_z, H, d));
+  int num_cu = 0;
+  PA_TRY(check_device(&num_cu));
+  const PartialLayout L = make_partial_layout(R, Jq, 1, c_z, H);
+  const int64_t hd = H * 32;
+  const int Ppq = (int)pad32(Jq);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  tm_begin(s);
+  pa::PackF32Args pk{};
+  pk.wq = p->w_q;
+  pk.wk = p->w_k;
+  pk.wv = p->w_v;
+  pk.wg = p->w_g;
+  pk.gamma = p->ln_gamma;
+  pk.beta = p->ln_beta;
+  pk.b_g = p->b_g;
+  pk.wo = p->w_o;
+  pk.w_hi = ws_at(p, L.w_hi);
+  pk.w_lo = ws_at(p, L.w_lo);
+  pk.cst = reinterpret_cast<float*>(ws_at(p, L.cst));
+  pk.wo_hi = ws_at(p, L.wo_hi);
+  pk.wo_lo = ws_at(p, L.wo_lo);
+  pk.c_in = (int)c_z;
+  pk.hd = (int)hd;
+  pk.H = (int)H;
+  pk.nqkvg = (int)(4 * hd / 32);
+  pk.c_out = (int)c_z;
+  PA_TRY(hip_status(pa::launch_pack_f32(pk, s), "weight packing launch"));
+  tm_mark(s, "pack");
+  pa::ProjF32Args pj{};   // the gate of the query pairs: blocks [3*hd/32, 4*hd/32)
+  pj.x = q_pairs;
+  pj.xs_r = Jq * c_z;
+  pj.xs_p = c_z;
+  pj.eps = p->ln_eps;
+  pj.w_hi = pk.w_hi;
+  pj.w_lo = pk.w_lo;
+  pj.cst = pk.cst;
+  pj.b_first = (int)(3 * hd / 32);
+  pj.nqkvg = (int)(hd / 32);
+  pj.hd = (int)hd;
+  pj.g_ws = reinterpret_cast<float*>(ws_at(p, L.g));
+  pj.c_in = (int)c_z;
+  pj.H = (int)H;
+  pj.nrows = (int)R;
+  pj.P = (int)Jq;
+  pj.Pp = Ppq;
+  PA_TRY(hip_status(pa::launch_proj_f32(pj, num_cu, s), "gate projection launch"));
+  tm_mark(s, "projection");
+  pa::AttnF32Args at{};
+  at.g_ws = pj.g_ws;
+  at.wo_hi = pk.wo_hi;
+  at.wo_lo = pk.wo_lo;
+  at.b_o = p->b_o;
+  at.out = out;
+  at.os_r = Jq * c_z;
+  at.os_p = c_z;
+  at.H = (int)H;
+  at.c_out = (int)c_z;
+  at.nrows = (int)R;
+  at.P = (int)Jq;
+  at.Pp = Ppq;
+  at.o_part = const_cast<float*>(o);
+  PA_TRY(hip_status(pa::launch_finish_f32(at, s), "finish launch"));
+  tm_mark(s, "finish");
   return PAIRATTN_OK;
 }
 

@@ -81,6 +81,14 @@ _SIGNATURES = {
     "pairattn_tri_chunked_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64, _I32, _I64]),
     "pairattn_tri_chunked_fwd": (ctypes.c_int, [_P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I32, _I64, _P]),
     "pairattn_validate_tri_chunked": (ctypes.c_int, [_P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I32, _I64]),
+    "pairattn_tri_partial_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64, _I64, _I64, _I32]),
+    "pairattn_tri_partial_fwd": (ctypes.c_int, [_P, _P, _P, _P, _PP, _P, _P, _I32, _I64, _I64, _I64, _I64, _I64, _I64,
+                                                _P]),
+    "pairattn_tri_partial_finish_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64, _I64, _I32]),
+    "pairattn_tri_partial_finish": (ctypes.c_int, [_P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I64, _P]),
+    "pairattn_validate_tri_partial": (ctypes.c_int, [_P, _P, _P, _P, _PP, _P, _P, _I64, _I64, _I64, _I64, _I64,
+                                                     _I64]),
+    "pairattn_validate_tri_partial_finish": (ctypes.c_int, [_P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I64]),
     "pairattn_validate_tri": (ctypes.c_int, [_P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I32]),
     "pairattn_validate_msa": (ctypes.c_int, [_P, _P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I64, _I64]),
     "pairattn_validate_rows": (ctypes.c_int, [_P, _P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I64]),
@@ -211,6 +219,39 @@ def pairattn_tri_chunked_fwd(z, mask, params, out, I, c_z, H, d, orientation, bl
 def pairattn_validate_tri_chunked(z, mask, params, out, I, c_z, H, d, orientation, block) -> int:
     return load().pairattn_validate_tri_chunked(_ptr(z), _ptr(mask), ctypes.byref(params.struct()), _ptr(out), I,
                                                 c_z, H, d, orientation, block)
+
+
+def pairattn_tri_partial_workspace_bytes(R, Jq, Kn, c_z, H, d, dtype) -> int:
+    return load().pairattn_tri_partial_workspace_bytes(R, Jq, Kn, c_z, H, d, dtype)
+
+
+def pairattn_tri_partial_fwd(q_pairs, kv_pairs, bias, mask, params, o, lse, accumulate, R, Jq, Kn, c_z, H, d,
+                             stream=None, check=True) -> int:
+    st = load().pairattn_tri_partial_fwd(_ptr(q_pairs), _ptr(kv_pairs), _ptr(bias), _ptr(mask),
+                                         ctypes.byref(params.struct()), _ptr(o), _ptr(lse), 1 if accumulate else 0,
+                                         R, Jq, Kn, c_z, H, d, _stream(stream))
+    return _check(st, "pairattn_tri_partial_fwd") if check else st
+
+
+def pairattn_tri_partial_finish_workspace_bytes(R, Jq, c_z, H, d, dtype) -> int:
+    return load().pairattn_tri_partial_finish_workspace_bytes(R, Jq, c_z, H, d, dtype)
+
+
+def pairattn_tri_partial_finish(q_pairs, o, params, out, R, Jq, c_z, H, d, stream=None, check=True) -> int:
+    st = load().pairattn_tri_partial_finish(_ptr(q_pairs), _ptr(o), ctypes.byref(params.struct()), _ptr(out), R, Jq,
+                                            c_z, H, d, _stream(stream))
+    return _check(st, "pairattn_tri_partial_finish") if check else st
+
+
+def pairattn_validate_tri_partial(q_pairs, kv_pairs, bias, mask, params, o, lse, R, Jq, Kn, c_z, H, d) -> int:
+    return load().pairattn_validate_tri_partial(_ptr(q_pairs), _ptr(kv_pairs), _ptr(bias), _ptr(mask),
+                                                ctypes.byref(params.struct()), _ptr(o), _ptr(lse), R, Jq, Kn, c_z,
+                                                H, d)
+
+
+def pairattn_validate_tri_partial_finish(q_pairs, o, params, out, R, Jq, c_z, H, d) -> int:
+    return load().pairattn_validate_tri_partial_finish(_ptr(q_pairs), _ptr(o), ctypes.byref(params.struct()),
+                                                       _ptr(out), R, Jq, c_z, H, d)
 
 
 def pairattn_validate_tri(z, mask, params, out, I, c_z, H, d, orientation) -> int:

@@ -238,3 +238,55 @@ def test_validate_tri_chunked_ok():
     need = lib.pairattn_tri_chunked_workspace_bytes(300, 128, 4, 32, lib.PAIRATTN_F32, 64)
     p = _params(lib.PAIRATTN_F32, ws=WS, ws_bytes=need)
     assert lib.pairattn_validate_tri_chunked(Z, None, p, OUT, 300, 128, 4, 32, 0, 64) == lib.PAIRATTN_OK
+
+
+# ----------------------------------------------------------------------------
+# partial attention (one key shard) and its finish
+# ----------------------------------------------------------------------------
+QP, KP, BIAS, O_, LSE = A + 100 * MB, A + 200 * MB, A + 300 * MB, A + 400 * MB, A + 500 * MB
+
+
+def test_partial_workspace_sizes():
+    assert lib.pairattn_tri_partial_workspace_bytes(4, 64, 96, 128, 4, 32, lib.PAIRATTN_F32) > 0
+    # built on the fp32 path only
+    assert lib.pairattn_tri_partial_workspace_bytes(4, 64, 96, 128, 4, 32, lib.PAIRATTN_BF16) == 0
+    assert lib.pairattn_tri_partial_workspace_bytes(4, 64, 0, 128, 4, 32, lib.PAIRATTN_F32) == 0
+    a = lib.pairattn_tri_partial_workspace_bytes(4, 64, 96, 128, 4, 32, lib.PAIRATTN_F32)
+    b = lib.pairattn_tri_partial_workspace_bytes(4, 64, 192, 128, 4, 32, lib.PAIRATTN_F32)
+    assert b > a
+    assert lib.pairattn_tri_partial_finish_workspace_bytes(4, 64, 128, 4, 32, lib.PAIRATTN_F32) > 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), lib.PAIRATTN_OK),
+    (dict(dtype=lib.PAIRATTN_BF16), lib.PAIRATTN_ERR_UNSUPPORTED),
+    (dict(o=None), lib.PAIRATTN_ERR_ARG),
+    (dict(lse=LSE + 4), lib.PAIRATTN_ERR_ARG),               # misaligned
+    (dict(Kn=0), lib.PAIRATTN_ERR_ARG),
+    (dict(o=QP), lib.PAIRATTN_ERR_ARG),                      # o overlaps the query pairs
+    (dict(lse=O_ + 64), lib.PAIRATTN_ERR_ARG),               # lse overlaps o
+    (dict(ws_short=True), lib.PAIRATTN_ERR_WORKSPACE),
+])
+def test_validate_tri_partial(kw, status):
+    dt = kw.get("dtype", lib.PAIRATTN_F32)
+    need = lib.pairattn_tri_partial_workspace_bytes(3, 40, 70, 128, 4, 32, lib.PAIRATTN_F32)
+    p = _params(dt, ws=WS, ws_bytes=need - (256 if kw.get("ws_short") else 0))
+    a = dict(q=QP, k=KP, b=BIAS, m=None, o=O_, lse=LSE, R=3, Jq=40, Kn=70)
+    a.update({k: v for k, v in kw.items() if k in a})
+    st = lib.pairattn_validate_tri_partial(a["q"], a["k"], a["b"], a["m"], p, a["o"], a["lse"], a["R"], a["Jq"],
+                                           a["Kn"], 128, 4, 32)
+    assert st == status, lib.last_error()
+    if status != lib.PAIRATTN_OK:
+        st2 = lib.pairattn_tri_partial_fwd(a["q"], a["k"], a["b"], a["m"], p, a["o"], a["lse"], 0, a["R"], a["Jq"],
+                                           a["Kn"], 128, 4, 32, stream=0, check=False)
+        assert st2 == status
+
+
+def test_validate_tri_partial_finish():
+    need = lib.pairattn_tri_partial_finish_workspace_bytes(3, 40, 128, 4, 32, lib.PAIRATTN_F32)
+    p = _params(lib.PAIRATTN_F32, ws=WS, ws_bytes=need)
+    assert lib.pairattn_validate_tri_partial_finish(QP, O_, p, OUT, 3, 40, 128, 4, 32) == lib.PAIRATTN_OK
+    assert lib.pairattn_validate_tri_partial_finish(QP, O_, p, QP, 3, 40, 128, 4, 32) == lib.PAIRATTN_ERR_ARG
+    pb = _params(lib.PAIRATTN_BF16, ws=WS, ws_bytes=need)
+    assert lib.pairattn_validate_tri_partial_finish(QP, O_, pb, OUT, 3, 40, 128, 4, 32) == \
+        lib.PAIRATTN_ERR_UNSUPPORTED
