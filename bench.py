@@ -197,7 +197,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=24, help="oracle sample size (rows, about 0.35-1.4 s each by host)")
     ap.add_argument("--extra", action="store_true", help="also time MSA row attention and the row block")
-    ap.add_argument("--workload", choices=["tri_bf16_i1536", "msa_fp32_s5120_i384", "tri_bf16_i16384_chunked"],
+    ap.add_argument("--workload", choices=["tri_bf16_i1536", "msa_fp32_s5120_i384", "tri_bf16_i16384_chunked",
+                                           "ring_fp32_i1536_grid2x2"],
                     default="tri_bf16_i1536",
                     help="time only the fp32 extra-MSA workload, or chunked triangle attention at I = 16384 "
                          "(one JSON line)")
@@ -234,7 +235,8 @@ def main() -> int:
     lib.load()
     torch.cuda.set_device(0)
     if args.workload != "tri_bf16_i1536":
-        fn = msa_fp32_workload if args.workload == "msa_fp32_s5120_i384" else chunked_workload
+        fn = {"msa_fp32_s5120_i384": msa_fp32_workload, "tri_bf16_i16384_chunked": chunked_workload,
+              "ring_fp32_i1536_grid2x2": ring_workload}[args.workload]
         print(json.dumps({"workload": args.workload, **fn(args, device, inputs, lib, torch)}), flush=True)
         return 0
     cfg = inputs.CONFIGS["tri_bf16_i1536"]
@@ -472,6 +474,49 @@ def chunked_workload(args, device, inputs, lib, torch) -> dict:
            "one_pass_workspace_bytes": lib.pairattn_tri_workspace_bytes(I, c, H, d, lib.PAIRATTN_BF16),
            "z_bytes": I * I * c * 2, "frac_of_peak": f / (ms * 1e-3) / 1e12 / PEAK_MFMA_16BIT_TFLOPS}
     del run, z
+    torch.cuda.empty_cache()
+    return res
+
+
+def ring_workload(args, device, inputs, lib, torch) -> dict:
+    """One device's share of starting-node attention of Z[1536, 1536, 128]
+    fp32 on a 2 x 2 grid: its 768 rows x 768 query columns against the two
+    768-column key shards in ring order (partial, partial merged, finish),
+    beside the one-pass fp32 call on the same 768 rows (all 1536 queries,
+    i.e. twice the queries) for the rate comparison."""
+    I, c, H, d, half = 1536, 128, 4, 32, 768
+    log("ring: generating Z[1536,1536,128] fp32 on the device")
+    z = inputs.make_z_device(I, c, 11, dtype="f32")
+    p = inputs.make_chunked_params(c, H, d, 11, dtype="f32")
+    zq = z[:half, :half].contiguous()                   # this device's pairs: rows A, columns B
+    shards = [z[:half, :half].contiguous(), z[:half, half:].contiguous()]
+    bias = torch.empty((H, I, I), dtype=torch.float32, device="cuda")
+    pr = device.make_params(p, "f32")
+    lib.pairattn_tri_bias(z, pr, bias, I, c, H, lib.PAIRATTN_START)
+    btiles = [bias[:, :half, :half].contiguous(), bias[:, :half, half:].contiguous()]
+    n = max(lib.pairattn_tri_partial_workspace_bytes(half, half, half, c, H, d, lib.PAIRATTN_F32),
+            lib.pairattn_tri_partial_finish_workspace_bytes(half, half, c, H, d, lib.PAIRATTN_F32))
+    prm = device.make_params(p, "f32", n)
+    o = torch.empty((half, half, H * d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((half, H, half), dtype=torch.float32, device="cuda")
+    out = torch.empty((half, half, c), dtype=torch.float32, device="cuda")
+
+    def step():
+        for sidx in range(2):
+            lib.pairattn_tri_partial_fwd(zq, shards[sidx], btiles[sidx], None, prm, o, lse, sidx > 0, half, half,
+                                         half, c, H, d)
+        lib.pairattn_tri_partial_finish(zq, o, prm, out, half, half, c, H, d)
+
+    steps = max(3, args.steps)
+    ms = _time(step, steps, 2, torch)
+    f = 4.0 * half * half * I * H * d + 2.0 * half * half * H * d * c     # attention + output projection
+    rows = device.RowsRunner(z, z[:half].contiguous(), None, p, H, "f32")
+    rows.compute_bias()
+    ms_rows = _time(rows.rows, steps, 2, torch)
+    f_rows = 4.0 * half * I * I * H * d + 2.0 * half * I * H * d * c
+    res = {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12, "rows": half, "queries": half, "keys": I, "shards": 2,
+           "one_pass_rows_ms": ms_rows, "one_pass_rows_tflops": f_rows / (ms_rows * 1e-3) / 1e12}
+    del rows, z, shards, bias, o, lse, out
     torch.cuda.empty_cache()
     return res
 
