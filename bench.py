@@ -220,7 +220,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (no collectives); "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (no collectives); "
               "run with --gpus 1", file=sys.stderr)
         return 2
 
