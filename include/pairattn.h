@@ -179,9 +179,9 @@ int pairattn_tri_chunked_fwd(const void *z, const uint8_t *mask, const pairattn_
  * same rows, kept as a per-head output and its log-sum-exp so that shards
  * combine exactly (Design-CP page, Metodologia 1, 2D grid sharding: queries
  * split along rows, keys/values along columns and passed around a ring,
- * attention never formed as an I x I matrix).  fp32 path only
- * (params->dtype = PAIRATTN_F32; PAIRATTN_BF16 returns
- * PAIRATTN_ERR_UNSUPPORTED).
+ * attention never formed as an I x I matrix).  Both paths: q_pairs and
+ * kv_pairs in params->dtype (fp32, or bf16 with the bf16 path's fp16
+ * operands); o, lse and bias are float either way.
  *   q_pairs  [R][Jq][c_z]  the device's query pairs (rows r, their columns)
  *   kv_pairs [R][Kn][c_z]  one shard of key pairs of the same rows
  *   bias     [H][Jq][Kn]   float, natural-log units, for these queries/keys
@@ -203,7 +203,7 @@ int pairattn_tri_partial_fwd(const void *q_pairs, const void *kv_pairs, const fl
 
 /* The end of the ring: out[r][j] = (sigmoid(LN(q_pairs) W_g + b_g) * o) W_o
  * + b_o for the assembled o of pairattn_tri_partial_fwd.  out [R][Jq][c_z]
- * float.  Workspace: pairattn_tri_partial_finish_workspace_bytes. */
+ * in params->dtype.  Workspace: pairattn_tri_partial_finish_workspace_bytes. */
 size_t pairattn_tri_partial_finish_workspace_bytes(int64_t R, int64_t Jq, int64_t c_z, int64_t H,
                                                    int64_t d, int32_t dtype);
 int pairattn_tri_partial_finish(const void *q_pairs, const float *o, const pairattn_params *p,

@@ -132,12 +132,20 @@ struct AttnShape {
   static constexpr int WAIT = NKV == 3 ? NCW : 0;
 };
 
-template <int H, int C_OUT, bool HAS_MASK>
+// MODE 0: one pass over all keys, gate and output projection into `out`.
+// MODE 1: one shard of keys (nbq_in query blocks, Pk_in keys in nbk_in
+//         blocks); the per-head output o = O / l and its log-sum-exp
+//         lse = ln l + m ln 2 go to o_part [nrows][P][H*32] and lse_part
+//         [nrows][H][P].  MODE 2: merged into the o_part / lse_part already
+//         there (log-sum-exp weights).
+template <int H, int C_OUT, bool HAS_MASK, int MODE>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(
     const f16* __restrict__ q_ws, const f16* __restrict__ k_ws, const f16* __restrict__ v_ws,
     const f16* __restrict__ g_ws, const f16* __restrict__ bias, const uint32_t* __restrict__ mask_bits,
     const f16* __restrict__ woT, const bf16* __restrict__ b_o, bf16* __restrict__ out, int64_t os_r,
-    int64_t os_p, int nrows, int P, int Pp, int n_qg, int n_rg) {
+    int64_t os_p, int nrows, int P, int Pp, int n_qg, int n_rg, int nbq_in, int Pk_in, int nbk_in,
+    float* __restrict__ o_part, float* __restrict__ lse_part) {
+  static_assert(MODE >= 0 && MODE <= 2, "mode");
   static_assert(H == 4 || H == 8, "4 or 8 heads");
   using SH = AttnShape<H>;
   constexpr int HD = H * 32;
@@ -170,7 +178,10 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int qb0_wg = qg * SH::QWG;           // first query block of the workgroup
   const int qb0 = qb0_wg + qgrp * QW;        // first query block of this wave
 
-  const int nkb = Pp / 32;
+  // key blocks, query blocks and keys (all from Pp and P in the one-pass form)
+  const int nkb = MODE == 0 ? Pp / 32 : nbk_in;
+  const int nbq = MODE == 0 ? Pp / 32 : nbq_in;
+  const int Pk = MODE == 0 ? P : Pk_in;
 
   int rows_c[RW];
 #pragma unroll
@@ -187,10 +198,10 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     shifted[rr] = false;
 #pragma unroll
     for (int qq = 0; qq < QW; ++qq) {
-      const int qblk = min(qb0 + qq, nkb - 1);
+      const int qblk = min(qb0 + qq, nbq - 1);
       const int64_t rh = (int64_t)rows_c[rr] * H + h;
-      Q[rr][qq][0] = ld16(q_ws + qkv_chunk(rh, nkb, qblk, 0) + lane * 8);
-      Q[rr][qq][1] = ld16(q_ws + qkv_chunk(rh, nkb, qblk, 1) + lane * 8);
+      Q[rr][qq][0] = ld16(q_ws + qkv_chunk(rh, nbq, qblk, 0) + lane * 8);
+      Q[rr][qq][1] = ld16(q_ws + qkv_chunk(rh, nbq, qblk, 1) + lane * 8);
       O[rr][qq] = f32x16{};
       m_sh[rr][qq] = 0.0f;
       l_run[rr][qq] = 0.0f;
@@ -221,8 +232,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   for (int j = 0; j < NCB; ++j) {
     const int ib = wave + 8 * j;
     const int t = ib >> 1, c = ib & 1;        // tile (query block, head), chunk
-    const int qb = min(qb0_wg + t / H, nkb - 1), hh = t % H;
-    b_src[j] = bias + b16_chunk(hh, nkb, qb, 0, c);
+    const int qb = min(qb0_wg + t / H, nbq - 1), hh = t % H;
+    b_src[j] = bias + b16_chunk(hh, nbq, nkb, qb, 0, c);
     b_off[j] = t * SH::B_TILE + c * 1024;
   }
   constexpr int NU = RW * QW;   // units per wave and key block, query-block major
@@ -258,7 +269,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     if constexpr (HAS_MASK) {
       return mask_bits[(int64_t)rows_c[rr] * nkb + kb];
     } else {
-      const int n = P - kb * 32;
+      const int n = Pk - kb * 32;
       return n >= 32 ? 0xffffffffu : (n <= 0 ? 0u : ((1u << n) - 1u));
     }
   };
@@ -289,15 +300,17 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     for (int t = 0; t < KO; ++t) Wo[t] = ld16(woT + (int64_t)(cb_w * 32 + lq) * HD + t * 16 + g * 8);
   };
   auto load_epi = [&]() {
+    if constexpr (MODE == 0) {
 #pragma unroll
-    for (int rr = 0; rr < RW; ++rr)
+      for (int rr = 0; rr < RW; ++rr)
 #pragma unroll
-      for (int qq = 0; qq < QW; ++qq) {
-        const int64_t rh = (int64_t)rows_c[rr] * H + h;
-        const f16* gp = g_ws + qkv_chunk(rh, nkb, min(qb0 + qq, nkb - 1), 0) + lane * 8;
-        Gt[rr][qq][0] = ld16(gp);
-        Gt[rr][qq][1] = ld16(gp + 512);
-      }
+        for (int qq = 0; qq < QW; ++qq) {
+          const int64_t rh = (int64_t)rows_c[rr] * H + h;
+          const f16* gp = g_ws + qkv_chunk(rh, nbq, min(qb0 + qq, nbq - 1), 0) + lane * 8;
+          Gt[rr][qq][0] = ld16(gp);
+          Gt[rr][qq][1] = ld16(gp + 512);
+        }
+    }
   };
 
   // One sweep over all key blocks.
@@ -727,7 +740,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
   bool epi_loaded = false;
   if constexpr (H == 4 && !HAS_MASK) {
-    if (P == Pp) sweep_pipe(std::integral_constant<bool, false>{});
+    if (Pk == nkb * 32) sweep_pipe(std::integral_constant<bool, false>{});
     else sweep_pipe(std::integral_constant<bool, true>{});
     epi_loaded = true;
   } else {
@@ -763,6 +776,55 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       __syncthreads();   // the rings are idle before the o tiles overwrite them
       load_epi();   // (reloaded, so that the gate tiles are not live across the rerun)
     }
+  }
+  if constexpr (MODE != 0) {
+    // ---- one key shard: o and lse per (row, head, query), written or merged ----
+    constexpr float kLn2 = 0.6931471805599453f;
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+      for (int qq = 0; qq < QW; ++qq) {
+        const int r = r0 + rr, q = (qb0 + qq) * 32 + lq;
+        const float ltot = l_run[rr][qq] + __shfl_xor(l_run[rr][qq], 32, 64);
+        if (r >= nrows || q >= P) continue;
+        const bool any = ltot > 0.0f;
+        // l sums 2^(s - m) over the kept keys, s the logit in log2 units
+        const float lse_new = any ? (m_sh[rr][qq] + __builtin_log2f(ltot)) * kLn2 : -__builtin_inff();
+        const float inv = any ? 1.0f / ltot : 0.0f;
+        float wn = 1.0f, wo = 0.0f, lse = lse_new;
+        float* lse_at = lse_part + ((int64_t)r * H + h) * P + q;
+        if constexpr (MODE == 2) {
+          const float lse_old = *lse_at;
+          const float mx = __builtin_fmaxf(lse_old, lse_new);
+          if (mx == -__builtin_inff()) {
+            wn = 0.0f;   // no kept key in either part: o stays 0, lse -inf
+          } else {
+            wo = __expf(lse_old - mx);
+            wn = __expf(lse_new - mx);
+            const float den = wo + wn;
+            lse = mx + __logf(den);
+            wo /= den;
+            wn /= den;
+          }
+        }
+        // O register jj*4+e holds channel jj*8 + g*4 + e of head h
+        float* orow = o_part + ((int64_t)r * P + q) * (H * 32) + h * 32 + 4 * g;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          f32x4* dst = reinterpret_cast<f32x4*>(orow + 8 * jj);
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = O[rr][qq][4 * jj + e] * inv * wn;
+          if constexpr (MODE == 2) {
+            const f32x4 old = *dst;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += old[e] * wo;
+          }
+          *dst = v;
+        }
+        if (g == 0) *lse_at = lse;
+      }
+    return;
   }
   load_wo();
 
@@ -881,36 +943,130 @@ hipError_t launch_mask_bits(const uint8_t* mask, int64_t ms_r, int64_t ms_k, uin
   return hipGetLastError();
 }
 
-template <int H, int C_OUT, bool HAS_MASK>
-static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
-  using SH = AttnShape<H>;
-  const int nkb = a.Pp / 32;
-  // the sweeps assume at least one key block and rows to work on
-  if (nkb < 1 || a.Pp != nkb * 32 || a.P < 1 || a.P > a.Pp || a.nrows < 1) return hipErrorInvalidValue;
-  const int n_qg = (nkb + SH::QWG - 1) / SH::QWG;
-  const int n_rg = (a.nrows + SH::RWG - 1) / SH::RWG;
-  const int64_t n = (int64_t)n_qg * n_rg;
-  hipLaunchKernelGGL((attn_kernel<H, C_OUT, HAS_MASK>), dim3((unsigned)n), dim3(512), 0, s, (const f16*)a.q_ws,
-                     (const f16*)a.k_ws, (const f16*)a.v_ws, (const f16*)a.g_ws, (const f16*)a.bias, a.mask_bits,
-                     (const f16*)a.woT, (const bf16*)a.b_o, (bf16*)a.out, a.os_r, a.os_p, a.nrows, a.P, a.Pp, n_qg,
-                     n_rg);
-  return hipGetLastError();
+// Gate, output projection and store of merged partial outputs (the end of
+// ring attention): for each (row r, query block) tile,
+//   og = o_part * gate   as fp16 into LDS (gate: sigmoid applied, layout of q)
+//   out = og W_o + b_o   (C_OUT/32 output blocks of K = H*32 over 4 waves)
+template <int H, int C_OUT>
+__global__ __launch_bounds__(256) void attn_finish_kernel(const f16* __restrict__ g_ws,
+                                                          const float* __restrict__ o_part,
+                                                          const f16* __restrict__ woT, const bf16* __restrict__ b_o,
+                                                          bf16* __restrict__ out, int64_t os_r, int64_t os_p,
+                                                          int nrows, int P, int nbq) {
+  constexpr int HD = H * 32, OP = HD + 8, KO = HD / 16, CBN = C_OUT / 32;
+  __shared__ __attribute__((aligned(16))) f16 og[32 * OP];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int lq = lane & 31, g = lane >> 5;
+  const int64_t ntiles = (int64_t)nrows * nbq;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int r = (int)(tile / nbq), qb = (int)(tile % nbq);
+    // groups of 4 channels: 16 bytes of o, 8 bytes of the gate
+    for (int gi = tid; gi < 32 * HD / 4; gi += 256) {
+      const int q = gi / (HD / 4), c4 = (gi % (HD / 4)) * 4;
+      const int pos = qb * 32 + q;
+      f32x4 ov = {};
+      if (pos < P) ov = *reinterpret_cast<const f32x4*>(o_part + ((int64_t)r * P + pos) * HD + c4);
+      const f16x4 gv =
+          *reinterpret_cast<const f16x4*>(g_ws + q_off((int64_t)r * H + c4 / 32, nbq, pos, c4 % 32));
+      f16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = f2h_sat(ov[e] * (float)gv[e]);
+      *reinterpret_cast<f16x4*>(og + q * OP + c4) = v;
+    }
+    __syncthreads();
+    const int pos = qb * 32 + lq;
+    for (int blk = wave; blk < CBN; blk += 4) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int t = 0; t < KO; ++t)
+        acc = mfma32(ld16(woT + (int64_t)(blk * 32 + lq) * HD + t * 16 + g * 8),
+                     lds_f16x8((const char*)(og + lq * OP + t * 16 + g * 8)), acc);
+      if (pos < P) {
+        bf16* o = out + (int64_t)r * os_r + (int64_t)pos * os_p + blk * 32;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          bf16x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int c = jj * 8 + g * 4 + e;
+            ov[e] = f2bf(acc[jj * 4 + e] + (b_o != nullptr ? bf2f(b_o[blk * 32 + c]) : 0.0f));
+          }
+          st8(o + jj * 8 + g * 4, ov);
+        }
+      }
+    }
+    __syncthreads();   // og is rewritten by the next tile
+  }
 }
 
 template <int H, int C_OUT>
+static hipError_t finish_dispatch(const AttnArgs& a, hipStream_t s) {
+  const int nbq = a.Pp / 32;
+  if (nbq < 1 || a.Pp != nbq * 32 || a.P < 1 || a.P > a.Pp || a.nrows < 1 || a.o_part == nullptr)
+    return hipErrorInvalidValue;
+  const int64_t ntiles = (int64_t)a.nrows * nbq;
+  const int blocks = (int)std::min<int64_t>(ntiles, 65536);
+  hipLaunchKernelGGL((attn_finish_kernel<H, C_OUT>), dim3(blocks), dim3(256), 0, s, (const f16*)a.g_ws,
+                     (const float*)a.o_part, (const f16*)a.woT, (const bf16*)a.b_o, (bf16*)a.out, a.os_r, a.os_p,
+                     a.nrows, a.P, nbq);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish_bf16(const AttnArgs& a, hipStream_t s) {
+  if (a.H == 4) {
+    if (a.c_out == 64) return finish_dispatch<4, 64>(a, s);
+    if (a.c_out == 128) return finish_dispatch<4, 128>(a, s);
+    if (a.c_out == 256) return finish_dispatch<4, 256>(a, s);
+  } else if (a.H == 8) {
+    if (a.c_out == 64) return finish_dispatch<8, 64>(a, s);
+    if (a.c_out == 128) return finish_dispatch<8, 128>(a, s);
+    if (a.c_out == 256) return finish_dispatch<8, 256>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int H, int C_OUT, bool HAS_MASK, int MODE>
+static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
+  using SH = AttnShape<H>;
+  const int nbq = a.Pp / 32;
+  // the sweeps assume at least one key block and rows to work on
+  if (nbq < 1 || a.Pp != nbq * 32 || a.P < 1 || a.P > a.Pp || a.nrows < 1) return hipErrorInvalidValue;
+  const int nbk = MODE == 0 ? nbq : a.Ppk / 32;
+  const int Pk = MODE == 0 ? a.P : a.Pk;
+  if (MODE != 0 && (nbk < 1 || a.Ppk != nbk * 32 || Pk < 1 || Pk > a.Ppk || a.o_part == nullptr ||
+                    a.lse_part == nullptr))
+    return hipErrorInvalidValue;
+  const int n_qg = (nbq + SH::QWG - 1) / SH::QWG;
+  const int n_rg = (a.nrows + SH::RWG - 1) / SH::RWG;
+  const int64_t n = (int64_t)n_qg * n_rg;
+  hipLaunchKernelGGL((attn_kernel<H, C_OUT, HAS_MASK, MODE>), dim3((unsigned)n), dim3(512), 0, s,
+                     (const f16*)a.q_ws, (const f16*)a.k_ws, (const f16*)a.v_ws, (const f16*)a.g_ws,
+                     (const f16*)a.bias, a.mask_bits, (const f16*)a.woT, (const bf16*)a.b_o, (bf16*)a.out, a.os_r,
+                     a.os_p, a.nrows, a.P, a.Pp, n_qg, n_rg, nbq, Pk, nbk, a.o_part, a.lse_part);
+  return hipGetLastError();
+}
+
+template <int H, int C_OUT, int MODE>
 static hipError_t attn_dispatch_m(const AttnArgs& a, hipStream_t s) {
-  return a.mask_bits != nullptr ? attn_dispatch<H, C_OUT, true>(a, s) : attn_dispatch<H, C_OUT, false>(a, s);
+  return a.mask_bits != nullptr ? attn_dispatch<H, C_OUT, true, MODE>(a, s)
+                                : attn_dispatch<H, C_OUT, false, MODE>(a, s);
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
+  if (a.mode == 1 || a.mode == 2) {   // no output projection: one instance per head count
+    if (a.H == 4) return a.mode == 1 ? attn_dispatch_m<4, 128, 1>(a, s) : attn_dispatch_m<4, 128, 2>(a, s);
+    if (a.H == 8) return a.mode == 1 ? attn_dispatch_m<8, 128, 1>(a, s) : attn_dispatch_m<8, 128, 2>(a, s);
+    return hipErrorInvalidValue;
+  }
+  if (a.mode != 0) return hipErrorInvalidValue;
   if (a.H == 4) {
-    if (a.c_out == 64) return attn_dispatch_m<4, 64>(a, s);
-    if (a.c_out == 128) return attn_dispatch_m<4, 128>(a, s);
-    if (a.c_out == 256) return attn_dispatch_m<4, 256>(a, s);
+    if (a.c_out == 64) return attn_dispatch_m<4, 64, 0>(a, s);
+    if (a.c_out == 128) return attn_dispatch_m<4, 128, 0>(a, s);
+    if (a.c_out == 256) return attn_dispatch_m<4, 256, 0>(a, s);
   } else if (a.H == 8) {
-    if (a.c_out == 64) return attn_dispatch_m<8, 64>(a, s);
-    if (a.c_out == 128) return attn_dispatch_m<8, 128>(a, s);
-    if (a.c_out == 256) return attn_dispatch_m<8, 256>(a, s);
+    if (a.c_out == 64) return attn_dispatch_m<8, 64, 0>(a, s);
+    if (a.c_out == 128) return attn_dispatch_m<8, 128, 0>(a, s);
+    if (a.c_out == 256) return attn_dispatch_m<8, 256, 0>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -81,15 +81,16 @@ __device__ __forceinline__ int64_t v_off(int64_t rh, int nb, int pos, int d) {
   const int x = pos & 31;
   return ((((rh * nb + (pos >> 5)) * 2 + slot_t(x)) * 64 + d + 32 * slot_hg(x)) << 3) + slot_e(x);
 }
-__device__ __forceinline__ int64_t b16_off(int h, int nb, int q, int k) {
+// bias of nbq query blocks by nbk key blocks (both nb for the square bias)
+__device__ __forceinline__ int64_t b16_off(int h, int nbq, int nbk, int q, int k) {
   const int x = k & 31;
-  return (((((int64_t)h * nb + (q >> 5)) * nb + (k >> 5)) * 2 + slot_t(x)) * 64 + (q & 31) + 32 * slot_hg(x)) * 8 +
+  return (((((int64_t)h * nbq + (q >> 5)) * nbk + (k >> 5)) * 2 + slot_t(x)) * 64 + (q & 31) + 32 * slot_hg(x)) * 8 +
          slot_e(x);
 }
 // start of chunk `c` of block (a, b): element offsets for the 16-byte-per-lane reads
 __device__ __forceinline__ int64_t qkv_chunk(int64_t rh, int nb, int blk, int c) { return ((rh * nb + blk) * 2 + c) * 512; }
-__device__ __forceinline__ int64_t b16_chunk(int h, int nb, int qb, int kb, int c) {
-  return ((((int64_t)h * nb + qb) * nb + kb) * 2 + c) * 512;
+__device__ __forceinline__ int64_t b16_chunk(int h, int nbq, int nbk, int qb, int kb, int c) {
+  return ((((int64_t)h * nbq + qb) * nbk + kb) * 2 + c) * 512;
 }
 
 // Sum over an aligned group of `width` lanes (width a power of two <= 64).

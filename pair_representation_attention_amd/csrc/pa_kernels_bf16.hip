@@ -238,6 +238,9 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
     for (int b = 0; b < SH::NBLK; ++b) {
       const int col = col0 + b * 32;
       const int tensor = col / HD;            // 0 q, 1 k, 2 v, 3 g
+      // a NULL plane is not wanted (partial attention projects the query and
+      // the key pairs separately)
+      if ((tensor == 0 ? q_ws : tensor == 1 ? k_ws : tensor == 2 ? v_ws : g_ws) == nullptr) continue;
       const int hcol = col - tensor * HD;     // first column within the tensor
       const int64_t rh = (int64_t)r * H + hcol / 32;
       const int64_t chunk0 = (rh * nb + (p0 >> 5)) * 2;   // chunk of (rh, position block), t = 0
@@ -297,9 +300,9 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
         for (int j = 0; j < 4; ++j) {          // heads (< 8) are rows g*4 + j of registers 0..3
           const int hh = acc_row(j, g);
           if (hh < H) {
-            b16[b16_off(hh, nb, r, p)] = valid ? f2h_sat((acc[j] + cbb[hh]) * bias_scale) : f2h(0.0f);
+            b16[b16_off(hh, nb, nb, r, p)] = valid ? f2h_sat((acc[j] + cbb[hh]) * bias_scale) : f2h(0.0f);
             if (r == P - 1)   // the padded query rows get zeros at the same keys
-              for (int rp = P; rp < Pp; ++rp) b16[b16_off(hh, nb, rp, p)] = f2h(0.0f);
+              for (int rp = P; rp < Pp; ++rp) b16[b16_off(hh, nb, nb, rp, p)] = f2h(0.0f);
           }
         }
       } else if (valid) {    // caller layout [H][P][P] float
@@ -313,17 +316,24 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
   }
 }
 
-// Copy of a caller-provided bias [H][P][P] (float, natural-log units) into
-// the attention layout (fp16 operand order, log2 units, zero padding).
-__global__ void bias_to_attn_layout_kernel(const float* __restrict__ src, f16* __restrict__ dst, int H, int P,
-                                           int Pp) {
-  const int64_t total = (int64_t)H * Pp * Pp;
-  const int nb = Pp / 32;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int h = (int)(i / ((int64_t)Pp * Pp));
-    const int64_t rem = i % ((int64_t)Pp * Pp);
-    const int q = (int)(rem / Pp), k = (int)(rem % Pp);
-    dst[b16_off(h, nb, q, k)] = (q < P && k < P) ? f2h_sat(src[((int64_t)h * P + q) * P + k] * kLog2e) : f2h(0.0f);
+// Copy of a caller-provided bias [H][Pq][Pk] (float, natural-log units) into
+// the attention layout (fp16 operand order, log2 units, Ppq x Ppk with zero
+// padding).  Each thread converts 8 consecutive keys of one query, whose
+// source is 32 contiguous bytes.
+__global__ void bias_to_attn_layout_kernel(const float* __restrict__ src, f16* __restrict__ dst, int H, int Pq,
+                                           int Pk, int Ppq, int Ppk) {
+  const int nbq = Ppq / 32, nbk = Ppk / 32;
+  const int64_t groups = (int64_t)H * Ppq * (Ppk / 8);
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < groups; i += (int64_t)gridDim.x * blockDim.x) {
+    const int k0 = (int)(i % (Ppk / 8)) * 8;
+    const int64_t hq = i / (Ppk / 8);
+    const int h = (int)(hq / Ppq), q = (int)(hq % Ppq);
+    const float* row = src + ((int64_t)h * Pq + q) * Pk;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = k0 + e;
+      dst[b16_off(h, nbq, nbk, q, k)] = (q < Pq && k < Pk) ? f2h_sat(row[k] * kLog2e) : f2h(0.0f);
+    }
   }
 }
 
@@ -336,10 +346,12 @@ __global__ void bias_to_attn_layout_kernel(const float* __restrict__ src, f16* _
 
 namespace pa {
 
-hipError_t launch_bias_to_attn_layout(const float* src, void* dst, int H, int P, int Pp, hipStream_t s) {
-  const int64_t total = (int64_t)H * Pp * Pp;
-  const int blocks = (int)std::min<int64_t>((total + 255) / 256, 8192);
-  hipLaunchKernelGGL(bias_to_attn_layout_kernel, dim3(blocks), dim3(256), 0, s, src, (f16*)dst, H, P, Pp);
+hipError_t launch_bias_to_attn_layout(const float* src, void* dst, int H, int Pq, int Pk, int Ppq, int Ppk,
+                                      hipStream_t s) {
+  const int64_t groups = (int64_t)H * Ppq * (Ppk / 8);
+  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((groups + 255) / 256, 8192));
+  hipLaunchKernelGGL(bias_to_attn_layout_kernel, dim3(blocks), dim3(256), 0, s, src, (f16*)dst, H, Pq, Pk, Ppq,
+                     Ppk);
   return hipGetLastError();
 }
 

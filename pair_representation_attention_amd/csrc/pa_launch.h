@@ -36,14 +36,26 @@ struct AttnArgs {
   const void *woT, *b_o;
   void* out;                     // element (r, p, c) at out[r*os_r + p*os_p + c]
   int64_t os_r, os_p;
-  int H, c_out, nrows, P, Pp;
+  int H, c_out, nrows;
+  int P, Pp;                     // queries (and keys in mode 0)
+  // 0: one pass (gate, output projection, out); 1: one shard of Pk keys
+  // (Ppk padded): its o and lse into o_part [nrows][P][H*32] / lse_part
+  // [nrows][H][P]; 2: merged into the o_part / lse_part already there
+  int mode;
+  int Pk, Ppk;
+  float *o_part, *lse_part;
 };
 
 hipError_t launch_pack_bf16(const PackArgs& a, hipStream_t s);
-hipError_t launch_bias_to_attn_layout(const float* src, void* dst, int H, int P, int Pp, hipStream_t s);
+// caller bias [H][Pq][Pk] float (natural-log units) -> attention layout, Ppq x Ppk
+hipError_t launch_bias_to_attn_layout(const float* src, void* dst, int H, int Pq, int Pk, int Ppq, int Ppk,
+                                      hipStream_t s);
 // mode 0: q,k,v,g   1: q,k,v,g + bias   2: bias only
 hipError_t launch_proj_bf16(const ProjArgs& a, int mode, int num_cu, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+// gate (g_ws, layout of q), output projection and bf16 store of merged partial
+// outputs o_part (fields g_ws, woT, b_o, out, os_r, os_p, H, c_out, nrows, P, Pp, o_part)
+hipError_t launch_finish_bf16(const AttnArgs& a, hipStream_t s);
 // keep bits [nrows][nkb] for the bf16 attention (mask may be NULL: all keys < P kept)
 hipError_t launch_mask_bits(const uint8_t* mask, int64_t ms_r, int64_t ms_k, uint32_t* bits, int nrows, int P,
                             int nkb, hipStream_t s);

@@ -91,14 +91,36 @@ Layout make_layout(int64_t nrows, int64_t P, int64_t c_in, int64_t c_out, int64_
   return L;
 }
 
-// Partial attention (fp32 path): R rows of Jq query pairs against Kn key
-// pairs.  Queries get q (and, for the finish, the gate); keys get k and v.
+// Partial attention: R rows of Jq query pairs against Kn key pairs.  Queries
+// get q (and, for the finish, the gate); keys get k and v.
 struct PartialLayout {
   size_t w_hi = 0, w_lo = 0, cst = 0, wo_hi = 0, wo_lo = 0, q = 0, q_lo = 0, k = 0, k_lo = 0, v = 0, v_lo = 0, g = 0,
          bias = 0, bits = 0, total = 0;
+  size_t wT = 0, woT = 0;   // bf16 path: packed fp16 weights
 };
-PartialLayout make_partial_layout(int64_t R, int64_t Jq, int64_t Kn, int64_t c, int64_t H) {
+PartialLayout make_partial_layout(int64_t R, int64_t Jq, int64_t Kn, int64_t c, int64_t H, int32_t dtype) {
   PartialLayout L;
+  if (dtype == PAIRATTN_BF16) {
+    const int64_t hd = H * 32;
+    const int64_t Ppq = pad32(Jq), Ppk = pad32(Kn);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+      const size_t at = off;
+      off += align_up(bytes);
+      return at;
+    };
+    L.wT = take((size_t)4 * hd * c * 2);
+    L.woT = take((size_t)c * hd * 2);
+    const size_t qplane = (size_t)R * H * Ppq * 32 * 2, kplane = (size_t)R * H * Ppk * 32 * 2;
+    L.q = take(qplane);
+    L.g = take(qplane);
+    L.k = take(kplane);
+    L.v = take(kplane);
+    L.bias = take((size_t)H * Ppq * Ppk * 2);   // fp16 operand order, log2 units
+    L.bits = take((size_t)R * (Ppk / 32) * 4);
+    L.total = off;
+    return L;
+  }
   const int64_t hd = H * 32;
   const int64_t Ppq = pad32(Jq), Ppk = pad32(Kn);
   size_t off = 0;
@@ -388,10 +410,10 @@ int pairattn_validate_tri_chunked(const void* z, const uint8_t* mask, const pair
 
 size_t pairattn_tri_partial_workspace_bytes(int64_t R, int64_t Jq, int64_t Kn, int64_t c_z, int64_t H, int64_t d,
                                             int32_t dtype) {
-  if (dtype != PAIRATTN_F32 || R < 1 || Jq < 1 || Kn < 1 || d != 32 || !supported_h(H) || !supported_c(c_z) ||
-      Jq > kMaxPositions || Kn > kMaxPositions)
+  if ((dtype != PAIRATTN_F32 && dtype != PAIRATTN_BF16) || R < 1 || Jq < 1 || Kn < 1 || d != 32 ||
+      !supported_h(H) || !supported_c(c_z) || Jq > kMaxPositions || Kn > kMaxPositions)
     return 0;
-  return make_partial_layout(R, Jq, Kn, c_z, H).total;
+  return make_partial_layout(R, Jq, Kn, c_z, H, dtype).total;
 }
 
 int pairattn_validate_tri_partial(const void* q_pairs, const void* kv_pairs, const float* bias, const uint8_t* mask,
@@ -399,8 +421,6 @@ int pairattn_validate_tri_partial(const void* q_pairs, const void* kv_pairs, con
                                   int64_t Kn, int64_t c_z, int64_t H, int64_t d) {
   g_err[0] = '\0';
   PA_TRY(check_params(p, true, false));
-  if (p->dtype != PAIRATTN_F32)
-    return fail(PAIRATTN_ERR_UNSUPPORTED, "partial attention is built on the fp32 path only (dtype PAIRATTN_F32)");
   if (q_pairs == nullptr || kv_pairs == nullptr || bias == nullptr || o == nullptr || lse == nullptr)
     return fail(PAIRATTN_ERR_ARG, "q_pairs, kv_pairs, bias, o and lse must not be NULL");
   if (!aligned16(q_pairs) || !aligned16(kv_pairs) || !aligned16(bias) || !aligned16(o) || !aligned16(lse))
@@ -409,7 +429,7 @@ int pairattn_validate_tri_partial(const void* q_pairs, const void* kv_pairs, con
   PA_TRY(check_shape_common(std::max(Jq, Kn), c_z, H, d, p->dtype));
   PA_TRY(check_rows_limit(R, p->dtype));
   const size_t obytes = (size_t)R * Jq * H * d * 4, lbytes = (size_t)R * H * Jq * 4;
-  const size_t qbytes = (size_t)R * Jq * c_z * 4, kbytes = (size_t)R * Kn * c_z * 4;
+  const size_t qbytes = (size_t)R * Jq * c_z * elt_bytes(p->dtype), kbytes = (size_t)R * Kn * c_z * elt_bytes(p->dtype);
   if (overlaps(o, obytes, lse, lbytes)) return fail(PAIRATTN_ERR_ARG, "o overlaps lse");
   for (const void* in : {q_pairs, kv_pairs, (const void*)bias}) {
     const size_t nb = in == q_pairs ? qbytes : in == kv_pairs ? kbytes : (size_t)H * Jq * Kn * 4;
@@ -559,7 +579,7 @@ static int run_row_attention_bf16(const pairattn_params* p, const Layout& L, hip
     mark("pair_bias");
   }
   if (ra.bias_given != nullptr) {   // row block: caller's bias -> attention layout
-    PA_TRY(hip_status(pa::launch_bias_to_attn_layout(ra.bias_given, bias_ws, (int)ra.H, (int)ra.P, Pp, s),
+    PA_TRY(hip_status(pa::launch_bias_to_attn_layout(ra.bias_given, bias_ws, (int)ra.H, (int)ra.P, (int)ra.P, Pp, Pp, s),
                       "bias copy launch"));
     mark("bias_copy");
   }
@@ -912,11 +932,73 @@ int pairattn_tri_partial_fwd(const void* q_pairs, const void* kv_pairs, const fl
   PA_TRY(pairattn_validate_tri_partial(q_pairs, kv_pairs, bias, mask, p, o, lse, R, Jq, Kn, c_z, H, d));
   int num_cu = 0;
   PA_TRY(check_device(&num_cu));
-  const PartialLayout L = make_partial_layout(R, Jq, Kn, c_z, H);
+  const PartialLayout L = make_partial_layout(R, Jq, Kn, c_z, H, p->dtype);
   const int64_t hd = H * 32;
   const int Ppq = (int)pad32(Jq), Ppk = (int)pad32(Kn);
   hipStream_t s = static_cast<hipStream_t>(stream);
   tm_begin(s);
+  if (p->dtype == PAIRATTN_BF16) {
+    pa::PackArgs pk{p->w_q, p->w_k, p->w_v, p->w_g, p->w_o, ws_at(p, L.wT), ws_at(p, L.woT), (int)c_z, (int)hd,
+                    (int)c_z};
+    PA_TRY(hip_status(pa::launch_pack_bf16(pk, s), "weight packing launch"));
+    tm_mark(s, "pack");
+    // q of the query pairs, k and v of the key pairs (the other planes NULL)
+    pa::ProjArgs pj{};
+    pj.x = q_pairs;
+    pj.xs_r = Jq * c_z;
+    pj.xs_p = c_z;
+    pj.gamma = p->ln_gamma;
+    pj.beta = p->ln_beta;
+    pj.eps = p->ln_eps;
+    pj.wT = ws_at(p, L.wT);
+    pj.b_g = p->b_g;
+    pj.q_scale = 1.4426950408889634f / std::sqrt(32.0f);
+    pj.q_ws = ws_at(p, L.q);
+    pj.c_in = (int)c_z;
+    pj.hd = (int)hd;
+    pj.H = (int)H;
+    pj.nrows = (int)R;
+    pj.P = (int)Jq;
+    pj.Pp = Ppq;
+    PA_TRY(hip_status(pa::launch_proj_bf16(pj, 0, num_cu, s), "query projection launch"));
+    pj.x = kv_pairs;
+    pj.xs_r = Kn * c_z;
+    pj.q_ws = nullptr;
+    pj.k_ws = ws_at(p, L.k);
+    pj.v_ws = ws_at(p, L.v);
+    pj.P = (int)Kn;
+    pj.Pp = Ppk;
+    PA_TRY(hip_status(pa::launch_proj_bf16(pj, 0, num_cu, s), "key projection launch"));
+    tm_mark(s, "projection");
+    void* bias_ws = ws_at(p, L.bias);
+    PA_TRY(hip_status(pa::launch_bias_to_attn_layout(bias, bias_ws, (int)H, (int)Jq, (int)Kn, Ppq, Ppk, s),
+                      "bias copy launch"));
+    tm_mark(s, "bias_copy");
+    uint32_t* bits = reinterpret_cast<uint32_t*>(ws_at(p, L.bits));
+    if (mask != nullptr) {
+      PA_TRY(hip_status(pa::launch_mask_bits(mask, Kn, 1, bits, (int)R, (int)Kn, Ppk / 32, s), "mask bits launch"));
+      tm_mark(s, "mask_bits");
+    }
+    pa::AttnArgs at{};
+    at.q_ws = ws_at(p, L.q);
+    at.k_ws = ws_at(p, L.k);
+    at.v_ws = ws_at(p, L.v);
+    at.bias = bias_ws;
+    at.mask_bits = mask != nullptr ? bits : nullptr;
+    at.H = (int)H;
+    at.c_out = (int)c_z;
+    at.nrows = (int)R;
+    at.P = (int)Jq;
+    at.Pp = Ppq;
+    at.mode = accumulate ? 2 : 1;
+    at.Pk = (int)Kn;
+    at.Ppk = Ppk;
+    at.o_part = o;
+    at.lse_part = lse;
+    PA_TRY(hip_status(pa::launch_attn_bf16(at, s), "attention launch"));
+    tm_mark(s, "attention");
+    return PAIRATTN_OK;
+  }
   pa::PackF32Args pk{};
   pk.wq = p->w_q;
   pk.wk = p->w_k;
@@ -1011,8 +1093,6 @@ int pairattn_validate_tri_partial_finish(const void* q_pairs, const float* o, co
                                          const void* out, int64_t R, int64_t Jq, int64_t c_z, int64_t H, int64_t d) {
   g_err[0] = '\0';
   PA_TRY(check_params(p, true, false));
-  if (p->dtype != PAIRATTN_F32)
-    return fail(PAIRATTN_ERR_UNSUPPORTED, "partial attention is built on the fp32 path only (dtype PAIRATTN_F32)");
   if (q_pairs == nullptr || o == nullptr || out == nullptr)
     return fail(PAIRATTN_ERR_ARG, "q_pairs, o and out must not be NULL");
   if (!aligned16(q_pairs) || !aligned16(o) || !aligned16(out))
@@ -1020,7 +1100,7 @@ int pairattn_validate_tri_partial_finish(const void* q_pairs, const float* o, co
   if (R < 1 || Jq < 1) return fail(PAIRATTN_ERR_ARG, "R and Jq must be >= 1");
   PA_TRY(check_shape_common(Jq, c_z, H, d, p->dtype));
   PA_TRY(check_rows_limit(R, p->dtype));
-  const size_t obytes = (size_t)R * Jq * c_z * 4;
+  const size_t obytes = (size_t)R * Jq * c_z * elt_bytes(p->dtype);
   if (overlaps(out, obytes, q_pairs, obytes)) return fail(PAIRATTN_ERR_ARG, "out overlaps q_pairs");
   if (overlaps(out, obytes, o, (size_t)R * Jq * H * d * 4)) return fail(PAIRATTN_ERR_ARG, "out overlaps o");
   PA_TRY(check_workspace(p, pairattn_tri_partial_finish_workspace_bytes(R, Jq, c_z, H, d, p->dtype)));
@@ -1033,11 +1113,52 @@ int pairattn_tri_partial_finish(const void* q_pairs, const float* o, const paira
   PA_TRY(pairattn_validate_tri_partial_finish(q_pairs, o, p, out, R, Jq, c_z, H, d));
   int num_cu = 0;
   PA_TRY(check_device(&num_cu));
-  const PartialLayout L = make_partial_layout(R, Jq, 1, c_z, H);
+  const PartialLayout L = make_partial_layout(R, Jq, 1, c_z, H, p->dtype);
   const int64_t hd = H * 32;
   const int Ppq = (int)pad32(Jq);
   hipStream_t s = static_cast<hipStream_t>(stream);
   tm_begin(s);
+  if (p->dtype == PAIRATTN_BF16) {
+    pa::PackArgs pk{p->w_q, p->w_k, p->w_v, p->w_g, p->w_o, ws_at(p, L.wT), ws_at(p, L.woT), (int)c_z, (int)hd,
+                    (int)c_z};
+    PA_TRY(hip_status(pa::launch_pack_bf16(pk, s), "weight packing launch"));
+    tm_mark(s, "pack");
+    pa::ProjArgs pj{};   // the gate of the query pairs only
+    pj.x = q_pairs;
+    pj.xs_r = Jq * c_z;
+    pj.xs_p = c_z;
+    pj.gamma = p->ln_gamma;
+    pj.beta = p->ln_beta;
+    pj.eps = p->ln_eps;
+    pj.wT = ws_at(p, L.wT);
+    pj.b_g = p->b_g;
+    pj.q_scale = 1.4426950408889634f / std::sqrt(32.0f);
+    pj.g_ws = ws_at(p, L.g);
+    pj.c_in = (int)c_z;
+    pj.hd = (int)hd;
+    pj.H = (int)H;
+    pj.nrows = (int)R;
+    pj.P = (int)Jq;
+    pj.Pp = Ppq;
+    PA_TRY(hip_status(pa::launch_proj_bf16(pj, 0, num_cu, s), "gate projection launch"));
+    tm_mark(s, "projection");
+    pa::AttnArgs at{};
+    at.g_ws = pj.g_ws;
+    at.woT = ws_at(p, L.woT);
+    at.b_o = p->b_o;
+    at.out = out;
+    at.os_r = Jq * c_z;
+    at.os_p = c_z;
+    at.H = (int)H;
+    at.c_out = (int)c_z;
+    at.nrows = (int)R;
+    at.P = (int)Jq;
+    at.Pp = Ppq;
+    at.o_part = const_cast<float*>(o);
+    PA_TRY(hip_status(pa::launch_finish_bf16(at, s), "finish launch"));
+    tm_mark(s, "finish");
+    return PAIRATTN_OK;
+  }
   pa::PackF32Args pk{};
   pk.wq = p->w_q;
   pk.wk = p->w_k;

@@ -247,19 +247,23 @@ QP, KP, BIAS, O_, LSE = A + 100 * MB, A + 200 * MB, A + 300 * MB, A + 400 * MB, 
 
 
 def test_partial_workspace_sizes():
-    assert lib.pairattn_tri_partial_workspace_bytes(4, 64, 96, 128, 4, 32, lib.PAIRATTN_F32) > 0
-    # built on the fp32 path only
-    assert lib.pairattn_tri_partial_workspace_bytes(4, 64, 96, 128, 4, 32, lib.PAIRATTN_BF16) == 0
-    assert lib.pairattn_tri_partial_workspace_bytes(4, 64, 0, 128, 4, 32, lib.PAIRATTN_F32) == 0
-    a = lib.pairattn_tri_partial_workspace_bytes(4, 64, 96, 128, 4, 32, lib.PAIRATTN_F32)
-    b = lib.pairattn_tri_partial_workspace_bytes(4, 64, 192, 128, 4, 32, lib.PAIRATTN_F32)
-    assert b > a
-    assert lib.pairattn_tri_partial_finish_workspace_bytes(4, 64, 128, 4, 32, lib.PAIRATTN_F32) > 0
+    for dt in (lib.PAIRATTN_F32, lib.PAIRATTN_BF16):
+        assert lib.pairattn_tri_partial_workspace_bytes(4, 64, 96, 128, 4, 32, dt) > 0
+        assert lib.pairattn_tri_partial_workspace_bytes(4, 64, 0, 128, 4, 32, dt) == 0
+        a = lib.pairattn_tri_partial_workspace_bytes(4, 64, 96, 128, 4, 32, dt)
+        b = lib.pairattn_tri_partial_workspace_bytes(4, 64, 192, 128, 4, 32, dt)
+        assert b > a
+        assert lib.pairattn_tri_partial_finish_workspace_bytes(4, 64, 128, 4, 32, dt) > 0
+    assert lib.pairattn_tri_partial_workspace_bytes(4, 64, 96, 128, 4, 32, 7) == 0   # unknown dtype
+    # the bf16 path keeps single fp16 planes (no lo planes): a smaller workspace
+    assert lib.pairattn_tri_partial_workspace_bytes(4, 64, 96, 128, 4, 32, lib.PAIRATTN_BF16) < \
+        lib.pairattn_tri_partial_workspace_bytes(4, 64, 96, 128, 4, 32, lib.PAIRATTN_F32)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(), lib.PAIRATTN_OK),
-    (dict(dtype=lib.PAIRATTN_BF16), lib.PAIRATTN_ERR_UNSUPPORTED),
+    (dict(dtype=lib.PAIRATTN_BF16), lib.PAIRATTN_OK),
+    (dict(dtype=lib.PAIRATTN_BF16, ws_short=True), lib.PAIRATTN_ERR_WORKSPACE),
     (dict(o=None), lib.PAIRATTN_ERR_ARG),
     (dict(lse=LSE + 4), lib.PAIRATTN_ERR_ARG),               # misaligned
     (dict(Kn=0), lib.PAIRATTN_ERR_ARG),
@@ -269,7 +273,7 @@ def test_partial_workspace_sizes():
 ])
 def test_validate_tri_partial(kw, status):
     dt = kw.get("dtype", lib.PAIRATTN_F32)
-    need = lib.pairattn_tri_partial_workspace_bytes(3, 40, 70, 128, 4, 32, lib.PAIRATTN_F32)
+    need = lib.pairattn_tri_partial_workspace_bytes(3, 40, 70, 128, 4, 32, dt)
     p = _params(dt, ws=WS, ws_bytes=need - (256 if kw.get("ws_short") else 0))
     a = dict(q=QP, k=KP, b=BIAS, m=None, o=O_, lse=LSE, R=3, Jq=40, Kn=70)
     a.update({k: v for k, v in kw.items() if k in a})
@@ -287,6 +291,9 @@ def test_validate_tri_partial_finish():
     p = _params(lib.PAIRATTN_F32, ws=WS, ws_bytes=need)
     assert lib.pairattn_validate_tri_partial_finish(QP, O_, p, OUT, 3, 40, 128, 4, 32) == lib.PAIRATTN_OK
     assert lib.pairattn_validate_tri_partial_finish(QP, O_, p, QP, 3, 40, 128, 4, 32) == lib.PAIRATTN_ERR_ARG
-    pb = _params(lib.PAIRATTN_BF16, ws=WS, ws_bytes=need)
+    nb = lib.pairattn_tri_partial_finish_workspace_bytes(3, 40, 128, 4, 32, lib.PAIRATTN_BF16)
+    pb = _params(lib.PAIRATTN_BF16, ws=WS, ws_bytes=nb)
+    assert lib.pairattn_validate_tri_partial_finish(QP, O_, pb, OUT, 3, 40, 128, 4, 32) == lib.PAIRATTN_OK
+    pb = _params(lib.PAIRATTN_BF16, ws=WS, ws_bytes=nb - 256)
     assert lib.pairattn_validate_tri_partial_finish(QP, O_, pb, OUT, 3, 40, 128, 4, 32) == \
-        lib.PAIRATTN_ERR_UNSUPPORTED
+        lib.PAIRATTN_ERR_WORKSPACE
