@@ -198,7 +198,7 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=24, help="oracle sample size (rows, about 0.35-1.4 s each by host)")
     ap.add_argument("--extra", action="store_true", help="also time MSA row attention and the row block")
     ap.add_argument("--workload", choices=["tri_bf16_i1536", "msa_fp32_s5120_i384", "tri_bf16_i16384_chunked",
-                                           "ring_fp32_i1536_grid2x2"],
+                                           "ring_fp32_i1536_grid2x2", "ring_bf16_i1536_grid2x2"],
                     default="tri_bf16_i1536",
                     help="time only the fp32 extra-MSA workload, or chunked triangle attention at I = 16384 "
                          "(one JSON line)")
@@ -236,7 +236,7 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.workload != "tri_bf16_i1536":
         fn = {"msa_fp32_s5120_i384": msa_fp32_workload, "tri_bf16_i16384_chunked": chunked_workload,
-              "ring_fp32_i1536_grid2x2": ring_workload}[args.workload]
+              "ring_fp32_i1536_grid2x2": ring_workload, "ring_bf16_i1536_grid2x2": ring_workload}[args.workload]
         print(json.dumps({"workload": args.workload, **fn(args, device, inputs, lib, torch)}), flush=True)
         return 0
     cfg = inputs.CONFIGS["tri_bf16_i1536"]
@@ -480,41 +480,62 @@ def chunked_workload(args, device, inputs, lib, torch) -> dict:
 
 def ring_workload(args, device, inputs, lib, torch) -> dict:
     """One device's share of starting-node attention of Z[1536, 1536, 128]
-    fp32 on a 2 x 2 grid: its 768 rows x 768 query columns against the two
-    768-column key shards in ring order (partial, partial merged, finish),
-    beside the one-pass fp32 call on the same 768 rows (all 1536 queries,
-    i.e. twice the queries) for the rate comparison."""
+    (fp32 or bf16) on a 2 x 2 grid: its 768 rows x 768 query columns against
+    the two 768-column key shards in ring order (partial, partial merged,
+    finish), beside the one-pass call on the same 768 rows (all 1536
+    queries, i.e. twice the queries) for the rate comparison.  The attention
+    kernel of the partial calls is timed with HIP events on its launch
+    stream (a second pass, after the timed steps)."""
+    import numpy as np
+
+    dt = "bf16" if "bf16" in args.workload else "f32"
+    code = device.dtype_code(dt)
     I, c, H, d, half = 1536, 128, 4, 32, 768
-    log("ring: generating Z[1536,1536,128] fp32 on the device")
-    z = inputs.make_z_device(I, c, 11, dtype="f32")
-    p = inputs.make_chunked_params(c, H, d, 11, dtype="f32")
+    log(f"ring: generating Z[1536,1536,128] {dt} on the device")
+    z = inputs.make_z_device(I, c, 11, dtype=dt)
+    p = inputs.make_chunked_params(c, H, d, 11, dtype=dt)
     zq = z[:half, :half].contiguous()                   # this device's pairs: rows A, columns B
     shards = [z[:half, :half].contiguous(), z[:half, half:].contiguous()]
     bias = torch.empty((H, I, I), dtype=torch.float32, device="cuda")
-    pr = device.make_params(p, "f32")
+    pr = device.make_params(p, dt)
     lib.pairattn_tri_bias(z, pr, bias, I, c, H, lib.PAIRATTN_START)
     btiles = [bias[:, :half, :half].contiguous(), bias[:, :half, half:].contiguous()]
-    n = max(lib.pairattn_tri_partial_workspace_bytes(half, half, half, c, H, d, lib.PAIRATTN_F32),
-            lib.pairattn_tri_partial_finish_workspace_bytes(half, half, c, H, d, lib.PAIRATTN_F32))
-    prm = device.make_params(p, "f32", n)
+    n = max(lib.pairattn_tri_partial_workspace_bytes(half, half, half, c, H, d, code),
+            lib.pairattn_tri_partial_finish_workspace_bytes(half, half, c, H, d, code))
+    prm = device.make_params(p, dt, n)
     o = torch.empty((half, half, H * d), dtype=torch.float32, device="cuda")
     lse = torch.empty((half, H, half), dtype=torch.float32, device="cuda")
-    out = torch.empty((half, half, c), dtype=torch.float32, device="cuda")
+    out = torch.empty((half, half, c), dtype=device.torch_dtype(dt), device="cuda")
+    stages = {}
 
-    def step():
+    def step(record=False):
         for sidx in range(2):
             lib.pairattn_tri_partial_fwd(zq, shards[sidx], btiles[sidx], None, prm, o, lse, sidx > 0, half, half,
                                          half, c, H, d)
+            if record:
+                for name, ms in lib.pairattn_timing_read():
+                    stages.setdefault(name, []).append(ms)
         lib.pairattn_tri_partial_finish(zq, o, prm, out, half, half, c, H, d)
+        if record:
+            for name, ms in lib.pairattn_timing_read():
+                stages.setdefault("finish_" + name, []).append(ms)
 
     steps = max(3, args.steps)
     ms = _time(step, steps, 2, torch)
+    lib.pairattn_timing_enable(True)
+    for _ in range(steps):
+        step(True)
+    lib.pairattn_timing_enable(False)
     f = 4.0 * half * half * I * H * d + 2.0 * half * half * H * d * c     # attention + output projection
-    rows = device.RowsRunner(z, z[:half].contiguous(), None, p, H, "f32")
+    f_shard = 4.0 * half * half * half * H * d                              # one partial attention launch
+    attn_ms = float(np.mean(stages["attention"]))
+    rows = device.RowsRunner(z, z[:half].contiguous(), None, p, H, dt)
     rows.compute_bias()
     ms_rows = _time(rows.rows, steps, 2, torch)
     f_rows = 4.0 * half * I * I * H * d + 2.0 * half * I * H * d * c
-    res = {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12, "rows": half, "queries": half, "keys": I, "shards": 2,
+    res = {"dtype": dt, "ms": ms, "tflops": f / (ms * 1e-3) / 1e12, "rows": half, "queries": half, "keys": I,
+           "shards": 2, "shard_attention_ms": attn_ms, "shard_attention_tflops": f_shard / (attn_ms * 1e-3) / 1e12,
+           "stage_ms": {k: float(np.mean(v)) for k, v in stages.items()},
            "one_pass_rows_ms": ms_rows, "one_pass_rows_tflops": f_rows / (ms_rows * 1e-3) / 1e12}
     del rows, z, shards, bias, o, lse, out
     torch.cuda.empty_cache()
