@@ -25,32 +25,59 @@
 namespace pa {
 
 // --------------------------------------------------------------------------
-// weight packing: transposed fp16 copies so that every MFMA operand lane
-// reads 16 contiguous bytes.  bf16 -> fp16 is exact for magnitudes in
-// [2^-14, 65504]; smaller weights keep an absolute error below 2^-25.
-//   wT  [4*HD][C_IN]  rows: q cols, k cols, v cols, g cols
-//   woT [C_OUT][HD]
+// weight packing, once per call.
+//   wimg [4*HD/32][C_IN/16][64][8] fp16: the projection operand image of
+//        gamma o W (LayerNorm's scale folded into the q|k|v|g columns), in
+//        the order the projection keeps it in LDS: block b of 32 columns,
+//        K-step t, lane l holds column b*32 + l%32 and channels
+//        t*16 + (l/32)*8 .. +7.
+//   cst  [4*HD] float: beta . W per column (LayerNorm's shift), plus the gate
+//        bias for the g columns.
+//   woT  [C_OUT][HD] fp16: W_o transposed (the output projection operand).
+// bf16 -> fp16 is exact for magnitudes in [2^-14, 65504]; smaller values
+// keep an absolute error below 2^-25; larger ones saturate.
 // --------------------------------------------------------------------------
 __global__ void pack_weights_kernel(const bf16* __restrict__ wq, const bf16* __restrict__ wk,
                                     const bf16* __restrict__ wv, const bf16* __restrict__ wg,
-                                    const bf16* __restrict__ wo, f16* __restrict__ wT,
-                                    f16* __restrict__ woT, int c_in, int hd, int c_out) {
-  const int64_t n_w = (int64_t)4 * hd * c_in;
+                                    const bf16* __restrict__ wo, const bf16* __restrict__ gamma,
+                                    f16* __restrict__ wimg, f16* __restrict__ woT, int c_in, int hd, int c_out) {
+  const int ks = c_in / 16;
+  const int64_t n_w = (int64_t)4 * hd / 32 * ks * 64;   // 8-element lane slots of the image
   const int64_t n_o = (int64_t)c_out * hd;
-  const int64_t total = n_w + n_o;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_w + n_o;
        i += (int64_t)gridDim.x * blockDim.x) {
     if (i < n_w) {
-      const int row = (int)(i / c_in), k = (int)(i % c_in);
-      const int t = row / hd, col = row % hd;
-      const bf16* src = t == 0 ? wq : t == 1 ? wk : t == 2 ? wv : wg;
-      wT[i] = f2h_sat(bf2f(src[(int64_t)k * hd + col]));
+      const int l = (int)(i & 63), t = (int)((i >> 6) % ks), b = (int)((i >> 6) / ks);
+      const int col = b * 32 + (l & 31), k0 = t * 16 + (l >> 5) * 8;
+      const int tensor = col / hd, c = col % hd;
+      const bf16* src = tensor == 0 ? wq : tensor == 1 ? wk : tensor == 2 ? wv : wg;
+      f16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = f2h_sat(bf2f(src[(int64_t)(k0 + e) * hd + c]) * bf2f(gamma[k0 + e]));
+      *reinterpret_cast<f16x8*>(wimg + i * 8) = o;
     } else {
       const int64_t j = i - n_w;
       const int c = (int)(j / hd), k = (int)(j % hd);
       woT[j] = f2h_sat(bf2f(wo[(int64_t)k * c_out + c]));
     }
   }
+}
+
+// cst[col] = sum_k beta[k] W[k][col] (+ b_g for the gate columns): one wave
+// per column, fp32 partial sums over lanes, then a wave reduction.
+__global__ void pack_consts_kernel(const bf16* __restrict__ wq, const bf16* __restrict__ wk,
+                                   const bf16* __restrict__ wv, const bf16* __restrict__ wg,
+                                   const bf16* __restrict__ beta, const bf16* __restrict__ b_g,
+                                   float* __restrict__ cst, int c_in, int hd) {
+  const int col = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (col >= 4 * hd) return;
+  const int tensor = col / hd, c = col % hd;
+  const bf16* src = tensor == 0 ? wq : tensor == 1 ? wk : tensor == 2 ? wv : wg;
+  float acc = 0.0f;
+  for (int k = lane; k < c_in; k += kWave) acc += bf2f(beta[k]) * bf2f(src[(int64_t)k * hd + c]);
+  acc = group_sum<kWave>(acc);
+  if (lane == 0) cst[col] = acc + (tensor == 3 && b_g != nullptr ? bf2f(b_g[c]) : 0.0f);
 }
 
 // --------------------------------------------------------------------------
@@ -67,9 +94,10 @@ __global__ void pack_weights_kernel(const bf16* __restrict__ wq, const bf16* __r
 // before the current tile is computed.
 //
 // The weight operands of this workgroup's NCOL projection columns sit in
-// LDS in operand order ([column block][K-step][lane][8]), loaded once; so
-// do LayerNorm's gamma and beta, the gate bias and, when the pair bias is
-// produced, the w_b operand (rows = heads, zero beyond H).
+// LDS in operand order ([column block][K-step][lane][8]), copied once from
+// the packed image (LayerNorm's gamma already folded in) with the column
+// constants; when the pair bias is produced, so is the w_b operand (rows =
+// heads, zero beyond H), folded here.
 //   MODE 0: q, k, v, g          MODE 1: q, k, v, g and the pair bias
 //   MODE 2: pair bias only (NCOL = 0)
 // Column group blockIdx.y covers columns [y*NCOL, (y+1)*NCOL) of q|k|v|g;
@@ -94,8 +122,8 @@ constexpr int kProjThreads = 512;
 template <int C_IN, int HD, int NCOL, int MODE>
 __global__ __launch_bounds__(kProjThreads) void proj_kernel(
     const bf16* __restrict__ x, int64_t xs_r, int64_t xs_p, int tile_rmajor, const bf16* __restrict__ gamma,
-    const bf16* __restrict__ beta, float eps, const f16* __restrict__ wT, const bf16* __restrict__ wb,
-    const bf16* __restrict__ b_g, float q_scale, f16* __restrict__ q_ws, f16* __restrict__ k_ws,
+    const bf16* __restrict__ beta, float eps, const f16* __restrict__ wimg, const float* __restrict__ cst,
+    const bf16* __restrict__ wb, float q_scale, f16* __restrict__ q_ws, f16* __restrict__ k_ws,
     f16* __restrict__ v_ws, f16* __restrict__ g_ws, float* __restrict__ bias, int bias_swizzled, float bias_scale,
     int nrows, int P, int Pp, int H) {
   using SH = ProjShape<C_IN, HD, NCOL, MODE>;
@@ -117,24 +145,14 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
   // LayerNorm's affine map is folded into the projection:
   //   ((x-mu)*rstd*gamma + beta) . W = ((x-mu)*rstd) . (gamma o W) + beta . W
   // so the operands hold gamma o W and the per-column constants beta . W
-  // (plus the gate bias for g columns) are added to the accumulators.
-  for (int i = tid; i < SH::NBLK * KS * 64; i += kProjThreads) {
-    const int l = i & 63, t = (i >> 6) % KS, b = (i >> 6) / KS;
-    const int k0 = t * 16 + (l >> 5) * 8;
-    const f16x8 w = ld16(wT + (int64_t)(col0 + b * 32 + (l & 31)) * C_IN + k0);
-    f16x8 o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = f2h_sat((float)w[e] * bf2f(gamma[k0 + e]));
-    *reinterpret_cast<f16x8*>(w_lds + i * 8) = o;
+  // (plus the gate bias for g columns) are added to the accumulators.  Both
+  // come packed: a linear copy of this group's slice.
+  {
+    const f16x8* src = reinterpret_cast<const f16x8*>(wimg) + (int64_t)(col0 / 32) * KS * 64;
+    f16x8* dst = reinterpret_cast<f16x8*>(w_lds);
+    for (int i = tid; i < SH::NBLK * KS * 64; i += kProjThreads) dst[i] = src[i];
   }
-  for (int n = tid; n < NCOL; n += kProjThreads) {
-    const f16* wr = wT + (int64_t)(col0 + n) * C_IN;
-    float acc = 0.0f;
-    for (int k = 0; k < C_IN; ++k) acc += bf2f(beta[k]) * (float)wr[k];
-    const int col = col0 + n;
-    if (col >= 3 * HD && b_g != nullptr) acc += bf2f(b_g[col - 3 * HD]);
-    cb[n] = acc;
-  }
+  for (int n = tid; n < NCOL; n += kProjThreads) cb[n] = cst[col0 + n];
   if (SH::HAS_BIAS) {
     for (int i = tid; i < KS * 64; i += kProjThreads) {
       const int l = i & 63, t = i >> 6, hh = l & 31;
@@ -356,12 +374,19 @@ hipError_t launch_bias_to_attn_layout(const float* src, void* dst, int H, int Pq
 }
 
 hipError_t launch_pack_bf16(const PackArgs& a, hipStream_t s) {
-  const int64_t total = (int64_t)4 * a.hd * a.c_in + (int64_t)a.c_out * a.hd;
+  if (a.c_in % 16 != 0 || a.hd % 32 != 0) return hipErrorInvalidValue;
+  const int64_t total = (int64_t)4 * a.hd * a.c_in / 8 + (int64_t)a.c_out * a.hd;
   const int threads = 256;
   const int blocks = (int)std::min<int64_t>((total + threads - 1) / threads, 4096);
   hipLaunchKernelGGL(pack_weights_kernel, dim3(blocks), dim3(threads), 0, s, (const bf16*)a.wq, (const bf16*)a.wk,
-                     (const bf16*)a.wv, (const bf16*)a.wg, (const bf16*)a.wo, (f16*)a.wT, (f16*)a.woT, a.c_in,
-                     a.hd, a.c_out);
+                     (const bf16*)a.wv, (const bf16*)a.wg, (const bf16*)a.wo, (const bf16*)a.gamma, (f16*)a.wT,
+                     (f16*)a.woT, a.c_in, a.hd, a.c_out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int cols = 4 * a.hd, per_block = threads / kWave;
+  hipLaunchKernelGGL(pack_consts_kernel, dim3((cols + per_block - 1) / per_block), dim3(threads), 0, s,
+                     (const bf16*)a.wq, (const bf16*)a.wk, (const bf16*)a.wv, (const bf16*)a.wg, (const bf16*)a.beta,
+                     (const bf16*)a.b_g, a.cst, a.c_in, a.hd);
   return hipGetLastError();
 }
 
@@ -381,11 +406,14 @@ static hipError_t proj_dispatch(const ProjArgs& a, int num_cu, hipStream_t s) {
     wg_per_cu = n;
   }
   const int64_t want = (ntiles + kProjThreads / kWave - 1) / (kProjThreads / kWave);
-  const int grid_x = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)num_cu * wg_per_cu));
+  // one resident wave of workgroups: the column groups of a position range
+  // run at the same time (their reads of x meet in the caches) and each CU
+  // fills its LDS operands once
+  const int grid_x = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)num_cu * wg_per_cu / groups));
   const int rmajor = a.xs_p <= a.xs_r ? 1 : 0;
   hipLaunchKernelGGL((proj_kernel<C_IN, HD, NCOL, MODE>), dim3(grid_x, groups), dim3(kProjThreads), 0, s,
                      (const bf16*)a.x, a.xs_r, a.xs_p, rmajor, (const bf16*)a.gamma, (const bf16*)a.beta, a.eps,
-                     (const f16*)a.wT, (const bf16*)a.wb, (const bf16*)a.b_g, a.q_scale, (f16*)a.q_ws,
+                     (const f16*)a.wT, a.cst, (const bf16*)a.wb, a.q_scale, (f16*)a.q_ws,
                      (f16*)a.k_ws, (f16*)a.v_ws, (f16*)a.g_ws, a.bias, a.bias_swizzled, a.bias_scale, a.nrows, a.P,
                      a.Pp, a.H);
   return hipGetLastError();

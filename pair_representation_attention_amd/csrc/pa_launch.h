@@ -8,7 +8,9 @@ namespace pa {
 
 struct PackArgs {
   const void *wq, *wk, *wv, *wg, *wo;  // natural layouts
-  void *wT, *woT;                      // packed copies in the workspace
+  const void *gamma, *beta, *b_g;      // LayerNorm of the projected tensor, gate bias (may be NULL)
+  void *wT, *woT;                      // packed images in the workspace: gamma o W (operand order), W_o^T
+  float* cst;                          // [4*hd] column constants beta . W (+ b_g)
   int c_in, hd, c_out;
 };
 
@@ -19,8 +21,9 @@ struct ProjArgs {
   int64_t xs_r, xs_p;
   const void *gamma, *beta;
   float eps;
-  const void* wT;                // packed q|k|v|g weights
-  const void *wb, *b_g;          // w_b [c_in][H], gate bias [H*32]
+  const void* wT;                // packed q|k|v|g operand image (launch_pack_bf16)
+  const float* cst;              // its column constants
+  const void* wb;                // w_b [c_in][H]
   float q_scale;
   void *q_ws, *k_ws, *v_ws, *g_ws;
   float* bias;                   // pair bias output (rows = the projected rows r); fp16 when swizzled

@@ -62,6 +62,7 @@ Layout make_layout(int64_t nrows, int64_t P, int64_t c_in, int64_t c_out, int64_
   const size_t plane = (size_t)nrows * H * Pp * 32 * 2;   // one fp16 q/k/v plane
   if (dtype == PAIRATTN_BF16) {
     L.wT = take((size_t)4 * hd * c_in * 2);
+    L.cst = take((size_t)4 * hd * 4);
     L.woT = take((size_t)c_out * hd * 2);
     L.q = take(plane);
     L.k = take(plane);
@@ -110,6 +111,7 @@ PartialLayout make_partial_layout(int64_t R, int64_t Jq, int64_t Kn, int64_t c, 
       return at;
     };
     L.wT = take((size_t)4 * hd * c * 2);
+    L.cst = take((size_t)4 * hd * 4);
     L.woT = take((size_t)c * hd * 2);
     const size_t qplane = (size_t)R * H * Ppq * 32 * 2, kplane = (size_t)R * H * Ppk * 32 * 2;
     L.q = take(qplane);
@@ -529,7 +531,6 @@ static int run_row_attention_bf16(const pairattn_params* p, const Layout& L, hip
   pj.beta = p->ln_beta;
   pj.eps = p->ln_eps;
   pj.wb = p->w_b;
-  pj.b_g = p->b_g;
   pj.q_ws = ws_at(p, L.q);
   pj.k_ws = ws_at(p, L.k);
   pj.v_ws = ws_at(p, L.v);
@@ -548,11 +549,25 @@ static int run_row_attention_bf16(const pairattn_params* p, const Layout& L, hip
     if (!ra.nested) tm_mark(s, stage);
   };
   if (!ra.nested) tm_begin(s);
-  pa::PackArgs pk{p->w_q, p->w_k, p->w_v, p->w_g, p->w_o, ws_at(p, L.wT), ws_at(p, L.woT), (int)ra.c, (int)hd,
-                  (int)ra.c};
+  pa::PackArgs pk{};
+  pk.wq = p->w_q;
+  pk.wk = p->w_k;
+  pk.wv = p->w_v;
+  pk.wg = p->w_g;
+  pk.wo = p->w_o;
+  pk.gamma = p->ln_gamma;
+  pk.beta = p->ln_beta;
+  pk.b_g = p->b_g;
+  pk.wT = ws_at(p, L.wT);
+  pk.woT = ws_at(p, L.woT);
+  pk.cst = reinterpret_cast<float*>(ws_at(p, L.cst));
+  pk.c_in = (int)ra.c;
+  pk.hd = (int)hd;
+  pk.c_out = (int)ra.c;
   PA_TRY(hip_status(pa::launch_pack_bf16(pk, s), "weight packing launch"));
   mark("pack");
   pj.wT = ws_at(p, L.wT);
+  pj.cst = reinterpret_cast<const float*>(ws_at(p, L.cst));
   pj.q_scale = 1.4426950408889634f / std::sqrt(32.0f);
   PA_TRY(hip_status(pa::launch_proj_bf16(pj, ra.bias_in_proj ? 1 : 0, num_cu, s), "projection launch"));
   mark("projection");
@@ -938,8 +953,21 @@ int pairattn_tri_partial_fwd(const void* q_pairs, const void* kv_pairs, const fl
   hipStream_t s = static_cast<hipStream_t>(stream);
   tm_begin(s);
   if (p->dtype == PAIRATTN_BF16) {
-    pa::PackArgs pk{p->w_q, p->w_k, p->w_v, p->w_g, p->w_o, ws_at(p, L.wT), ws_at(p, L.woT), (int)c_z, (int)hd,
-                    (int)c_z};
+    pa::PackArgs pk{};
+    pk.wq = p->w_q;
+    pk.wk = p->w_k;
+    pk.wv = p->w_v;
+    pk.wg = p->w_g;
+    pk.wo = p->w_o;
+    pk.gamma = p->ln_gamma;
+    pk.beta = p->ln_beta;
+    pk.b_g = p->b_g;
+    pk.wT = ws_at(p, L.wT);
+    pk.woT = ws_at(p, L.woT);
+    pk.cst = reinterpret_cast<float*>(ws_at(p, L.cst));
+    pk.c_in = (int)c_z;
+    pk.hd = (int)hd;
+    pk.c_out = (int)c_z;
     PA_TRY(hip_status(pa::launch_pack_bf16(pk, s), "weight packing launch"));
     tm_mark(s, "pack");
     // q of the query pairs, k and v of the key pairs (the other planes NULL)
@@ -951,7 +979,7 @@ int pairattn_tri_partial_fwd(const void* q_pairs, const void* kv_pairs, const fl
     pj.beta = p->ln_beta;
     pj.eps = p->ln_eps;
     pj.wT = ws_at(p, L.wT);
-    pj.b_g = p->b_g;
+    pj.cst = reinterpret_cast<const float*>(ws_at(p, L.cst));
     pj.q_scale = 1.4426950408889634f / std::sqrt(32.0f);
     pj.q_ws = ws_at(p, L.q);
     pj.c_in = (int)c_z;
@@ -1119,8 +1147,21 @@ int pairattn_tri_partial_finish(const void* q_pairs, const float* o, const paira
   hipStream_t s = static_cast<hipStream_t>(stream);
   tm_begin(s);
   if (p->dtype == PAIRATTN_BF16) {
-    pa::PackArgs pk{p->w_q, p->w_k, p->w_v, p->w_g, p->w_o, ws_at(p, L.wT), ws_at(p, L.woT), (int)c_z, (int)hd,
-                    (int)c_z};
+    pa::PackArgs pk{};
+    pk.wq = p->w_q;
+    pk.wk = p->w_k;
+    pk.wv = p->w_v;
+    pk.wg = p->w_g;
+    pk.wo = p->w_o;
+    pk.gamma = p->ln_gamma;
+    pk.beta = p->ln_beta;
+    pk.b_g = p->b_g;
+    pk.wT = ws_at(p, L.wT);
+    pk.woT = ws_at(p, L.woT);
+    pk.cst = reinterpret_cast<float*>(ws_at(p, L.cst));
+    pk.c_in = (int)c_z;
+    pk.hd = (int)hd;
+    pk.c_out = (int)c_z;
     PA_TRY(hip_status(pa::launch_pack_bf16(pk, s), "weight packing launch"));
     tm_mark(s, "pack");
     pa::ProjArgs pj{};   // the gate of the query pairs only
@@ -1131,7 +1172,7 @@ int pairattn_tri_partial_finish(const void* q_pairs, const float* o, const paira
     pj.beta = p->ln_beta;
     pj.eps = p->ln_eps;
     pj.wT = ws_at(p, L.wT);
-    pj.b_g = p->b_g;
+    pj.cst = reinterpret_cast<const float*>(ws_at(p, L.cst));
     pj.q_scale = 1.4426950408889634f / std::sqrt(32.0f);
     pj.g_ws = ws_at(p, L.g);
     pj.c_in = (int)c_z;
