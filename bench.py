@@ -204,6 +204,9 @@ def main() -> int:
                          "(one JSON line)")
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="MIB",
                     help="after timing, run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="only time the ROCm library's dense bf16/fp16 GEMM (torch.mm, n = 4096 and 8192): "
+                         "the matrix-core rate a tuned dense kernel reaches on this device (one JSON line)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 --pmc counter CSVs and exit")
     ap.add_argument("--copy-mib", type=float, default=1024.0, help="copy size used in the --pmc runs")
@@ -232,8 +235,11 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    lib.load()
     torch.cuda.set_device(0)
+    if args.gemm_probe:
+        print(json.dumps({"gemm_probe": gemm_probe(torch)}), flush=True)
+        return 0
+    lib.load()
     if args.workload != "tri_bf16_i1536":
         fn = {"msa_fp32_s5120_i384": msa_fp32_workload, "tri_bf16_i16384_chunked": chunked_workload,
               "ring_fp32_i1536_grid2x2": ring_workload, "ring_bf16_i1536_grid2x2": ring_workload}[args.workload]
@@ -359,6 +365,21 @@ def main() -> int:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
     return 0
+
+
+def gemm_probe(torch) -> dict:
+    """Calibration, not part of the path: the dense GEMM of the ROCm library
+    (torch.mm on contiguous operands) at n = 4096 and 8192, in TFLOP/s."""
+    out = {}
+    for name, dt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
+        for n in (4096, 8192):
+            a = torch.randn(n, n, device="cuda", dtype=dt)
+            b = torch.randn(n, n, device="cuda", dtype=dt)
+            ms = _time(lambda: torch.mm(a, b), 20, 3, torch)
+            out[f"{name}_n{n}"] = {"ms": ms, "tflops": 2.0 * n ** 3 / (ms * 1e-3) / 1e12,
+                                   "frac_of_peak": 2.0 * n ** 3 / (ms * 1e-3) / 1e12 / PEAK_MFMA_16BIT_TFLOPS}
+            del a, b
+    return out
 
 
 def _time(fn, steps, warmup, torch):

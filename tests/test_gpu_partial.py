@@ -285,3 +285,45 @@ def test_ring_bf16_over_a_2x2_grid_i512():
     check(got, full, "bf16", "bf16 2x2 ring = one pass")
     sample = np.random.default_rng(1).choice(I, 5, replace=False)
     check(got[sample], oracle.tri_start(z, None, p.as_dict(), H, rows=sample), "bf16", "bf16 2x2 ring, sampled rows")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_cfg_ring_i1536_grid2x2(dtype):
+    """The ring step at the size and in the launch sequence the benchmark
+    times: Z[1536, 1536, 128] drawn on the device, the tile of rows 0..767
+    and columns 0..767 on a 2 x 2 grid, its own key shard, then the other
+    (merged), then the finish.  Sampled (row, query) outputs against the
+    oracle, which reads only the rows of Z it needs."""
+    lib, dev = _lib(), _dev()
+    I, c, H, d, half, seed = 1536, 128, 4, 32, 768, 11
+    print(f"[cfg ring] {dtype}: generating Z[{I},{I},{c}] on the device", flush=True)
+    z = inputs.make_z_device(I, c, seed, dtype=dtype)
+    p = inputs.make_chunked_params(c, H, d, seed, dtype=dtype)
+    bias = torch.empty((H, I, I), dtype=torch.float32, device="cuda")
+    lib.pairattn_tri_bias(z, dev.make_params(p, dtype), bias, I, c, H, lib.PAIRATTN_START)
+    zq = z[:half, :half].contiguous()
+    shards = [z[:half, :half].contiguous(), z[:half, half:].contiguous()]
+    btiles = [bias[:, :half, :half].contiguous(), bias[:, :half, half:].contiguous()]
+    code = dev.dtype_code(dtype)
+    n = max(lib.pairattn_tri_partial_workspace_bytes(half, half, half, c, H, d, code),
+            lib.pairattn_tri_partial_finish_workspace_bytes(half, half, c, H, d, code))
+    prm = dev.make_params(p, dtype, n)
+    o = torch.empty((half, half, H * d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((half, H, half), dtype=torch.float32, device="cuda")
+    out = torch.empty((half, half, c), dtype=dev.torch_dtype(dtype), device="cuda")
+    for sidx in range(2):
+        lib.pairattn_tri_partial_fwd(zq, shards[sidx], btiles[sidx], None, prm, o, lse, sidx > 0, half, half, half,
+                                     c, H, d)
+    lib.pairattn_tri_partial_finish(zq, o, prm, out, half, half, c, H, d)
+    torch.cuda.synchronize()
+    rows = np.array([0, 401, half - 1])
+    queries = np.array([0, 5, 700, half - 1])
+    g = out[torch.as_tensor(rows, device="cuda")][:, torch.as_tensor(queries, device="cuda")]
+    pd = p.as_dict()
+    zr = z[torch.as_tensor(rows, device="cuda")].float().cpu().numpy().astype(np.float64)
+    zqr = z[torch.as_tensor(queries, device="cuda")].float().cpu().numpy().astype(np.float64)
+    bias_q = oracle.attention_bias(zqr, pd, H, oracle.START)         # [H, Q, I] for these queries
+    ref = oracle.tri_rows(zr, bias_q, None, pd, H, queries=queries, bias_restricted=True)
+    check(gpu_to_f64(g), ref, dtype, f"cfg ring_{dtype}_i1536_grid2x2 rows={rows.tolist()}")
+    del z, bias, zq, shards, btiles, o, lse, out, prm
+    torch.cuda.empty_cache()
