@@ -9,12 +9,12 @@
 //
 // Work decomposition
 //   unit = 32 queries x 32 keys of one (row, head)
-//   workgroup = 8 waves covering RWG = 2 rows x QWG query blocks x H heads
-//     H = 4: QWG = 4, wave = (head, query-block pair), 2 x 2 units per key block
-//     H = 8: QWG = 1, wave = head,                     2 x 1 units per key block
+//   workgroup = 8 waves covering RWG rows x QWG query blocks x H heads
+//     H = 4: RWG = 2, QWG = 4, wave = (head, query-block pair), 2 x 2 units per key block
+//     H = 8: RWG = 1, QWG = 2, wave = head (both query blocks),  1 x 2 units per key block
 //   per key block and unit (S^T is keys x queries, log2 units):
 //     S^T = K Q^T + C      two MFMAs; C = the fp16 bias tile widened to fp32
-//                          by VALU converts (shared by both rows)
+//                          by VALU converts (shared by the workgroup's rows)
 //     p = exp2(S - m)      rounded to fp16 (the P operand); l += sum of p
 //     O^T += V^T P^T       two MFMAs
 //   Softmax shift m per (row, query): a first sweep uses m = 0 with no
@@ -31,7 +31,8 @@
 // every copy is a contiguous 1 KB read, every LDS read a conflict-free
 // ds_read_b128, and the S^T accumulator (rows = keys in natural order) is
 // already the K-slot order of the P operand.
-// Bytes moved per unit: 4 KB K/V / 4 query blocks + 2 KB bias / 2 rows.
+// Bytes moved per unit: 4 KB K/V / 4 query blocks + 2 KB bias / 2 rows (H = 4),
+// 4 KB K/V / 2 query blocks + 2 KB bias (H = 8).
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -107,16 +108,18 @@ __device__ __forceinline__ float sum16_f16(const f16x8& a, const f16x8& b) {
 
 template <int H>
 struct AttnShape {
-  static constexpr int QW = H == 4 ? 2 : 1;        // query blocks per wave
+  static constexpr int QW = 2;                     // query blocks per wave
   static constexpr int QG = 8 / H;                 // query-block groups per workgroup
   static constexpr int QWG = QW * QG;              // query blocks per workgroup
-  static constexpr int RWG = 2;                    // rows per workgroup (every wave does both)
+  // rows per workgroup (every wave does all): 2 at H = 4; 1 at H = 8, so
+  // that a K/V stage is 32 KB and the ring three stages deep
+  static constexpr int RWG = H == 4 ? 2 : 1;
   static constexpr int KV_TILE = 4096;             // K (2 chunks) + V (2 chunks) of one (row, head)
   static constexpr int B_TILE = 2048;              // fp16 bias tile (2 chunks) of one (query block, head)
-  static constexpr int KV_STAGE = RWG * H * KV_TILE;   // 32 KB (H=4) or 64 KB (H=8)
-  static constexpr int B_STAGE = QWG * H * B_TILE;     // 32 KB (H=4) or 16 KB (H=8)
+  static constexpr int KV_STAGE = RWG * H * KV_TILE;   // 32 KB
+  static constexpr int B_STAGE = QWG * H * B_TILE;     // 32 KB
   // K/V ring of NKV stages (NKV-1 key blocks ahead), bias ring of 2 (one
-  // block ahead): 3 x 32 + 2 x 32 KB (H=4) or 2 x 64 + 2 x 16 KB (H=8)
+  // block ahead): 3 x 32 + 2 x 32 KB
   static constexpr int NKV = 3 * KV_STAGE + 2 * B_STAGE <= 160 * 1024 ? 3 : 2;
   static constexpr int LDS_KV = NKV * KV_STAGE;
   static constexpr int LDS_B = 2 * B_STAGE;
