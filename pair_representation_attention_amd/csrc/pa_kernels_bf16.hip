@@ -336,22 +336,29 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
 
 // Copy of a caller-provided bias [H][Pq][Pk] (float, natural-log units) into
 // the attention layout (fp16 operand order, log2 units, Ppq x Ppk with zero
-// padding).  Each thread converts 8 consecutive keys of one query, whose
-// source is 32 contiguous bytes.
+// padding).  Each thread writes one lane's 16-byte slot of a chunk, so the
+// stores of a wave are one contiguous 1 KB; its 8 keys are two runs of 4 in
+// the source row.
 __global__ void bias_to_attn_layout_kernel(const float* __restrict__ src, f16* __restrict__ dst, int H, int Pq,
                                            int Pk, int Ppq, int Ppk) {
   const int nbq = Ppq / 32, nbk = Ppk / 32;
-  const int64_t groups = (int64_t)H * Ppq * (Ppk / 8);
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < groups; i += (int64_t)gridDim.x * blockDim.x) {
-    const int k0 = (int)(i % (Ppk / 8)) * 8;
-    const int64_t hq = i / (Ppk / 8);
-    const int h = (int)(hq / Ppq), q = (int)(hq % Ppq);
+  const int64_t slots = (int64_t)H * nbq * nbk * 2 * 64;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < slots; i += (int64_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(i & 63);
+    const int64_t c = i >> 6;                         // chunk (h, qb, kb, t)
+    const int t = (int)(c & 1);
+    const int kb = (int)((c >> 1) % nbk);
+    const int64_t hq = (c >> 1) / nbk;
+    const int qb = (int)(hq % nbq), h = (int)(hq / nbq);
+    const int q = qb * 32 + (lane & 31), hg = lane >> 5;
     const float* row = src + ((int64_t)h * Pq + q) * Pk;
+    f16x8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int k = k0 + e;
-      dst[b16_off(h, nbq, nbk, q, k)] = (q < Pq && k < Pk) ? f2h_sat(row[k] * kLog2e) : f2h(0.0f);
+      const int k = kb * 32 + slot_x(t, hg, e);
+      o[e] = (q < Pq && k < Pk) ? f2h_sat(row[k] * kLog2e) : f2h(0.0f);
     }
+    *reinterpret_cast<f16x8*>(dst + i * 8) = o;
   }
 }
 
@@ -366,8 +373,8 @@ namespace pa {
 
 hipError_t launch_bias_to_attn_layout(const float* src, void* dst, int H, int Pq, int Pk, int Ppq, int Ppk,
                                       hipStream_t s) {
-  const int64_t groups = (int64_t)H * Ppq * (Ppk / 8);
-  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((groups + 255) / 256, 8192));
+  const int64_t slots = (int64_t)H * Ppq * Ppk / 8;
+  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((slots + 255) / 256, 16384));
   hipLaunchKernelGGL(bias_to_attn_layout_kernel, dim3(blocks), dim3(256), 0, s, src, (f16*)dst, H, Pq, Pk, Ppq,
                      Ppk);
   return hipGetLastError();
