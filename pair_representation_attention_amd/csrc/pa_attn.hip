@@ -1042,6 +1042,7 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
   const int n_qg = (nbq + SH::QWG - 1) / SH::QWG;
   const int n_rg = (a.nrows + SH::RWG - 1) / SH::RWG;
   const int64_t n = (int64_t)n_qg * n_rg;
+  if (n > 0x7fffffffLL) return hipErrorInvalidValue;   // one-dimensional grid
   hipLaunchKernelGGL((attn_kernel<H, C_OUT, HAS_MASK, MODE>), dim3((unsigned)n), dim3(512), 0, s,
                      (const f16*)a.q_ws, (const f16*)a.k_ws, (const f16*)a.v_ws, (const f16*)a.g_ws,
                      (const f16*)a.bias, a.mask_bits, (const f16*)a.woT, (const bf16*)a.b_o, (bf16*)a.out, a.os_r,

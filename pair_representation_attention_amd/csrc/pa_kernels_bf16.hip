@@ -367,6 +367,8 @@ __global__ void bias_to_attn_layout_kernel(const float* __restrict__ src, f16* _
 // ----------------------------------------------------------------------------
 // launchers (called from the host API in pairattn_api.hip)
 // ----------------------------------------------------------------------------
+#include <atomic>
+
 #include "pa_launch.h"
 
 namespace pa {
@@ -403,7 +405,10 @@ static hipError_t proj_dispatch(const ProjArgs& a, int num_cu, hipStream_t s) {
   constexpr int NCOL = MODE == 2 ? 0 : std::min(4 * HD, 65536 / C_IN);
   constexpr int groups = MODE == 2 ? 1 : 4 * HD / NCOL;
   const int64_t ntiles = (int64_t)(a.Pp / 32) * a.nrows;
-  static int wg_per_cu = 0;   // resident workgroups per CU (registers and LDS), asked once per instance
+  // resident workgroups per CU (registers and LDS), asked once per instance;
+  // concurrent first calls ask the same question and store the same answer
+  static std::atomic<int> wg_cache{0};
+  int wg_per_cu = wg_cache.load(std::memory_order_relaxed);
   if (wg_per_cu == 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, proj_kernel<C_IN, HD, NCOL, MODE>, kProjThreads, 0) !=
@@ -411,6 +416,7 @@ static hipError_t proj_dispatch(const ProjArgs& a, int num_cu, hipStream_t s) {
         n < 1)
       n = 1;
     wg_per_cu = n;
+    wg_cache.store(n, std::memory_order_relaxed);
   }
   const int64_t want = (ntiles + kProjThreads / kWave - 1) / (kProjThreads / kWave);
   // one resident wave of workgroups: the column groups of a position range
