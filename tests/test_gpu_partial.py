@@ -187,7 +187,8 @@ def test_ring_over_a_2x2_grid_i512():
 # bf16 path (the same kernels as the one-pass bf16 attention, with a partial
 # epilogue)
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("c,H,mask", [(128, 4, "random"), (128, 4, "none"), (64, 8, "random"), (256, 4, "none")])
+@pytest.mark.parametrize("c,H,mask", [(128, 4, "random"), (128, 4, "none"), (64, 8, "random"), (256, 4, "none"),
+                                        (256, 8, "random")])
 def test_partial_bf16_single_shard_and_finish(c, H, mask):
     """One shard holding every key (H = 4 without a mask runs the pipelined
     sweep, with one the generic sweep; H = 8 the generic sweep)."""
