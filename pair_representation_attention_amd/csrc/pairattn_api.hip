@@ -303,7 +303,7 @@ void tm_mark(hipStream_t s, const char* stage) {
 // ============================================================================
 extern "C" {
 
-int pairattn_version(void) { return 10000; }
+int pairattn_version(void) { return 10100; }
 
 int pairattn_timing_enable(int enable) {
   const int prev = g_tm.enabled ? 1 : 0;
