@@ -516,7 +516,7 @@ def ring_workload(args, device, inputs, lib, torch) -> dict:
     z = inputs.make_z_device(I, c, 11, dtype=dt)
     p = inputs.make_chunked_params(c, H, d, 11, dtype=dt)
     zq = z[:half, :half].contiguous()                   # this device's pairs: rows A, columns B
-    shards = [z[:half, :half].contiguous(), z[:half, half:].contiguous()]
+    shards = [zq, z[:half, half:].contiguous()]         # its own shard is its query pairs
     bias = torch.empty((H, I, I), dtype=torch.float32, device="cuda")
     pr = device.make_params(p, dt)
     lib.pairattn_tri_bias(z, pr, bias, I, c, H, lib.PAIRATTN_START)

@@ -192,8 +192,9 @@ int pairattn_tri_chunked_fwd(const void *z, const uint8_t *mask, const pairattn_
  *                          (-inf with none)
  * accumulate = 0 writes o and lse; accumulate != 0 merges this shard into
  * the o and lse already there: lse' = ln(e^lse + e^lse_s),
- * o' = e^(lse - lse') o + e^(lse_s - lse') o_s.  Workspace:
- * pairattn_tri_partial_workspace_bytes. */
+ * o' = e^(lse - lse') o + e^(lse_s - lse') o_s.  kv_pairs may be q_pairs
+ * itself (Kn = Jq: the device's own shard); q, k and v then come from one
+ * pass over it.  Workspace: pairattn_tri_partial_workspace_bytes. */
 size_t pairattn_tri_partial_workspace_bytes(int64_t R, int64_t Jq, int64_t Kn, int64_t c_z,
                                             int64_t H, int64_t d, int32_t dtype);
 int pairattn_tri_partial_fwd(const void *q_pairs, const void *kv_pairs, const float *bias,

@@ -988,15 +988,23 @@ int pairattn_tri_partial_fwd(const void* q_pairs, const void* kv_pairs, const fl
     pj.nrows = (int)R;
     pj.P = (int)Jq;
     pj.Pp = Ppq;
+    // the device's own shard (the query pairs' buffer): q, k and v in one pass
+    const bool own = kv_pairs == q_pairs && Kn == Jq;
+    if (own) {
+      pj.k_ws = ws_at(p, L.k);
+      pj.v_ws = ws_at(p, L.v);
+    }
     PA_TRY(hip_status(pa::launch_proj_bf16(pj, 0, num_cu, s), "query projection launch"));
-    pj.x = kv_pairs;
-    pj.xs_r = Kn * c_z;
-    pj.q_ws = nullptr;
-    pj.k_ws = ws_at(p, L.k);
-    pj.v_ws = ws_at(p, L.v);
-    pj.P = (int)Kn;
-    pj.Pp = Ppk;
-    PA_TRY(hip_status(pa::launch_proj_bf16(pj, 0, num_cu, s), "key projection launch"));
+    if (!own) {
+      pj.x = kv_pairs;
+      pj.xs_r = Kn * c_z;
+      pj.q_ws = nullptr;
+      pj.k_ws = ws_at(p, L.k);
+      pj.v_ws = ws_at(p, L.v);
+      pj.P = (int)Kn;
+      pj.Pp = Ppk;
+      PA_TRY(hip_status(pa::launch_proj_bf16(pj, 0, num_cu, s), "key projection launch"));
+    }
     tm_mark(s, "projection");
     void* bias_ws = ws_at(p, L.bias);
     PA_TRY(hip_status(pa::launch_bias_to_attn_layout(bias, bias_ws, (int)H, (int)Jq, (int)Kn, Ppq, Ppk, s),
@@ -1067,17 +1075,21 @@ int pairattn_tri_partial_fwd(const void* q_pairs, const void* kv_pairs, const fl
   pj.xs_r = Jq * c_z;
   pj.xs_p = c_z;
   pj.b_first = 0;
-  pj.nqkvg = (int)(hd / 32);
+  // the device's own shard (the query pairs' buffer): q, k and v in one pass
+  const bool own = kv_pairs == q_pairs && Kn == Jq;
+  pj.nqkvg = (int)((own ? 3 : 1) * hd / 32);
   pj.P = (int)Jq;
   pj.Pp = Ppq;
   PA_TRY(hip_status(pa::launch_proj_f32(pj, num_cu, s), "query projection launch"));
-  pj.x = kv_pairs;
-  pj.xs_r = Kn * c_z;
-  pj.b_first = (int)(hd / 32);
-  pj.nqkvg = (int)(2 * hd / 32);
-  pj.P = (int)Kn;
-  pj.Pp = Ppk;
-  PA_TRY(hip_status(pa::launch_proj_f32(pj, num_cu, s), "key projection launch"));
+  if (!own) {
+    pj.x = kv_pairs;
+    pj.xs_r = Kn * c_z;
+    pj.b_first = (int)(hd / 32);
+    pj.nqkvg = (int)(2 * hd / 32);
+    pj.P = (int)Kn;
+    pj.Pp = Ppk;
+    PA_TRY(hip_status(pa::launch_proj_f32(pj, num_cu, s), "key projection launch"));
+  }
   tm_mark(s, "projection");
   float* bias_ws = reinterpret_cast<float*>(ws_at(p, L.bias));
   PA_TRY(hip_status(pa::launch_bias_to_f32_layout(bias, bias_ws, (int)H, (int)Jq, (int)Kn, Ppq, Ppk, s),

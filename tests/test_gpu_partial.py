@@ -78,6 +78,15 @@ class _Partial:
                                      kv_pairs.shape[1], self.c, self.H, 32)
         torch.cuda.synchronize()
 
+    def own_shard(self, bias, mask, accumulate):
+        """The device's own shard: kv_pairs is the query pairs' buffer itself."""
+        lib = _lib()
+        b = _t(bias)
+        m = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask, np.uint8)).to("cuda")
+        lib.pairattn_tri_partial_fwd(self.q, self.q, b, m, self.params, self.o, self.lse, accumulate, self.R,
+                                     self.Jq, self.Jq, self.c, self.H, 32)
+        torch.cuda.synchronize()
+
     def finish(self):
         _lib().pairattn_tri_partial_finish(self.q, self.o, self.params, self.out, self.R, self.Jq, self.c, self.H, 32)
         torch.cuda.synchronize()
@@ -303,7 +312,7 @@ def test_cfg_ring_i1536_grid2x2(dtype):
     bias = torch.empty((H, I, I), dtype=torch.float32, device="cuda")
     lib.pairattn_tri_bias(z, dev.make_params(p, dtype), bias, I, c, H, lib.PAIRATTN_START)
     zq = z[:half, :half].contiguous()
-    shards = [z[:half, :half].contiguous(), z[:half, half:].contiguous()]
+    shards = [zq, z[:half, half:].contiguous()]            # the own shard is the query pairs' buffer
     btiles = [bias[:, :half, :half].contiguous(), bias[:, :half, half:].contiguous()]
     code = dev.dtype_code(dtype)
     n = max(lib.pairattn_tri_partial_workspace_bytes(half, half, half, c, H, d, code),
@@ -328,3 +337,19 @@ def test_cfg_ring_i1536_grid2x2(dtype):
     check(gpu_to_f64(g), ref, dtype, f"cfg ring_{dtype}_i1536_grid2x2 rows={rows.tolist()}")
     del z, bias, zq, shards, btiles, o, lse, out, prm
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("masked", [False, True])
+def test_own_shard_from_the_query_buffer_bitwise(dtype, masked):
+    """kv_pairs given as the query pairs' own buffer (one projection pass for
+    q, k and v) gives the same o and lse, bit for bit, as a copy of it."""
+    case, p, bias, _ = _case(70, 128, 4, seed=199, mask="random" if masked else "none", dtype=dtype)
+    z = case.z
+    rows = np.arange(3, 9)
+    m = None if not masked else case.mask[rows]
+    a = _Partial(z[rows], p, 4, 70, dtype)
+    a.own_shard(bias, m, 0)
+    b = _Partial(z[rows], p, 4, 70, dtype)
+    b.shard(z[rows], bias, m, 0)
+    assert torch.equal(a.o, b.o) and torch.equal(a.lse, b.lse)
