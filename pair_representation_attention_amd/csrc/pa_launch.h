@@ -63,6 +63,25 @@ hipError_t launch_finish_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_mask_bits(const uint8_t* mask, int64_t ms_r, int64_t ms_k, uint32_t* bits, int nrows, int P,
                             int nkb, hipStream_t s);
 
+// The fused end of the bf16 ring: out = (sigmoid(LN(x) W_g + b_g) * o) W_o + b_o
+// for query pairs x (element (r, p, ch) at x[r*xs_r + p*xs_p + ch]) and the
+// assembled per-head outputs o_part [nrows][P][H*32]; wimg / cst / woT come
+// from launch_pack_bf16.  Supported where its LDS operands fit.
+struct FinishFusedArgs {
+  const void* x;
+  int64_t xs_r, xs_p;
+  float eps;
+  const void* wimg;
+  const float* cst;
+  const float* o_part;
+  const void *woT, *b_o;
+  void* out;
+  int64_t os_r, os_p;
+  int c, H, nrows, P, Pp;
+};
+bool finish_fused_bf16_supported(int c, int H);
+hipError_t launch_finish_fused_bf16(const FinishFusedArgs& a, int num_cu, hipStream_t s);
+
 // ---- fp32 path (fp16-pair operands on the matrix cores) ----
 // Packs the gamma-folded q|k|v|g projection operands (nqkvg blocks of 32
 // columns) and, when wo != NULL, the W_o operand.

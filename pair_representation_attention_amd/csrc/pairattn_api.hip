@@ -1176,6 +1176,29 @@ int pairattn_tri_partial_finish(const void* q_pairs, const float* o, const paira
     pk.c_out = (int)c_z;
     PA_TRY(hip_status(pa::launch_pack_bf16(pk, s), "weight packing launch"));
     tm_mark(s, "pack");
+    if (pa::finish_fused_bf16_supported((int)c_z, (int)H)) {   // the gate computed where it is used
+      pa::FinishFusedArgs fa{};
+      fa.x = q_pairs;
+      fa.xs_r = Jq * c_z;
+      fa.xs_p = c_z;
+      fa.eps = p->ln_eps;
+      fa.wimg = ws_at(p, L.wT);
+      fa.cst = reinterpret_cast<const float*>(ws_at(p, L.cst));
+      fa.o_part = o;
+      fa.woT = ws_at(p, L.woT);
+      fa.b_o = p->b_o;
+      fa.out = out;
+      fa.os_r = Jq * c_z;
+      fa.os_p = c_z;
+      fa.c = (int)c_z;
+      fa.H = (int)H;
+      fa.nrows = (int)R;
+      fa.P = (int)Jq;
+      fa.Pp = Ppq;
+      PA_TRY(hip_status(pa::launch_finish_fused_bf16(fa, num_cu, s), "finish launch"));
+      tm_mark(s, "finish");
+      return PAIRATTN_OK;
+    }
     pa::ProjArgs pj{};   // the gate of the query pairs only
     pj.x = q_pairs;
     pj.xs_r = Jq * c_z;
