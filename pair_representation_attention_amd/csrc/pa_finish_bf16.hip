@@ -83,6 +83,18 @@ __global__ __launch_bounds__(256) void finish_fused_kernel(
     load_tile(tile + stride, pre);
     const int r = (int)(tile / nbq), p = (int)(tile % nbq) * 32 + lq;
     const bool valid = p < P;
+    const float* orow = o_part + ((int64_t)r * P + (valid ? p : 0)) * HD;
+    // at H = 4 the tile's o values (64 registers) are loaded before
+    // LayerNorm, so that their latency hides behind it
+    constexpr bool OPF = H == 4;
+    f32x4 opre[OPF ? H : 1][OPF ? 4 : 1];
+    if constexpr (OPF) {
+#pragma unroll
+      for (int b = 0; b < H; ++b)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          opre[b][jj] = valid ? *reinterpret_cast<const f32x4*>(orow + b * 32 + jj * 8 + g * 4) : f32x4{};
+    }
 
     // ---- LayerNorm (two passes, fp32) ----
     float s = 0.0f;
@@ -109,8 +121,7 @@ __global__ __launch_bounds__(256) void finish_fused_kernel(
       for (int e = 0; e < 8; ++e) X[t][e] = f2h_sat((bf2f(raw[t][e]) - mean) * rstd);
 
     // ---- per head: gate, times o, into the wave's LDS tile ----
-    const float* orow = o_part + ((int64_t)r * P + (valid ? p : 0)) * HD;
-#pragma unroll 2
+#pragma unroll
     for (int b = 0; b < H; ++b) {
       f32x16 acc = {};
 #pragma unroll
@@ -121,7 +132,8 @@ __global__ __launch_bounds__(256) void finish_fused_kernel(
       for (int jj = 0; jj < 4; ++jj) {
         const int ch = jj * 8 + g * 4;
         f32x4 ov = {};
-        if (valid) ov = *reinterpret_cast<const f32x4*>(orow + b * 32 + ch);
+        if constexpr (OPF) ov = opre[b][jj];
+        else if (valid) ov = *reinterpret_cast<const f32x4*>(orow + b * 32 + ch);
         const f32x4 cc = *reinterpret_cast<const f32x4*>(cg + b * 32 + ch);
         f16x4 v;
 #pragma unroll
