@@ -471,3 +471,103 @@ def test_partial_finish_over_all_keys_is_the_row_form():
     out = oracle.tri_partial_finish(z[rows], o, p, 2)
     ref = oracle.tri_rows(z[rows], bias, case.mask[rows], p, 2)
     assert np.allclose(out, ref, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# the parity metrics themselves: hand-computed values, and planted mistakes
+# ----------------------------------------------------------------------------
+# max_abs  = max |y - ref|
+# mean_rel = sum |y - ref| / sum |ref|   (aggregate: the elementwise mean of
+#            |y - ref| / |ref| is ill-conditioned where outputs sit near 0)
+METRIC_CASES = [
+    # y, ref, max_abs, mean_rel -- worked by hand
+    ([1.0, 2.0, -1.0], [1.0, 1.0, -3.0], 2.0, 3.0 / 5.0),      # |d| = 0, 1, 2;  sum|ref| = 5
+    ([1.0, 2.0, -3.0], [1.0, 4.0, -1.0], 2.0, 4.0 / 6.0),      # d = 0, -2, -2;  sum|ref| = 6
+    ([[0.5, -0.5], [2.0, 0.0]], [[0.25, -1.0], [2.0, 1.0]], 1.0, 1.75 / 4.25),   # |d| = .25 .5 0 1
+    ([3.0], [3.0], 0.0, 0.0),
+]
+
+
+def _metric_pins_hold() -> bool:
+    for y, ref, ma, mr in METRIC_CASES:
+        if abs(oracle.max_abs_err(np.array(y), np.array(ref)) - ma) > 1e-15:
+            return False
+        if abs(oracle.mean_rel_err(np.array(y), np.array(ref)) - mr) > 1e-15:
+            return False
+    return True
+
+
+def test_parity_metrics_on_hand_computed_values():
+    assert _metric_pins_hold()
+    # symmetric in sign: a sign flip of both arguments changes nothing
+    for y, ref, ma, mr in METRIC_CASES:
+        assert oracle.max_abs_err(-np.array(y), -np.array(ref)) == pytest.approx(ma, abs=1e-15)
+        assert oracle.mean_rel_err(-np.array(y), -np.array(ref)) == pytest.approx(mr, abs=1e-15)
+    # bf16-sized inputs in fp64: nothing is rounded to the inputs' dtype
+    y = np.array([1.0 + 2.0 ** -20], np.float64)
+    assert oracle.max_abs_err(y, np.array([1.0])) == 2.0 ** -20
+
+
+def test_parity_check_rejects_what_it_must():
+    """The GPU tests' comparison: a result within both bf16 bounds passes; a
+    shape mismatch, a non-finite value and each bound alone are failures."""
+    import parity_common as pc
+    ref = np.ones((4, 4))
+    pc.check(ref + 1e-3, ref, "bf16", "within")             # max_abs 1e-3, mean_rel 1e-3
+    bad = ref.copy()
+    bad[2, 3] += 0.03                                       # max_abs 3e-2 > 2e-2, mean_rel 1.9e-3
+    with pytest.raises(AssertionError, match="max_abs"):
+        pc.check(bad, ref, "bf16", "max_abs alone")
+    with pytest.raises(AssertionError, match="mean_rel"):
+        pc.check(ref * 1.006, ref, "bf16", "mean_rel alone")   # max_abs 6e-3, mean_rel 6e-3 > 5e-3
+    nan = ref.copy()
+    nan[0, 0] = np.nan
+    with pytest.raises(AssertionError, match="non-finite"):
+        pc.check(nan, ref, "bf16", "nan")
+    with pytest.raises(AssertionError):
+        pc.check(ref[:3], ref, "bf16", "shape")
+    pc.check(ref + 9e-5, ref, "f32", "f32 within")
+    with pytest.raises(AssertionError, match="max_abs"):
+        pc.check(ref + 1.1e-4, ref, "f32", "f32 max_abs")
+
+
+def _max_abs_signed(y, ref):
+    return float(np.max(np.asarray(y, np.float64) - np.asarray(ref, np.float64)))
+
+
+def _max_abs_relative(y, ref):
+    ref = np.asarray(ref, np.float64)
+    return float(np.max(np.abs(np.asarray(y, np.float64) - ref) / np.maximum(np.abs(ref), 1e-300)))
+
+
+def _mean_rel_elementwise(y, ref):
+    ref = np.asarray(ref, np.float64)
+    return float(np.mean(np.abs(np.asarray(y, np.float64) - ref) / np.abs(ref)))
+
+
+def _mean_rel_den_from_y(y, ref):
+    y = np.asarray(y, np.float64)
+    return float(np.sum(np.abs(y - np.asarray(ref, np.float64))) / np.sum(np.abs(y)))
+
+
+def _mean_rel_signed(y, ref):
+    y, ref = np.asarray(y, np.float64), np.asarray(ref, np.float64)
+    return float(abs(np.sum(y - ref)) / np.sum(np.abs(ref)))
+
+
+METRIC_MUTANTS = {
+    "max_abs_signed_difference": ("max_abs_err", _max_abs_signed),
+    "max_abs_relative": ("max_abs_err", _max_abs_relative),
+    "mean_rel_elementwise_mean": ("mean_rel_err", _mean_rel_elementwise),
+    "mean_rel_denominator_from_y": ("mean_rel_err", _mean_rel_den_from_y),
+    "mean_rel_signed_sum": ("mean_rel_err", _mean_rel_signed),
+}
+
+
+@pytest.mark.parametrize("name", sorted(METRIC_MUTANTS))
+def test_planted_metric_mistake_is_caught(name, monkeypatch):
+    assert _metric_pins_hold()
+    attr, repl = METRIC_MUTANTS[name]
+    monkeypatch.setattr(O, attr, repl)
+    monkeypatch.setattr(oracle, attr, repl)
+    assert not _metric_pins_hold(), f"metric mutant {name} was not detected"
