@@ -14,8 +14,10 @@
 //     H = 8: RWG = 1, QWG = 2, wave = head (both query blocks),  1 x 2 units per key block
 //   per key block and unit (S^T is keys x queries, log2 units):
 //     S^T = K Q^T + C      two MFMAs; C = the fp16 bias tile widened to fp32
-//                          by VALU converts (shared by the workgroup's rows)
+//                          by four 4x4x4 MFMAs (shared by the workgroup's rows)
 //     p = exp2(S - m)      rounded to fp16 (the P operand); l += sum of p
+//                          (four 4x4x4 MFMAs against ones on the pipelined
+//                          sweep, fp16 dot products on the generic one)
 //     O^T += V^T P^T       two MFMAs
 //   Softmax shift m per (row, query): a first sweep uses m = 0 with no
 //   per-unit test; afterwards every l must be finite (no fp16 weight
@@ -81,6 +83,33 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 __device__ __forceinline__ f16x8 lds_f16x8(const char* p) { return *reinterpret_cast<const f16x8*>(p); }
+
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// v_mfma_f32_4x4x4_16b_f16: 16 independent 4x4x4 products.  Lane 4b+i holds
+// row i of A_b and lane 4b+j column j of B_b (4 fp16 each, k = 0..3); output
+// register i of lane 4b+j is D_b[i][j].  So with A = the lane's unit vector
+// e_(lane%4) every lane gets its own four B values widened to fp32 (exact),
+// and with A = ones every output register of a lane gets the fp32 sum of its
+// own four B values.  Either way only 1/16 of the multiplier work of a 32x32
+// product, on the matrix cores instead of the VALU.
+__device__ __forceinline__ f32x4 mfma4(const f16x4& a, const f16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x4 lo4(const f16x8& v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3); }
+__device__ __forceinline__ f16x4 hi4(const f16x8& v) { return __builtin_shufflevector(v, v, 4, 5, 6, 7); }
+
+// The fp16 bias tile of a lane (the 16 values of its S^T accumulator slots)
+// widened to the fp32 C operand of the logits product: four 4x4x4 products
+// against the lane's unit vector `ident`.
+__device__ __forceinline__ f32x16 widen_bias(const f16x8& b0, const f16x8& b1, const f16x4& ident) {
+  const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  const f32x8 c01 = __builtin_shufflevector(mfma4(ident, lo4(b0), z4), mfma4(ident, hi4(b0), z4), 0, 1, 2, 3, 4, 5,
+                                            6, 7);
+  const f32x8 c23 = __builtin_shufflevector(mfma4(ident, lo4(b1), z4), mfma4(ident, hi4(b1), z4), 0, 1, 2, 3, 4, 5,
+                                            6, 7);
+  return __builtin_shufflevector(c01, c23, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+}
 
 // s where bit `lane` of the wave-uniform mask is set, else -inf: one
 // v_cndmask with the mask as its scalar condition.  (A compiler builtin, not
@@ -161,6 +190,13 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int lq = lane & 31, g = lane >> 5;
   const int h = wave % H;
   const int qgrp = wave / H;
+  // A operands of the 4x4x4 products: this lane's unit vector, and ones
+  f16x4 ident4, ones4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ident4[e] = (f16)(e == (lane & 3) ? 1.0f : 0.0f);
+    ones4[e] = (f16)1.0f;
+  }
 
   // XCD-aware tile order: consecutive workgroup ids are spread round-robin
   // over the 8 XCDs, so give each XCD a contiguous range of logical tiles,
@@ -375,16 +411,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         Bt[qq][0] = lds_f16x8(bt);
         Bt[qq][1] = lds_f16x8(bt + 1024);
       }
-      auto bias_c = [&](int qq) -> f32x16 {
-        const f16x8 b0 = Bt[qq][0], b1 = Bt[qq][1];
-        f32x16 c;
-  #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          c[e] = (float)b0[e];
-          c[8 + e] = (float)b1[e];
-        }
-        return c;
-      };
+      auto bias_c = [&](int qq) -> f32x16 { return widen_bias(Bt[qq][0], Bt[qq][1], ident4); };
       auto qk = [&](int rr, int qq, const f32x16& C) -> f32x16 {
         const f32x16 S = mfma32(K[rr][0], Q[rr][qq][0], C);
         return mfma32(K[rr][1], Q[rr][qq][1], S);
@@ -526,7 +553,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
    if constexpr (QW == 2 && RW == 2 && NCW == 4) {
     using T = std::integral_constant<bool, true>;
     using F = std::integral_constant<bool, false>;
-    float l2[RW][QW];   // second partial row sum (keys 16..31 of each unit's lane half)
+    f32x4 lacc[RW][QW];   // row sums of the sweep (every element holds the lane's sum)
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
       row_has_key[rr] = true;   // P >= 1: every row has a kept key
@@ -535,7 +562,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         O[rr][qq] = f32x16{};
         m_sh[rr][qq] = 0.0f;
         l_run[rr][qq] = 0.0f;
-        l2[rr][qq] = 0.0f;
+        lacc[rr][qq] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
     }
     // copy sources: one wave-uniform base per ring, per-lane byte offsets
@@ -566,15 +593,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     auto b_tile = [&](int kb, int qq) -> const char* {
       return b_lds + (kb & 1) * SH::B_STAGE + ((qgrp * QW + qq) * H + h) * SH::B_TILE + lane * 16;
     };
-    auto cvt_bias = [&](const f16x8* b) -> f32x16 {
-      f32x16 c;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        c[e] = (float)b[0][e];
-        c[8 + e] = (float)b[1][e];
-      }
-      return c;
-    };
+    auto cvt_bias = [&](const f16x8* b) -> f32x16 { return widen_bias(b[0], b[1], ident4); };
     auto barrier = [&]() {
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
@@ -582,15 +601,15 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     };
     // softmax of S (one unit) with the next unit's logits (NEXT) and this
     // unit's P.V product issued between its exp2 groups; the row sums
-    // accumulate in la (keys of chunk 0) and lb (chunk 1).  MASKED: keys
+    // accumulate in lacc by 4x4x4 products of the fp16 weights with ones
+    // (every element of lacc holds the lane's running sum).  MASKED: keys
     // whose bit in `bits` is clear get -inf first (register j holds key
     // (j/4)*8 + g*4 + j%4, so the select's lane mask is built on the scalar
     // unit).
     auto stream = [&](auto nextc, auto maskc, const f32x16& S_in, f32x16& Sn, const f16x8* kn, const f16x8* qn,
-                      const f32x16& cn, const f16x8* v, f32x16& o, float& la, float& lb, uint32_t bits) {
+                      const f32x16& cn, const f16x8* v, f32x16& o, f32x4& lacc, uint32_t bits) {
       constexpr bool NEXT = decltype(nextc)::value;
       constexpr bool MASKED = decltype(maskc)::value;
-      const f16x2 one = {(f16)1.0f, (f16)1.0f};
       float e[16];
       f16x8 p0, p1;
       f32x16 S = S_in;
@@ -625,13 +644,13 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       for (int j = 12; j < 16; ++j) e[j] = fast_exp2(S[j]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) p1[j] = f2h(e[8 + j]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) la = __builtin_amdgcn_fdot2(f16x2{p0[2 * j], p0[2 * j + 1]}, one, la, false);
+      lacc = mfma4(ones4, lo4(p0), lacc);
+      lacc = mfma4(ones4, hi4(p0), lacc);
       __builtin_amdgcn_sched_barrier(0);
       o = mfma32(v[1], p1, o);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) lb = __builtin_amdgcn_fdot2(f16x2{p1[2 * j], p1[2 * j + 1]}, one, lb, false);
+      lacc = mfma4(ones4, lo4(p1), lacc);
+      lacc = mfma4(ones4, hi4(p1), lacc);
       __builtin_amdgcn_sched_barrier(0);
     };
     struct Regs {
@@ -679,17 +698,16 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       __builtin_amdgcn_s_setprio(3);
       if constexpr (MORE) copy_kv(kb + 2, 2, 4);
       else load_epi();
-      stream(T{}, maskc, S_pipe, Sn, r.K[1], Q[1][0], C_pipe, r.V[0], O[0][0], l_run[0][0], l2[0][0], bits0);
+      stream(T{}, maskc, S_pipe, Sn, r.K[1], Q[1][0], C_pipe, r.V[0], O[0][0], lacc[0][0], bits0);
       S_pipe = Sn;
       C_pipe = cvt_bias(r.B1);
       // stream 1: unit (1, 0); next (0, 1)
       __builtin_amdgcn_s_setprio(2);
-      stream(T{}, maskc, S_pipe, Sn, r.K[0], Q[0][1], C_pipe, r.V[1], O[1][0], l_run[1][0], l2[1][0], bits1);
+      stream(T{}, maskc, S_pipe, Sn, r.K[0], Q[0][1], C_pipe, r.V[1], O[1][0], lacc[1][0], bits1);
       S_pipe = Sn;
       // stream 2: unit (0, 1); next (1, 1); block kb+1 published
       __builtin_amdgcn_s_setprio(1);
       f16x8 Bn0[2];
-      f32x16 Cn;
       if constexpr (MORE) {
         wait_vmcnt<NCW>();
         barrier();
@@ -699,7 +717,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         for (int c = 0; c < 2; ++c) Bn0[c] = lds_f16x8(b_tile(kb + 1, 0) + c * 1024);
         copy_b(kb + 2);
       }
-      stream(T{}, maskc, S_pipe, Sn, r.K[1], Q[1][1], C_pipe, r.V[0], O[0][1], l_run[0][1], l2[0][1], bits0);
+      stream(T{}, maskc, S_pipe, Sn, r.K[1], Q[1][1], C_pipe, r.V[0], O[0][1], lacc[0][1], bits0);
       S_pipe = Sn;
       if constexpr (MORE) {
 #pragma unroll
@@ -707,11 +725,11 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
           r.K[1][c] = lds_f16x8(kv_tile(kb + 1, 1) + c * 1024);
           r.V[0][c] = lds_f16x8(kv_tile(kb + 1, 0) + 2048 + c * 1024);
         }
-        Cn = cvt_bias(Bn0);
+        C_pipe = cvt_bias(Bn0);   // the bias of query block 1 had its last use in stream 2
       }
       // stream 3: unit (1, 1); next = unit (0, 0) of block kb+1
       __builtin_amdgcn_s_setprio(0);
-      stream(morec, maskc, S_pipe, Sn, r.K[0], Q[0][0], Cn, r.V[1], O[1][1], l_run[1][1], l2[1][1], bits1);
+      stream(morec, maskc, S_pipe, Sn, r.K[0], Q[0][0], C_pipe, r.V[1], O[1][1], lacc[1][1], bits1);
       if constexpr (MORE) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -719,7 +737,6 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
           r.B1[c] = lds_f16x8(b_tile(kb + 1, 1) + c * 1024);
         }
         copy_kv(kb + 3, 0, 2);
-        C_pipe = Cn;
         S_pipe = Sn;
       }
     };
@@ -737,7 +754,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr)
 #pragma unroll
-      for (int qq = 0; qq < QW; ++qq) l_run[rr][qq] += l2[rr][qq];
+      for (int qq = 0; qq < QW; ++qq) l_run[rr][qq] = lacc[rr][qq][0];
    }
   };
 
