@@ -120,6 +120,25 @@ int pairattn_tri_fwd(const void *z, const uint8_t *mask, const pairattn_params *
                      int64_t I, int64_t c_z, int64_t H, int64_t d, int32_t orientation,
                      void *stream);
 
+/* Allocation-free form of pairattn_tri_fwd, for callers that cannot allocate
+ * device memory or hand over a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, layout,
+ * arithmetic and result as pairattn_tri_fwd (the same kernels run); the
+ * workspace and workspace_bytes fields of *p are ignored.  Its workspace is
+ * a static device array of PAIRATTN_NOALLOC_SCRATCH_BYTES per GPU, held from
+ * the library's first use on that GPU until the process ends.  Problems whose
+ * pairattn_tri_workspace_bytes exceeds it return PAIRATTN_ERR_UNSUPPORTED
+ * before any device call (I <= 507 for bf16 at H = 4, I <= 352 for fp32 at
+ * H = 4 or bf16 at H = 8, I <= 252 for fp32 at H = 8).  Nothing in the
+ * array needs to start at zero: each call overwrites what it reads.  Every
+ * call on one GPU shares that GPU's array, so calls that overlap on one GPU
+ * (other streams, other host threads) race; serialise them.  Timing marks
+ * (pairattn_timing_enable) are not recorded for this call. */
+#define PAIRATTN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int pairattn_tri_fwd_noalloc(const void *z, const uint8_t *mask, const pairattn_params *p,
+                             void *out, int64_t I, int64_t c_z, int64_t H, int64_t d,
+                             int32_t orientation, void *stream);
+
 /* MSA row attention with pair bias.
  *   m    [S][I][c_m] MSA representation; z [I][I][c_z] pair representation
  *   mask [S][I] uint8 or NULL (key j of sequence s kept iff mask[s][j])

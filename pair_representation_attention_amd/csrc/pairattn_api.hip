@@ -290,6 +290,8 @@ void tm_begin(hipStream_t s) {
   t.n = 1;
 }
 
+void tm_reset() { g_tm.n = 0; }
+
 void tm_mark(hipStream_t s, const char* stage) {
   Timing& t = g_tm;
   if (!t.enabled || t.n == 0 || t.n >= kMaxMarks) return;
@@ -298,6 +300,38 @@ void tm_mark(hipStream_t s, const char* stage) {
   ++t.n;
 }
 
+}  // namespace
+
+// ---- static scratch of the allocation-free entry point ---------------------
+// One array per device: the code object's global segment, allocated when the
+// library's kernels load on that device and held until the process ends.  In
+// host code `scratch` names a host-side stand-in, never passed to a kernel:
+// its device address is looked up once per device (with that device current)
+// and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = PAIRATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+int scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(PAIRATTN_ERR_DEVICE, "no current HIP device");
+  if (dev >= 64) return fail(PAIRATTN_ERR_DEVICE, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* at = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&at, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || at == nullptr)
+      return fail(PAIRATTN_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    if ((reinterpret_cast<uintptr_t>(at) & (kAlign - 1)) != 0)
+      return fail(PAIRATTN_ERR_HIP, "scratch of device %d is not 256-byte aligned", dev);
+    g_scratch_ptr[dev] = at;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PAIRATTN_OK;
+}
 }  // namespace
 
 // ============================================================================
@@ -362,9 +396,12 @@ size_t pairattn_rows_workspace_bytes(int64_t R, int64_t I, int64_t c_z, int64_t 
   return make_layout(R, I, c_z, c_z, H, dtype).total;
 }
 
-int pairattn_validate_tri(const void* z, const uint8_t* mask, const pairattn_params* p, const void* out,
-                          int64_t I, int64_t c_z, int64_t H, int64_t d, int32_t orientation) {
-  g_err[0] = '\0';
+}  // extern "C"
+
+namespace {
+// Everything pairattn_validate_tri checks except the workspace.
+int validate_tri_args(const void* z, const uint8_t* mask, const pairattn_params* p, const void* out, int64_t I,
+                      int64_t c_z, int64_t H, int64_t d, int32_t orientation) {
   PA_TRY(check_params(p, true, false));
   if (z == nullptr || out == nullptr) return fail(PAIRATTN_ERR_ARG, "z and out must not be NULL");
   if (!aligned16(z) || !aligned16(out)) return fail(PAIRATTN_ERR_ARG, "z and out must be 16-byte aligned");
@@ -375,6 +412,17 @@ int pairattn_validate_tri(const void* z, const uint8_t* mask, const pairattn_par
   const size_t zbytes = (size_t)I * I * c_z * elt_bytes(p->dtype);
   if (overlaps(out, zbytes, z, zbytes)) return fail(PAIRATTN_ERR_ARG, "out overlaps z");
   if (mask != nullptr && overlaps(out, zbytes, mask, (size_t)I * I)) return fail(PAIRATTN_ERR_ARG, "out overlaps mask");
+  return PAIRATTN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int pairattn_validate_tri(const void* z, const uint8_t* mask, const pairattn_params* p, const void* out,
+                          int64_t I, int64_t c_z, int64_t H, int64_t d, int32_t orientation) {
+  g_err[0] = '\0';
+  PA_TRY(validate_tri_args(z, mask, p, out, I, c_z, H, d, orientation));
+  const size_t zbytes = (size_t)I * I * c_z * elt_bytes(p->dtype);
   const size_t need = pairattn_tri_workspace_bytes(I, c_z, H, d, p->dtype);
   PA_TRY(check_workspace(p, need));
   if (overlaps(out, zbytes, p->workspace, p->workspace_bytes)) return fail(PAIRATTN_ERR_ARG, "out overlaps the workspace");
@@ -780,6 +828,36 @@ int pairattn_tri_fwd(const void* z, const uint8_t* mask, const pairattn_params* 
   const int64_t ms_k = start ? 1 : I;
   const RowAttn ra{z, xs_r, xs_p, c_z, I, I, H, true, nullptr, 0, nullptr, mask, ms_r, ms_k, out, xs_r, xs_p};
   return run_row_attention(p, L, static_cast<hipStream_t>(stream), num_cu, ra);
+}
+
+int pairattn_tri_fwd_noalloc(const void* z, const uint8_t* mask, const pairattn_params* p, void* out, int64_t I,
+                             int64_t c_z, int64_t H, int64_t d, int32_t orientation, void* stream) {
+  g_err[0] = '\0';
+  // host checks first: arguments, then the size against the static scratch
+  PA_TRY(validate_tri_args(z, mask, p, out, I, c_z, H, d, orientation));
+  const size_t need = pairattn_tri_workspace_bytes(I, c_z, H, d, p->dtype);
+  if (need > kScratchBytes)
+    return fail(PAIRATTN_ERR_UNSUPPORTED,
+                "I=%lld needs %zu bytes of scratch; the allocation-free call has %zu (pass a workspace to "
+                "pairattn_tri_fwd instead)",
+                (long long)I, need, kScratchBytes);
+  void* ws = nullptr;
+  PA_TRY(scratch_for_current_device(&ws));
+  int num_cu = 0;
+  PA_TRY(check_device(&num_cu));
+  tm_reset();   // no timing marks: recording them would create events
+  pairattn_params q = *p;
+  q.workspace = ws;
+  q.workspace_bytes = kScratchBytes;
+  const Layout L = make_layout(I, I, c_z, c_z, H, q.dtype);
+  const bool start = orientation == PAIRATTN_START;
+  const int64_t xs_r = start ? I * c_z : c_z;
+  const int64_t xs_p = start ? c_z : I * c_z;
+  const int64_t ms_r = start ? I : 1;
+  const int64_t ms_k = start ? 1 : I;
+  RowAttn ra{z, xs_r, xs_p, c_z, I, I, H, true, nullptr, 0, nullptr, mask, ms_r, ms_k, out, xs_r, xs_p};
+  ra.nested = true;
+  return run_row_attention(&q, L, static_cast<hipStream_t>(stream), num_cu, ra);
 }
 
 int pairattn_msa_row_fwd(const void* m, const void* z, const uint8_t* mask, const pairattn_params* p, void* out,

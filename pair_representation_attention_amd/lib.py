@@ -26,6 +26,9 @@ PAIRATTN_ERR_WORKSPACE = 3
 PAIRATTN_ERR_DEVICE = 4
 PAIRATTN_ERR_HIP = 5
 
+# size of the static scratch of pairattn_tri_fwd_noalloc (PAIRATTN_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 256 << 20
+
 PAIRATTN_START = 0
 PAIRATTN_END = 1
 PAIRATTN_F32 = 0
@@ -75,6 +78,7 @@ _SIGNATURES = {
     "pairattn_msa_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64, _I64, _I64, _I32]),
     "pairattn_rows_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64, _I64, _I32]),
     "pairattn_tri_fwd": (ctypes.c_int, [_P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I32, _P]),
+    "pairattn_tri_fwd_noalloc": (ctypes.c_int, [_P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I32, _P]),
     "pairattn_msa_row_fwd": (ctypes.c_int, [_P, _P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
     "pairattn_tri_bias": (ctypes.c_int, [_P, _PP, _P, _I64, _I64, _I64, _I32, _P]),
     "pairattn_tri_rows_fwd": (ctypes.c_int, [_P, _P, _P, _PP, _P, _I64, _I64, _I64, _I64, _I64, _P]),
@@ -184,6 +188,12 @@ def pairattn_tri_fwd(z, mask, params, out, I, c_z, H, d, orientation, stream=Non
     st = load().pairattn_tri_fwd(_ptr(z), _ptr(mask), ctypes.byref(params.struct()), _ptr(out), I, c_z, H, d,
                                  orientation, _stream(stream))
     return _check(st, "pairattn_tri_fwd") if check else st
+
+
+def pairattn_tri_fwd_noalloc(z, mask, params, out, I, c_z, H, d, orientation, stream=None, check=True) -> int:
+    st = load().pairattn_tri_fwd_noalloc(_ptr(z), _ptr(mask), ctypes.byref(params.struct()), _ptr(out), I, c_z, H,
+                                         d, orientation, _stream(stream))
+    return _check(st, "pairattn_tri_fwd_noalloc") if check else st
 
 
 def pairattn_msa_row_fwd(m, z, mask, params, out, S, I, c_m, c_z, H, d, stream=None, check=True) -> int:

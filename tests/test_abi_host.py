@@ -297,3 +297,33 @@ def test_validate_tri_partial_finish():
     pb = _params(lib.PAIRATTN_BF16, ws=WS, ws_bytes=nb - 256)
     assert lib.pairattn_validate_tri_partial_finish(QP, O_, pb, OUT, 3, 40, 128, 4, 32) == \
         lib.PAIRATTN_ERR_WORKSPACE
+
+
+# ----------------------------------------------------------------------------
+# allocation-free triangle attention: host checks before any device call
+# ----------------------------------------------------------------------------
+def test_noalloc_host_checks(L):
+    p = _params(lib.PAIRATTN_BF16)   # no workspace: the call ignores those fields
+    # the largest bf16 problem at H = 4 that fits the static scratch, and the next
+    assert lib.pairattn_tri_workspace_bytes(507, 128, 4, 32, lib.PAIRATTN_BF16) <= lib.NOALLOC_SCRATCH_BYTES
+    assert lib.pairattn_tri_workspace_bytes(508, 128, 4, 32, lib.PAIRATTN_BF16) > lib.NOALLOC_SCRATCH_BYTES
+    st = lib.pairattn_tri_fwd_noalloc(Z, None, p, OUT, 508, 128, 4, 32, 0, stream=0, check=False)
+    assert st == lib.PAIRATTN_ERR_UNSUPPORTED and "scratch" in lib.last_error()
+    assert lib.pairattn_tri_fwd_noalloc(Z, None, p, OUT, 64, 128, 4, 32, 3, stream=0, check=False) == \
+        lib.PAIRATTN_ERR_ARG
+    assert lib.pairattn_tri_fwd_noalloc(Z, None, p, OUT, 64, 128, 4, 48, 0, stream=0, check=False) == \
+        lib.PAIRATTN_ERR_UNSUPPORTED
+    assert lib.pairattn_tri_fwd_noalloc(Z, None, p, Z, 64, 128, 4, 32, 0, stream=0, check=False) == \
+        lib.PAIRATTN_ERR_ARG   # out overlaps z
+    f = _params(lib.PAIRATTN_F32)
+    st = lib.pairattn_tri_fwd_noalloc(Z, None, f, OUT, 353, 128, 4, 32, 1, stream=0, check=False)
+    assert st == lib.PAIRATTN_ERR_UNSUPPORTED
+
+
+def test_noalloc_without_device_reports_it():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st = lib.pairattn_tri_fwd_noalloc(Z, None, _params(lib.PAIRATTN_BF16), OUT, 64, 128, 4, 32, 0, stream=0,
+                                      check=False)
+    assert st == lib.PAIRATTN_ERR_DEVICE, lib.last_error()
