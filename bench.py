@@ -41,6 +41,11 @@ METRIC = "triangle-attn bf16 TFLOP/s + pair-rows/s at I=1536; % of MFMA peak"
 PEAK_MFMA_16BIT_TFLOPS = 2516.6          # 256 CU x 4096 flop/clk x 2.4 GHz (bf16 = fp16 dense)
 PEAK_HBM_GBS = 8000.0
 PEAK_MFMA_FP32_TFLOPS = 157.3           # dense fp32 matrix peak
+# exp2 issue ceiling at the nominal clock: 1024 SIMDs x 64 lanes per 8 cycles x 2.4 GHz
+PEAK_EXP2_PER_S = 1024 * 64 / 8 * 2.4e9
+# what the path computes in: bf16 in and out, every matrix product on fp16
+# operands with fp32 accumulation, LayerNorm and softmax in fp32
+DTYPE_LABEL = "bf16 I/O, fp16 MFMA operands, fp32 accumulation and softmax"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_tri_bf16_i1536.json")
 CSRC = os.path.join(ROOT, "pair_representation_attention_amd", "csrc")
 # source files each kernel is compiled from (a counter summary is valid for one source state)
@@ -93,6 +98,91 @@ def proj_kernel_bytes(R: int, I: int, c: int, H: int, d: int, with_bias: bool = 
     read the R x I positions of x once, write q, k, v, g and the pair bias."""
     hd = H * d
     return 2.0 * R * I * c + 4 * 2.0 * R * I * hd + (2.0 * H * I * I if with_bias else 0.0)
+
+
+def softmax_elements(R: int, I: int, H: int) -> float:
+    """exp2 evaluations of one attention launch: one per (row, head, query, key)."""
+    return float(R) * I * I * H
+
+
+def stream_rates(R: int, I: int, c: int, H: int, d: int, attn_ms: float, proj_ms: float) -> dict:
+    """Bytes and rates of the pair-bias and gate streams (bf16 path, one
+    orientation): the projection writes both once; the attention reads the
+    gate once and copies the bias tiles of its query blocks into LDS for
+    every block of 2 rows (from L2 and the last-level cache: the bias is
+    19 MB at I = 1536), i.e. I/2 times over."""
+    Pp = (I + 31) // 32 * 32
+    bias = 2.0 * H * Pp * Pp                  # fp16, padded, log2 units
+    gate = 2.0 * R * Pp * H * d               # fp16, layout of q
+    bias_lds = bias * ((R + 1) // 2)          # every 2-row workgroup group sweeps all key blocks
+    return {
+        "bias": {"bytes": bias, "written_gbs_over_projection": bias / (proj_ms * 1e-3) / 1e9,
+                 "copied_to_lds_bytes_per_attention_launch": bias_lds,
+                 "copied_to_lds_gbs": bias_lds / (attn_ms * 1e-3) / 1e9},
+        "gate": {"bytes": gate, "written_gbs_over_projection": gate / (proj_ms * 1e-3) / 1e9,
+                 "read_gbs_over_attention": gate / (attn_ms * 1e-3) / 1e9},
+    }
+
+
+def per_kernel_pass(lib, torch, stream, step, steps: int, prefixes) -> dict:
+    """Run `steps` steps with the library's per-kernel events on; each step
+    makes len(prefixes) calls.  Returns {prefix + stage: [ms per launch]}
+    and the step time of this pass under "_step_ms"."""
+    lib.pairattn_timing_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    marks = lib.pairattn_timing_read()
+    torch.cuda.synchronize()
+    lib.pairattn_timing_enable(False)
+    out = {"_step_ms": e0.elapsed_time(e1) / steps}
+    # each call's marks start with "pack"; calls alternate over the prefixes
+    call = -1
+    for name, ms in marks:
+        if name == "pack":
+            call += 1
+        out.setdefault(prefixes[call % len(prefixes)] + name, []).append(ms)
+    return out
+
+
+def calibrate_exp2(lib, torch, stream, iters: int = 4096, reps: int = 3) -> dict:
+    """The device's exp2 throughput (pairattn_calibrate_exp2), timed with
+    events on the launch stream: the ceiling of the softmax's exp2 issue."""
+    out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    lib.pairattn_calibrate_exp2(out, iters, stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        lib.pairattn_calibrate_exp2(out, iters, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    n = 2048 * 256 * 8 * iters
+    return {"exp2_per_launch": n, "ms": ms, "exp2_per_s": n / (ms * 1e-3),
+            "cycles_per_wave_exp2_at_2.4GHz": 1024 * 64 * 2.4e9 / (n / (ms * 1e-3))}
+
+
+def cpu_info() -> dict:
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = None
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "affinity_cpus": aff}
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -185,6 +275,7 @@ def cpu_baseline(case, H: int, d: int, rows: int) -> dict:
         "sample": f"starting-node rows {sel.tolist()} of Z[{I},{I},{c}] (all queries, pair bias over all "
                   f"{I}x{I} pairs), fp64 numpy; {dt:.1f} s; flops counted as for the GPU",
         "seconds": dt,
+        **cpu_info(),
     }
 
 
@@ -196,7 +287,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=24, help="oracle sample size (rows, about 0.35-1.4 s each by host)")
-    ap.add_argument("--extra", action="store_true", help="also time MSA row attention and the row block")
+    ap.add_argument("--extra", action="store_true",
+                    help="also time the fp32 I=64 and padded I=384 triangle configurations, the padded I=1536 "
+                         "module, MSA row attention, the row block and the extra-MSA fp32 workload")
     ap.add_argument("--workload", choices=["tri_bf16_i1536", "msa_fp32_s5120_i384", "tri_bf16_i16384_chunked",
                                            "ring_fp32_i1536_grid2x2", "ring_bf16_i1536_grid2x2"],
                     default="tri_bf16_i1536",
@@ -204,9 +297,6 @@ def main() -> int:
                          "(one JSON line)")
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="MIB",
                     help="after timing, run a plain device copy of MIB MiB (counter calibration)")
-    ap.add_argument("--gemm-probe", action="store_true",
-                    help="only time the ROCm library's dense bf16/fp16 GEMM (torch.mm, n = 4096 and 8192): "
-                         "the matrix-core rate a tuned dense kernel reaches on this device (one JSON line)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 --pmc counter CSVs and exit")
     ap.add_argument("--copy-mib", type=float, default=1024.0, help="copy size used in the --pmc runs")
@@ -236,9 +326,6 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
-    if args.gemm_probe:
-        print(json.dumps({"gemm_probe": gemm_probe(torch)}), flush=True)
-        return 0
     lib.load()
     if args.workload != "tri_bf16_i1536":
         fn = {"msa_fp32_s5120_i384": msa_fp32_workload, "tri_bf16_i16384_chunked": chunked_workload,
@@ -263,27 +350,26 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    # timed region; per-kernel HIP events on the same stream
-    lib.pairattn_timing_enable(True)
-    stage_ms = {}
+    # timed region: K steps, nothing recorded between them
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        start(lib.PAIRATTN_START, stream)
-        for name, ms in lib.pairattn_timing_read():
-            stage_ms.setdefault("start_" + name, []).append(ms)
-        end(lib.PAIRATTN_END, stream)
-        for name, ms in lib.pairattn_timing_read():
-            stage_ms.setdefault("end_" + name, []).append(ms)
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    lib.pairattn_timing_enable(False)
     ms_step = ev0.elapsed_time(ev1) / args.steps
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (host wall {wall / args.steps * 1e3:.3f} ms/step)")
+
+    # per-kernel pass: the same K steps again with HIP events recorded by the
+    # library on the launch stream after each kernel (no host wait until the
+    # end), for the kernels' launch times
+    stage_ms = per_kernel_pass(lib, torch, stream, step, args.steps, ("start_", "end_"))
+    ms_step_marked = stage_ms.pop("_step_ms")
+    log(f"per-kernel pass: {ms_step_marked:.3f} ms/step")
 
     f = tri_module_flops(I, I, c, H, d)
     step_flops = 2 * f["total"]
@@ -320,6 +406,23 @@ def main() -> int:
     }
     kernels = {k: float(np.mean(v)) for k, v in sorted(stage_ms.items())}
 
+    # second roof: one exp2 per logit against the device's measured exp2 rate
+    exp_cal = calibrate_exp2(lib, torch, stream)
+    exps = softmax_elements(I, I, H)
+    exp_rate = exps / (attn_ms * 1e-3)
+    roof_exp = {
+        "kernel": roof["kernel"],
+        "bound": "exp2 issue",
+        "achieved": exp_rate / 1e12,
+        "peak": exp_cal["exp2_per_s"] / 1e12,
+        "peak_nominal": PEAK_EXP2_PER_S / 1e12,
+        "unit": "Texp2/s",
+        "frac": exp_rate / exp_cal["exp2_per_s"],
+        "exp2_per_launch": exps,
+        "calibration": exp_cal,
+    }
+    streams = stream_rates(I, I, c, H, d, attn_ms, proj_ms)
+
     result = {
         "metric": METRIC,
         "value": tflops,
@@ -331,16 +434,19 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": DTYPE_LABEL,
         "data": "synthetic",
         "config": {"workload": "tri_bf16_i1536", "I": I, "c_z": c, "H": H, "d": d, "mask": "none",
                    "orientations": ["start", "end"], "seed": cfg["seed"]},
         "pair_rows_per_s": pair_rows,
         "frac_of_peak": tflops / PEAK_MFMA_16BIT_TFLOPS,
         "step_flops": step_flops,
+        "ms_per_step_per_kernel_pass": ms_step_marked,
         "kernels_ms": kernels,
         "roofline": roof,
+        "roofline_second": roof_exp,
         "roofline_projection": roof_proj,
+        "streams": streams,
     }
 
     if args.extra:
@@ -367,21 +473,6 @@ def main() -> int:
     return 0
 
 
-def gemm_probe(torch) -> dict:
-    """Calibration, not part of the path: the dense GEMM of the ROCm library
-    (torch.mm on contiguous operands) at n = 4096 and 8192, in TFLOP/s."""
-    out = {}
-    for name, dt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
-        for n in (4096, 8192):
-            a = torch.randn(n, n, device="cuda", dtype=dt)
-            b = torch.randn(n, n, device="cuda", dtype=dt)
-            ms = _time(lambda: torch.mm(a, b), 20, 3, torch)
-            out[f"{name}_n{n}"] = {"ms": ms, "tflops": 2.0 * n ** 3 / (ms * 1e-3) / 1e12,
-                                   "frac_of_peak": 2.0 * n ** 3 / (ms * 1e-3) / 1e12 / PEAK_MFMA_16BIT_TFLOPS}
-            del a, b
-    return out
-
-
 def _time(fn, steps, warmup, torch):
     for _ in range(warmup):
         fn()
@@ -396,8 +487,51 @@ def _time(fn, steps, warmup, torch):
     return e0.elapsed_time(e1) / steps
 
 
+def tri_config_workload(name, args, device, inputs, lib, torch, np, orientations=(0, 1), mask_override=None):
+    """One triangle-attention configuration: module time of the given
+    orientations back to back (uninstrumented), the per-kernel split from a
+    second pass, TFLOP/s and pair-rows/s."""
+    cfg = inputs.CONFIGS[name]
+    I, c, H, d, dt = cfg["I"], cfg["c"], cfg["H"], cfg["d"], cfg["dtype"]
+    mask = cfg["mask"] if mask_override is None else mask_override
+    log(f"extra: {name} mask={mask} orientations={list(orientations)}")
+    case = inputs.make_tri_case(I=I, c=c, H=H, d=d, dtype=dt, mask=mask, seed=cfg["seed"])
+    runs = [device.TriRunner(case.z, case.mask, case.params_start if o == 0 else case.params_end, H, dt)
+            for o in orientations]
+    for r in runs[1:]:
+        r.z, r.mask = runs[0].z, runs[0].mask
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for o, r in zip(orientations, runs):
+            r(o, stream)
+
+    steps = max(3, args.steps)
+    ms = _time(step, steps, 2, torch)
+    st = per_kernel_pass(lib, torch, stream, step, steps, tuple(f"o{o}_" for o in orientations))
+    st.pop("_step_ms")
+    f = tri_module_flops(I, I, c, H, d)["total"] * len(orientations)
+    res = {"I": I, "dtype": dt, "mask": mask, "orientations": list(orientations), "ms": ms,
+           "tflops": f / (ms * 1e-3) / 1e12, "pair_rows_per_s": I * len(orientations) / (ms * 1e-3),
+           "kernels_ms": {k: float(np.mean(v)) for k, v in sorted(st.items())}}
+    att = [v for k, v in st.items() if k.endswith("attention")]
+    if att:
+        a_ms = float(np.mean([x for v in att for x in v]))
+        res["attention_tflops"] = attn_kernel_flops(I, I, c, H, d) / (a_ms * 1e-3) / 1e12
+    del runs, case
+    torch.cuda.empty_cache()
+    return res
+
+
 def extra_workloads(args, device, inputs, lib, torch, np) -> dict:
     out = {}
+    # the other triangle configurations: fp32 I = 64 (starting node) and the
+    # padded bf16 I = 384 (both orientations); the module of I = 1536 under
+    # the padding mask of the I = 384 configuration (last 10% of residues)
+    out["tri_fp32_i64"] = tri_config_workload("tri_fp32_i64", args, device, inputs, lib, torch, np, (0,))
+    out["tri_bf16_i384_pad"] = tri_config_workload("tri_bf16_i384_pad", args, device, inputs, lib, torch, np)
+    out["tri_bf16_i1536_pad"] = tri_config_workload("tri_bf16_i1536", args, device, inputs, lib, torch, np,
+                                                    mask_override="pad")
     cfg = inputs.CONFIGS["msa_bf16_s512_i384"]
     log("extra: MSA row attention S=512 I=384")
     case = inputs.make_msa_case(S=cfg["S"], I=cfg["I"], c_m=cfg["c_m"], c_z=cfg["c_z"], H=cfg["H"], d=cfg["d"],

@@ -255,15 +255,27 @@ int pairattn_validate_rows(const void *z_rows, const float *bias, const uint8_t 
 
 /* Per-kernel timing of the calling thread's launches (instrumentation).
  * pairattn_timing_enable(1) makes every later entry point on this thread
- * record HIP events on its stream around each kernel it launches; it
- * returns the previous setting.  pairattn_timing_read waits for the last
- * call's final event and writes up to `cap` stage durations in ms
- * (stages in launch order: "pack", "projection", "pair_bias", "attention")
- * and their static names; it returns the number written, 0 when timing
- * is off or nothing was recorded, or -PAIRATTN_ERR_HIP on a HIP failure.
- * `ms` or `names` may be NULL. */
+ * record HIP events on its stream at its start and after each kernel it
+ * launches, with no host wait (a pool of 1024 events per thread, created by
+ * the enabling call; marks beyond it are dropped until the next read).  It
+ * returns the previous setting, or -PAIRATTN_ERR_HIP if the events could not
+ * be created.  pairattn_timing_read waits for the last event recorded and
+ * writes up to `cap` stage durations in ms, of every call since the last
+ * read, in launch order ("pack", "projection", "pair_bias", "mask_bits",
+ * "attention", ...), with their static names; it returns the number
+ * written, 0 when timing is off or nothing was recorded, or
+ * -PAIRATTN_ERR_HIP on a HIP failure.  `ms` or `names` may be NULL. */
 int pairattn_timing_enable(int enable);
 int pairattn_timing_read(float *ms, const char **names, int cap);
+
+/* Calibration of the softmax's second roof (instrumentation, not part of
+ * the method): one launch on `stream` of 2048 x 256 threads, each running 8
+ * independent chains of `iters` exp2 instructions (x <- exp2(-x)), so that
+ * the issue rate of exp2 bounds it; each thread writes one float (a value
+ * that keeps its chains live) to out[524288] (device, 16-byte aligned).
+ * One launch evaluates 4194304 * iters exp2 per lane; timed with events on
+ * `stream`, it gives this device's exp2 throughput.  iters in [1, 2^24]. */
+int pairattn_calibrate_exp2(float *out, int64_t iters, void *stream);
 
 /* Static description of a status code. */
 const char *pairattn_status_string(int status);

@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpairattn.so")
 
-SOURCES = ["pairattn_api.hip", "pa_kernels_bf16.hip", "pa_attn.hip", "pa_kernels_f32.hip", "pa_finish_bf16.hip"]
+SOURCES = ["pairattn_api.hip", "pa_kernels_bf16.hip", "pa_attn.hip", "pa_kernels_f32.hip", "pa_finish_bf16.hip",
+           "pa_calib.hip"]
 ARCH = "gfx950"
 
 

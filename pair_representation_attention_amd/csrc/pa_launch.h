@@ -56,6 +56,9 @@ hipError_t launch_bias_to_attn_layout(const float* src, void* dst, int H, int Pq
 // mode 0: q,k,v,g   1: q,k,v,g + bias   2: bias only
 hipError_t launch_proj_bf16(const ProjArgs& a, int mode, int num_cu, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+// exp2 issue-rate calibration: 2048 x 256 threads, 8 chains of `iters` exp2
+// each, one float per thread into out
+hipError_t launch_calib_exp2(float* out, int iters, hipStream_t s);
 // gate (g_ws, layout of q), output projection and bf16 store of merged partial
 // outputs o_part (fields g_ws, woT, b_o, out, os_r, os_p, H, c_out, nrows, P, Pp, o_part)
 hipError_t launch_finish_bf16(const AttnArgs& a, hipStream_t s);

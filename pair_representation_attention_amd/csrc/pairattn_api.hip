@@ -267,34 +267,30 @@ int check_workspace(const pairattn_params* p, size_t need) {
 char* ws_at(const pairattn_params* p, size_t off) { return static_cast<char*>(p->workspace) + off; }
 
 // ---- optional per-kernel timing (HIP events on the call's stream) ----------
-constexpr int kMaxMarks = 8;
+// A pool of events per thread, created when timing is enabled; every call
+// records a boundary and one event after each kernel, with no host wait, so
+// that many calls can be timed back to back and read at once.
+constexpr int kPool = 1024;
 struct Timing {
   bool enabled = false;
   bool created = false;
-  hipEvent_t ev[kMaxMarks];
-  const char* name[kMaxMarks];
+  hipEvent_t ev[kPool];
+  const char* name[kPool];   // nullptr: the start of a call
   int n = 0;
 };
 thread_local Timing g_tm;
 
 void tm_begin(hipStream_t s) {
   Timing& t = g_tm;
-  t.n = 0;
-  if (!t.enabled) return;
-  if (!t.created) {
-    for (int i = 0; i < kMaxMarks; ++i) (void)hipEventCreate(&t.ev[i]);
-    t.created = true;
-  }
-  (void)hipEventRecord(t.ev[0], s);
-  t.name[0] = "";
-  t.n = 1;
+  if (!t.enabled || !t.created || t.n >= kPool) return;
+  (void)hipEventRecord(t.ev[t.n], s);
+  t.name[t.n] = nullptr;
+  ++t.n;
 }
-
-void tm_reset() { g_tm.n = 0; }
 
 void tm_mark(hipStream_t s, const char* stage) {
   Timing& t = g_tm;
-  if (!t.enabled || t.n == 0 || t.n >= kMaxMarks) return;
+  if (!t.enabled || t.n == 0 || t.n >= kPool) return;
   (void)hipEventRecord(t.ev[t.n], s);
   t.name[t.n] = stage;
   ++t.n;
@@ -340,24 +336,48 @@ extern "C" {
 int pairattn_version(void) { return 10100; }
 
 int pairattn_timing_enable(int enable) {
-  const int prev = g_tm.enabled ? 1 : 0;
-  g_tm.enabled = enable != 0;
-  g_tm.n = 0;
+  Timing& t = g_tm;
+  const int prev = t.enabled ? 1 : 0;
+  if (enable && !t.created) {
+    for (int i = 0; i < kPool; ++i)
+      if (hipEventCreate(&t.ev[i]) != hipSuccess) {
+        for (int j = 0; j < i; ++j) (void)hipEventDestroy(t.ev[j]);
+        return -PAIRATTN_ERR_HIP;
+      }
+    t.created = true;
+  }
+  t.enabled = enable != 0;
+  t.n = 0;
   return prev;
 }
 
 int pairattn_timing_read(float* ms, const char** names, int cap) {
   Timing& t = g_tm;
-  if (!t.enabled || t.n < 2) return 0;
+  if (!t.enabled || t.n < 2) {
+    t.n = 0;
+    return 0;
+  }
   if (hipEventSynchronize(t.ev[t.n - 1]) != hipSuccess) return -PAIRATTN_ERR_HIP;
   int k = 0;
-  for (int i = 1; i < t.n && k < cap; ++i, ++k) {
+  for (int i = 1; i < t.n && k < cap; ++i) {
+    if (t.name[i] == nullptr) continue;   // the start of the next call
     float v = 0.0f;
     if (hipEventElapsedTime(&v, t.ev[i - 1], t.ev[i]) != hipSuccess) return -PAIRATTN_ERR_HIP;
     if (ms != nullptr) ms[k] = v;
     if (names != nullptr) names[k] = t.name[i];
+    ++k;
   }
+  t.n = 0;
   return k;
+}
+
+int pairattn_calibrate_exp2(float* out, int64_t iters, void* stream) {
+  g_err[0] = '\0';
+  if (out == nullptr || !aligned16(out)) return fail(PAIRATTN_ERR_ARG, "out must be a 16-byte aligned device pointer");
+  if (iters < 1 || iters > (1LL << 24)) return fail(PAIRATTN_ERR_ARG, "iters must be in [1, 2^24]");
+  int num_cu = 0;
+  PA_TRY(check_device(&num_cu));
+  return hip_status(pa::launch_calib_exp2(out, (int)iters, static_cast<hipStream_t>(stream)), "exp2 calibration launch");
 }
 
 const char* pairattn_status_string(int status) {
@@ -845,7 +865,6 @@ int pairattn_tri_fwd_noalloc(const void* z, const uint8_t* mask, const pairattn_
   PA_TRY(scratch_for_current_device(&ws));
   int num_cu = 0;
   PA_TRY(check_device(&num_cu));
-  tm_reset();   // no timing marks: recording them would create events
   pairattn_params q = *p;
   q.workspace = ws;
   q.workspace_bytes = kScratchBytes;

@@ -102,6 +102,7 @@ _SIGNATURES = {
     "pairattn_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "pairattn_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p),
                                             ctypes.c_int]),
+    "pairattn_calibrate_exp2": (ctypes.c_int, [_P, _I64, _P]),
 }
 
 
@@ -280,11 +281,20 @@ def pairattn_validate_rows(z_rows, bias, mask_rows, params, out_rows, R, I, c_z,
 
 
 def pairattn_timing_enable(enable: bool) -> bool:
-    return bool(load().pairattn_timing_enable(1 if enable else 0))
+    st = load().pairattn_timing_enable(1 if enable else 0)
+    if st < 0:
+        raise PairAttnError(-st, "pairattn_timing_enable", last_error())
+    return bool(st)
 
 
-def pairattn_timing_read(cap: int = 8) -> list:
-    """[(stage name, ms), ...] of the last call on this thread (waits for it)."""
+def pairattn_calibrate_exp2(out, iters: int, stream=None, check=True) -> int:
+    st = load().pairattn_calibrate_exp2(_ptr(out), iters, _stream(stream))
+    return _check(st, "pairattn_calibrate_exp2") if check else st
+
+
+def pairattn_timing_read(cap: int = 1024) -> list:
+    """[(stage name, ms), ...] of every call on this thread since the last
+    read, in launch order (waits for the last one)."""
     ms = (ctypes.c_float * cap)()
     names = (ctypes.c_char_p * cap)()
     n = load().pairattn_timing_read(ms, names, cap)

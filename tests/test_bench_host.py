@@ -92,3 +92,72 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_second_roof_counts():
+    # one exp2 per (row, head, query, key): 1536^3 * 4 = 1.45e10 per launch
+    assert bench.softmax_elements(1536, 1536, 4) == 1536 ** 3 * 4
+    # nominal exp2 issue ceiling: 1024 SIMDs x 64 lanes / 8 cycles at 2.4 GHz
+    assert bench.PEAK_EXP2_PER_S == pytest.approx(1.96608e13)
+
+
+def test_stream_rates_i1536():
+    s = bench.stream_rates(1536, 1536, 128, 4, 32, attn_ms=3.0, proj_ms=0.75)
+    assert s["bias"]["bytes"] == 2 * 4 * 1536 * 1536                      # fp16 [H][Pp][Pp]
+    assert s["gate"]["bytes"] == 2 * 1536 * 1536 * 128                     # fp16, H d per pair
+    assert s["bias"]["copied_to_lds_bytes_per_attention_launch"] == s["bias"]["bytes"] * 768
+    assert s["gate"]["read_gbs_over_attention"] == pytest.approx(s["gate"]["bytes"] / 3e-3 / 1e9)
+    # padded sizes: I = 100 pads to 128 positions
+    s = bench.stream_rates(100, 100, 128, 4, 32, 1.0, 1.0)
+    assert s["bias"]["bytes"] == 2 * 4 * 128 * 128
+
+
+class _FakeLib:
+    """Records enable calls and returns canned marks (two calls of a step)."""
+
+    def __init__(self, marks):
+        self.marks, self.enabled = marks, []
+
+    def pairattn_timing_enable(self, on):
+        self.enabled.append(on)
+
+    def pairattn_timing_read(self):
+        return self.marks
+
+
+class _FakeEvent:
+    def __init__(self, enable_timing=True):
+        pass
+
+    def record(self, stream=None):
+        pass
+
+    def elapsed_time(self, other):
+        return 8.0
+
+
+class _FakeTorch:
+    class cuda:
+        Event = _FakeEvent
+
+        @staticmethod
+        def synchronize():
+            pass
+
+
+def test_per_kernel_pass_groups_calls_by_pack_mark():
+    marks = [("pack", 0.01), ("projection", 0.7), ("attention", 3.0),
+             ("pack", 0.01), ("projection", 0.8), ("mask_bits", 0.02), ("attention", 3.2)] * 2
+    L = _FakeLib(marks)
+    steps = []
+    out = bench.per_kernel_pass(L, _FakeTorch, None, lambda: steps.append(1), 2, ("start_", "end_"))
+    assert L.enabled == [True, False] and len(steps) == 2
+    assert out["_step_ms"] == 4.0
+    assert out["start_attention"] == [3.0, 3.0] and out["end_attention"] == [3.2, 3.2]
+    assert out["end_mask_bits"] == [0.02, 0.02] and "start_mask_bits" not in out
+
+
+def test_cpu_info_names_the_host():
+    info = bench.cpu_info()
+    assert info["logical_cpus"] >= 1
+    assert set(info) == {"cpu_model", "logical_cpus", "affinity_cpus"}
