@@ -111,11 +111,51 @@ __device__ __forceinline__ f32x16 widen_bias(const f16x8& b0, const f16x8& b1, c
   return __builtin_shufflevector(c01, c23, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
 }
 
+// Lane mask of accumulator register j (key k0 = (j/4)*8 + j%4 in lane half 0,
+// key k0 + 4 in lane half 1) from a block's keep bits: each half is bit k0
+// (or k0 + 4) sign-extended to 32 bits, one scalar bit-field extract each.
+// Volatile, so that the compiler computes each mask where it is used instead
+// of keeping all 16 of a block alive in scalar registers across the units.
+template <int K0>
+__device__ __forceinline__ uint64_t key_lanes(uint32_t bits) {
+  uint32_t lo, hi;
+  asm volatile("s_bfe_i32 %0, %2, %3\n\ts_bfe_i32 %1, %2, %4"
+               : "=s"(lo), "=s"(hi)
+               : "s"(bits), "i"(K0 | (1 << 16)), "i"((K0 + 4) | (1 << 16)));
+  return ((uint64_t)hi << 32) | lo;
+}
+template <int J>
+__device__ __forceinline__ float keep_reg(float s, uint32_t bits);
+
 // s where bit `lane` of the wave-uniform mask is set, else -inf: one
 // v_cndmask with the mask as its scalar condition.  (A compiler builtin, not
 // inline asm, so that the wait states after the MFMA producing s are known.)
 __device__ __forceinline__ float keep_or_neg_inf(float s, uint64_t lanes) {
   return __builtin_amdgcn_inverse_ballot_w64(lanes) ? s : -__builtin_inff();
+}
+// accumulator register J of a unit, -inf where its key is masked
+template <int J>
+__device__ __forceinline__ float keep_reg(float s, uint32_t bits) {
+  return keep_or_neg_inf(s, key_lanes<(J >> 2) * 8 + (J & 3)>(bits));
+}
+// all 16 registers of a unit's S^T accumulator
+__device__ __forceinline__ void keep_unit(f32x16& S, uint32_t bits) {
+  S[0] = keep_reg<0>(S[0], bits);
+  S[1] = keep_reg<1>(S[1], bits);
+  S[2] = keep_reg<2>(S[2], bits);
+  S[3] = keep_reg<3>(S[3], bits);
+  S[4] = keep_reg<4>(S[4], bits);
+  S[5] = keep_reg<5>(S[5], bits);
+  S[6] = keep_reg<6>(S[6], bits);
+  S[7] = keep_reg<7>(S[7], bits);
+  S[8] = keep_reg<8>(S[8], bits);
+  S[9] = keep_reg<9>(S[9], bits);
+  S[10] = keep_reg<10>(S[10], bits);
+  S[11] = keep_reg<11>(S[11], bits);
+  S[12] = keep_reg<12>(S[12], bits);
+  S[13] = keep_reg<13>(S[13], bits);
+  S[14] = keep_reg<14>(S[14], bits);
+  S[15] = keep_reg<15>(S[15], bits);
 }
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -174,7 +214,7 @@ template <int H, int C_OUT, bool HAS_MASK, int MODE>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(
     const f16* __restrict__ q_ws, const f16* __restrict__ k_ws, const f16* __restrict__ v_ws,
     const f16* __restrict__ g_ws, const f16* __restrict__ bias, const uint32_t* __restrict__ mask_bits,
-    const f16* __restrict__ woT, const bf16* __restrict__ b_o, bf16* __restrict__ out, int64_t os_r,
+    const int* __restrict__ mask_range, const f16* __restrict__ woT, const bf16* __restrict__ b_o, bf16* __restrict__ out, int64_t os_r,
     int64_t os_p, int nrows, int P, int Pp, int n_qg, int n_rg, int nbq_in, int Pk_in, int nbk_in,
     float* __restrict__ o_part, float* __restrict__ lse_part) {
   static_assert(MODE >= 0 && MODE <= 2, "mode");
@@ -450,14 +490,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             // Register j holds key (j/4)*8 + g*4 + j%4: its keep bit depends only
             // on the lane half g, so the select's lane mask is built on the
             // scalar unit (no per-lane bit tests).
-            const uint32_t b = bits_cur[rr];
-    #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const int k0 = (j >> 2) * 8 + (j & 3);
-              const uint64_t lanes = (((b >> k0) & 1u) ? 0x00000000ffffffffull : 0ull) |
-                                     (((b >> (k0 + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
-              S[j] = keep_or_neg_inf(S[j], lanes);
-            }
+            keep_unit(S, bits_cur[rr]);
           }
           if (!FAST && shifted[rr]) {
     #pragma unroll
@@ -547,16 +580,26 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // one finishes its block early and idles at the barrier while the younger
   // one runs the rest alone; with the ladder the wave that is behind in the
   // block wins the issue arbitration, and both reach the barrier together.
-  auto sweep_pipe = [&](auto anyc) {
-   // ANY: P is not a multiple of 32, so the last block holds keys past P
-   constexpr bool ANY = decltype(anyc)::value;
+  //
+  // The sweep runs over key blocks [lo, hi): every kept key of the
+  // workgroup's rows lies there, so the blocks outside hold none and are
+  // skipped (the fast sweep's sums do not depend on which blocks without a
+  // kept key are left out).
+  //   KMODE 0: no mask, P a multiple of 32 (lo = 0, hi = nkb): no select
+  //   KMODE 1: no mask, only the last block holds keys past P
+  //   KMODE 2: a mask; lo, hi from the rows' ranges; every block runs the
+  //            masked streams, where a block whose keys are all kept skips
+  //            the select on a uniform branch.  (Separate unmasked and
+  //            masked loops in one kernel need more than 256 registers, and
+  //            the spill reloads would drain the copies in flight.)
+  auto sweep_pipe = [&](auto kmodec, int lo, int hi) {
+   constexpr int KMODE = decltype(kmodec)::value;
    if constexpr (QW == 2 && RW == 2 && NCW == 4) {
     using T = std::integral_constant<bool, true>;
     using F = std::integral_constant<bool, false>;
     f32x4 lacc[RW][QW];   // row sums of the sweep (every element holds the lane's sum)
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
-      row_has_key[rr] = true;   // P >= 1: every row has a kept key
 #pragma unroll
       for (int qq = 0; qq < QW; ++qq) {
         O[rr][qq] = f32x16{};
@@ -614,13 +657,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       f16x8 p0, p1;
       f32x16 S = S_in;
       if constexpr (MASKED) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int k0 = (j >> 2) * 8 + (j & 3);
-          const uint64_t lanes = (((bits >> k0) & 1u) ? 0x00000000ffffffffull : 0ull) |
-                                 (((bits >> (k0 + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
-          S[j] = keep_or_neg_inf(S[j], lanes);
-        }
+        if (bits != 0xffffffffu) keep_unit(S, bits);   // uniform: a block with every key kept skips the select
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -659,11 +696,11 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     Regs ra;
     f32x16 S_pipe, C_pipe;   // logits of the unit the next stream runs; bias accumulator of its query block
 
-    // prologue: stages of blocks 0 and 1 and Q land together (one latency
-    // instead of two), barrier, block 0 in registers
-    copy_b(0);
-    copy_kv(0, 0, NCW);
-    copy_kv(1, 0, NCW);
+    // prologue: stages of blocks lo and lo+1 and Q land together (one
+    // latency instead of two), barrier, block lo in registers
+    copy_b(lo);
+    copy_kv(lo, 0, NCW);
+    copy_kv(lo + 1, 0, NCW);
     wait_q();
     barrier();
     {
@@ -671,17 +708,17 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
       for (int rr = 0; rr < RW; ++rr)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) ra.K[rr][c] = lds_f16x8(kv_tile(0, rr) + c * 1024);
+        for (int c = 0; c < 2; ++c) ra.K[rr][c] = lds_f16x8(kv_tile(lo, rr) + c * 1024);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) B0[c] = lds_f16x8(b_tile(0, 0) + c * 1024);
-      copy_b(1);
-      copy_kv(2, 0, 2);
+      for (int c = 0; c < 2; ++c) B0[c] = lds_f16x8(b_tile(lo, 0) + c * 1024);
+      copy_b(lo + 1);
+      copy_kv(lo + 2, 0, 2);
 #pragma unroll
       for (int rr = 0; rr < RW; ++rr)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) ra.V[rr][c] = lds_f16x8(kv_tile(0, rr) + 2048 + c * 1024);
+        for (int c = 0; c < 2; ++c) ra.V[rr][c] = lds_f16x8(kv_tile(lo, rr) + 2048 + c * 1024);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) ra.B1[c] = lds_f16x8(b_tile(0, 1) + c * 1024);
+      for (int c = 0; c < 2; ++c) ra.B1[c] = lds_f16x8(b_tile(lo, 1) + c * 1024);
       C_pipe = cvt_bias(B0);
       S_pipe = mfma32(ra.K[0][1], Q[0][0][1], mfma32(ra.K[0][0], Q[0][0][0], C_pipe));
     }
@@ -740,15 +777,17 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         S_pipe = Sn;
       }
     };
-    if constexpr (!ANY) {
-      for (int kb = 0; kb + 1 < nkb; ++kb) block(kb, T{}, F{}, ra, ~0u, ~0u);
-      block(nkb - 1, F{}, F{}, ra, ~0u, ~0u);
+    int kb = lo;
+    if constexpr (KMODE == 0) {
+      for (; kb + 1 < hi; ++kb) block(kb, T{}, F{}, ra, ~0u, ~0u);
+      block(kb, F{}, F{}, ra, ~0u, ~0u);
+    } else if constexpr (KMODE == 1) {
+      for (; kb + 1 < hi; ++kb) block(kb, T{}, F{}, ra, ~0u, ~0u);
+      const uint32_t bl = keep_bits(0, kb);   // the last block: keys past P dropped
+      block(kb, F{}, T{}, ra, bl, bl);
     } else {
-      // only the last block holds keys past P (no mask here)
-      static_assert(!HAS_MASK, "masked inputs take the generic sweep");
-      for (int kb = 0; kb + 1 < nkb; ++kb) block(kb, T{}, F{}, ra, ~0u, ~0u);
-      const uint32_t bl = keep_bits(0, nkb - 1);
-      block(nkb - 1, F{}, T{}, ra, bl, bl);
+      for (; kb + 1 < hi; ++kb) block(kb, T{}, T{}, ra, keep_bits(0, kb), keep_bits(1, kb));
+      block(kb, F{}, T{}, ra, keep_bits(0, kb), keep_bits(1, kb));
     }
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
@@ -759,10 +798,40 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   };
 
   bool epi_loaded = false;
-  if constexpr (H == 4 && !HAS_MASK) {
-    if (Pk == nkb * 32) sweep_pipe(std::integral_constant<bool, false>{});
-    else sweep_pipe(std::integral_constant<bool, true>{});
-    epi_loaded = true;
+  if constexpr (H == 4) {
+    if constexpr (!HAS_MASK) {
+#pragma unroll
+      for (int rr = 0; rr < RW; ++rr) row_has_key[rr] = true;   // P >= 1: every row has a kept key
+      if (Pk == nkb * 32) sweep_pipe(std::integral_constant<int, 0>{}, 0, nkb);
+      else sweep_pipe(std::integral_constant<int, 1>{}, 0, nkb);
+      epi_loaded = true;
+    } else {
+      // key-block range of each row: [lo, hi) holds its kept keys (lo = nkb,
+      // hi = 0 without any)
+      int rlo[RW], rhi[RW];
+#pragma unroll
+      for (int rr = 0; rr < RW; ++rr) {
+        const int* rg = mask_range + (int64_t)rows_c[rr] * 2;
+        rlo[rr] = rg[0];
+        rhi[rr] = rg[1];
+        row_has_key[rr] = rlo[rr] < rhi[rr];
+      }
+      const int lo = min(rlo[0], rlo[1]), hi = max(rhi[0], rhi[1]);
+      if (lo < hi) {
+        sweep_pipe(std::integral_constant<int, 2>{}, lo, hi);
+        epi_loaded = true;
+      } else {   // no kept key in either row: o = 0
+        wait_q();
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+          for (int qq = 0; qq < QW; ++qq) {
+            O[rr][qq] = f32x16{};
+            m_sh[rr][qq] = 0.0f;
+            l_run[rr][qq] = 0.0f;
+          }
+      }
+    }
   } else {
     sweep(std::integral_constant<bool, true>{});
   }
@@ -954,12 +1023,40 @@ __global__ void mask_bits_kernel(const uint8_t* __restrict__ mask, int64_t ms_r,
   }
 }
 
+// Key-block range of each row from its keep bits, one wave per row:
+// range[2r] = lo, the first block with a kept key (nkb if none);
+// range[2r+1] = hi, one past the last such block (0 if none).
+__global__ void mask_range_kernel(const uint32_t* __restrict__ bits, int nrows, int nkb, int* __restrict__ range) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t row = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / kWave;
+  if (row >= nrows) return;   // uniform over the wave
+  const uint32_t* w = bits + row * nkb;
+  int lo = nkb, hi = 0;
+  for (int base = 0; base < nkb; base += kWave) {
+    const int kb = base + lane;
+    const uint64_t ne = __ballot(kb < nkb && w[kb] != 0u);
+    if (ne != 0) {
+      if (lo == nkb) lo = base + __builtin_ctzll(ne);
+      hi = base + kWave - __builtin_clzll(ne);
+    }
+  }
+  if (lane == 0) {
+    range[row * 2 + 0] = lo;
+    range[row * 2 + 1] = hi;
+  }
+}
+
 hipError_t launch_mask_bits(const uint8_t* mask, int64_t ms_r, int64_t ms_k, uint32_t* bits, int nrows, int P,
                             int nkb, hipStream_t s) {
   const int64_t nwords = (int64_t)nrows * nkb;
   const int64_t waves = (nwords + 1) / 2;
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((waves + 3) / 4, 4096));
   hipLaunchKernelGGL(mask_bits_kernel, dim3(blocks), dim3(256), 0, s, mask, ms_r, ms_k, bits, nrows, P, nkb);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int rblocks = (int)(((int64_t)nrows + 3) / 4);   // 4 waves (rows) per block
+  hipLaunchKernelGGL(mask_range_kernel, dim3(rblocks), dim3(256), 0, s, bits, nrows, nkb,
+                     mask_range_of(bits, nrows, nkb));
   return hipGetLastError();
 }
 
@@ -1062,13 +1159,14 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
   if (n > 0x7fffffffLL) return hipErrorInvalidValue;   // one-dimensional grid
   hipLaunchKernelGGL((attn_kernel<H, C_OUT, HAS_MASK, MODE>), dim3((unsigned)n), dim3(512), 0, s,
                      (const f16*)a.q_ws, (const f16*)a.k_ws, (const f16*)a.v_ws, (const f16*)a.g_ws,
-                     (const f16*)a.bias, a.mask_bits, (const f16*)a.woT, (const bf16*)a.b_o, (bf16*)a.out, a.os_r,
+                     (const f16*)a.bias, a.mask_bits, a.mask_range, (const f16*)a.woT, (const bf16*)a.b_o, (bf16*)a.out, a.os_r,
                      a.os_p, a.nrows, a.P, a.Pp, n_qg, n_rg, nbq, Pk, nbk, a.o_part, a.lse_part);
   return hipGetLastError();
 }
 
 template <int H, int C_OUT, int MODE>
 static hipError_t attn_dispatch_m(const AttnArgs& a, hipStream_t s) {
+  if (a.mask_bits != nullptr && a.mask_range == nullptr) return hipErrorInvalidValue;   // ranges come with the bits
   return a.mask_bits != nullptr ? attn_dispatch<H, C_OUT, true, MODE>(a, s)
                                 : attn_dispatch<H, C_OUT, false, MODE>(a, s);
 }

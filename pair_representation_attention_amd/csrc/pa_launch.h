@@ -36,6 +36,7 @@ struct AttnArgs {
   const void *q_ws, *k_ws, *v_ws, *g_ws;
   const void* bias;              // attention layout (fp16, log2 units)
   const uint32_t* mask_bits;     // keep bits per (row, 32-key block), see launch_mask_bits; NULL = no mask
+  const int* mask_range;         // per row: first block with a kept key, one past the last (with mask_bits)
   const void *woT, *b_o;
   void* out;                     // element (r, p, c) at out[r*os_r + p*os_p + c]
   int64_t os_r, os_p;
@@ -62,9 +63,17 @@ hipError_t launch_calib_exp2(float* out, int iters, hipStream_t s);
 // gate (g_ws, layout of q), output projection and bf16 store of merged partial
 // outputs o_part (fields g_ws, woT, b_o, out, os_r, os_p, H, c_out, nrows, P, Pp, o_part)
 hipError_t launch_finish_bf16(const AttnArgs& a, hipStream_t s);
-// keep bits [nrows][nkb] for the bf16 attention (mask may be NULL: all keys < P kept)
+// keep bits [nrows][nkb] for the attention (mask may be NULL: all keys < P
+// kept), followed by each row's key-block range [nrows][2] (mask_range_of)
 hipError_t launch_mask_bits(const uint8_t* mask, int64_t ms_r, int64_t ms_k, uint32_t* bits, int nrows, int P,
                             int nkb, hipStream_t s);
+// workspace bytes of the keep bits and the ranges, and where the ranges start
+inline size_t mask_bits_bytes(int64_t nrows, int64_t nkb) {
+  return (size_t)((nrows * nkb + 3) / 4 * 4) * 4 + (size_t)nrows * 8;
+}
+inline int* mask_range_of(uint32_t* bits, int64_t nrows, int64_t nkb) {
+  return reinterpret_cast<int*>(bits + (nrows * nkb + 3) / 4 * 4);
+}
 
 // The fused end of the bf16 ring: out = (sigmoid(LN(x) W_g + b_g) * o) W_o + b_o
 // for query pairs x (element (r, p, ch) at x[r*xs_r + p*xs_p + ch]) and the

@@ -87,7 +87,7 @@ Layout make_layout(int64_t nrows, int64_t P, int64_t c_in, int64_t c_out, int64_
     L.g = take(2 * plane);                     // float, O^T tile images
     L.bias = take((size_t)H * Pp * Pp * 4);    // float, S^T tile images
   }
-  L.bits = take((size_t)nrows * (Pp / 32) * 4);
+  L.bits = take(pa::mask_bits_bytes(nrows, Pp / 32));
   L.total = off;
   return L;
 }
@@ -119,7 +119,7 @@ PartialLayout make_partial_layout(int64_t R, int64_t Jq, int64_t Kn, int64_t c, 
     L.k = take(kplane);
     L.v = take(kplane);
     L.bias = take((size_t)H * Ppq * Ppk * 2);   // fp16 operand order, log2 units
-    L.bits = take((size_t)R * (Ppk / 32) * 4);
+    L.bits = take(pa::mask_bits_bytes(R, Ppk / 32));
     L.total = off;
     return L;
   }
@@ -146,7 +146,7 @@ PartialLayout make_partial_layout(int64_t R, int64_t Jq, int64_t Kn, int64_t c, 
   L.v_lo = take(kplane);
   L.g = take(2 * qplane);
   L.bias = take((size_t)H * Ppq * Ppk * 4);
-  L.bits = take((size_t)R * (Ppk / 32) * 4);
+  L.bits = take(pa::mask_bits_bytes(R, Ppk / 32));
   L.total = off;
   return L;
 }
@@ -677,6 +677,7 @@ static int run_row_attention_bf16(const pairattn_params* p, const Layout& L, hip
   // the keys past P, which it computes)
   uint32_t* bits = reinterpret_cast<uint32_t*>(ws_at(p, L.bits));
   at.mask_bits = ra.mask != nullptr ? bits : nullptr;
+  at.mask_range = ra.mask != nullptr ? pa::mask_range_of(bits, ra.nrows, Pp / 32) : nullptr;
   at.woT = ws_at(p, L.woT);
   at.b_o = p->b_o;
   at.out = ra.out;
@@ -1118,6 +1119,7 @@ int pairattn_tri_partial_fwd(const void* q_pairs, const void* kv_pairs, const fl
     at.v_ws = ws_at(p, L.v);
     at.bias = bias_ws;
     at.mask_bits = mask != nullptr ? bits : nullptr;
+    at.mask_range = mask != nullptr ? pa::mask_range_of(bits, R, Ppk / 32) : nullptr;
     at.H = (int)H;
     at.c_out = (int)c_z;
     at.nrows = (int)R;

@@ -62,6 +62,67 @@ def test_tri_other_widths(c, H):
 
 
 # ----------------------------------------------------------------------------
+# masks whose 32-key blocks are all kept, all masked or mixed, row by row.
+# The bf16 kernel sweeps only the blocks between the first and the last one
+# with a kept key in either row of a workgroup (rows 2r and 2r+1), runs every
+# block there through its masked units, and skips the select where all 32
+# keys are kept; rows without a kept key skip the sweep.  The patterns below
+# put leading and trailing empty blocks, empty blocks in the middle, full
+# blocks, single kept keys, fully masked rows and rows whose partner row
+# differs into one mask (START reads its rows, END its columns).
+# ----------------------------------------------------------------------------
+def _block_mix_mask(I: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    nb = (I + 31) // 32
+    m = np.zeros((I, I), np.uint8)
+    for i in range(I):
+        kind = i % 8
+        if kind == 0:                       # every key
+            m[i, :] = 1
+        elif kind == 1:                     # a prefix ending inside a block (the padding pattern)
+            m[i, : rng.integers(1, I)] = 1
+        elif kind == 2:                     # nothing: out = b_o
+            pass
+        elif kind == 3:                     # a suffix starting inside a block (leading empty blocks)
+            m[i, rng.integers(0, I):] = 1
+        elif kind == 4:                     # random blocks fully kept, fully masked or Bernoulli
+            for b in range(nb):
+                r = rng.integers(0, 3)
+                sl = slice(b * 32, min(I, b * 32 + 32))
+                m[i, sl] = 1 if r == 0 else (0 if r == 1 else (rng.random(sl.stop - sl.start) < 0.5))
+        elif kind == 5:                     # one kept key
+            m[i, rng.integers(0, I)] = 1
+        elif kind == 6:                     # two kept runs with empty blocks between them
+            a = rng.integers(0, max(1, I // 4))
+            b = rng.integers(I // 2, I)
+            m[i, a: a + 40] = 1
+            m[i, b:] = 1
+        else:                               # Bernoulli(0.95)
+            m[i, :] = rng.random(I) < 0.95
+    return m
+
+
+@pytest.mark.parametrize("I", [160, 200, 384])
+def test_block_mixed_masks(I):
+    case = inputs.make_tri_case(I=I, c=128, H=4, d=32, dtype="bf16", mask="none", seed=300 + I, affine=True,
+                                biases=True)
+    rows = _block_mix_mask(I, seed=I)      # line i: the keys of attention row i
+    dev = _dev()
+    for ori, p in ((0, case.params_start), (1, case.params_end)):
+        # START keeps key k of row i iff mask[i, k]; END keeps key k of column j iff mask[k, j]
+        mask = rows if ori == 0 else np.ascontiguousarray(rows.T)
+        got = gpu_to_f64(dev.TriRunner(case.z, mask, p, 4, "bf16")(ori))
+        ref = oracle.tri_fwd(case.z, mask, p.as_dict(), 4, ori)
+        check(got, ref, "bf16", f"block-mixed mask I={I} ori={ori}")
+        # rows (START) or columns (END) without a kept key give out = b_o exactly
+        none = np.where(~rows.any(axis=1))[0]
+        assert len(none) > 0
+        bo = inputs.round_to_bf16(p.b_o.astype(np.float32)).astype(np.float64)
+        sel = got[none, :, :] if ori == 0 else got[:, none, :]
+        assert np.array_equal(sel, np.broadcast_to(bo, sel.shape))
+
+
+# ----------------------------------------------------------------------------
 # logits far from zero: the kernel's zero-shift sweep cannot represent the
 # softmax weights there (fp16 overflow above 2^16, too little mass below), so
 # the workgroup sweeps again with per-query shifts.  The pair-bias offset is
