@@ -71,8 +71,12 @@ def test_cfg_tri_bf16_i16384_chunked():
     p = inputs.make_chunked_params(c, H, d, cfg["seed"])
     run = _dev().TriChunkedRunner(z, None, p, H, "bf16", block)
     print(f"[cfg chunked] workspace {run.workspace_bytes / 1e9:.1f} GB", flush=True)
-    lines = np.array([0, 1023, 1024, 8191, I - 1])     # rows (START) / columns (END), across blocks
-    queries = np.array([0, 5, 4097, I - 2])
+    # two lines (an even row and the next, the bf16 kernel's workgroup pair)
+    # in each of the 16 blocks, at positions that move through the block
+    lines = np.array(sorted({b * block + off + e for b in range(I // block)
+                             for off in [(b * 389) % (block - 1) & ~1] for e in (0, 1)} | {0, I - 1}))
+    assert all(len([x for x in lines if x // block == b]) >= 2 for b in range(I // block))
+    queries = np.array([0, 5, 1023, 1024, 4097, 8190, 12001, I - 2])
     pd = p.as_dict()
     for ori in (0, 1):
         got = run(ori)

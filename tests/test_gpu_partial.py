@@ -326,8 +326,9 @@ def test_cfg_ring_i1536_grid2x2(dtype):
                                      c, H, d)
     lib.pairattn_tri_partial_finish(zq, o, prm, out, half, half, c, H, d)
     torch.cuda.synchronize()
-    rows = np.array([0, 401, half - 1])
-    queries = np.array([0, 5, 700, half - 1])
+    # both rows of 5 workgroup pairs across the tile; queries in 6 of its 24 query blocks
+    rows = np.array([0, 1, 200, 201, 383, 384, 590, 591, half - 2, half - 1])
+    queries = np.array([0, 5, 31, 32, 300, 511, 512, 700, half - 1])
     g = out[torch.as_tensor(rows, device="cuda")][:, torch.as_tensor(queries, device="cuda")]
     pd = p.as_dict()
     zr = z[torch.as_tensor(rows, device="cuda")].float().cpu().numpy().astype(np.float64)
