@@ -44,9 +44,13 @@
  *     product is formed from fp16 pairs (hi = fp16(x), lo = fp16(x - hi);
  *     hi.hi + hi.lo + lo.hi on the fp16 matrix cores, fp32 accumulation), so
  *     each product carries a relative error below 2^-21.  On both paths
- *     intermediate values (normalised activations, q, k, v, the softmax
- *     weights, the gated o) must stay below 65504 in magnitude, the fp16
- *     range; inputs in the usual ranges of these models do.
+ *     intermediate values (normalised activations, gamma o W, q, k, v, the
+ *     pair bias in log2 units, the softmax weights, the gated o) must stay
+ *     below 65504 in magnitude, the fp16 range; inputs in the usual ranges of
+ *     these models do.  Beyond it, PAIRATTN_BF16 saturates them at +-65504:
+ *     the output stays finite and the same on every call, but it is no
+ *     longer the method's result, and the call still returns PAIRATTN_OK.
+ *     On PAIRATTN_F32 they overflow to infinity.
  *   - Supported shapes: d = 32; H in {4, 8}; c, c_m, c_z in {64, 128, 256};
  *     any I >= 1, S >= 1, R >= 1.  Anything else returns
  *     PAIRATTN_ERR_UNSUPPORTED; there is no fallback path.

@@ -5,8 +5,9 @@ the same name.  Tensors may be torch tensors (their device pointer is
 passed), raw integer addresses, or None (NULL).  PyTorch is used for device
 memory and streams; no computation happens here.
 
-The shared library is loaded on first use from this package directory and
-a missing library raises ``PairAttnLibraryMissing``: there is no fallback.
+The shared library is loaded on first use from this package directory (or
+from the path in PAIRATTN_LIB, e.g. the host-sanitized build) and a missing
+library raises ``PairAttnLibraryMissing``: there is no fallback.
 """
 from __future__ import annotations
 
@@ -111,7 +112,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    path = path or LIB_PATH
+    path = path or os.environ.get("PAIRATTN_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise PairAttnLibraryMissing(
             f"{path} not found: build it with `python -m pair_representation_attention_amd.build`")

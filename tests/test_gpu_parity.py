@@ -375,6 +375,35 @@ def test_bias_entry_point_matches_oracle():
     print(f"[bias] max err {err.max():.3e}, max err/bound {np.max(err / bound):.3f}", flush=True)
 
 
+@pytest.mark.parametrize("gamma", [2.0 ** 12, 2.0 ** 20])
+def test_fp16_range_edge_saturates_finite_and_deterministic(gamma):
+    """The bf16 path's intermediates at and beyond the fp16 range (documented
+    in pairattn.h).  gamma = 2^12 puts q, k and v near the edge (|k| ~ 4e3 x
+    N(0,1), logits ~ 1e7, far past where the zero-shift sweep holds: the
+    shifted rerun);
+    gamma = 2^20 puts gamma o W and every q, k, v past 65504, so they
+    saturate.  Either way the output must be finite, equal on every call,
+    and within the largest magnitude the saturated operands allow."""
+    case = inputs.make_tri_case(I=64, c=128, H=4, d=32, dtype="bf16", mask="random", seed=41, affine=True,
+                                biases=True)
+    p = case.params_start
+    p.ln_gamma = np.full(128, gamma, np.float32)          # a power of two: bf16-exact
+    dev = _dev()
+    for ori in (0, 1):
+        run = dev.TriRunner(case.z, case.mask, p, 4, "bf16")
+        a = run(ori).clone()
+        b = run(ori).clone()
+        torch.cuda.synchronize()
+        g = gpu_to_f64(a)
+        assert np.all(np.isfinite(g)), f"gamma={gamma} ori={ori}: non-finite output"
+        assert torch.equal(a, b), f"gamma={gamma} ori={ori}: not deterministic"
+        # o is a convex combination of v (|v| <= 65504), the gate is at most 1:
+        # |out| <= 65504 * sum_c |W_o| + |b_o| per channel
+        lim = 65504.0 * np.abs(p.w_o.astype(np.float64)).sum(0) + np.abs(p.b_o.astype(np.float64))
+        assert np.all(np.abs(g) <= lim * (1 + 2 ** -7))
+        print(f"[range] gamma={gamma:g} ori={ori}: max |out| {np.abs(g).max():.3e}", flush=True)
+
+
 def test_deterministic_bitwise():
     case = inputs.make_tri_case(I=130, c=128, H=4, d=32, dtype="bf16", mask="random", seed=9)
     dev = _dev()
