@@ -290,8 +290,9 @@ def main() -> int:
     ap.add_argument("--extra", action="store_true",
                     help="also time the fp32 I=64 and padded I=384 triangle configurations, the padded I=1536 "
                          "module, MSA row attention, the row block and the extra-MSA fp32 workload")
-    ap.add_argument("--workload", choices=["tri_bf16_i1536", "msa_fp32_s5120_i384", "tri_bf16_i16384_chunked",
-                                           "ring_fp32_i1536_grid2x2", "ring_bf16_i1536_grid2x2"],
+    ap.add_argument("--workload", choices=["tri_bf16_i1536", "msa_bf16_s512_i384", "msa_fp32_s5120_i384",
+                                           "tri_bf16_i16384_chunked", "ring_fp32_i1536_grid2x2",
+                                           "ring_bf16_i1536_grid2x2", "tri_bf16_i384_pad", "tri_fp32_i64"],
                     default="tri_bf16_i1536",
                     help="time only the fp32 extra-MSA workload, or chunked triangle attention at I = 16384 "
                          "(one JSON line)")
@@ -329,7 +330,11 @@ def main() -> int:
     lib.load()
     if args.workload != "tri_bf16_i1536":
         fn = {"msa_fp32_s5120_i384": msa_fp32_workload, "tri_bf16_i16384_chunked": chunked_workload,
-              "ring_fp32_i1536_grid2x2": ring_workload, "ring_bf16_i1536_grid2x2": ring_workload}[args.workload]
+              "ring_fp32_i1536_grid2x2": ring_workload, "ring_bf16_i1536_grid2x2": ring_workload,
+              "msa_bf16_s512_i384": msa_bf16_workload,
+              "tri_bf16_i384_pad": lambda *a: tri_config_workload("tri_bf16_i384_pad", *a, np=np),
+              "tri_fp32_i64": lambda *a: tri_config_workload("tri_fp32_i64", *a, np=np, orientations=(0,))}[
+            args.workload]
         print(json.dumps({"workload": args.workload, **fn(args, device, inputs, lib, torch)}), flush=True)
         return 0
     cfg = inputs.CONFIGS["tri_bf16_i1536"]
@@ -523,6 +528,30 @@ def tri_config_workload(name, args, device, inputs, lib, torch, np, orientations
     return res
 
 
+def msa_bf16_workload(args, device, inputs, lib, torch) -> dict:
+    """MSA row attention with pair bias, bf16: M[512,384,256], Z[384,384,128],
+    H = 8, Bernoulli(0.95) keys: whole-call time and the per-kernel split."""
+    import numpy as np
+    cfg = inputs.CONFIGS["msa_bf16_s512_i384"]
+    log("MSA row attention S=512 I=384 bf16")
+    case = inputs.make_msa_case(S=cfg["S"], I=cfg["I"], c_m=cfg["c_m"], c_z=cfg["c_z"], H=cfg["H"], d=cfg["d"],
+                                dtype=cfg["dtype"], mask=cfg["mask"], seed=cfg["seed"])
+    run = device.MsaRunner(case.m, case.z, case.mask, case.params, cfg["H"], "bf16")
+    stream = torch.cuda.current_stream()
+    steps = max(3, args.steps)
+    ms = _time(run, steps, 2, torch)
+    st = per_kernel_pass(lib, torch, stream, lambda: run(stream), steps, ("",))
+    st.pop("_step_ms")
+    f = msa_module_flops(cfg["S"], cfg["I"], cfg["c_m"], cfg["c_z"], cfg["H"], cfg["d"])["total"]
+    fa = attn_kernel_flops(cfg["S"], cfg["I"], cfg["c_m"], cfg["H"], cfg["d"])
+    kern = {k: float(np.mean(v)) for k, v in sorted(st.items())}
+    res = {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12, "rows_per_s": cfg["S"] / (ms * 1e-3), "kernels_ms": kern,
+           "attention_tflops": fa / (kern["attention"] * 1e-3) / 1e12}
+    del run, case
+    torch.cuda.empty_cache()
+    return res
+
+
 def extra_workloads(args, device, inputs, lib, torch, np) -> dict:
     out = {}
     # the other triangle configurations: fp32 I = 64 (starting node) and the
@@ -532,16 +561,7 @@ def extra_workloads(args, device, inputs, lib, torch, np) -> dict:
     out["tri_bf16_i384_pad"] = tri_config_workload("tri_bf16_i384_pad", args, device, inputs, lib, torch, np)
     out["tri_bf16_i1536_pad"] = tri_config_workload("tri_bf16_i1536", args, device, inputs, lib, torch, np,
                                                     mask_override="pad")
-    cfg = inputs.CONFIGS["msa_bf16_s512_i384"]
-    log("extra: MSA row attention S=512 I=384")
-    case = inputs.make_msa_case(S=cfg["S"], I=cfg["I"], c_m=cfg["c_m"], c_z=cfg["c_z"], H=cfg["H"], d=cfg["d"],
-                                dtype=cfg["dtype"], mask=cfg["mask"], seed=cfg["seed"])
-    run = device.MsaRunner(case.m, case.z, case.mask, case.params, cfg["H"], "bf16")
-    ms = _time(run, max(3, args.steps), 2, torch)
-    f = msa_module_flops(cfg["S"], cfg["I"], cfg["c_m"], cfg["c_z"], cfg["H"], cfg["d"])["total"]
-    out["msa_bf16_s512_i384"] = {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12, "rows_per_s": cfg["S"] / (ms * 1e-3)}
-    del run
-    torch.cuda.empty_cache()
+    out["msa_bf16_s512_i384"] = msa_bf16_workload(args, device, inputs, lib, torch)
 
     # row block: 512 starting-node rows of Z[4096,4096,128], bias from the whole Z
     cfg = inputs.CONFIGS["rows_bf16_i4096_r512"]

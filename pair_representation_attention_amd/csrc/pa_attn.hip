@@ -11,7 +11,7 @@
 //   unit = 32 queries x 32 keys of one (row, head)
 //   workgroup = 8 waves covering RWG rows x QWG query blocks x H heads
 //     H = 4: RWG = 2, QWG = 4, wave = (head, query-block pair), 2 x 2 units per key block
-//     H = 8: RWG = 1, QWG = 2, wave = head (both query blocks),  1 x 2 units per key block
+//     H = 8: RWG = 1, QWG = 3, wave = head (all 3 query blocks), 1 x 3 units per key block
 //   per key block and unit (S^T is keys x queries, log2 units):
 //     S^T = K Q^T + C      two MFMAs; C = the fp16 bias tile widened to fp32
 //                          by four 4x4x4 MFMAs (shared by the workgroup's rows)
@@ -34,7 +34,7 @@
 // ds_read_b128, and the S^T accumulator (rows = keys in natural order) is
 // already the K-slot order of the P operand.
 // Bytes moved per unit: 4 KB K/V / 4 query blocks + 2 KB bias / 2 rows (H = 4),
-// 4 KB K/V / 2 query blocks + 2 KB bias (H = 8).
+// 4 KB K/V / 3 query blocks + 2 KB bias (H = 8).
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -177,7 +177,10 @@ __device__ __forceinline__ float sum16_f16(const f16x8& a, const f16x8& b) {
 
 template <int H>
 struct AttnShape {
-  static constexpr int QW = 2;                     // query blocks per wave
+  // query blocks per wave: 3 at H = 8 (fewer workgroups, so fewer reloads of
+  // K/V and of the 256-wide W_o per query; its 48 KB bias stages leave room
+  // for a K/V ring two stages deep)
+  static constexpr int QW = H == 8 ? 3 : 2;
   static constexpr int QG = 8 / H;                 // query-block groups per workgroup
   static constexpr int QWG = QW * QG;              // query blocks per workgroup
   // rows per workgroup (every wave does all): 2 at H = 4; 1 at H = 8, so
@@ -188,7 +191,7 @@ struct AttnShape {
   static constexpr int KV_STAGE = RWG * H * KV_TILE;   // 32 KB
   static constexpr int B_STAGE = QWG * H * B_TILE;     // 32 KB
   // K/V ring of NKV stages (NKV-1 key blocks ahead), bias ring of 2 (one
-  // block ahead): 3 x 32 + 2 x 32 KB
+  // block ahead): 3 x 32 + 2 x 32 KB at H = 4, 2 x 32 + 2 x 48 KB at H = 8
   static constexpr int NKV = 3 * KV_STAGE + 2 * B_STAGE <= 160 * 1024 ? 3 : 2;
   static constexpr int LDS_KV = NKV * KV_STAGE;
   static constexpr int LDS_B = 2 * B_STAGE;
@@ -475,7 +478,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
           // the pipelined sweep: the wave that is behind in the block wins
           // the issue arbitration)
           if (u == 0) __builtin_amdgcn_s_setprio(3);
-          else if (u == 1) __builtin_amdgcn_s_setprio(NU == 4 ? 2 : 0);
+          else if (u == 1) __builtin_amdgcn_s_setprio(NU >= 3 ? 2 : 0);
           else if (u == 2) __builtin_amdgcn_s_setprio(1);
           else __builtin_amdgcn_s_setprio(0);
           copies_for_unit(kb, u);
