@@ -48,6 +48,22 @@ __device__ __forceinline__ f16 f2h_sat(float v) { return (f16)__builtin_fminf(__
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// sigmoid(x) = 1 / (1 + e^-x) with the hardware reciprocal (1 ulp) instead of
+// an IEEE division (about ten instructions): exact to fp32 rounding for the
+// gate, which is then rounded to fp16 (bf16 path) or used in fp32.  Large
+// negative x gives rcp(inf) = 0, large positive x gives 1.
+__device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
+// The bf16 path packs the gate columns of the projection scaled by -log2(e)
+// (and the q columns by log2(e)/sqrt(d), d = 32): for such a column,
+// t = -x log2(e) and sigmoid(x) = 1 / (1 + 2^t).
+__host__ __device__ constexpr float column_scale(int tensor) {
+  return tensor == 0 ? 0.2550348616f : tensor == 3 ? -1.4426950409f : 1.0f;
+}
+__device__ __forceinline__ float sigmoid_from_log2(float t) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+}
+
 // ---------------------------------------------------------------------------
 // Operand-ordered workspace layouts of the bf16 path.  Each 1 KB chunk is the
 // register image of one MFMA operand for a wave (lane l owns bytes l*16..+16),

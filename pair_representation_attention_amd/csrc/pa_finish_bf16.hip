@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void finish_fused_kernel(
         f16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float gate = 1.0f / (1.0f + __expf(-(acc[jj * 4 + e] + cc[e])));
+          const float gate = sigmoid_from_log2(acc[jj * 4 + e] + cc[e]);   // columns scaled by -log2(e)
           v[e] = f2h_sat(ov[e] * gate);
         }
         *reinterpret_cast<f16x4*>(og + lq * OP + b * 32 + ch) = v;

@@ -15,9 +15,11 @@
 // which every kernel takes as strides.  The ending node is thus read with
 // strided loads of Z and written with strided stores; Z is never transposed.
 //
-// Workspace (Pp = P rounded up to 32; padded positions hold zeros); q, k, v
-// and the bias use the operand-ordered layouts of pa_device.h:
-//   q, k, v  nrows*H*Pp*32 fp16 (q scaled by log2(e)/sqrt(d))
+// Workspace (Pp = P rounded up to 32); q, k, v and the bias use the
+// operand-ordered layouts of pa_device.h:
+//   q, k, v  nrows*H*Pp*32 fp16 (q scaled by log2(e)/sqrt(d)); padded
+//            positions: v zero, q and k finite (keys past P are dropped by
+//            every sweep, queries past P never stored)
 //   g        nrows*H*Pp*32 fp16 in the layout of q, sigmoid already applied
 //   bias     H*Pp*Pp fp16, log2 units (natural bias * log2(e)), zero padding
 #include "pa_device.h"
@@ -41,6 +43,9 @@ __global__ void pack_weights_kernel(const bf16* __restrict__ wq, const bf16* __r
                                     const bf16* __restrict__ wv, const bf16* __restrict__ wg,
                                     const bf16* __restrict__ wo, const bf16* __restrict__ gamma,
                                     f16* __restrict__ wimg, f16* __restrict__ woT, int c_in, int hd, int c_out) {
+  // q columns carry the logit scale log2(e)/sqrt(d) and the gate columns
+  // -log2(e): the projection then stores q = acc + c and forms the gate as
+  // 1 / (1 + 2^(acc + c)) with no multiply per element
   const int ks = c_in / 16;
   const int64_t n_w = (int64_t)4 * hd / 32 * ks * 64;   // 8-element lane slots of the image
   const int64_t n_o = (int64_t)c_out * hd;
@@ -51,9 +56,10 @@ __global__ void pack_weights_kernel(const bf16* __restrict__ wq, const bf16* __r
       const int col = b * 32 + (l & 31), k0 = t * 16 + (l >> 5) * 8;
       const int tensor = col / hd, c = col % hd;
       const bf16* src = tensor == 0 ? wq : tensor == 1 ? wk : tensor == 2 ? wv : wg;
+      const float sc = column_scale(tensor);
       f16x8 o;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = f2h_sat(bf2f(src[(int64_t)(k0 + e) * hd + c]) * bf2f(gamma[k0 + e]));
+      for (int e = 0; e < 8; ++e) o[e] = f2h_sat(bf2f(src[(int64_t)(k0 + e) * hd + c]) * bf2f(gamma[k0 + e]) * sc);
       *reinterpret_cast<f16x8*>(wimg + i * 8) = o;
     } else {
       const int64_t j = i - n_w;
@@ -63,8 +69,9 @@ __global__ void pack_weights_kernel(const bf16* __restrict__ wq, const bf16* __r
   }
 }
 
-// cst[col] = sum_k beta[k] W[k][col] (+ b_g for the gate columns): one wave
-// per column, fp32 partial sums over lanes, then a wave reduction.
+// cst[col] = (sum_k beta[k] W[k][col] (+ b_g for the gate columns)) times the
+// column's scale: one wave per column, fp32 partial sums over lanes, then a
+// wave reduction.
 __global__ void pack_consts_kernel(const bf16* __restrict__ wq, const bf16* __restrict__ wk,
                                    const bf16* __restrict__ wv, const bf16* __restrict__ wg,
                                    const bf16* __restrict__ beta, const bf16* __restrict__ b_g,
@@ -77,7 +84,7 @@ __global__ void pack_consts_kernel(const bf16* __restrict__ wq, const bf16* __re
   float acc = 0.0f;
   for (int k = lane; k < c_in; k += kWave) acc += bf2f(beta[k]) * bf2f(src[(int64_t)k * hd + c]);
   acc = group_sum<kWave>(acc);
-  if (lane == 0) cst[col] = acc + (tensor == 3 && b_g != nullptr ? bf2f(b_g[c]) : 0.0f);
+  if (lane == 0) cst[col] = (acc + (tensor == 3 && b_g != nullptr ? bf2f(b_g[c]) : 0.0f)) * column_scale(tensor);
 }
 
 // --------------------------------------------------------------------------
@@ -123,7 +130,7 @@ template <int C_IN, int HD, int NCOL, int MODE>
 __global__ __launch_bounds__(kProjThreads) void proj_kernel(
     const bf16* __restrict__ x, int64_t xs_r, int64_t xs_p, int tile_rmajor, const bf16* __restrict__ gamma,
     const bf16* __restrict__ beta, float eps, const f16* __restrict__ wimg, const float* __restrict__ cst,
-    const bf16* __restrict__ wb, float q_scale, f16* __restrict__ q_ws, f16* __restrict__ k_ws,
+    const bf16* __restrict__ wb, f16* __restrict__ q_ws, f16* __restrict__ k_ws,
     f16* __restrict__ v_ws, f16* __restrict__ g_ws, float* __restrict__ bias, int bias_swizzled, float bias_scale,
     int nrows, int P, int Pp, int H) {
   using SH = ProjShape<C_IN, HD, NCOL, MODE>;
@@ -136,7 +143,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
   float* cbb = cb + NCOL;                                                      // [8] pair-bias constants
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int lq = lane & 31, g = lane >> 5;
   const int col0 = blockIdx.y * NCOL;
   const bool do_bias = SH::HAS_BIAS && blockIdx.y == 0;
@@ -269,12 +276,18 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
 #pragma unroll
         for (int t = 0; t < KS; ++t) acc = mfma32(X[t], *reinterpret_cast<const f16x8*>(wop + t * 512), acc);
         const float c = cbk[lq];
+        const bool full_tile = p0 + 32 <= P;   // uniform: no padded position in this tile
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           f16x8 o;
+          if (full_tile) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            o[e] = p0 + slot_x(t, g, e) < P ? f2h_sat(acc[8 * t + e] + c) : f2h(0.0f);
+            for (int e = 0; e < 8; ++e) o[e] = f2h_sat(acc[8 * t + e] + c);
+          } else {   // padded positions (keys past P) hold zeros: their weight is 0, so P.V must see 0
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              o[e] = p0 + slot_x(t, g, e) < P ? f2h_sat(acc[8 * t + e] + c) : f2h(0.0f);
+          }
           st16(v_ws + (chunk0 + t) * 512 + lane * 8, o);
         }
       } else {                                // out^T = W^T X^T: rows = channels, lane = position
@@ -287,18 +300,20 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
           const f32x4 c1 = *reinterpret_cast<const f32x4*>(cbk + 16 * t + 8 + 4 * g);
           f16x8 o;
           if (tensor <= 1) {
-            const float sc = valid ? (tensor == 0 ? q_scale : 1.0f) : 0.0f;
+            // q (scale folded into its columns) and k; padded positions keep
+            // finite values: every sweep drops keys past P, and queries past
+            // P are never stored
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              o[e] = f2h_sat((acc[8 * t + e] + c0[e]) * sc);
-              o[4 + e] = f2h_sat((acc[8 * t + 4 + e] + c1[e]) * sc);
+              o[e] = f2h_sat(acc[8 * t + e] + c0[e]);
+              o[4 + e] = f2h_sat(acc[8 * t + 4 + e] + c1[e]);
             }
             st16((tensor == 0 ? q_ws : k_ws) + (chunk0 + t) * 512 + lane * 8, o);
           } else {                            // gate: sigmoid, same layout as q
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              o[e] = f2h(1.0f / (1.0f + __expf(-(acc[8 * t + e] + c0[e]))));
-              o[4 + e] = f2h(1.0f / (1.0f + __expf(-(acc[8 * t + 4 + e] + c1[e]))));
+              o[e] = f2h(sigmoid_from_log2(acc[8 * t + e] + c0[e]));
+              o[4 + e] = f2h(sigmoid_from_log2(acc[8 * t + 4 + e] + c1[e]));
             }
             st16(g_ws + (chunk0 + t) * 512 + lane * 8, o);
           }
@@ -426,7 +441,7 @@ static hipError_t proj_dispatch(const ProjArgs& a, int num_cu, hipStream_t s) {
   const int rmajor = a.xs_p <= a.xs_r ? 1 : 0;
   hipLaunchKernelGGL((proj_kernel<C_IN, HD, NCOL, MODE>), dim3(grid_x, groups), dim3(kProjThreads), 0, s,
                      (const bf16*)a.x, a.xs_r, a.xs_p, rmajor, (const bf16*)a.gamma, (const bf16*)a.beta, a.eps,
-                     (const f16*)a.wT, a.cst, (const bf16*)a.wb, a.q_scale, (f16*)a.q_ws,
+                     (const f16*)a.wT, a.cst, (const bf16*)a.wb, (f16*)a.q_ws,
                      (f16*)a.k_ws, (f16*)a.v_ws, (f16*)a.g_ws, a.bias, a.bias_swizzled, a.bias_scale, a.nrows, a.P,
                      a.Pp, a.H);
   return hipGetLastError();

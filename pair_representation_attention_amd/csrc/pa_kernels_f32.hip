@@ -354,7 +354,7 @@ __global__ __launch_bounds__(ProjF32Shape<C_IN>::THREADS) void proj_f32_kernel(
           } else {                                // gate: sigmoid, O^T image in fp32
             f32x16 o;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) o[j] = 1.0f / (1.0f + __expf(-(acc[j] + cb[acc_row(j, g)])));
+            for (int j = 0; j < 16; ++j) o[j] = sigmoid_fast(acc[j] + cb[acc_row(j, g)]);
             float* dst = g_ws + ((rh * nb + (p0 >> 5)) * 64 + lane) * 16;
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4)

@@ -24,8 +24,7 @@ struct ProjArgs {
   const void* wT;                // packed q|k|v|g operand image (launch_pack_bf16)
   const float* cst;              // its column constants
   const void* wb;                // w_b [c_in][H]
-  float q_scale;
-  void *q_ws, *k_ws, *v_ws, *g_ws;
+  void *q_ws, *k_ws, *v_ws, *g_ws;  // q and the gate from columns packed with their scales (column_scale)
   float* bias;                   // pair bias output (rows = the projected rows r); fp16 when swizzled
   int bias_swizzled;             // 1: attention layout (fp16 operand order, Pp x Pp, zero padded); 0: [H][P][P] float
   float bias_scale;              // multiplies the stored bias (log2(e) for the attention layout)

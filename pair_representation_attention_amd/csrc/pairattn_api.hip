@@ -636,7 +636,6 @@ static int run_row_attention_bf16(const pairattn_params* p, const Layout& L, hip
   mark("pack");
   pj.wT = ws_at(p, L.wT);
   pj.cst = reinterpret_cast<const float*>(ws_at(p, L.cst));
-  pj.q_scale = 1.4426950408889634f / std::sqrt(32.0f);
   PA_TRY(hip_status(pa::launch_proj_bf16(pj, ra.bias_in_proj ? 1 : 0, num_cu, s), "projection launch"));
   mark("projection");
 
@@ -1078,7 +1077,6 @@ int pairattn_tri_partial_fwd(const void* q_pairs, const void* kv_pairs, const fl
     pj.eps = p->ln_eps;
     pj.wT = ws_at(p, L.wT);
     pj.cst = reinterpret_cast<const float*>(ws_at(p, L.cst));
-    pj.q_scale = 1.4426950408889634f / std::sqrt(32.0f);
     pj.q_ws = ws_at(p, L.q);
     pj.c_in = (int)c_z;
     pj.hd = (int)hd;
@@ -1307,7 +1305,6 @@ int pairattn_tri_partial_finish(const void* q_pairs, const float* o, const paira
     pj.eps = p->ln_eps;
     pj.wT = ws_at(p, L.wT);
     pj.cst = reinterpret_cast<const float*>(ws_at(p, L.cst));
-    pj.q_scale = 1.4426950408889634f / std::sqrt(32.0f);
     pj.g_ws = ws_at(p, L.g);
     pj.c_in = (int)c_z;
     pj.hd = (int)hd;
