@@ -194,13 +194,16 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
       p0 = (int)(tile / nrows) * 32;
     }
   };
+  // element offset of this lane's position and channel half within a tile
+  // (the tile's own offset is wave-uniform and computed on the scalar unit)
+  const int64_t lane_off = (int64_t)lq * xs_p + g * 8;
   auto load_tile = [&](int64_t tile, bf16x8* raw) {
     if (tile < ntiles) {
       int r, p0;
       tile_rp(tile, r, p0);
       const int p = p0 + lq;
       if (p < P) {
-        const bf16* src = x + (int64_t)r * xs_r + (int64_t)p * xs_p + g * 8;
+        const bf16* src = x + ((int64_t)r * xs_r + (int64_t)p0 * xs_p) + lane_off;
 #pragma unroll
         for (int t = 0; t < KS; ++t) raw[t] = ld16(src + t * 16);
         return;
@@ -216,15 +219,14 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
 #pragma unroll
   for (int f = 0; f < PF; ++f) load_tile(tile + f * stride, pre[f]);
 
-  for (; tile < ntiles; tile += stride) {
-    bf16x8 raw[KS];
+  // The PF buffers take the tiles in turn (unrolled, so that each is a fixed
+  // set of registers): a tile's rows are read by LayerNorm, then its buffer
+  // is refilled with the tile PF strides ahead.
+  while (tile < ntiles) {
 #pragma unroll
-    for (int t = 0; t < KS; ++t) raw[t] = pre[0][t];
-#pragma unroll
-    for (int f = 0; f + 1 < PF; ++f)
-#pragma unroll
-      for (int t = 0; t < KS; ++t) pre[f][t] = pre[f + 1][t];
-    load_tile(tile + PF * stride, pre[PF - 1]);
+   for (int u = 0; u < PF; ++u) {
+    if (tile >= ntiles) break;
+    const bf16x8* raw = pre[u];
 
     int r, p0;
     tile_rp(tile, r, p0);
@@ -249,11 +251,13 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
       }
     s2 += __shfl_xor(s2, 32, 64);
     const float rstd = 1.0f / __builtin_sqrtf(s2 * (1.0f / C_IN) + eps);
+    // |x - mean| * rstd <= sqrt(C_IN - 1) < 16 for any row: no saturation needed
     f16x8 X[KS];
 #pragma unroll
     for (int t = 0; t < KS; ++t)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) X[t][e] = f2h_sat((bf2f(raw[t][e]) - mean) * rstd);
+      for (int e = 0; e < 8; ++e) X[t][e] = f2h((bf2f(raw[t][e]) - mean) * rstd);
+    load_tile(tile + PF * stride, pre[u]);
 
     // ---- q | k | v | g column blocks ----
     // Register 8t+e of lane half g holds accumulator row slot_x(t, g, e), so
@@ -346,6 +350,8 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
         }
       }
     }
+    tile += stride;
+   }
   }
 }
 
