@@ -186,7 +186,7 @@ __global__ __launch_bounds__(ProjF32Shape<C_IN>::THREADS) void proj_f32_kernel(
   f16* wl_lo = wl_hi + SH::NB * KS * 512;
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int lq = lane & 31, g = lane >> 5;
   const int nblk = nqkvg + with_bias;
   const int b0 = blockIdx.y * SH::NB;
@@ -231,13 +231,16 @@ __global__ __launch_bounds__(ProjF32Shape<C_IN>::THREADS) void proj_f32_kernel(
     }
   };
   // this lane's raw channels of a tile (zeros past P or past the last tile)
+  // element offset of this lane's position and channel half within a tile
+  // (the tile's own offset is wave-uniform and computed on the scalar unit)
+  const int64_t lane_off = (int64_t)lq * xs_p + g * 8;
   auto load_raw = [&](int64_t tile, float (*raw)[8]) {
     if (tile < ntiles) {
       int r, p0;
       tile_rp(tile, r, p0);
       const int p = p0 + lq;
       if (p < P) {
-        const float* src = x + (int64_t)r * xs_r + (int64_t)p * xs_p + g * 8;
+        const float* src = x + ((int64_t)r * xs_r + (int64_t)p0 * xs_p) + lane_off;
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
           const f32x4 a = *reinterpret_cast<const f32x4*>(src + t * 16);
