@@ -168,6 +168,23 @@ def calibrate_exp2(lib, torch, stream, iters: int = 4096, reps: int = 3) -> dict
             "cycles_per_wave_exp2_at_2.4GHz": 1024 * 64 * 2.4e9 / (n / (ms * 1e-3))}
 
 
+def copy_probe(torch, mib: float) -> None:
+    """Plain device copies and fills of `mib` MiB, outside any timed region:
+    the reference kernels whose FETCH_SIZE / WRITE_SIZE scale the counters of
+    a rocprofv3 --pmc run, and (in a kernel trace) this device's read+write
+    and write-only HBM rates."""
+    n = int(mib * 1024 * 1024)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    for _ in range(2):
+        dst.fill_(3)
+    torch.cuda.synchronize()
+    log(f"copy probe: {mib} MiB copied x 2, filled x 2")
+    del src, dst
+
+
 def cpu_info() -> dict:
     model = None
     try:
@@ -292,7 +309,8 @@ def main() -> int:
                          "module, MSA row attention, the row block and the extra-MSA fp32 workload")
     ap.add_argument("--workload", choices=["tri_bf16_i1536", "msa_bf16_s512_i384", "msa_fp32_s5120_i384",
                                            "tri_bf16_i16384_chunked", "ring_fp32_i1536_grid2x2",
-                                           "ring_bf16_i1536_grid2x2", "tri_bf16_i384_pad", "tri_fp32_i64"],
+                                           "ring_bf16_i1536_grid2x2", "tri_bf16_i384_pad", "tri_fp32_i64",
+                                           "rows_bf16_i4096_r512"],
                     default="tri_bf16_i1536",
                     help="time only the fp32 extra-MSA workload, or chunked triangle attention at I = 16384 "
                          "(one JSON line)")
@@ -331,11 +349,14 @@ def main() -> int:
     if args.workload != "tri_bf16_i1536":
         fn = {"msa_fp32_s5120_i384": msa_fp32_workload, "tri_bf16_i16384_chunked": chunked_workload,
               "ring_fp32_i1536_grid2x2": ring_workload, "ring_bf16_i1536_grid2x2": ring_workload,
-              "msa_bf16_s512_i384": msa_bf16_workload,
+              "msa_bf16_s512_i384": msa_bf16_workload, "rows_bf16_i4096_r512": rows_workload,
               "tri_bf16_i384_pad": lambda *a: tri_config_workload("tri_bf16_i384_pad", *a, np=np),
               "tri_fp32_i64": lambda *a: tri_config_workload("tri_fp32_i64", *a, np=np, orientations=(0,))}[
             args.workload]
-        print(json.dumps({"workload": args.workload, **fn(args, device, inputs, lib, torch)}), flush=True)
+        res = fn(args, device, inputs, lib, torch)
+        if args.copy_probe > 0:
+            copy_probe(torch, args.copy_probe)
+        print(json.dumps({"workload": args.workload, **res}), flush=True)
         return 0
     cfg = inputs.CONFIGS["tri_bf16_i1536"]
     I, c, H, d = cfg["I"], cfg["c"], cfg["H"], cfg["d"]
@@ -457,15 +478,8 @@ def main() -> int:
     if args.extra:
         result["extra"] = extra_workloads(args, device, inputs, lib, torch, np)
 
-    if args.copy_probe > 0:   # plain device copy of a known size, outside the timed region
-        n = int(args.copy_probe * 1024 * 1024)
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copy probe: {args.copy_probe} MiB x 2")
-        del src, dst
+    if args.copy_probe > 0:
+        copy_probe(torch, args.copy_probe)
 
     del start, end
     torch.cuda.empty_cache()
@@ -552,6 +566,30 @@ def msa_bf16_workload(args, device, inputs, lib, torch) -> dict:
     return res
 
 
+def rows_workload(args, device, inputs, lib, torch) -> dict:
+    """Row block: 512 starting-node rows of Z[4096,4096,128] (a 171-residue
+    block tiled 24 times plus noise), the bias from the whole Z
+    (pairattn_tri_bias), then the rows (pairattn_tri_rows_fwd)."""
+    import numpy as np
+    cfg = inputs.CONFIGS["rows_bf16_i4096_r512"]
+    I, R, c, H, d = cfg["I"], cfg["R"], cfg["c"], cfg["H"], cfg["d"]
+    log(f"row block, {R} rows of Z[{I},{I},{c}]")
+    case = inputs.make_rows_case(I=I, R=R, c=c, H=H, d=d, asu=cfg["asu"], noise=cfg["noise"], seed=cfg["seed"])
+    zf = torch.from_numpy(case.zbits.view(np.int16)).to("cuda").view(torch.bfloat16)
+    rr = device.RowsRunner(zf, zf[case.r0:case.r0 + R], None, case.params, H, "bf16")
+    del case
+    steps = max(3, args.steps)
+    ms_bias = _time(rr.compute_bias, steps, 2, torch)
+    ms_rows = _time(rr.rows, steps, 2, torch)
+    ms = _time(rr, steps, 2, torch)
+    f = tri_module_flops(R, I, c, H, d, with_bias=True)["total"]
+    res = {"ms": ms, "ms_bias": ms_bias, "ms_rows": ms_rows, "tflops": f / (ms * 1e-3) / 1e12,
+           "rows_per_s": R / (ms * 1e-3)}
+    del rr, zf
+    torch.cuda.empty_cache()
+    return res
+
+
 def extra_workloads(args, device, inputs, lib, torch, np) -> dict:
     out = {}
     # the other triangle configurations: fp32 I = 64 (starting node) and the
@@ -563,23 +601,7 @@ def extra_workloads(args, device, inputs, lib, torch, np) -> dict:
                                                     mask_override="pad")
     out["msa_bf16_s512_i384"] = msa_bf16_workload(args, device, inputs, lib, torch)
 
-    # row block: 512 starting-node rows of Z[4096,4096,128], bias from the whole Z
-    cfg = inputs.CONFIGS["rows_bf16_i4096_r512"]
-    I, R, c, H, d = cfg["I"], cfg["R"], cfg["c"], cfg["H"], cfg["d"]
-    log(f"extra: row block, {R} rows of Z[{I},{I},{c}]")
-    case = inputs.make_rows_case(I=I, R=R, c=c, H=H, d=d, asu=cfg["asu"], noise=cfg["noise"], seed=cfg["seed"])
-    zf = torch.from_numpy(case.zbits.view(np.int16)).to("cuda").view(torch.bfloat16)
-    rr = device.RowsRunner(zf, zf[case.r0:case.r0 + R], None, case.params, H, "bf16")
-    del case
-    steps = max(3, args.steps)
-    ms_bias = _time(rr.compute_bias, steps, 2, torch)
-    ms_rows = _time(rr.rows, steps, 2, torch)
-    ms = _time(rr, steps, 2, torch)
-    f = tri_module_flops(R, I, c, H, d, with_bias=True)["total"]
-    out["rows_bf16_i4096_r512"] = {"ms": ms, "ms_bias": ms_bias, "ms_rows": ms_rows,
-                                   "tflops": f / (ms * 1e-3) / 1e12, "rows_per_s": R / (ms * 1e-3)}
-    del rr, zf
-    torch.cuda.empty_cache()
+    out["rows_bf16_i4096_r512"] = rows_workload(args, device, inputs, lib, torch)
 
     out["msa_fp32_s5120_i384"] = msa_fp32_workload(args, device, inputs, lib, torch)
     return out
