@@ -1003,44 +1003,35 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
 }
 
-// keep bits per (row, 32-key block): bit b of word (r, kb) = key kb*32+b is
-// kept (key < P and mask[r*ms_r + key*ms_k] != 0, or no mask).  Each wave
-// packs two words with one ballot (lane halves).
+// Keep bits and key-block range of each row, one wave per row:
+//   bits[r][kb]: bit b = key kb*32+b is kept (key < P and mask[r*ms_r +
+//                key*ms_k] != 0, or no mask); a ballot of the wave packs the
+//                words of two blocks at once
+//   range[2r] = lo, the first block with a kept key (nkb if none);
+//   range[2r+1] = hi, one past the last such block (0 if none)
 __global__ void mask_bits_kernel(const uint8_t* __restrict__ mask, int64_t ms_r, int64_t ms_k,
-                                 uint32_t* __restrict__ bits, int nrows, int P, int nkb) {
-  const int64_t nwords = (int64_t)nrows * nkb;
-  const int lane = threadIdx.x % kWave;
-  const int64_t wave0 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / kWave;
-  const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
-  for (int64_t w = wave0 * 2; w < nwords; w += nwaves * 2) {
-    const int64_t word = w + (lane >> 5);
-    bool keep = false;
-    if (word < nwords) {
-      const int r = (int)(word / nkb), kb = (int)(word % nkb);
-      const int key = kb * 32 + (lane & 31);
-      keep = key < P && (mask == nullptr || mask[(int64_t)r * ms_r + (int64_t)key * ms_k] != 0);
-    }
-    const uint64_t b = __ballot(keep);
-    if (lane == 0) bits[w] = (uint32_t)b;
-    if (lane == 32 && word < nwords) bits[word] = (uint32_t)(b >> 32);
-  }
-}
-
-// Key-block range of each row from its keep bits, one wave per row:
-// range[2r] = lo, the first block with a kept key (nkb if none);
-// range[2r+1] = hi, one past the last such block (0 if none).
-__global__ void mask_range_kernel(const uint32_t* __restrict__ bits, int nrows, int nkb, int* __restrict__ range) {
+                                 uint32_t* __restrict__ bits, int* __restrict__ range, int nrows, int P, int nkb) {
   const int lane = threadIdx.x % kWave;
   const int64_t row = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / kWave;
   if (row >= nrows) return;   // uniform over the wave
-  const uint32_t* w = bits + row * nkb;
+  const uint8_t* mrow = mask != nullptr ? mask + row * ms_r : nullptr;
+  uint32_t* brow = bits + row * nkb;
   int lo = nkb, hi = 0;
-  for (int base = 0; base < nkb; base += kWave) {
-    const int kb = base + lane;
-    const uint64_t ne = __ballot(kb < nkb && w[kb] != 0u);
-    if (ne != 0) {
-      if (lo == nkb) lo = base + __builtin_ctzll(ne);
-      hi = base + kWave - __builtin_clzll(ne);
+  for (int kb0 = 0; kb0 < nkb; kb0 += 2) {
+    const int kb = kb0 + (lane >> 5);
+    const int key = kb * 32 + (lane & 31);
+    const bool keep = kb < nkb && key < P && (mrow == nullptr || mrow[(int64_t)key * ms_k] != 0);
+    const uint64_t m = __ballot(keep);
+    const uint32_t w0 = (uint32_t)m, w1 = (uint32_t)(m >> 32);
+    if (lane == 0) brow[kb0] = w0;
+    if (lane == 32 && kb0 + 1 < nkb) brow[kb0 + 1] = w1;
+    if (w0 != 0u) {
+      lo = min(lo, kb0);
+      hi = kb0 + 1;
+    }
+    if (w1 != 0u) {
+      lo = min(lo, kb0 + 1);
+      hi = kb0 + 2;
     }
   }
   if (lane == 0) {
@@ -1051,15 +1042,9 @@ __global__ void mask_range_kernel(const uint32_t* __restrict__ bits, int nrows, 
 
 hipError_t launch_mask_bits(const uint8_t* mask, int64_t ms_r, int64_t ms_k, uint32_t* bits, int nrows, int P,
                             int nkb, hipStream_t s) {
-  const int64_t nwords = (int64_t)nrows * nkb;
-  const int64_t waves = (nwords + 1) / 2;
-  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((waves + 3) / 4, 4096));
-  hipLaunchKernelGGL(mask_bits_kernel, dim3(blocks), dim3(256), 0, s, mask, ms_r, ms_k, bits, nrows, P, nkb);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int rblocks = (int)(((int64_t)nrows + 3) / 4);   // 4 waves (rows) per block
-  hipLaunchKernelGGL(mask_range_kernel, dim3(rblocks), dim3(256), 0, s, bits, nrows, nkb,
-                     mask_range_of(bits, nrows, nkb));
+  const int blocks = (int)(((int64_t)nrows + 3) / 4);   // 4 waves (rows) per block
+  hipLaunchKernelGGL(mask_bits_kernel, dim3(blocks), dim3(256), 0, s, mask, ms_r, ms_k, bits,
+                     mask_range_of(bits, nrows, nkb), nrows, P, nkb);
   return hipGetLastError();
 }
 

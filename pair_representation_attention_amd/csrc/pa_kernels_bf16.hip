@@ -39,10 +39,9 @@ namespace pa {
 // bf16 -> fp16 is exact for magnitudes in [2^-14, 65504]; smaller values
 // keep an absolute error below 2^-25; larger ones saturate.
 // --------------------------------------------------------------------------
-__global__ void pack_weights_kernel(const bf16* __restrict__ wq, const bf16* __restrict__ wk,
-                                    const bf16* __restrict__ wv, const bf16* __restrict__ wg,
-                                    const bf16* __restrict__ wo, const bf16* __restrict__ gamma,
-                                    f16* __restrict__ wimg, f16* __restrict__ woT, int c_in, int hd, int c_out) {
+__device__ void pack_weights(const bf16* __restrict__ wq, const bf16* __restrict__ wk, const bf16* __restrict__ wv,
+                             const bf16* __restrict__ wg, const bf16* __restrict__ wo, const bf16* __restrict__ gamma,
+                             f16* __restrict__ wimg, f16* __restrict__ woT, int c_in, int hd, int c_out) {
   // q columns carry the logit scale log2(e)/sqrt(d) and the gate columns
   // -log2(e): the projection then stores q = acc + c and forms the gate as
   // 1 / (1 + 2^(acc + c)) with no multiply per element
@@ -72,10 +71,9 @@ __global__ void pack_weights_kernel(const bf16* __restrict__ wq, const bf16* __r
 // cst[col] = (sum_k beta[k] W[k][col] (+ b_g for the gate columns)) times the
 // column's scale: one wave per column, fp32 partial sums over lanes, then a
 // wave reduction.
-__global__ void pack_consts_kernel(const bf16* __restrict__ wq, const bf16* __restrict__ wk,
-                                   const bf16* __restrict__ wv, const bf16* __restrict__ wg,
-                                   const bf16* __restrict__ beta, const bf16* __restrict__ b_g,
-                                   float* __restrict__ cst, int c_in, int hd) {
+__device__ void pack_consts(const bf16* __restrict__ wq, const bf16* __restrict__ wk, const bf16* __restrict__ wv,
+                            const bf16* __restrict__ wg, const bf16* __restrict__ beta, const bf16* __restrict__ b_g,
+                            float* __restrict__ cst, int c_in, int hd) {
   const int col = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   if (col >= 4 * hd) return;
@@ -85,6 +83,15 @@ __global__ void pack_consts_kernel(const bf16* __restrict__ wq, const bf16* __re
   for (int k = lane; k < c_in; k += kWave) acc += bf2f(beta[k]) * bf2f(src[(int64_t)k * hd + c]);
   acc = group_sum<kWave>(acc);
   if (lane == 0) cst[col] = (acc + (tensor == 3 && b_g != nullptr ? bf2f(b_g[c]) : 0.0f)) * column_scale(tensor);
+}
+
+// One launch for both: blockIdx.y = 0 packs the weights, 1 the constants.
+__global__ void pack_kernel(const bf16* __restrict__ wq, const bf16* __restrict__ wk, const bf16* __restrict__ wv,
+                            const bf16* __restrict__ wg, const bf16* __restrict__ wo, const bf16* __restrict__ gamma,
+                            const bf16* __restrict__ beta, const bf16* __restrict__ b_g, f16* __restrict__ wimg,
+                            f16* __restrict__ woT, float* __restrict__ cst, int c_in, int hd, int c_out) {
+  if (blockIdx.y == 0) pack_weights(wq, wk, wv, wg, wo, gamma, wimg, woT, c_in, hd, c_out);
+  else pack_consts(wq, wk, wv, wg, beta, b_g, cst, c_in, hd);
 }
 
 // --------------------------------------------------------------------------
@@ -407,16 +414,13 @@ hipError_t launch_pack_bf16(const PackArgs& a, hipStream_t s) {
   if (a.c_in % 16 != 0 || a.hd % 32 != 0) return hipErrorInvalidValue;
   const int64_t total = (int64_t)4 * a.hd * a.c_in / 8 + (int64_t)a.c_out * a.hd;
   const int threads = 256;
-  const int blocks = (int)std::min<int64_t>((total + threads - 1) / threads, 4096);
-  hipLaunchKernelGGL(pack_weights_kernel, dim3(blocks), dim3(threads), 0, s, (const bf16*)a.wq, (const bf16*)a.wk,
-                     (const bf16*)a.wv, (const bf16*)a.wg, (const bf16*)a.wo, (const bf16*)a.gamma, (f16*)a.wT,
-                     (f16*)a.woT, a.c_in, a.hd, a.c_out);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const int blocks_w = (int)std::min<int64_t>((total + threads - 1) / threads, 4096);   // grid-stride
   const int cols = 4 * a.hd, per_block = threads / kWave;
-  hipLaunchKernelGGL(pack_consts_kernel, dim3((cols + per_block - 1) / per_block), dim3(threads), 0, s,
-                     (const bf16*)a.wq, (const bf16*)a.wk, (const bf16*)a.wv, (const bf16*)a.wg, (const bf16*)a.beta,
-                     (const bf16*)a.b_g, a.cst, a.c_in, a.hd);
+  const int blocks_c = (cols + per_block - 1) / per_block;                              // one wave per column
+  hipLaunchKernelGGL(pack_kernel, dim3(std::max(blocks_w, blocks_c), 2), dim3(threads), 0, s, (const bf16*)a.wq,
+                     (const bf16*)a.wk, (const bf16*)a.wv, (const bf16*)a.wg, (const bf16*)a.wo,
+                     (const bf16*)a.gamma, (const bf16*)a.beta, (const bf16*)a.b_g, (f16*)a.wT, (f16*)a.woT, a.cst,
+                     a.c_in, a.hd, a.c_out);
   return hipGetLastError();
 }
 
