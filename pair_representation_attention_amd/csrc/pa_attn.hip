@@ -82,6 +82,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt lgkmcnt(0) (LDS reads and scalar loads), vmcnt and expcnt at their no-wait maxima
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
 __device__ __forceinline__ f16x8 lds_f16x8(const char* p) { return *reinterpret_cast<const f16x8*>(p); }
 
 typedef float f32x8 __attribute__((ext_vector_type(8)));
@@ -111,6 +114,20 @@ __device__ __forceinline__ f32x16 widen_bias(const f16x8& b0, const f16x8& b1, c
   return __builtin_shufflevector(c01, c23, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
 }
 
+// The same with accumulator inputs m (registers in the order of the S^T
+// accumulator): every output is its bias value plus m, so -inf in m masks a
+// key in the logits product that takes this as its C operand.
+__device__ __forceinline__ f32x16 widen_bias_acc(const f16x8& b0, const f16x8& b1, const f16x4& ident,
+                                                 const f32x16& m) {
+  const f32x8 c01 = __builtin_shufflevector(mfma4(ident, lo4(b0), __builtin_shufflevector(m, m, 0, 1, 2, 3)),
+                                            mfma4(ident, hi4(b0), __builtin_shufflevector(m, m, 4, 5, 6, 7)), 0, 1,
+                                            2, 3, 4, 5, 6, 7);
+  const f32x8 c23 = __builtin_shufflevector(mfma4(ident, lo4(b1), __builtin_shufflevector(m, m, 8, 9, 10, 11)),
+                                            mfma4(ident, hi4(b1), __builtin_shufflevector(m, m, 12, 13, 14, 15)), 0,
+                                            1, 2, 3, 4, 5, 6, 7);
+  return __builtin_shufflevector(c01, c23, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+}
+
 // Lane mask of accumulator register j (key k0 = (j/4)*8 + j%4 in lane half 0,
 // key k0 + 4 in lane half 1) from a block's keep bits: each half is bit k0
 // (or k0 + 4) sign-extended to 32 bits, one scalar bit-field extract each.
@@ -119,8 +136,10 @@ __device__ __forceinline__ f32x16 widen_bias(const f16x8& b0, const f16x8& b1, c
 template <int K0>
 __device__ __forceinline__ uint64_t key_lanes(uint32_t bits) {
   uint32_t lo, hi;
+  // early-clobber outputs: the first is written before the second
+  // instruction reads `bits`, so neither may share its register
   asm volatile("s_bfe_i32 %0, %2, %3\n\ts_bfe_i32 %1, %2, %4"
-               : "=s"(lo), "=s"(hi)
+               : "=&s"(lo), "=&s"(hi)
                : "s"(bits), "i"(K0 | (1 << 16)), "i"((K0 + 4) | (1 << 16)));
   return ((uint64_t)hi << 32) | lo;
 }
@@ -555,6 +574,61 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
   };
 
+  auto cvt_bias = [&](const f16x8* b) -> f32x16 { return widen_bias(b[0], b[1], ident4); };
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // softmax of S (one unit) with the next unit's logits (NEXT) and this
+  // unit's P.V product issued between its exp2 groups; the row sums
+  // accumulate in lacc by 4x4x4 products of the fp16 weights with ones
+  // (every element of lacc holds the lane's running sum).  MASKED: keys
+  // whose bit in `bits` is clear get -inf first (register j holds key
+  // (j/4)*8 + g*4 + j%4, so the select's lane mask is built on the scalar
+  // unit).
+  auto stream = [&](auto nextc, auto maskc, const f32x16& S_in, f32x16& Sn, const f16x8* kn, const f16x8* qn,
+                    const f32x16& cn, const f16x8* v, f32x16& o, f32x4& lacc, uint32_t bits) {
+    constexpr bool NEXT = decltype(nextc)::value;
+    constexpr bool MASKED = decltype(maskc)::value;
+    float e[16];
+    f16x8 p0, p1;
+    f32x16 S = S_in;
+    if constexpr (MASKED) {
+      if (bits != 0xffffffffu) keep_unit(S, bits);   // uniform: a block with every key kept skips the select
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e[j] = fast_exp2(S[j]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) Sn = mfma32(kn[0], qn[0], cn);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 4; j < 8; ++j) e[j] = fast_exp2(S[j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p0[j] = f2h(e[j]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) Sn = mfma32(kn[1], qn[1], Sn);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 8; j < 12; ++j) e[j] = fast_exp2(S[j]);
+    __builtin_amdgcn_sched_barrier(0);
+    o = mfma32(v[0], p0, o);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 12; j < 16; ++j) e[j] = fast_exp2(S[j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p1[j] = f2h(e[8 + j]);
+    lacc = mfma4(ones4, lo4(p0), lacc);
+    lacc = mfma4(ones4, hi4(p0), lacc);
+    __builtin_amdgcn_sched_barrier(0);
+    o = mfma32(v[1], p1, o);
+    __builtin_amdgcn_sched_barrier(0);
+    lacc = mfma4(ones4, lo4(p1), lacc);
+    lacc = mfma4(ones4, hi4(p1), lacc);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   // Software-pipelined form of the fast sweep for blocks without masked
   // keys (no mask, P a multiple of 32; H = 4, four units per wave and key
   // block).  Unit order within a block: (row 0, qb 0), (1, 0), (0, 1),
@@ -638,60 +712,6 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     };
     auto b_tile = [&](int kb, int qq) -> const char* {
       return b_lds + (kb & 1) * SH::B_STAGE + ((qgrp * QW + qq) * H + h) * SH::B_TILE + lane * 16;
-    };
-    auto cvt_bias = [&](const f16x8* b) -> f32x16 { return widen_bias(b[0], b[1], ident4); };
-    auto barrier = [&]() {
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    };
-    // softmax of S (one unit) with the next unit's logits (NEXT) and this
-    // unit's P.V product issued between its exp2 groups; the row sums
-    // accumulate in lacc by 4x4x4 products of the fp16 weights with ones
-    // (every element of lacc holds the lane's running sum).  MASKED: keys
-    // whose bit in `bits` is clear get -inf first (register j holds key
-    // (j/4)*8 + g*4 + j%4, so the select's lane mask is built on the scalar
-    // unit).
-    auto stream = [&](auto nextc, auto maskc, const f32x16& S_in, f32x16& Sn, const f16x8* kn, const f16x8* qn,
-                      const f32x16& cn, const f16x8* v, f32x16& o, f32x4& lacc, uint32_t bits) {
-      constexpr bool NEXT = decltype(nextc)::value;
-      constexpr bool MASKED = decltype(maskc)::value;
-      float e[16];
-      f16x8 p0, p1;
-      f32x16 S = S_in;
-      if constexpr (MASKED) {
-        if (bits != 0xffffffffu) keep_unit(S, bits);   // uniform: a block with every key kept skips the select
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) e[j] = fast_exp2(S[j]);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (NEXT) Sn = mfma32(kn[0], qn[0], cn);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 4; j < 8; ++j) e[j] = fast_exp2(S[j]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) p0[j] = f2h(e[j]);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (NEXT) Sn = mfma32(kn[1], qn[1], Sn);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 8; j < 12; ++j) e[j] = fast_exp2(S[j]);
-      __builtin_amdgcn_sched_barrier(0);
-      o = mfma32(v[0], p0, o);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 12; j < 16; ++j) e[j] = fast_exp2(S[j]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) p1[j] = f2h(e[8 + j]);
-      lacc = mfma4(ones4, lo4(p0), lacc);
-      lacc = mfma4(ones4, hi4(p0), lacc);
-      __builtin_amdgcn_sched_barrier(0);
-      o = mfma32(v[1], p1, o);
-      __builtin_amdgcn_sched_barrier(0);
-      lacc = mfma4(ones4, lo4(p1), lacc);
-      lacc = mfma4(ones4, hi4(p1), lacc);
-      __builtin_amdgcn_sched_barrier(0);
     };
     struct Regs {
       f16x8 K[RW][2], V[RW][2], B1[2];   // K and V tiles of both rows, bias tile of query block 1
@@ -800,6 +820,154 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
    }
   };
 
+  // Software-pipelined form of the fast sweep at H = 8 (one row and three
+  // query blocks per wave).  No tile is shared between waves here: a wave's
+  // K/V tile is its (row, head), its bias tiles are its head's tiles of the
+  // workgroup's query blocks.  So each wave copies exactly its own chunks
+  // into the ring stages and waits for its own copies only; no barrier
+  // orders the rings.  Every tile of block kb is in registers before the
+  // block runs, so its stage is refilled with block kb+2 after the first
+  // stream (once the reads of the stage have landed).
+  //   stream 0 of kb: unit of query block 0, logits of query block 1; then
+  //                   the copies of block kb+2
+  //   stream 1 of kb: query block 1, logits of query block 2; then block
+  //                   kb+1's K and bias tiles into registers (its copies
+  //                   waited for)
+  //   stream 2 of kb: query block 2, logits of query block 0 of block kb+1;
+  //                   then block kb+1's V tiles
+  // KMODE as in sweep_pipe (masks enter through the bias operand, see
+  // set_mask); the sweep runs over the row's key blocks [lo, hi).
+  auto sweep_pipe8 = [&](auto kmodec, int lo, int hi) {
+   constexpr int KMODE = decltype(kmodec)::value;
+   if constexpr (H == 8 && RW == 1 && QW == 3) {
+    using T = std::integral_constant<bool, true>;
+    using F = std::integral_constant<bool, false>;
+    f32x4 lacc[QW];   // row sums (every element holds the lane's sum)
+#pragma unroll
+    for (int qq = 0; qq < QW; ++qq) {
+      O[0][qq] = f32x16{};
+      m_sh[0][qq] = 0.0f;
+      l_run[0][qq] = 0.0f;
+      lacc[qq] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // copy sources: wave-uniform bases (block 0) and per-lane byte offsets
+    const int64_t rh = (int64_t)rows_c[0] * H + h;
+    const f16* k_base = k_ws + qkv_chunk(rh, nkb, 0, 0);
+    const f16* v_base = v_ws + qkv_chunk(rh, nkb, 0, 0);
+    const int64_t b_first = b16_chunk(h, nbq, nkb, min(qb0_wg, nbq - 1), 0, 0);
+    const f16* b_base = bias + b_first;
+    const uint32_t lane16 = lane * 16;
+    uint32_t b_voff[QW];
+#pragma unroll
+    for (int qq = 0; qq < QW; ++qq)
+      b_voff[qq] = (uint32_t)((b16_chunk(h, nbq, nkb, min(qb0_wg + qq, nbq - 1), 0, 0) - b_first) * 2) + lane16;
+    // this wave's tiles in the stages (the layout of the shared rings)
+    auto kv_at = [&](int kb) -> char* { return kv_lds + (kb % SH::NKV) * SH::KV_STAGE + h * SH::KV_TILE; };
+    auto b_at = [&](int kb, int qq) -> char* { return b_lds + (kb & 1) * SH::B_STAGE + (qq * H + h) * SH::B_TILE; };
+    // the wave's ten chunks of block kb: K0 K1 V0 V1 and both chunks of each bias tile
+    constexpr int NCPB = 4 + 2 * QW;
+    auto copy_block = [&](int kb) {
+      const int64_t e = (int64_t)kb * 1024;
+      const uint32_t kv = (uint32_t)(uintptr_t)(lds_void_t*)kv_at(kb);
+      g2lds16_sbase(k_base + e, lane16, kv);
+      g2lds16_sbase(k_base + e, lane16 + 1024, kv + 1024);
+      g2lds16_sbase(v_base + e, lane16, kv + 2048);
+      g2lds16_sbase(v_base + e, lane16 + 1024, kv + 3072);
+#pragma unroll
+      for (int qq = 0; qq < QW; ++qq) {
+        const uint32_t bl = (uint32_t)(uintptr_t)(lds_void_t*)b_at(kb, qq);
+        g2lds16_sbase(b_base + e, b_voff[qq], bl);
+        g2lds16_sbase(b_base + e, b_voff[qq] + 1024, bl + 1024);
+      }
+    };
+    auto read2 = [&](f16x8* dst, const char* tile) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) dst[c] = lds_f16x8(tile + lane * 16 + c * 1024);
+    };
+    // Masked keys (KMODE 1, 2): the three units of a block share one row, so
+    // the block's keep bits become one mask operand MB (0 or -inf per
+    // accumulator register), added to the bias by the products that widen
+    // it: the logits of masked keys are -inf from the start, with no select
+    // per unit.
+    f32x16 MB;
+    auto set_mask = [&](uint32_t bits) {
+      if constexpr (KMODE != 0) {
+        MB = f32x16{};
+        if (bits != 0xffffffffu) keep_unit(MB, bits);   // uniform
+      }
+    };
+    auto cvt = [&](const f16x8* b) -> f32x16 {
+      if constexpr (KMODE == 0) return cvt_bias(b);
+      else return widen_bias_acc(b[0], b[1], ident4, MB);
+    };
+
+    // prologue: blocks lo and lo+1 and Q land together, block lo into registers
+    copy_block(lo);
+    if (lo + 1 < hi) copy_block(lo + 1);
+    wait_q();
+    f16x8 K[2], V[2], B1[2], B2[2];
+    f32x16 S_pipe;
+    {
+      f16x8 B0[2];
+      read2(K, kv_at(lo));
+      read2(B0, b_at(lo, 0));
+      read2(V, kv_at(lo) + 2048);
+      read2(B1, b_at(lo, 1));
+      read2(B2, b_at(lo, 2));
+      set_mask(keep_bits(0, lo));
+      S_pipe = mfma32(K[1], Q[0][0][1], mfma32(K[0], Q[0][0][0], cvt(B0)));
+    }
+    // bits_next: keep bits of block kb+1 (KMODE 1, 2)
+    auto block = [&](int kb, auto morec, uint32_t bits_next) {
+      constexpr bool MORE = decltype(morec)::value;
+      f32x16 Sn, C;
+      // stream 0: query block 0; next query block 1
+      __builtin_amdgcn_s_setprio(3);
+      if constexpr (!MORE) load_epi();
+      C = cvt(B1);
+      stream(T{}, F{}, S_pipe, Sn, K, Q[0][1], C, V, O[0][0], lacc[0], ~0u);
+      S_pipe = Sn;
+      if constexpr (MORE) {
+        if (kb + 2 < hi) {
+          wait_lgkm0();   // every read of this block's stage has landed
+          copy_block(kb + 2);
+        }
+      }
+      // stream 1: query block 1; next query block 2
+      __builtin_amdgcn_s_setprio(2);
+      C = cvt(B2);
+      stream(T{}, F{}, S_pipe, Sn, K, Q[0][2], C, V, O[0][1], lacc[1], ~0u);
+      S_pipe = Sn;
+      if constexpr (MORE) {
+        // block kb+1 landed (only block kb+2's copies may still be in flight)
+        if (kb + 2 < hi) wait_vmcnt<NCPB>();
+        else wait_vmcnt<0>();
+        f16x8 B0n[2];
+        read2(K, kv_at(kb + 1));
+        read2(B0n, b_at(kb + 1, 0));
+        read2(B1, b_at(kb + 1, 1));
+        read2(B2, b_at(kb + 1, 2));
+        set_mask(bits_next);
+        C = cvt(B0n);
+      }
+      // stream 2: query block 2; next query block 0 of block kb+1
+      __builtin_amdgcn_s_setprio(1);
+      stream(morec, F{}, S_pipe, Sn, K, Q[0][0], C, V, O[0][2], lacc[2], ~0u);
+      if constexpr (MORE) {
+        read2(V, kv_at(kb + 1) + 2048);
+        S_pipe = Sn;
+      }
+    };
+    // (KMODE 1: only the last block drops keys, those past P)
+    int kb = lo;
+    for (; kb + 1 < hi; ++kb) block(kb, T{}, KMODE == 0 ? ~0u : keep_bits(0, kb + 1));
+    block(kb, F{}, ~0u);
+    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int qq = 0; qq < QW; ++qq) l_run[0][qq] = lacc[qq][0];
+   }
+  };
+
   bool epi_loaded = false;
   if constexpr (H == 4) {
     if constexpr (!HAS_MASK) {
@@ -835,8 +1003,27 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
           }
       }
     }
+  } else if constexpr (!HAS_MASK) {
+    row_has_key[0] = true;   // P >= 1: the row has a kept key
+    if (Pk == nkb * 32) sweep_pipe8(std::integral_constant<int, 0>{}, 0, nkb);
+    else sweep_pipe8(std::integral_constant<int, 1>{}, 0, nkb);
+    epi_loaded = true;
   } else {
-    sweep(std::integral_constant<bool, true>{});
+    const int* rg = mask_range + (int64_t)rows_c[0] * 2;
+    const int lo = rg[0], hi = rg[1];
+    row_has_key[0] = lo < hi;
+    if (lo < hi) {
+      sweep_pipe8(std::integral_constant<int, 2>{}, lo, hi);
+      epi_loaded = true;
+    } else {   // no kept key in the row: o = 0
+      wait_q();
+#pragma unroll
+      for (int qq = 0; qq < QW; ++qq) {
+        O[0][qq] = f32x16{};
+        m_sh[0][qq] = 0.0f;
+        l_run[0][qq] = 0.0f;
+      }
+    }
   }
   if (!epi_loaded) load_epi();
   __builtin_amdgcn_s_setprio(0);
