@@ -417,9 +417,11 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // One sweep over all key blocks.
   //   FAST: p = exp2(S) with no shift and no per-unit test, so the units of
   //         a block form one basic block.  Valid when every sum l stays finite
-  //         (no fp16 weight overflowed) and is at least 1 for rows with a kept
-  //         key (the largest weights are normal fp16 numbers); checked after
-  //         the sweep, and the workgroup sweeps again with SAFE otherwise.
+  //         (no fp16 weight, nor in the pipelined sweeps an fp16 partial sum
+  //         of four weights, overflowed) and is at least 1 for rows with a
+  //         kept key (the largest weights are normal fp16 numbers); checked
+  //         after the sweep, and the workgroup sweeps again with SAFE
+  //         otherwise.
   //   SAFE: a per-(row, query) shift chosen on the row's first block with a
   //         kept key and raised whenever a block sum passes 2^15.
   auto sweep = [&](auto fastc) {
@@ -581,9 +583,12 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     asm volatile("" ::: "memory");
   };
   // softmax of S (one unit) with the next unit's logits (NEXT) and this
-  // unit's P.V product issued between its exp2 groups; the row sums
-  // accumulate in lacc by 4x4x4 products of the fp16 weights with ones
-  // (every element of lacc holds the lane's running sum).  MASKED: keys
+  // unit's P.V product issued between its exp2 groups.  The row sums: the
+  // 16 fp16 weights of a lane are added in fp16 to four sums of four
+  // (packed adds), which one 4x4x4 product with ones adds into lacc in fp32
+  // (every element of lacc holds the lane's running sum).  A partial sum
+  // that overflows fp16 makes l infinite, which the check after the fast
+  // sweep sends to the shifted rerun.  MASKED: keys
   // whose bit in `bits` is clear get -inf first (register j holds key
   // (j/4)*8 + g*4 + j%4, so the select's lane mask is built on the scalar
   // unit).
@@ -619,13 +624,13 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     for (int j = 12; j < 16; ++j) e[j] = fast_exp2(S[j]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) p1[j] = f2h(e[8 + j]);
-    lacc = mfma4(ones4, lo4(p0), lacc);
-    lacc = mfma4(ones4, hi4(p0), lacc);
     __builtin_amdgcn_sched_barrier(0);
     o = mfma32(v[1], p1, o);
     __builtin_amdgcn_sched_barrier(0);
-    lacc = mfma4(ones4, lo4(p1), lacc);
-    lacc = mfma4(ones4, hi4(p1), lacc);
+    {
+      const f16x8 ps = p0 + p1;                     // four packed fp16 adds
+      lacc = mfma4(ones4, lo4(ps) + hi4(ps), lacc);   // two more, then one product
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
 
