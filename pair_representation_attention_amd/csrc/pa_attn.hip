@@ -1160,40 +1160,79 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       }
     }
   };
-  if constexpr (NBLK % 8 == 0) {
-    // every wave owns NBLK/8 output blocks of each row: their MFMA chains
-    // are interleaved, so that no MFMA waits for the one before it
-    constexpr int NB = NBLK / 8 * RW;
-    f32x16 acc[NB];
+  // every wave owns the output blocks blk = wave + 8j of each row (all of
+  // channel block cb_w): their MFMA chains are interleaved, so that no MFMA
+  // waits for the one before it
+  constexpr int NBW = (NBLK + 7) / 8;
+  f32x16 acc[RW][NBW];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) acc[i] = f32x16{};
+  for (int rr = 0; rr < RW; ++rr)
 #pragma unroll
-    for (int t = 0; t < KO; ++t)
+    for (int j = 0; j < NBW; ++j) acc[rr][j] = f32x16{};
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int rr = i / (NBLK / 8), qbl = (wave + 8 * (i % (NBLK / 8))) / CBN;
-        const f16* src = o_lds + ((rr * SH::QWG + qbl) * 32 + lq) * OP + g * 8;
-        acc[i] = mfma32(Wo[t], lds_f16x8((const char*)(src + t * 16)), acc[i]);
+  for (int t = 0; t < KO; ++t)
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        const int blk = wave + 8 * j;
+        if (NBLK % 8 == 0 || blk < NBLK) {   // uniform
+          const f16* src = o_lds + ((rr * SH::QWG + blk / CBN) * 32 + lq) * OP + g * 8;
+          acc[rr][j] = mfma32(Wo[t], lds_f16x8((const char*)(src + t * 16)), acc[rr][j]);
+        }
       }
+  if constexpr (C_OUT <= HD) {
+    // The workgroup's output tile (+ b_o, bf16) is staged in LDS over the o
+    // tiles, then stored query row by query row, 16 bytes per lane: the
+    // C_OUT channels of a query are contiguous at the caller's strides (and
+    // the whole tile is one run when positions are), so every store
+    // instruction writes whole cache lines, not 64-byte pieces of 32 rows.
+    constexpr int SP = C_OUT + 8;          // staged row pitch (bf16), rows 16-byte aligned
+    constexpr int NQ = SH::QWG * 32;       // queries of the workgroup
+    constexpr int CH = C_OUT / 8;          // 16-byte chunks of a query row
+    static_assert(RW * NQ * SP * 2 <= SH::LDS_KV, "staged output tile fits the K/V ring");
+    bf16* st_lds = reinterpret_cast<bf16*>(kv_lds);
+    __syncthreads();   // every wave has read the o tiles
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int rr = i / (NBLK / 8), qbl = (wave + 8 * (i % (NBLK / 8))) / CBN;
-      store_block(rr, qbl, acc[i]);
+    for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        const int blk = wave + 8 * j;
+        if (NBLK % 8 == 0 || blk < NBLK) {
+          bf16* o = st_lds + ((rr * SH::QWG + blk / CBN) * 32 + lq) * SP + cb_w * 32;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            bf16x4 ov;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int c = jj * 8 + g * 4 + e;
+              const float bo = b_o != nullptr ? bf2f(b_o[cb_w * 32 + c]) : 0.0f;
+              ov[e] = f2bf(acc[rr][j][jj * 4 + e] + bo);
+            }
+            st8(o + jj * 8 + g * 4, ov);
+          }
+        }
+      }
+    __syncthreads();
+    for (int i = threadIdx.x; i < RW * NQ * CH; i += 512) {
+      const int ch = i % CH, row = i / CH;
+      const int rr = row / NQ, qi = row % NQ;
+      const int r = r0 + rr, q = qb0_wg * 32 + qi;
+      if (r < nrows && q < P)
+        *reinterpret_cast<bf16x8*>(out + (int64_t)r * os_r + (int64_t)q * os_p + ch * 8) =
+            *reinterpret_cast<const bf16x8*>(st_lds + row * SP + ch * 8);
     }
   } else {
 #pragma unroll
-    for (int rr = 0; rr < RW; ++rr) {
-      for (int blk = wave; blk < NBLK; blk += 8) {
-        const int qbl = blk / CBN;             // query block within the workgroup
-        const f16* src = o_lds + ((rr * SH::QWG + qbl) * 32 + lq) * OP + g * 8;
-        f32x16 acc = {};
+    for (int rr = 0; rr < RW; ++rr)
 #pragma unroll
-        for (int t = 0; t < KO; ++t) acc = mfma32(Wo[t], lds_f16x8((const char*)(src + t * 16)), acc);
-        store_block(rr, qbl, acc);
+      for (int j = 0; j < NBW; ++j) {
+        const int blk = wave + 8 * j;
+        if (NBLK % 8 == 0 || blk < NBLK) store_block(rr, blk / CBN, acc[rr][j]);
       }
-    }
   }
 }
+
 
 // Keep bits and key-block range of each row, one wave per row:
 //   bits[r][kb]: bit b = key kb*32+b is kept (key < P and mask[r*ms_r +
