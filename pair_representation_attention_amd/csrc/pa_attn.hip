@@ -396,9 +396,13 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   constexpr int KO = HD / 16;
   const int cb_w = wave % CBN;
   f16x8 Gt[RW][QW][2], Wo[KO];
+  bf16x4 Bo[4];   // b_o of this lane's output channels cb_w*32 + jj*8 + g*4 + 0..3
   auto load_wo = [&]() {
 #pragma unroll
     for (int t = 0; t < KO; ++t) Wo[t] = ld16(woT + (int64_t)(cb_w * 32 + lq) * HD + t * 16 + g * 8);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      Bo[jj] = b_o != nullptr ? *reinterpret_cast<const bf16x4*>(b_o + cb_w * 32 + jj * 8 + g * 4) : bf16x4{};
   };
   auto load_epi = [&]() {
     if constexpr (MODE == 0) {
@@ -1033,6 +1037,9 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   if (!epi_loaded) load_epi();
   __builtin_amdgcn_s_setprio(0);
   wait_vm0();   // this wave's copies (dummies past the end included) have landed
+  // The output projection's operands (W_o rows, b_o) go out now: their
+  // latency passes while the workgroup gathers for the check below.
+  if constexpr (MODE == 0) load_wo();
   bool bad = false;
 #pragma unroll
   for (int rr = 0; rr < RW; ++rr)
@@ -1042,15 +1049,18 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       bad = bad || !(lt < __builtin_inff()) || (row_has_key[rr] && lt < 1.0f);
     }
   // Workgroup-wide "any wave bad", through the last words of the bias ring.
-  // After the first barrier every copy of every wave has landed and no wave
-  // reads the rings any more; a rerun writes that stage only after the first
-  // barrier of its own loop, which every wave reaches after reading the flags.
+  // After the first barrier every copy of every wave has landed (each waited
+  // for its own above) and no wave reads the rings any more; a rerun writes
+  // that stage only after the first barrier of its own loop, which every
+  // wave reaches after reading the flags.  Bare barriers: __syncthreads
+  // would also wait for the W_o loads in flight.
   {
     int* flag = reinterpret_cast<int*>(b_lds + SH::LDS_B - 8 * sizeof(int));
     const bool wbad = __ballot(bad) != 0;
-    __syncthreads();
+    barrier();
     if (lane == 0) flag[wave] = wbad ? 1 : 0;
-    __syncthreads();
+    wait_lgkm0();
+    barrier();
     int any = 0;
 #pragma unroll
     for (int w = 0; w < 8; ++w) any |= flag[w];
@@ -1058,7 +1068,9 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       sweep(std::integral_constant<bool, false>{});
       wait_vm0();
       __syncthreads();   // the rings are idle before the o tiles overwrite them
-      load_epi();   // (reloaded, so that the gate tiles are not live across the rerun)
+      // (reloaded, so that neither is live across the rerun)
+      load_epi();
+      if constexpr (MODE == 0) load_wo();
     }
   }
   if constexpr (MODE != 0) {
@@ -1110,7 +1122,6 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       }
     return;
   }
-  load_wo();
 
   // ---- epilogue: normalise, gate, output projection (both rows at once) ----
   constexpr int OP = HD + 8;                 // o tile pitch (fp16 elements)
@@ -1152,9 +1163,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         bf16x4 ov;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int c = jj * 8 + g * 4 + e;
-          const float bo = b_o != nullptr ? bf2f(b_o[cb_w * 32 + c]) : 0.0f;
-          ov[e] = f2bf(acc[jj * 4 + e] + bo);
+          ov[e] = f2bf(acc[jj * 4 + e] + bf2f(Bo[jj][e]));
         }
         st8(o + jj * 8 + g * 4, ov);
       }
@@ -1205,9 +1214,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             bf16x4 ov;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int c = jj * 8 + g * 4 + e;
-              const float bo = b_o != nullptr ? bf2f(b_o[cb_w * 32 + c]) : 0.0f;
-              ov[e] = f2bf(acc[rr][j][jj * 4 + e] + bo);
+              ov[e] = f2bf(acc[rr][j][jj * 4 + e] + bf2f(Bo[jj][e]));
             }
             st8(o + jj * 8 + g * 4, ov);
           }
