@@ -1241,41 +1241,12 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 }
 
 
-// Keep bits and key-block range of each row, one wave per row:
-//   bits[r][kb]: bit b = key kb*32+b is kept (key < P and mask[r*ms_r +
-//                key*ms_k] != 0, or no mask); a ballot of the wave packs the
-//                words of two blocks at once
-//   range[2r] = lo, the first block with a kept key (nkb if none);
-//   range[2r+1] = hi, one past the last such block (0 if none)
+// Keep bits and key-block range of each row, one wave per row (mask_bits_row)
 __global__ void mask_bits_kernel(const uint8_t* __restrict__ mask, int64_t ms_r, int64_t ms_k,
                                  uint32_t* __restrict__ bits, int* __restrict__ range, int nrows, int P, int nkb) {
-  const int lane = threadIdx.x % kWave;
   const int64_t row = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / kWave;
   if (row >= nrows) return;   // uniform over the wave
-  const uint8_t* mrow = mask != nullptr ? mask + row * ms_r : nullptr;
-  uint32_t* brow = bits + row * nkb;
-  int lo = nkb, hi = 0;
-  for (int kb0 = 0; kb0 < nkb; kb0 += 2) {
-    const int kb = kb0 + (lane >> 5);
-    const int key = kb * 32 + (lane & 31);
-    const bool keep = kb < nkb && key < P && (mrow == nullptr || mrow[(int64_t)key * ms_k] != 0);
-    const uint64_t m = __ballot(keep);
-    const uint32_t w0 = (uint32_t)m, w1 = (uint32_t)(m >> 32);
-    if (lane == 0) brow[kb0] = w0;
-    if (lane == 32 && kb0 + 1 < nkb) brow[kb0 + 1] = w1;
-    if (w0 != 0u) {
-      lo = min(lo, kb0);
-      hi = kb0 + 1;
-    }
-    if (w1 != 0u) {
-      lo = min(lo, kb0 + 1);
-      hi = kb0 + 2;
-    }
-  }
-  if (lane == 0) {
-    range[row * 2 + 0] = lo;
-    range[row * 2 + 1] = hi;
-  }
+  mask_bits_row(mask != nullptr ? mask + row * ms_r : nullptr, ms_k, bits + row * nkb, range + row * 2, P, nkb);
 }
 
 hipError_t launch_mask_bits(const uint8_t* mask, int64_t ms_r, int64_t ms_k, uint32_t* bits, int nrows, int P,

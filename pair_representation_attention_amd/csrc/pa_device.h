@@ -109,6 +109,54 @@ __device__ __forceinline__ int64_t b16_chunk(int h, int nbq, int nbk, int qb, in
   return ((((int64_t)h * nbq + qb) * nbk + kb) * 2 + c) * 512;
 }
 
+// Keep bits and key-block range of one row, by one wave:
+//   bits[kb]: bit b = key kb*32+b is kept (key < P and mrow[key*ms_k] != 0,
+//             or no mask); a ballot of the wave packs the words of two
+//             blocks at once
+//   range[0] = lo, the first block with a kept key (nkb if none);
+//   range[1] = hi, one past the last such block (0 if none)
+__device__ __forceinline__ void mask_bits_row(const uint8_t* __restrict__ mrow, int64_t ms_k,
+                                              uint32_t* __restrict__ brow, int* __restrict__ range, int P,
+                                              int nkb) {
+  const int lane = threadIdx.x % kWave;
+  int lo = nkb, hi = 0;
+  for (int kb0 = 0; kb0 < nkb; kb0 += 2) {
+    const int kb = kb0 + (lane >> 5);
+    const int key = kb * 32 + (lane & 31);
+    const bool keep = kb < nkb && key < P && (mrow == nullptr || mrow[(int64_t)key * ms_k] != 0);
+    const uint64_t m = __ballot(keep);
+    const uint32_t w0 = (uint32_t)m, w1 = (uint32_t)(m >> 32);
+    if (lane == 0) brow[kb0] = w0;
+    if (lane == 32 && kb0 + 1 < nkb) brow[kb0 + 1] = w1;
+    if (w0 != 0u) {
+      lo = min(lo, kb0);
+      hi = kb0 + 1;
+    }
+    if (w1 != 0u) {
+      lo = min(lo, kb0 + 1);
+      hi = kb0 + 2;
+    }
+  }
+  if (lane == 0) {
+    range[0] = lo;
+    range[1] = hi;
+  }
+}
+
+// beta . w_b[:, hh] (the pair-bias constant of head hh) by one wave: lane
+// partial sums in channel order, then a butterfly over the 64 lanes; every
+// lane returns the total.  One function for every place that forms it, so
+// that all of them give the same bits.
+__device__ __forceinline__ float pair_bias_const(const bf16* __restrict__ beta, const bf16* __restrict__ wb,
+                                                 int c_in, int H, int hh) {
+  const int lane = threadIdx.x % kWave;
+  float acc = 0.0f;
+  for (int k = lane; k < c_in; k += kWave) acc += bf2f(beta[k]) * bf2f(wb[(int64_t)k * H + hh]);
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+  return acc;
+}
+
 // Sum over an aligned group of `width` lanes (width a power of two <= 64).
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {

@@ -86,12 +86,55 @@ __device__ void pack_consts(const bf16* __restrict__ wq, const bf16* __restrict_
 }
 
 // One launch for both: blockIdx.y = 0 packs the weights, 1 the constants.
+// The pair-bias operand of the projection: w_b [c_in][H] with the
+// LayerNorm gamma of the biased tensor folded in, in the order the
+// projection keeps it in LDS (rows = heads, zero beyond H), and the
+// constants beta . w_b per head (pair_bias_const, as where the projection
+// builds the operand itself).
+__device__ void pack_bias_operand(const bf16* __restrict__ wb, const bf16* __restrict__ gamma,
+                                  const bf16* __restrict__ beta, f16* __restrict__ img, float* __restrict__ cbb,
+                                  int c_in, int H) {
+  const int ks = c_in / 16;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < ks * 64; i += gridDim.x * blockDim.x) {
+    const int l = i & 63, t = i >> 6, hh = l & 31;
+    const int k0 = t * 16 + (l >> 5) * 8;
+    f16x8 w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      w[e] = hh < H ? f2h_sat(bf2f(wb[(int64_t)(k0 + e) * H + hh]) * bf2f(gamma[k0 + e])) : f2h(0.0f);
+    *reinterpret_cast<f16x8*>(img + i * 8) = w;
+  }
+  // constants: one wave per head, heads 0..7 over the first two blocks
+  const int hh = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (hh < 8) {
+    const float c = hh < H ? pair_bias_const(beta, wb, c_in, H, hh) : 0.0f;
+    if (threadIdx.x % kWave == 0) cbb[hh] = c;
+  }
+}
+
+// One launch for a call's preparation, by blockIdx.y: 0 the q|k|v|g operand
+// image and W_o^T, 1 the column constants, 2 the pair-bias operand (when
+// wb_img is set), 3 the keep bits and key-block ranges of the mask rows
+// (when bits is set; one wave per row).
 __global__ void pack_kernel(const bf16* __restrict__ wq, const bf16* __restrict__ wk, const bf16* __restrict__ wv,
                             const bf16* __restrict__ wg, const bf16* __restrict__ wo, const bf16* __restrict__ gamma,
                             const bf16* __restrict__ beta, const bf16* __restrict__ b_g, f16* __restrict__ wimg,
-                            f16* __restrict__ woT, float* __restrict__ cst, int c_in, int hd, int c_out) {
-  if (blockIdx.y == 0) pack_weights(wq, wk, wv, wg, wo, gamma, wimg, woT, c_in, hd, c_out);
-  else pack_consts(wq, wk, wv, wg, beta, b_g, cst, c_in, hd);
+                            f16* __restrict__ woT, float* __restrict__ cst, int c_in, int hd, int c_out,
+                            const bf16* __restrict__ wb, const bf16* __restrict__ b_gamma,
+                            const bf16* __restrict__ b_beta, f16* __restrict__ wb_img, float* __restrict__ wb_cst,
+                            int b_c_in, int H, const uint8_t* __restrict__ mask, int64_t ms_r, int64_t ms_k,
+                            uint32_t* __restrict__ bits, int* __restrict__ range, int nrows, int P, int nkb) {
+  if (blockIdx.y == 0) {
+    pack_weights(wq, wk, wv, wg, wo, gamma, wimg, woT, c_in, hd, c_out);
+  } else if (blockIdx.y == 1) {
+    pack_consts(wq, wk, wv, wg, beta, b_g, cst, c_in, hd);
+  } else if (blockIdx.y == 2) {
+    if (wb_img != nullptr) pack_bias_operand(wb, b_gamma, b_beta, wb_img, wb_cst, b_c_in, H);
+  } else if (bits != nullptr) {
+    const int64_t row = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / kWave;
+    if (row < nrows)   // uniform over the wave
+      mask_bits_row(mask != nullptr ? mask + row * ms_r : nullptr, ms_k, bits + row * nkb, range + row * 2, P, nkb);
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -139,7 +182,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
     const bf16* __restrict__ beta, float eps, const f16* __restrict__ wimg, const float* __restrict__ cst,
     const bf16* __restrict__ wb, f16* __restrict__ q_ws, f16* __restrict__ k_ws,
     f16* __restrict__ v_ws, f16* __restrict__ g_ws, float* __restrict__ bias, int bias_swizzled, float bias_scale,
-    int nrows, int P, int Pp, int H) {
+    int nrows, int P, int Pp, int H, const f16* __restrict__ wb_img, const float* __restrict__ wb_cst) {
   using SH = ProjShape<C_IN, HD, NCOL, MODE>;
   constexpr int KS = SH::KS;
   constexpr int NW = kProjThreads / kWave;
@@ -167,7 +210,11 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
     for (int i = tid; i < SH::NBLK * KS * 64; i += kProjThreads) dst[i] = src[i];
   }
   for (int n = tid; n < NCOL; n += kProjThreads) cb[n] = cst[col0 + n];
-  if (SH::HAS_BIAS) {
+  if (SH::HAS_BIAS && wb_img != nullptr) {   // built by the preparation launch
+    for (int i = tid; i < KS * 64; i += kProjThreads)
+      *reinterpret_cast<f16x8*>(wb_lds + i * 8) = *reinterpret_cast<const f16x8*>(wb_img + i * 8);
+    if (tid < 8) cbb[tid] = wb_cst[tid];
+  } else if (SH::HAS_BIAS) {
     for (int i = tid; i < KS * 64; i += kProjThreads) {
       const int l = i & 63, t = i >> 6, hh = l & 31;
       const int k0 = t * 16 + (l >> 5) * 8;
@@ -177,11 +224,9 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
         w[e] = hh < H ? f2h_sat(bf2f(wb[(int64_t)(k0 + e) * H + hh]) * bf2f(gamma[k0 + e])) : f2h(0.0f);
       *reinterpret_cast<f16x8*>(wb_lds + i * 8) = w;
     }
-    if (tid < 8) {
-      float acc = 0.0f;
-      if (tid < H)
-        for (int k = 0; k < C_IN; ++k) acc += bf2f(beta[k]) * bf2f(wb[(int64_t)k * H + tid]);
-      cbb[tid] = acc;
+    {   // one wave per head (8 waves)
+      const float c = wave < H ? pair_bias_const(beta, wb, C_IN, H, wave) : 0.0f;
+      if (lane == 0) cbb[wave] = c;
     }
   }
   __syncthreads();
@@ -270,7 +315,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
     // Register 8t+e of lane half g holds accumulator row slot_x(t, g, e), so
     // registers 8t..8t+7 are exactly this lane's 16-byte slot of chunk t of
     // the operand image: every chunk is written as one contiguous 1 KB store.
-#pragma unroll 2
+#pragma unroll 4
     for (int b = 0; b < SH::NBLK; ++b) {
       const int col = col0 + b * 32;
       const int tensor = col / HD;            // 0 q, 1 k, 2 v, 3 g
@@ -412,15 +457,22 @@ hipError_t launch_bias_to_attn_layout(const float* src, void* dst, int H, int Pq
 
 hipError_t launch_pack_bf16(const PackArgs& a, hipStream_t s) {
   if (a.c_in % 16 != 0 || a.hd % 32 != 0) return hipErrorInvalidValue;
+  if (a.wb_img != nullptr && (a.b_c_in % 16 != 0 || a.b_c_in > 256 || a.H < 1 || a.H > 8)) return hipErrorInvalidValue;
   const int64_t total = (int64_t)4 * a.hd * a.c_in / 8 + (int64_t)a.c_out * a.hd;
   const int threads = 256;
   const int blocks_w = (int)std::min<int64_t>((total + threads - 1) / threads, 4096);   // grid-stride
   const int cols = 4 * a.hd, per_block = threads / kWave;
   const int blocks_c = (cols + per_block - 1) / per_block;                              // one wave per column
-  hipLaunchKernelGGL(pack_kernel, dim3(std::max(blocks_w, blocks_c), 2), dim3(threads), 0, s, (const bf16*)a.wq,
-                     (const bf16*)a.wk, (const bf16*)a.wv, (const bf16*)a.wg, (const bf16*)a.wo,
-                     (const bf16*)a.gamma, (const bf16*)a.beta, (const bf16*)a.b_g, (f16*)a.wT, (f16*)a.woT, a.cst,
-                     a.c_in, a.hd, a.c_out);
+  // (at least two blocks: their eight waves form the eight head constants)
+  const int blocks_b = a.wb_img != nullptr ? std::max(2, (a.b_c_in / 16 * 64 + threads - 1) / threads) : 0;
+  const int blocks_m = a.bits != nullptr ? (a.nrows + per_block - 1) / per_block : 0;   // one wave per row
+  const int blocks = std::max(std::max(blocks_w, blocks_c), std::max(blocks_b, blocks_m));
+  hipLaunchKernelGGL(pack_kernel, dim3(blocks, a.bits != nullptr ? 4 : a.wb_img != nullptr ? 3 : 2), dim3(threads), 0,
+                     s, (const bf16*)a.wq, (const bf16*)a.wk, (const bf16*)a.wv, (const bf16*)a.wg,
+                     (const bf16*)a.wo, (const bf16*)a.gamma, (const bf16*)a.beta, (const bf16*)a.b_g, (f16*)a.wT,
+                     (f16*)a.woT, a.cst, a.c_in, a.hd, a.c_out, (const bf16*)a.wb, (const bf16*)a.b_gamma,
+                     (const bf16*)a.b_beta, (f16*)a.wb_img, a.wb_cst, a.b_c_in, a.H, a.mask, a.ms_r, a.ms_k, a.bits,
+                     a.bits != nullptr ? mask_range_of(a.bits, a.nrows, a.nkb) : nullptr, a.nrows, a.P, a.nkb);
   return hipGetLastError();
 }
 
@@ -453,7 +505,7 @@ static hipError_t proj_dispatch(const ProjArgs& a, int num_cu, hipStream_t s) {
                      (const bf16*)a.x, a.xs_r, a.xs_p, rmajor, (const bf16*)a.gamma, (const bf16*)a.beta, a.eps,
                      (const f16*)a.wT, a.cst, (const bf16*)a.wb, (f16*)a.q_ws,
                      (f16*)a.k_ws, (f16*)a.v_ws, (f16*)a.g_ws, a.bias, a.bias_swizzled, a.bias_scale, a.nrows, a.P,
-                     a.Pp, a.H);
+                     a.Pp, a.H, (const f16*)a.wb_img, a.wb_cst);
   return hipGetLastError();
 }
 

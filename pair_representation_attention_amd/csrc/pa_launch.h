@@ -12,6 +12,19 @@ struct PackArgs {
   void *wT, *woT;                      // packed images in the workspace: gamma o W (operand order), W_o^T
   float* cst;                          // [4*hd] column constants beta . W (+ b_g)
   int c_in, hd, c_out;
+  // pair-bias operand (wb_img NULL: not built): w_b [b_c_in][H] with the
+  // LayerNorm gamma / beta of the biased tensor; image of b_c_in/16 KB and
+  // 8 constants, for ProjArgs.wb_img / wb_cst
+  const void *wb = nullptr, *b_gamma = nullptr, *b_beta = nullptr;
+  void* wb_img = nullptr;
+  float* wb_cst = nullptr;
+  int b_c_in = 0, H = 0;
+  // keep bits and ranges of nrows mask rows (bits NULL: none; layout of
+  // launch_mask_bits)
+  const uint8_t* mask = nullptr;
+  int64_t ms_r = 0, ms_k = 0;
+  uint32_t* bits = nullptr;
+  int nrows = 0, P = 0, nkb = 0;
 };
 
 // LayerNorm + projection of nrows x P positions.  Element (r, p, c) of the
@@ -29,6 +42,10 @@ struct ProjArgs {
   int bias_swizzled;             // 1: attention layout (fp16 operand order, Pp x Pp, zero padded); 0: [H][P][P] float
   float bias_scale;              // multiplies the stored bias (log2(e) for the attention layout)
   int c_in, hd, H, nrows, P, Pp;
+  // the pair-bias operand and constants from launch_pack_bf16 (NULL: each
+  // workgroup builds them from wb, gamma and beta)
+  const void* wb_img = nullptr;
+  const float* wb_cst = nullptr;
 };
 
 struct AttnArgs {

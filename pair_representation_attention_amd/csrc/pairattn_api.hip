@@ -40,9 +40,11 @@ constexpr int64_t kMaxRows = 65535LL * 4;
 constexpr int64_t kMaxPositions = 1LL << 20;
 
 // ---- workspace layout -----------------------------------------------------
+constexpr size_t kWbImgBytes = 256 / 16 * 1024;   // pair-bias operand image for up to 256 channels
+
 struct Layout {
   // bf16 path
-  size_t wT = 0, woT = 0, q = 0, k = 0, v = 0, g = 0, bias = 0, bits = 0;
+  size_t wT = 0, woT = 0, q = 0, k = 0, v = 0, g = 0, bias = 0, bits = 0, wb_img = 0;
   // fp32 path: hi/lo planes of q, k, v and of the packed weights
   size_t q_lo = 0, k_lo = 0, v_lo = 0, w_hi = 0, w_lo = 0, cst = 0, wo_hi = 0, wo_lo = 0;
   size_t total = 0;
@@ -63,6 +65,7 @@ Layout make_layout(int64_t nrows, int64_t P, int64_t c_in, int64_t c_out, int64_
   if (dtype == PAIRATTN_BF16) {
     L.wT = take((size_t)4 * hd * c_in * 2);
     L.cst = take((size_t)4 * hd * 4);
+    L.wb_img = take(kWbImgBytes + 8 * 4);   // pair-bias operand (c <= 256) and its 8 constants
     L.woT = take((size_t)c_out * hd * 2);
     L.q = take(plane);
     L.k = take(plane);
@@ -632,10 +635,37 @@ static int run_row_attention_bf16(const pairattn_params* p, const Layout& L, hip
   pk.c_in = (int)ra.c;
   pk.hd = (int)hd;
   pk.c_out = (int)ra.c;
+  // the same launch builds the pair-bias operand (bias from the projected
+  // tensor or from the pair tensor) and the keep bits of the mask
+  void* wb_img = ws_at(p, L.wb_img);
+  float* wb_cst = reinterpret_cast<float*>(static_cast<char*>(wb_img) + kWbImgBytes);
+  if (ra.bias_in_proj || ra.zb != nullptr) {
+    pk.wb = p->w_b;
+    pk.b_gamma = ra.zb != nullptr ? p->lnz_gamma : p->ln_gamma;
+    pk.b_beta = ra.zb != nullptr ? p->lnz_beta : p->ln_beta;
+    pk.b_c_in = (int)(ra.zb != nullptr ? ra.zb_c : ra.c);
+    pk.H = (int)ra.H;
+    pk.wb_img = wb_img;
+    pk.wb_cst = wb_cst;
+  }
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws_at(p, L.bits));
+  if (ra.mask != nullptr) {
+    pk.mask = ra.mask;
+    pk.ms_r = ra.ms_r;
+    pk.ms_k = ra.ms_k;
+    pk.bits = bits;
+    pk.nrows = (int)ra.nrows;
+    pk.P = (int)ra.P;
+    pk.nkb = Pp / 32;
+  }
   PA_TRY(hip_status(pa::launch_pack_bf16(pk, s), "weight packing launch"));
   mark("pack");
   pj.wT = ws_at(p, L.wT);
   pj.cst = reinterpret_cast<const float*>(ws_at(p, L.cst));
+  if (ra.bias_in_proj) {
+    pj.wb_img = wb_img;
+    pj.wb_cst = wb_cst;
+  }
   PA_TRY(hip_status(pa::launch_proj_bf16(pj, ra.bias_in_proj ? 1 : 0, num_cu, s), "projection launch"));
   mark("projection");
 
@@ -657,6 +687,8 @@ static int run_row_attention_bf16(const pairattn_params* p, const Layout& L, hip
     pb.nrows = (int)ra.P;
     pb.P = (int)ra.P;
     pb.Pp = Pp;
+    pb.wb_img = wb_img;
+    pb.wb_cst = wb_cst;
     PA_TRY(hip_status(pa::launch_proj_bf16(pb, 2, num_cu, s), "pair-bias launch"));
     mark("pair_bias");
   }
@@ -673,8 +705,7 @@ static int run_row_attention_bf16(const pairattn_params* p, const Layout& L, hip
   at.g_ws = pj.g_ws;
   at.bias = bias_ws;
   // keep bits only when there is a mask (without one the kernel drops just
-  // the keys past P, which it computes)
-  uint32_t* bits = reinterpret_cast<uint32_t*>(ws_at(p, L.bits));
+  // the keys past P, which it computes); built by the preparation launch
   at.mask_bits = ra.mask != nullptr ? bits : nullptr;
   at.mask_range = ra.mask != nullptr ? pa::mask_range_of(bits, ra.nrows, Pp / 32) : nullptr;
   at.woT = ws_at(p, L.woT);
@@ -687,11 +718,6 @@ static int run_row_attention_bf16(const pairattn_params* p, const Layout& L, hip
   at.nrows = (int)ra.nrows;
   at.P = (int)ra.P;
   at.Pp = Pp;
-  if (ra.mask != nullptr) {
-    PA_TRY(hip_status(pa::launch_mask_bits(ra.mask, ra.ms_r, ra.ms_k, bits, (int)ra.nrows, (int)ra.P, Pp / 32, s),
-                      "mask bits launch"));
-    mark("mask_bits");
-  }
   PA_TRY(hip_status(pa::launch_attn_bf16(at, s), "attention launch"));
   mark("attention");
   return PAIRATTN_OK;
