@@ -122,6 +122,48 @@ def test_block_mixed_masks(I):
         assert np.array_equal(sel, np.broadcast_to(bo, sel.shape))
 
 
+# The same patterns at H = 8, where a workgroup is one row and three query
+# blocks, each wave copies and reads only its own tiles, and a block's keep
+# bits enter the logits through the operand that widens the bias (-inf for
+# masked keys) instead of a select per unit.
+@pytest.mark.parametrize("I", [160, 200])
+def test_block_mixed_masks_h8(I):
+    case = inputs.make_tri_case(I=I, c=128, H=8, d=32, dtype="bf16", mask="none", seed=400 + I, affine=True,
+                                biases=True)
+    rows = _block_mix_mask(I, seed=I + 1)
+    dev = _dev()
+    for ori, p in ((0, case.params_start), (1, case.params_end)):
+        mask = rows if ori == 0 else np.ascontiguousarray(rows.T)
+        got = gpu_to_f64(dev.TriRunner(case.z, mask, p, 8, "bf16")(ori))
+        ref = oracle.tri_fwd(case.z, mask, p.as_dict(), 8, ori)
+        check(got, ref, "bf16", f"block-mixed mask H=8 I={I} ori={ori}")
+        none = np.where(~rows.any(axis=1))[0]
+        assert len(none) > 0
+        bo = inputs.round_to_bf16(p.b_o.astype(np.float32)).astype(np.float64)
+        sel = got[none, :, :] if ori == 0 else got[:, none, :]
+        assert np.array_equal(sel, np.broadcast_to(bo, sel.shape))
+
+
+# MSA row attention at H = 8 over several key blocks: without a mask and I a
+# multiple of 32 (no select at all; with 5 blocks the copies of block kb+2
+# go out while blocks kb and kb+1 are in flight), and with the block
+# patterns above as the sequences' masks (a sequence without a kept key
+# gives out = b_o).
+@pytest.mark.parametrize("S,I,mask", [(6, 96, "none"), (4, 160, "none"), (16, 200, "blocks")])
+def test_msa_h8_sweep_shapes(S, I, mask):
+    case = inputs.make_msa_case(S=S, I=I, c_m=256, c_z=128, H=8, d=32, dtype="bf16", mask="none", seed=500 + I,
+                                affine=True, biases=True)
+    m = None if mask == "none" else np.ascontiguousarray(_block_mix_mask(I, seed=I + 2)[:S])
+    got = gpu_to_f64(_dev().MsaRunner(case.m, case.z, m, case.params, 8, "bf16")())
+    ref = oracle.msa_row(case.m, case.z, m, case.params.as_dict(), 8)
+    check(got, ref, "bf16", f"msa H=8 S={S} I={I} mask={mask}")
+    if m is not None:
+        none = np.where(~m.any(axis=1))[0]
+        assert len(none) > 0
+        bo = inputs.round_to_bf16(case.params.b_o.astype(np.float32)).astype(np.float64)
+        assert np.array_equal(got[none], np.broadcast_to(bo, got[none].shape))
+
+
 # ----------------------------------------------------------------------------
 # logits far from zero: the kernel's zero-shift sweep cannot represent the
 # softmax weights there (fp16 overflow above 2^16, too little mass below), so
