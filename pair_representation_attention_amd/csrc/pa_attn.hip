@@ -301,6 +301,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     for (int qq = 0; qq < QW; ++qq) {
       const int qblk = min(qb0 + qq, nbq - 1);
       const int64_t rh = (int64_t)rows_c[rr] * H + h;
+      PA_DCHECK(qkv_chunk(rh, nbq, qblk, 1) + 512 <= (int64_t)nrows * H * nbq * 1024, 3);
       Q[rr][qq][0] = ld16(q_ws + qkv_chunk(rh, nbq, qblk, 0) + lane * 8);
       Q[rr][qq][1] = ld16(q_ws + qkv_chunk(rh, nbq, qblk, 1) + lane * 8);
       O[rr][qq] = f32x16{};
@@ -344,14 +345,23 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     char* base = kv_lds + (kb % SH::NKV) * SH::KV_STAGE;
 #pragma unroll
     for (int j = 0; j < NCW; ++j)
-      if (j >= j0 && j < j1) g2lds16_ring(kv_src[j] + (int64_t)kbc * 1024 + lane * 8, base + kv_off[j]);
+      if (j >= j0 && j < j1) {
+        PA_DCHECK((kv_src[j] - ((wave & 3) < 2 ? k_ws : v_ws)) + (int64_t)kbc * 1024 + 512 <=
+                      (int64_t)nrows * H * nkb * 1024, 0);   // one 512-element chunk
+        PA_DCHECK(kv_off[j] + 1024 <= SH::KV_STAGE, 2);
+        g2lds16_ring(kv_src[j] + (int64_t)kbc * 1024 + lane * 8, base + kv_off[j]);
+      }
   };
   auto stage_b = [&](int kb, int j0, int j1) {
     const int kbc = min(kb, nkb - 1);
     char* base = b_lds + (kb & 1) * SH::B_STAGE;
 #pragma unroll
     for (int j = 0; j < NCB; ++j)
-      if (j >= j0 && j < j1) g2lds16_ring(b_src[j] + (int64_t)kbc * 1024 + lane * 8, base + b_off[j]);
+      if (j >= j0 && j < j1) {
+        PA_DCHECK((b_src[j] - bias) + (int64_t)kbc * 1024 + 512 <= (int64_t)H * nbq * nkb * 1024, 1);
+        PA_DCHECK(b_off[j] + 1024 <= SH::B_STAGE, 2);
+        g2lds16_ring(b_src[j] + (int64_t)kbc * 1024 + lane * 8, base + b_off[j]);
+      }
   };
   // The copies of one block (bias stage kb+1, then K/V stage kb+NKV-1) are
   // spread over its units, so that the address unit works through them while
@@ -411,6 +421,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
         for (int qq = 0; qq < QW; ++qq) {
           const int64_t rh = (int64_t)rows_c[rr] * H + h;
+          PA_DCHECK(qkv_chunk(rh, nbq, min(qb0 + qq, nbq - 1), 1) + 512 <= (int64_t)nrows * H * nbq * 1024, 3);
           const f16* gp = g_ws + qkv_chunk(rh, nbq, min(qb0 + qq, nbq - 1), 0) + lane * 8;
           Gt[rr][qq][0] = ld16(gp);
           Gt[rr][qq][1] = ld16(gp + 512);
@@ -707,14 +718,22 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       const f16* src = kv_base + (int64_t)kbc * 1024;
       const uint32_t base = (uint32_t)(uintptr_t)(lds_void_t*)(kv_lds + (kb % SH::NKV) * SH::KV_STAGE);
 #pragma unroll
-      for (int j = j0; j < j1; ++j) g2lds16_sbase(src, kv_voff[j], base + kv_off[j]);
+      for (int j = j0; j < j1; ++j) {
+        PA_DCHECK((src - ((wave & 3) < 2 ? k_ws : v_ws)) * 2 + kv_voff[j] + 16 <= (int64_t)nrows * H * nkb * 2048, 0);
+        PA_DCHECK(kv_off[j] + 1024 <= SH::KV_STAGE, 2);
+        g2lds16_sbase(src, kv_voff[j], base + kv_off[j]);
+      }
     };
     auto copy_b = [&](int kb) {
       const int kbc = min(kb, nkb - 1);
       const f16* src = b_base + (int64_t)kbc * 1024;
       const uint32_t base = (uint32_t)(uintptr_t)(lds_void_t*)(b_lds + (kb & 1) * SH::B_STAGE);
 #pragma unroll
-      for (int j = 0; j < NCB; ++j) g2lds16_sbase(src, b_voff[j], base + b_off[j]);
+      for (int j = 0; j < NCB; ++j) {
+        PA_DCHECK((src - bias) * 2 + b_voff[j] + 16 <= (int64_t)H * nbq * nkb * 2048, 1);
+        PA_DCHECK(b_off[j] + 1024 <= SH::B_STAGE, 2);
+        g2lds16_sbase(src, b_voff[j], base + b_off[j]);
+      }
     };
     auto kv_tile = [&](int kb, int rr) -> const char* {
       return kv_lds + (kb % SH::NKV) * SH::KV_STAGE + (rr * H + h) * SH::KV_TILE + lane * 16;
@@ -877,6 +896,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     constexpr int NCPB = 4 + 2 * QW;
     auto copy_block = [&](int kb) {
       const int64_t e = (int64_t)kb * 1024;
+      PA_DCHECK((k_base - k_ws) + e + 1024 <= (int64_t)nrows * H * nkb * 1024, 0);
+      PA_DCHECK((b_base - bias) * 2 + e * 2 + b_voff[QW - 1] + 1024 + 16 <= (int64_t)H * nbq * nkb * 2048, 1);
       const uint32_t kv = (uint32_t)(uintptr_t)(lds_void_t*)kv_at(kb);
       g2lds16_sbase(k_base + e, lane16, kv);
       g2lds16_sbase(k_base + e, lane16 + 1024, kv + 1024);
@@ -1208,6 +1229,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       for (int j = 0; j < NBW; ++j) {
         const int blk = wave + 8 * j;
         if (NBLK % 8 == 0 || blk < NBLK) {
+          PA_DCHECK(((rr * SH::QWG + blk / CBN) * 32 + lq) * SP + cb_w * 32 + 32 <= RW * NQ * SP, 7);
           bf16* o = st_lds + ((rr * SH::QWG + blk / CBN) * 32 + lq) * SP + cb_w * 32;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
@@ -1248,6 +1270,8 @@ __global__ void mask_bits_kernel(const uint8_t* __restrict__ mask, int64_t ms_r,
   if (row >= nrows) return;   // uniform over the wave
   mask_bits_row(mask != nullptr ? mask + row * ms_r : nullptr, ms_k, bits + row * nkb, range + row * 2, P, nkb);
 }
+
+hipError_t debug_take_attn(unsigned int* out) { return pa_debug_take(out); }
 
 hipError_t launch_mask_bits(const uint8_t* mask, int64_t ms_r, int64_t ms_k, uint32_t* bits, int nrows, int P,
                             int nkb, hipStream_t s) {

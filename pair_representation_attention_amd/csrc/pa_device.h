@@ -109,6 +109,37 @@ __device__ __forceinline__ int64_t b16_chunk(int h, int nbq, int nbk, int qb, in
   return ((((int64_t)h * nbq + qb) * nbk + kb) * 2 + c) * 512;
 }
 
+// Index checks of the debug build (-DPA_DEBUG).  A failed check sets bit
+// `bit` of this source file's flag word with a vector atomic and the kernel
+// goes on, so a bad index is reported instead of trapping; the host takes
+// (reads and clears) the words after a call (pairattn_debug_status).  Bits:
+//   0 K/V copy source   1 bias copy source   2 LDS stage address
+//   3 q / gate tile     4 projection store   5 pair-bias store
+//   6 keep-bits word    7 staged output tile in LDS
+// In the release build the checks compile to nothing.
+#ifdef PA_DEBUG
+static __device__ unsigned int pa_dbg_flags;
+#define PA_DCHECK(cond, bit)                                                      \
+  do {                                                                            \
+    if (!(cond)) atomicOr(&pa_dbg_flags, 1u << (bit));                           \
+  } while (0)
+// this file's flag word, then cleared (host side)
+static inline hipError_t pa_debug_take(unsigned int* out) {
+  hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(pa_dbg_flags), sizeof(unsigned int));
+  if (e != hipSuccess) return e;
+  const unsigned int zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(pa_dbg_flags), &zero, sizeof(unsigned int));
+}
+#else
+#define PA_DCHECK(cond, bit) \
+  do {                       \
+  } while (0)
+static inline hipError_t pa_debug_take(unsigned int* out) {
+  *out = 0;
+  return hipSuccess;
+}
+#endif
+
 // Keep bits and key-block range of one row, by one wave:
 //   bits[kb]: bit b = key kb*32+b is kept (key < P and mrow[key*ms_k] != 0,
 //             or no mask); a ballot of the wave packs the words of two
@@ -126,6 +157,7 @@ __device__ __forceinline__ void mask_bits_row(const uint8_t* __restrict__ mrow, 
     const bool keep = kb < nkb && key < P && (mrow == nullptr || mrow[(int64_t)key * ms_k] != 0);
     const uint64_t m = __ballot(keep);
     const uint32_t w0 = (uint32_t)m, w1 = (uint32_t)(m >> 32);
+    PA_DCHECK(kb0 < nkb, 6);
     if (lane == 0) brow[kb0] = w0;
     if (lane == 32 && kb0 + 1 < nkb) brow[kb0 + 1] = w1;
     if (w0 != 0u) {

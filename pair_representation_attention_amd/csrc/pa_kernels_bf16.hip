@@ -344,6 +344,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
             for (int e = 0; e < 8; ++e)
               o[e] = p0 + slot_x(t, g, e) < P ? f2h_sat(acc[8 * t + e] + c) : f2h(0.0f);
           }
+          PA_DCHECK((chunk0 + t + 1) * 512 <= (int64_t)nrows * H * nb * 1024, 4);
           st16(v_ws + (chunk0 + t) * 512 + lane * 8, o);
         }
       } else {                                // out^T = W^T X^T: rows = channels, lane = position
@@ -364,6 +365,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
               o[e] = f2h_sat(acc[8 * t + e] + c0[e]);
               o[4 + e] = f2h_sat(acc[8 * t + 4 + e] + c1[e]);
             }
+            PA_DCHECK((chunk0 + t + 1) * 512 <= (int64_t)nrows * H * nb * 1024, 4);
             st16((tensor == 0 ? q_ws : k_ws) + (chunk0 + t) * 512 + lane * 8, o);
           } else {                            // gate: sigmoid, same layout as q
 #pragma unroll
@@ -371,6 +373,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
               o[e] = f2h(sigmoid_from_log2(acc[8 * t + e] + c0[e]));
               o[4 + e] = f2h(sigmoid_from_log2(acc[8 * t + 4 + e] + c1[e]));
             }
+            PA_DCHECK((chunk0 + t + 1) * 512 <= (int64_t)nrows * H * nb * 1024, 4);
             st16(g_ws + (chunk0 + t) * 512 + lane * 8, o);
           }
         }
@@ -389,6 +392,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
         for (int j = 0; j < 4; ++j) {          // heads (< 8) are rows g*4 + j of registers 0..3
           const int hh = acc_row(j, g);
           if (hh < H) {
+            PA_DCHECK(b16_off(hh, nb, nb, r, p) < (int64_t)H * nb * nb * 1024, 5);
             b16[b16_off(hh, nb, nb, r, p)] = valid ? f2h_sat((acc[j] + cbb[hh]) * bias_scale) : f2h(0.0f);
             if (r == P - 1)   // the padded query rows get zeros at the same keys
               for (int rp = P; rp < Pp; ++rp) b16[b16_off(hh, nb, nb, rp, p)] = f2h(0.0f);
@@ -454,6 +458,8 @@ hipError_t launch_bias_to_attn_layout(const float* src, void* dst, int H, int Pq
                      Ppk);
   return hipGetLastError();
 }
+
+hipError_t debug_take_bf16(unsigned int* out) { return pa_debug_take(out); }
 
 hipError_t launch_pack_bf16(const PackArgs& a, hipStream_t s) {
   if (a.c_in % 16 != 0 || a.hd % 32 != 0) return hipErrorInvalidValue;

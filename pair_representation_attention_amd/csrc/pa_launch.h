@@ -164,4 +164,9 @@ hipError_t launch_attn_f32(const AttnF32Args& a, hipStream_t s);
 // gate (g_ws), output projection and store of merged partial outputs o_part
 hipError_t launch_finish_f32(const AttnF32Args& a, hipStream_t s);
 
+// Flag words of the debug build's index checks, one per source file: each
+// call reads its file's word and clears it (0 in the release build).
+hipError_t debug_take_attn(unsigned int* out);
+hipError_t debug_take_bf16(unsigned int* out);
+
 }  // namespace pa

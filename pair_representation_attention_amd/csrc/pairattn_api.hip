@@ -383,6 +383,23 @@ int pairattn_calibrate_exp2(float* out, int64_t iters, void* stream) {
   return hip_status(pa::launch_calib_exp2(out, (int)iters, static_cast<hipStream_t>(stream)), "exp2 calibration launch");
 }
 
+int pairattn_debug_status(uint32_t* flags, int32_t* checking) {
+  g_err[0] = '\0';
+  unsigned int a = 0, b = 0;
+#ifdef PA_DEBUG
+  if (hipDeviceSynchronize() != hipSuccess) return fail(PAIRATTN_ERR_HIP, "device synchronisation failed");
+  if (pa::debug_take_attn(&a) != hipSuccess || pa::debug_take_bf16(&b) != hipSuccess)
+    return fail(PAIRATTN_ERR_HIP, "reading the debug flag words failed");
+#endif
+  if (flags != nullptr) *flags = a | b;
+#ifdef PA_DEBUG
+  if (checking != nullptr) *checking = 1;
+#else
+  if (checking != nullptr) *checking = 0;
+#endif
+  return PAIRATTN_OK;
+}
+
 const char* pairattn_status_string(int status) {
   switch (status) {
     case PAIRATTN_OK: return "ok";

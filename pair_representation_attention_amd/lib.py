@@ -18,6 +18,8 @@ from typing import Optional
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libpairattn.so")
+# the same library with the kernels' index checks on (pairattn_debug_status)
+DEBUG_LIB_PATH = os.path.join(PKG_DIR, "libpairattn_debug.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "pairattn.h")
 
 PAIRATTN_OK = 0
@@ -104,6 +106,7 @@ _SIGNATURES = {
     "pairattn_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p),
                                             ctypes.c_int]),
     "pairattn_calibrate_exp2": (ctypes.c_int, [_P, _I64, _P]),
+    "pairattn_debug_status": (ctypes.c_int, [_P, _P]),
 }
 
 
@@ -286,6 +289,15 @@ def pairattn_timing_enable(enable: bool) -> bool:
     if st < 0:
         raise PairAttnError(-st, "pairattn_timing_enable", last_error())
     return bool(st)
+
+
+def pairattn_debug_status():
+    """(flags, checking) of the debug build's index checks (flags cleared);
+    (0, 0) from the release build."""
+    f = ctypes.c_uint32(0)
+    c = ctypes.c_int32(0)
+    _check(load().pairattn_debug_status(ctypes.byref(f), ctypes.byref(c)), "pairattn_debug_status")
+    return int(f.value), int(c.value)
 
 
 def pairattn_calibrate_exp2(out, iters: int, stream=None, check=True) -> int:
