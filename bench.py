@@ -707,7 +707,9 @@ def ring_workload(args, device, inputs, lib, torch) -> dict:
 
     def step(record=False):
         for sidx in range(2):
-            lib.pairattn_tri_partial_fwd(zq, shards[sidx], btiles[sidx], None, prm, o, lse, sidx > 0, half, half,
+            # later shards merge, and reuse the packed weights and the projected q of the query pairs
+            flags = 0 if sidx == 0 else lib.PAIRATTN_PARTIAL_MERGE | lib.PAIRATTN_PARTIAL_Q_READY
+            lib.pairattn_tri_partial_fwd(zq, shards[sidx], btiles[sidx], None, prm, o, lse, flags, half, half,
                                          half, c, H, d)
             if record:
                 for name, ms in lib.pairattn_timing_read():

@@ -213,11 +213,20 @@ int pairattn_tri_chunked_fwd(const void *z, const uint8_t *mask, const pairattn_
  *                          over the shard's kept keys (0 with none)
  *   lse      [R][H][Jq]    float: ln sum_k exp(logit_k) over those keys
  *                          (-inf with none)
- * accumulate = 0 writes o and lse; accumulate != 0 merges this shard into
- * the o and lse already there: lse' = ln(e^lse + e^lse_s),
- * o' = e^(lse - lse') o + e^(lse_s - lse') o_s.  kv_pairs may be q_pairs
- * itself (Kn = Jq: the device's own shard); q, k and v then come from one
- * pass over it.  Workspace: pairattn_tri_partial_workspace_bytes. */
+ * accumulate holds bits: without PAIRATTN_PARTIAL_MERGE the call writes o
+ * and lse; with it the call merges this shard into the o and lse already
+ * there: lse' = ln(e^lse + e^lse_s), o' = e^(lse - lse') o + e^(lse_s -
+ * lse') o_s.  PAIRATTN_PARTIAL_Q_READY states that the workspace holds what
+ * the previous call with this workspace left: the packed weights and the
+ * projected q of the same q_pairs, params, R, Jq, c_z, H and d (the caller
+ * keeps them unchanged in between, e.g. along the shards of one ring step);
+ * neither is formed again.  Other bits: PAIRATTN_ERR_ARG.  kv_pairs may be
+ * q_pairs itself (Kn = Jq: the device's own shard); its k and v (and q
+ * unless ready) then come from one pass over it.  Workspace:
+ * pairattn_tri_partial_workspace_bytes (the q plane's place in it does not
+ * depend on Kn, so shards of any size share it). */
+#define PAIRATTN_PARTIAL_MERGE 1
+#define PAIRATTN_PARTIAL_Q_READY 2
 size_t pairattn_tri_partial_workspace_bytes(int64_t R, int64_t Jq, int64_t Kn, int64_t c_z,
                                             int64_t H, int64_t d, int32_t dtype);
 int pairattn_tri_partial_fwd(const void *q_pairs, const void *kv_pairs, const float *bias,

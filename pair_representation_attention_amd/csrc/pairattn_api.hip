@@ -1085,6 +1085,11 @@ int pairattn_tri_partial_fwd(const void* q_pairs, const void* kv_pairs, const fl
                              const pairattn_params* p, float* o, float* lse, int32_t accumulate, int64_t R, int64_t Jq,
                              int64_t Kn, int64_t c_z, int64_t H, int64_t d, void* stream) {
   PA_TRY(pairattn_validate_tri_partial(q_pairs, kv_pairs, bias, mask, p, o, lse, R, Jq, Kn, c_z, H, d));
+  if (accumulate & ~(PAIRATTN_PARTIAL_MERGE | PAIRATTN_PARTIAL_Q_READY))
+    return fail(PAIRATTN_ERR_ARG, "accumulate %d has bits other than PAIRATTN_PARTIAL_MERGE and PAIRATTN_PARTIAL_Q_READY",
+                accumulate);
+  const bool merge = (accumulate & PAIRATTN_PARTIAL_MERGE) != 0;
+  const bool q_ready = (accumulate & PAIRATTN_PARTIAL_Q_READY) != 0;
   int num_cu = 0;
   PA_TRY(check_device(&num_cu));
   const PartialLayout L = make_partial_layout(R, Jq, Kn, c_z, H, p->dtype);
@@ -1108,9 +1113,12 @@ int pairattn_tri_partial_fwd(const void* q_pairs, const void* kv_pairs, const fl
     pk.c_in = (int)c_z;
     pk.hd = (int)hd;
     pk.c_out = (int)c_z;
-    PA_TRY(hip_status(pa::launch_pack_bf16(pk, s), "weight packing launch"));
-    tm_mark(s, "pack");
-    // q of the query pairs, k and v of the key pairs (the other planes NULL)
+    if (!q_ready) {
+      PA_TRY(hip_status(pa::launch_pack_bf16(pk, s), "weight packing launch"));
+      tm_mark(s, "pack");
+    }
+    // q of the query pairs (unless ready), k and v of the key pairs (the
+    // other planes NULL)
     pa::ProjArgs pj{};
     pj.x = q_pairs;
     pj.xs_r = Jq * c_z;
@@ -1120,7 +1128,7 @@ int pairattn_tri_partial_fwd(const void* q_pairs, const void* kv_pairs, const fl
     pj.eps = p->ln_eps;
     pj.wT = ws_at(p, L.wT);
     pj.cst = reinterpret_cast<const float*>(ws_at(p, L.cst));
-    pj.q_ws = ws_at(p, L.q);
+    pj.q_ws = q_ready ? nullptr : ws_at(p, L.q);
     pj.c_in = (int)c_z;
     pj.hd = (int)hd;
     pj.H = (int)H;
@@ -1133,7 +1141,7 @@ int pairattn_tri_partial_fwd(const void* q_pairs, const void* kv_pairs, const fl
       pj.k_ws = ws_at(p, L.k);
       pj.v_ws = ws_at(p, L.v);
     }
-    PA_TRY(hip_status(pa::launch_proj_bf16(pj, 0, num_cu, s), "query projection launch"));
+    if (own || !q_ready) PA_TRY(hip_status(pa::launch_proj_bf16(pj, 0, num_cu, s), "query projection launch"));
     if (!own) {
       pj.x = kv_pairs;
       pj.xs_r = Kn * c_z;
@@ -1166,7 +1174,7 @@ int pairattn_tri_partial_fwd(const void* q_pairs, const void* kv_pairs, const fl
     at.nrows = (int)R;
     at.P = (int)Jq;
     at.Pp = Ppq;
-    at.mode = accumulate ? 2 : 1;
+    at.mode = merge ? 2 : 1;
     at.Pk = (int)Kn;
     at.Ppk = Ppk;
     at.o_part = o;
@@ -1190,9 +1198,12 @@ int pairattn_tri_partial_fwd(const void* q_pairs, const void* kv_pairs, const fl
   pk.hd = (int)hd;
   pk.H = (int)H;
   pk.nqkvg = (int)(4 * hd / 32);
-  PA_TRY(hip_status(pa::launch_pack_f32(pk, s), "weight packing launch"));
-  tm_mark(s, "pack");
-  // q of the query pairs (blocks [0, hd/32)), k and v of the key pairs (blocks [hd/32, 3*hd/32))
+  if (!q_ready) {
+    PA_TRY(hip_status(pa::launch_pack_f32(pk, s), "weight packing launch"));
+    tm_mark(s, "pack");
+  }
+  // q of the query pairs (blocks [0, hd/32); unless ready), k and v of the
+  // key pairs (blocks [hd/32, 3*hd/32))
   pa::ProjF32Args pj{};
   pj.eps = p->ln_eps;
   pj.w_hi = pk.w_hi;
@@ -1217,10 +1228,11 @@ int pairattn_tri_partial_fwd(const void* q_pairs, const void* kv_pairs, const fl
   pj.b_first = 0;
   // the device's own shard (the query pairs' buffer): q, k and v in one pass
   const bool own = kv_pairs == q_pairs && Kn == Jq;
-  pj.nqkvg = (int)((own ? 3 : 1) * hd / 32);
+  pj.b_first = q_ready ? (int)(hd / 32) : 0;
+  pj.nqkvg = (int)((own ? 3 : 1) * hd / 32) - pj.b_first;
   pj.P = (int)Jq;
   pj.Pp = Ppq;
-  PA_TRY(hip_status(pa::launch_proj_f32(pj, num_cu, s), "query projection launch"));
+  if (pj.nqkvg > 0) PA_TRY(hip_status(pa::launch_proj_f32(pj, num_cu, s), "query projection launch"));
   if (!own) {
     pj.x = kv_pairs;
     pj.xs_r = Kn * c_z;
@@ -1256,7 +1268,7 @@ int pairattn_tri_partial_fwd(const void* q_pairs, const void* kv_pairs, const fl
   at.Pp = Ppq;
   at.Pk = (int)Kn;
   at.Ppk = Ppk;
-  at.mode = accumulate ? 2 : 1;
+  at.mode = merge ? 2 : 1;
   at.o_part = o;
   at.lse_part = lse;
   PA_TRY(hip_status(pa::launch_attn_f32(at, s), "attention launch"));

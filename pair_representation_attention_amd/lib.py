@@ -32,6 +32,9 @@ PAIRATTN_ERR_HIP = 5
 # size of the static scratch of pairattn_tri_fwd_noalloc (PAIRATTN_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 256 << 20
 
+# bits of pairattn_tri_partial_fwd's accumulate argument
+PAIRATTN_PARTIAL_MERGE = 1
+PAIRATTN_PARTIAL_Q_READY = 2
 PAIRATTN_START = 0
 PAIRATTN_END = 1
 PAIRATTN_F32 = 0
@@ -243,7 +246,7 @@ def pairattn_tri_partial_workspace_bytes(R, Jq, Kn, c_z, H, d, dtype) -> int:
 def pairattn_tri_partial_fwd(q_pairs, kv_pairs, bias, mask, params, o, lse, accumulate, R, Jq, Kn, c_z, H, d,
                              stream=None, check=True) -> int:
     st = load().pairattn_tri_partial_fwd(_ptr(q_pairs), _ptr(kv_pairs), _ptr(bias), _ptr(mask),
-                                         ctypes.byref(params.struct()), _ptr(o), _ptr(lse), 1 if accumulate else 0,
+                                         ctypes.byref(params.struct()), _ptr(o), _ptr(lse), int(accumulate),
                                          R, Jq, Kn, c_z, H, d, _stream(stream))
     return _check(st, "pairattn_tri_partial_fwd") if check else st
 

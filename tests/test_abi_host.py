@@ -286,6 +286,17 @@ def test_validate_tri_partial(kw, status):
         assert st2 == status
 
 
+@pytest.mark.parametrize("flags", [4, 8, -1, 7])
+def test_partial_flags_outside_merge_and_q_ready_are_rejected(flags):
+    """accumulate holds PAIRATTN_PARTIAL_MERGE | PAIRATTN_PARTIAL_Q_READY only;
+    any other bit is refused before anything is launched."""
+    need = lib.pairattn_tri_partial_workspace_bytes(3, 40, 70, 128, 4, 32, lib.PAIRATTN_BF16)
+    p = _params(lib.PAIRATTN_BF16, ws=WS, ws_bytes=need)
+    st = lib.pairattn_tri_partial_fwd(QP, KP, BIAS, None, p, O_, LSE, flags, 3, 40, 70, 128, 4, 32, stream=0,
+                                      check=False)
+    assert st == lib.PAIRATTN_ERR_ARG and "accumulate" in lib.last_error()
+
+
 def test_validate_tri_partial_finish():
     need = lib.pairattn_tri_partial_finish_workspace_bytes(3, 40, 128, 4, 32, lib.PAIRATTN_F32)
     p = _params(lib.PAIRATTN_F32, ws=WS, ws_bytes=need)

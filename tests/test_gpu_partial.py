@@ -146,6 +146,35 @@ def test_partial_ragged_shards_merge_on_the_gpu():
     check(out, ref, "f32", "merged + finish = row form")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_partial_q_ready_equals_the_full_call(dtype):
+    """PAIRATTN_PARTIAL_Q_READY on the shards after the first (the workspace
+    keeps the packed weights and the projected q of the query pairs) gives
+    o and lse bit for bit equal to projecting q again; with the device's own
+    shard second, its k and v come from the query pairs as before."""
+    lib = _lib()
+    I, H = 96, 4
+    case, p, bias, _ = _case(I, 128, H, seed=95, dtype=dtype)
+    z, m = case.z, case.mask
+    rows = np.arange(30, 36)
+    qcols = np.arange(0, 48)
+    shards = [np.arange(48, 96), qcols]       # a foreign shard, then the query pairs' own
+    runs = []
+    for ready in (False, True):
+        pt = _Partial(z[rows][:, qcols], p, H, 48, dtype)
+        for n, ks in enumerate(shards):
+            flags = (lib.PAIRATTN_PARTIAL_MERGE if n > 0 else 0) | \
+                (lib.PAIRATTN_PARTIAL_Q_READY if ready and n > 0 else 0)
+            b = _t(bias[:, qcols][:, :, ks])
+            mk = torch.from_numpy(np.ascontiguousarray(m[rows][:, ks], np.uint8)).to("cuda")
+            kv = pt.q if n == 1 else _dev().to_device(z[rows][:, ks], dtype)
+            lib.pairattn_tri_partial_fwd(pt.q, kv, b, mk, pt.params, pt.o, pt.lse, flags, pt.R, pt.Jq, len(ks),
+                                         pt.c, H, 32)
+        torch.cuda.synchronize()
+        runs.append((pt.o.clone(), pt.lse.clone()))
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
+
+
 def test_partial_shard_with_no_kept_key_keeps_the_others():
     """A shard whose keys are all masked leaves o and lse as they were."""
     I, H = 64, 4
