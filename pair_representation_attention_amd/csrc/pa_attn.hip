@@ -1097,8 +1097,18 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   if constexpr (MODE != 0) {
     // ---- one key shard: o and lse per (row, head, query), written or merged ----
     constexpr float kLn2 = 0.6931471805599453f;
+    // Where one row's o tile fits the K/V ring, it is staged there (scaled
+    // by its merge weight, with the old o's weight beside it) and leaves as
+    // whole query rows of H*32 floats, so every store and merge load is a
+    // contiguous 1 KB per instruction; else each lane writes its own pieces.
+    constexpr int NQ = SH::QWG * 32;          // queries of the workgroup
+    constexpr int OPF = HD + 4;               // staged row pitch (floats): 16-byte rows, spread banks
+    constexpr bool STAGE_O = (NQ * OPF + NQ * H) * 4 <= SH::LDS_KV;
+    float* o_st = reinterpret_cast<float*>(kv_lds);
+    float* w_st = o_st + NQ * OPF;            // [NQ][H]: weight of the o already there (merge)
 #pragma unroll
-    for (int rr = 0; rr < RW; ++rr)
+    for (int rr = 0; rr < RW; ++rr) {
+      if (STAGE_O && rr > 0) __syncthreads();   // the previous row's stores have read the stage
 #pragma unroll
       for (int qq = 0; qq < QW; ++qq) {
         const int r = r0 + rr, q = (qb0 + qq) * 32 + lq;
@@ -1125,22 +1135,56 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
           }
         }
         // O register jj*4+e holds channel jj*8 + g*4 + e of head h
-        float* orow = o_part + ((int64_t)r * P + q) * (H * 32) + h * 32 + 4 * g;
+        if constexpr (STAGE_O) {
+          const int ql = (qgrp * QW + qq) * 32 + lq;
+          float* srow = o_st + ql * OPF + h * 32 + 4 * g;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          f32x4* dst = reinterpret_cast<f32x4*>(orow + 8 * jj);
-          f32x4 v;
+          for (int jj = 0; jj < 4; ++jj) {
+            f32x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = O[rr][qq][4 * jj + e] * inv * wn;
+            for (int e = 0; e < 4; ++e) v[e] = O[rr][qq][4 * jj + e] * inv * wn;
+            *reinterpret_cast<f32x4*>(srow + 8 * jj) = v;
+          }
+          if (MODE == 2 && g == 0) w_st[ql * H + h] = wo;
+        } else {
+          float* orow = o_part + ((int64_t)r * P + q) * (H * 32) + h * 32 + 4 * g;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            f32x4* dst = reinterpret_cast<f32x4*>(orow + 8 * jj);
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = O[rr][qq][4 * jj + e] * inv * wn;
+            if constexpr (MODE == 2) {
+              const f32x4 old = *dst;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] += old[e] * wo;
+            }
+            *dst = v;
+          }
+        }
+        if (g == 0) *lse_at = lse;
+      }
+      if constexpr (STAGE_O) {
+        __syncthreads();
+        constexpr int C4 = HD / 4;            // 16-byte pieces of a query row
+        const int r = r0 + rr;
+        for (int i = threadIdx.x; i < NQ * C4; i += 512) {
+          const int ql = i / C4, c4 = (i % C4) * 4;
+          const int q = qb0_wg * 32 + ql;
+          if (r >= nrows || q >= P) continue;
+          PA_DCHECK(ql * OPF + c4 + 4 <= NQ * OPF, 7);
+          f32x4 v = *reinterpret_cast<const f32x4*>(o_st + ql * OPF + c4);
+          f32x4* dst = reinterpret_cast<f32x4*>(o_part + ((int64_t)r * P + q) * HD + c4);
           if constexpr (MODE == 2) {
             const f32x4 old = *dst;
+            const float wo = w_st[ql * H + c4 / 32];
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] += old[e] * wo;
           }
           *dst = v;
         }
-        if (g == 0) *lse_at = lse;
       }
+    }
     return;
   }
 
