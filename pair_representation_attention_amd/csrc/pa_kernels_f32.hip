@@ -519,11 +519,13 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
   // stream before their first use, into registers whose last reader has
   // been issued (at most three of the four K/V tiles of two blocks are
   // live); the bias tile of unit u+3 at the end, into the C buffer that u+1
-  // has just consumed.
-  auto stream = [&](auto jc, auto nextc, int kb, KV& cur, KV& oth) {
+  // has just consumed.  FAST: shift 0 for every weight (no running
+  // maximum), the sweep that the check below accepts or reruns.
+  auto stream = [&](auto jc, auto nextc, auto fastc, int kb, KV& cur, KV& oth) {
     constexpr int J = decltype(jc)::value;
     constexpr int JN = 1 - J;
     constexpr bool NEXT = decltype(nextc)::value;
+    constexpr bool FAST = decltype(fastc)::value;
     f32x16& Sc = J ? SB : SA;
     f32x16& Sn = J ? SA : SB;
     f32x16& Cn = J ? CA : CB;
@@ -548,22 +550,24 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         Sc[j] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? Sc[j] : -__builtin_inff();
       }
     }
-    float bm = Sc[0];
+    if constexpr (!FAST) {
+      float bm = Sc[0];
 #pragma unroll
-    for (int j = 1; j < 16; ++j) bm = __builtin_fmaxf(bm, Sc[j]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
-      bm = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float mn = bm > m[J] + 8.0f ? bm : m[J];
-    if (__builtin_amdgcn_ballot_w64(mn != m[J]) != 0) {
-      const float alpha = fast_exp2(m[J] - mn);   // 0 while m is -inf
+      for (int j = 1; j < 16; ++j) bm = __builtin_fmaxf(bm, Sc[j]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+        bm = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float mn = bm > m[J] + 8.0f ? bm : m[J];
+      if (__builtin_amdgcn_ballot_w64(mn != m[J]) != 0) {
+        const float alpha = fast_exp2(m[J] - mn);   // 0 while m is -inf
 #pragma unroll
-      for (int j = 0; j < 16; ++j) O[J][j] *= alpha;
-      l[J] *= alpha;
-      m[J] = mn;
+        for (int j = 0; j < 16; ++j) O[J][j] *= alpha;
+        l[J] *= alpha;
+        m[J] = mn;
+      }
     }
-    const float ms = m[J] == -__builtin_inff() ? 0.0f : m[J];
+    const float ms = FAST || m[J] == -__builtin_inff() ? 0.0f : m[J];
     __builtin_amdgcn_sched_barrier(0);
     // ---- softmax weights and fp16 pairs, with the MFMAs in between ----
     float p[16];
@@ -626,28 +630,11 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     if constexpr (J == 1 && HAS_MASK) bits_cur = bits_nxt;
   };
 
-  // prologue: K, V of block 0, the first bias tiles, the logits of unit 0
-  KV X, Y;   // key blocks of even / odd index
-  load_k(X, 0);
-  load_v(X, 0);
-  load_bias(CA, qb0, 0);
-  load_bias(CB, qb1, 0);
-  if (HAS_MASK) bits_cur = brow[0];
-  SA = mfma3(X.kh[0], X.kl[0], Qh[0][0], Ql[0][0], CA);
-  SA = mfma3(X.kh[1], X.kl[1], Qh[0][1], Ql[0][1], SA);
-  load_bias(CA, qb0, min(1, nbk - 1));
-
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using BT = std::true_type;
   using BF = std::false_type;
-  int kb = 0;
-  for (; kb + 2 < nbk; kb += 2) {
-    stream(I0{}, BT{}, kb, X, Y);
-    stream(I1{}, BT{}, kb, X, Y);
-    stream(I0{}, BT{}, kb + 1, Y, X);
-    stream(I1{}, BT{}, kb + 1, Y, X);
-  }
+  KV X, Y;   // key blocks of even / odd index
   // the gate tiles (read once, from HBM) are loaded two streams before the
   // sweep ends, so their latency hides under the last key block
   f32x16 G0, G1;
@@ -657,16 +644,75 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
       load_bias_like(G1, g_ws + (rh * nbq + qb1) * 1024);
     }
   };
-  if (nbk - kb == 2) {
-    stream(I0{}, BT{}, kb, X, Y);
-    stream(I1{}, BT{}, kb, X, Y);
-    load_gate();
-    stream(I0{}, BT{}, kb + 1, Y, X);
-    stream(I1{}, BF{}, kb + 1, Y, X);
-  } else {
-    load_gate();
-    stream(I0{}, BT{}, kb, X, Y);
-    stream(I1{}, BF{}, kb, X, Y);
+  auto sweep = [&](auto fastc) {
+    // prologue: K, V of block 0, the first bias tiles, the logits of unit 0
+    load_k(X, 0);
+    load_v(X, 0);
+    load_bias(CA, qb0, 0);
+    load_bias(CB, qb1, 0);
+    if (HAS_MASK) bits_cur = brow[0];
+    SA = mfma3(X.kh[0], X.kl[0], Qh[0][0], Ql[0][0], CA);
+    SA = mfma3(X.kh[1], X.kl[1], Qh[0][1], Ql[0][1], SA);
+    load_bias(CA, qb0, min(1, nbk - 1));
+    int kb = 0;
+    for (; kb + 2 < nbk; kb += 2) {
+      stream(I0{}, BT{}, fastc, kb, X, Y);
+      stream(I1{}, BT{}, fastc, kb, X, Y);
+      stream(I0{}, BT{}, fastc, kb + 1, Y, X);
+      stream(I1{}, BT{}, fastc, kb + 1, Y, X);
+    }
+    if (nbk - kb == 2) {
+      stream(I0{}, BT{}, fastc, kb, X, Y);
+      stream(I1{}, BT{}, fastc, kb, X, Y);
+      load_gate();
+      stream(I0{}, BT{}, fastc, kb + 1, Y, X);
+      stream(I1{}, BF{}, fastc, kb + 1, Y, X);
+    } else {
+      load_gate();
+      stream(I0{}, BT{}, fastc, kb, X, Y);
+      stream(I1{}, BF{}, fastc, kb, X, Y);
+    }
+  };
+
+  // Shift 0 first.  Its weights 2^s are exact as fp16 pairs (relative 2^-22)
+  // down to 2^-14 and within 2^-25 absolute below, the same bound as with
+  // the running maximum, as long as no weight passes 65504 (then l, their
+  // fp32 sum, does) and l >= 1 for every query of a row with a kept key.
+  // Where a query of this wave fails, the wave sweeps again with the running
+  // maximum (waves share nothing before the epilogue).
+  sweep(BT{});
+  {
+    bool bad = false, zero = false;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l[u]), __float_as_uint(l[u]), false, false);
+      const float lq = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      const int q = (u == 0 ? qb0 : qb1) * 32 + (lane & 31);
+      if (q < P) {
+        bad = bad || !(lq < 65504.0f) || (lq > 0.0f && lq < 1.0f);
+        zero = zero || lq == 0.0f;
+      }
+    }
+    bool rerun = __builtin_amdgcn_ballot_w64(bad) != 0;
+    if (!rerun && __builtin_amdgcn_ballot_w64(zero) != 0) {
+      // l = 0 is exact only for a row with no kept key
+      if constexpr (HAS_MASK) {
+        uint32_t kept = 0;
+        for (int b = 0; b < nbk; ++b) kept |= brow[b];
+        rerun = kept != 0;
+      } else {
+        rerun = true;
+      }
+    }
+    if (rerun) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        O[u] = f32x16{};
+        m[u] = -__builtin_inff();
+        l[u] = 0.0f;
+      }
+      sweep(BF{});
+    }
   }
 
   // ---- epilogue ----
@@ -733,7 +779,9 @@ __global__ __launch_bounds__(H * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
 // og = o * inv * G (o the O^T accumulator image of each head's wave, G the
 // gate tile) as fp16 pairs into LDS, one barrier, then the output tiles
 // (query block u, 32 columns cb) shared by the waves, each a K = H*32
-// contraction of og with W_o, + b_o, fp32 stores.
+// contraction of og with W_o.  The tiles (+ b_o) are staged over og in LDS
+// and leave one query block at a time as whole query rows, 16 bytes per lane
+// (a row's c_out channels are contiguous at the caller's strides).
 template <int H>
 __device__ __forceinline__ void gate_project_store(f16* og_lds, const f32x16 (&O)[2], const float (&inv)[2],
                                                    const f32x16& G0, const f32x16& G1, int h, int wave, int lane,
@@ -758,28 +806,60 @@ __device__ __forceinline__ void gate_project_store(f16* og_lds, const f32x16 (&O
       *reinterpret_cast<f16x8*>(dst + 512) = lo;
     }
   }
+  // this wave's output tiles: ti = wave + k*H of the 2*ncb (c_out <= 256)
+  constexpr int NT = 16 / H;
+  f32x16 acc[NT];
+  float bo[NT];
+#pragma unroll
+  for (int k = 0; k < NT; ++k) {
+    const int ti = wave + k * H;
+    const int c = (ti % ncb) * 32 + (lane & 31);
+    bo[k] = b_o != nullptr && ti < 2 * ncb ? b_o[c] : 0.0f;
+  }
   __syncthreads();
-  for (int ti = wave; ti < 2 * ncb; ti += H) {
+#pragma unroll
+  for (int k = 0; k < NT; ++k) {
+    const int ti = wave + k * H;
+    acc[k] = f32x16{};
+    if (ti >= 2 * ncb) continue;   // wave-uniform
     const int u = ti / ncb, cb = ti % ncb;
-    if (u == 1 && qb1 == qb0) continue;   // repeated block of an odd last group
-    f32x16 acc = {};
 #pragma unroll
     for (int hh = 0; hh < H; ++hh)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const f16* a = og_lds + ((((u * H + hh) * 2 + t) * 2) * 64 + lane) * 8;
         const int64_t wo = (((int64_t)cb * H + hh) * 2 + t) * 512;
-        acc = mfma3(*reinterpret_cast<const f16x8*>(a), *reinterpret_cast<const f16x8*>(a + 512),
-                    reinterpret_cast<const f16x8*>(wo_hi + wo)[lane], reinterpret_cast<const f16x8*>(wo_lo + wo)[lane],
-                    acc);
+        acc[k] = mfma3(*reinterpret_cast<const f16x8*>(a), *reinterpret_cast<const f16x8*>(a + 512),
+                       reinterpret_cast<const f16x8*>(wo_hi + wo)[lane],
+                       reinterpret_cast<const f16x8*>(wo_lo + wo)[lane], acc[k]);
       }
-    // rows = queries, lane = output column
-    const int c = cb * 32 + (lane & 31);
-    const float bo = b_o != nullptr ? b_o[c] : 0.0f;
+  }
+  // staged rows of 32 queries over og (every wave has read og after the
+  // barrier below); a padded pitch where it fits
+  constexpr int OG_FLOATS = H * 2048;
+  float* st = reinterpret_cast<float*>(og_lds);
+  const int sp = 32 * (c_out + 4) <= OG_FLOATS ? c_out + 4 : c_out;
+  const int nq4 = c_out / 4;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int q = (u == 0 ? qb0 : qb1) * 32 + acc_row(j, g);
-      if (q < P) out[(int64_t)r * os_r + (int64_t)q * os_p + c] = acc[j] + bo;
+  for (int u = 0; u < 2; ++u) {
+    if (u == 1 && qb1 == qb0) break;   // repeated block of an odd last group
+    __syncthreads();   // og read (u = 0) or the rows of block 0 stored (u = 1)
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+      const int ti = wave + k * H;
+      if (ti >= 2 * ncb || ti / ncb != u) continue;
+      // rows = queries, lane = output column
+      const int c = (ti % ncb) * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) st[acc_row(j, g) * sp + c] = acc[k][j] + bo[k];
+    }
+    __syncthreads();
+    const int q0 = (u == 0 ? qb0 : qb1) * 32;
+    for (int i = threadIdx.x; i < 32 * nq4; i += H * 64) {
+      const int row = i / nq4, c4 = i - row * nq4;
+      if (q0 + row < P)
+        *reinterpret_cast<f32x4*>(out + (int64_t)r * os_r + (int64_t)(q0 + row) * os_p + 4 * c4) =
+            *reinterpret_cast<const f32x4*>(st + row * sp + 4 * c4);
     }
   }
 }
@@ -908,7 +988,7 @@ static hipError_t attn_f32_dispatch_mode(const AttnF32Args& a, hipStream_t s) {
 
 hipError_t launch_attn_f32(const AttnF32Args& a, hipStream_t s) {
   if (a.Pp < 32 || a.Pp % 32 != 0 || a.P < 1 || a.P > a.Pp || a.Ppk < 32 || a.Ppk % 32 != 0 || a.nrows < 1 ||
-      a.c_out % 32 != 0 || (a.mode != 0 && (a.o_part == nullptr || a.lse_part == nullptr)))
+      a.c_out % 32 != 0 || a.c_out > 256 || (a.mode != 0 && (a.o_part == nullptr || a.lse_part == nullptr)))
     return hipErrorInvalidValue;
   const bool m = a.mask_bits != nullptr;
   if (a.H == 4) return m ? attn_f32_dispatch_mode<4, true>(a, s) : attn_f32_dispatch_mode<4, false>(a, s);
@@ -929,7 +1009,7 @@ static hipError_t finish_f32_dispatch(const AttnF32Args& a, hipStream_t s) {
 }
 
 hipError_t launch_finish_f32(const AttnF32Args& a, hipStream_t s) {
-  if (a.Pp < 32 || a.Pp % 32 != 0 || a.P < 1 || a.P > a.Pp || a.nrows < 1 || a.c_out % 32 != 0 ||
+  if (a.Pp < 32 || a.Pp % 32 != 0 || a.P < 1 || a.P > a.Pp || a.nrows < 1 || a.c_out % 32 != 0 || a.c_out > 256 ||
       a.o_part == nullptr)
     return hipErrorInvalidValue;
   if (a.H == 4) return finish_f32_dispatch<4>(a, s);

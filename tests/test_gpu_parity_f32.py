@@ -59,7 +59,11 @@ def test_f32_fully_masked_rows_give_b_o():
 
 # ----------------------------------------------------------------------------
 # the running maximum: logits spread over a wide range (the maximum is raised
-# many times along the keys) and logits offset far from zero
+# many times along the keys) and logits offset far from zero.  The kernel
+# sweeps with shift 0 first and sweeps again with the running maximum where a
+# query's l is not in [1, 65504): offsets of -60 (l < 1), +45 and +200 (a
+# weight past 65504) and -200 (every weight 0 in fp32, l = 0 for rows that
+# keep keys) take the second sweep; fully masked rows (l = 0 exactly) do not.
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("scale", [4.0, 8.0])
 def test_f32_wide_logits_rescale(scale):
@@ -73,7 +77,7 @@ def test_f32_wide_logits_rescale(scale):
     check(got, ref, "f32", f"f32 wide logits x{scale}")
 
 
-@pytest.mark.parametrize("t,keep", [(-60.0, 0), (45.0, 3), (200.0, 0)])
+@pytest.mark.parametrize("t,keep", [(-60.0, 0), (45.0, 3), (200.0, 0), (-200.0, 0), (-200.0, 3)])
 def test_f32_offset_logits(t, keep):
     """The pair bias offset by t for every head, through LayerNorm's beta:
     beta = t * w_b (w_b^T w_b)^-1 1 gives beta . w_b[:, h] = t.  The offset
