@@ -40,10 +40,6 @@
 
 namespace pa {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // 16 bytes per lane, global -> LDS at lds_base + lane*16 (lds_base
 // wave-uniform), issued from inline asm for the staging rings.  (The
 // compiler tracks every LDS-DMA copy of its own builtin in one slot and would
@@ -62,16 +58,9 @@ __device__ __forceinline__ void g2lds16_ring(const void* gsrc, char* lds_base) {
       : "memory");
 }
 
-// The same copy from a wave-uniform 64-bit base in scalar registers plus a
-// 32-bit per-lane byte offset (no vector address arithmetic per copy).
-__device__ __forceinline__ void g2lds16_sbase(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1" ::"v"(voff),
-      "s"(sbase), "s"(lds_addr)
-      : "memory");
-}
+// (g2lds16_sbase of pa_device.h is the same copy from a wave-uniform 64-bit
+// base in scalar registers plus a 32-bit per-lane byte offset, with no vector
+// address arithmetic per copy.)
 
 // s_waitcnt vmcnt(N) through the builtin (gfx9 immediate layout: vmcnt in
 // bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] at their no-wait

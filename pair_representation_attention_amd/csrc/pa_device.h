@@ -40,6 +40,28 @@ __device__ __forceinline__ void st8(bf16* p, const bf16x4& v) { *reinterpret_cas
 __device__ __forceinline__ void st8(f16* p, const f16x4& v) { *reinterpret_cast<f16x4*>(p) = v; }
 __device__ __forceinline__ void st16(f16* p, const f16x8& v) { *reinterpret_cast<f16x8*>(p) = v; }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// every vector memory operation of this wave (loads, stores, LDS copies) done
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16 bytes per lane, global -> LDS: global address sbase + voff (sbase a
+// wave-uniform 64-bit base in scalar registers, voff this lane's byte
+// offset), LDS address lds_addr + lane*16 (lds_addr wave-uniform).  Issued
+// from inline asm so that the compiler neither tracks the copy (it would
+// drain every copy in flight before each LDS read) nor orders it: the
+// kernels that use it wait for their copies explicitly.  The copy has no
+// register result and its address operands are read at issue; one wait
+// state separates the M0 write from the copy that reads it.
+__device__ __forceinline__ void g2lds16_sbase(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1" ::"v"(voff),
+      "s"(sbase), "s"(lds_addr)
+      : "memory");
+}
+
 __device__ __forceinline__ float bf2f(bf16 v) { return (float)v; }
 __device__ __forceinline__ bf16 f2bf(float v) { return (bf16)v; }   // round to nearest even
 __device__ __forceinline__ f16 f2h(float v) { return (f16)v; }       // round to nearest even

@@ -176,6 +176,152 @@ struct ProjShape {
 
 constexpr int kProjThreads = 512;
 
+// tile -> (row, first position): row-major when positions are contiguous in
+// memory, else position-block-major, so that the waves running at the same
+// time read neighbouring bytes of x.
+__device__ __forceinline__ void proj_tile_rp(int64_t tile, int nb, int nrows, int rmajor, int& r, int& p0) {
+  if (rmajor) {
+    r = (int)(tile / nb);
+    p0 = (int)(tile % nb) * 32;
+  } else {
+    r = (int)(tile % nrows);
+    p0 = (int)(tile / nrows) * 32;
+  }
+}
+
+// The raw rows of a tile into raw[t] (channels t*16 + half*8 .. +7 of the
+// lane's position; zeros past the last tile and past P).  lane_off is the
+// lane's element offset within a tile; the tile's own offset is
+// wave-uniform and computed on the scalar unit.
+template <int KS>
+__device__ __forceinline__ void proj_load_tile(const bf16* __restrict__ x, int64_t xs_r, int64_t xs_p,
+                                               int64_t lane_off, int64_t tile, int64_t ntiles, int nb, int nrows,
+                                               int rmajor, int P, int lq, bf16x8 (&raw)[KS]) {
+  if (tile < ntiles) {
+    int r, p0;
+    proj_tile_rp(tile, nb, nrows, rmajor, r, p0);
+    if (p0 + lq < P) {
+      const bf16* src = x + ((int64_t)r * xs_r + (int64_t)p0 * xs_p) + lane_off;
+#pragma unroll
+      for (int t = 0; t < KS; ++t) raw[t] = ld16(src + t * 16);
+      return;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < KS; ++t) raw[t] = bf16x8{};
+}
+
+// LayerNorm of the lane's position in registers (two passes, fp32, one
+// cross-half exchange per statistic) into the fp16 activation operand; the
+// affine map is folded into the packed weights.  |x - mean| * rstd <=
+// sqrt(C_IN - 1) < 16 for any row: no saturation needed.
+template <int KS>
+__device__ __forceinline__ void proj_layernorm(const bf16x8 (&raw)[KS], float eps, f16x8 (&X)[KS]) {
+  constexpr float inv_c = 1.0f / (KS * 16);
+  float s = 0.0f;
+#pragma unroll
+  for (int t = 0; t < KS; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += bf2f(raw[t][e]);
+  s += __shfl_xor(s, 32, 64);
+  const float mean = s * inv_c;
+  float s2 = 0.0f;
+#pragma unroll
+  for (int t = 0; t < KS; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = bf2f(raw[t][e]) - mean;
+      s2 += d * d;
+    }
+  s2 += __shfl_xor(s2, 32, 64);
+  const float rstd = 1.0f / __builtin_sqrtf(s2 * inv_c + eps);
+#pragma unroll
+  for (int t = 0; t < KS; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) X[t][e] = f2h((bf2f(raw[t][e]) - mean) * rstd);
+}
+
+// One 32-column block (first column col) of q|k|v|g for the tile of
+// positions p0 .. p0+31 of row r: the products of the normalised tile X with
+// the block's operand (wop: this lane's slot of K-step 0, K-steps 512 halfs
+// apart), + the block's column constants cbk, in the layout of its tensor.
+// The result is this lane's two 16-byte slots (chunks t = 0, 1 of the
+// tile's operand image, 512 halfs apart) and where they go (NULL: a plane
+// that is not wanted; partial attention projects the query and the key
+// pairs separately).
+struct QkvgOut {
+  f16* dst;
+  f16x8 o[2];
+};
+template <int KS, int HD>
+__device__ __forceinline__ QkvgOut qkvg_block(const f16x8 (&X)[KS], const f16* wop, const float* cbk, int col, int r,
+                                              int p0, int P, int H, int nb, int nrows, int lane, f16* q_ws,
+                                              f16* k_ws, f16* v_ws, f16* g_ws) {
+  const int lq = lane & 31, g = lane >> 5;
+  const int tensor = col / HD;            // 0 q, 1 k, 2 v, 3 g
+  f16* plane = tensor == 0 ? q_ws : tensor == 1 ? k_ws : tensor == 2 ? v_ws : g_ws;
+  QkvgOut res;
+  res.dst = nullptr;
+  if (plane == nullptr) return res;
+  const int hcol = col - tensor * HD;     // first column within the tensor
+  const int64_t rh = (int64_t)r * H + hcol / 32;
+  const int64_t chunk0 = (rh * nb + (p0 >> 5)) * 2;   // chunk of (rh, position block), t = 0
+  PA_DCHECK((chunk0 + 2) * 512 <= (int64_t)nrows * H * nb * 1024, 4);
+  res.dst = plane + chunk0 * 512 + lane * 8;
+  // Register 8t+e of lane half g holds accumulator row slot_x(t, g, e), so
+  // registers 8t..8t+7 are exactly this lane's 16-byte slot of chunk t of
+  // the operand image: every chunk is written as one contiguous 1 KB store.
+  f32x16 acc = {};
+  if (tensor == 2) {                      // v = X W: rows = positions, lane = channel lq
+#pragma unroll
+    for (int t = 0; t < KS; ++t) acc = mfma32(X[t], *reinterpret_cast<const f16x8*>(wop + t * 512), acc);
+    const float c = cbk[lq];
+    const bool full_tile = p0 + 32 <= P;   // uniform: no padded position in this tile
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (full_tile) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) res.o[t][e] = f2h_sat(acc[8 * t + e] + c);
+      } else {   // padded positions (keys past P) hold zeros: their weight is 0, so P.V must see 0
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          res.o[t][e] = p0 + slot_x(t, g, e) < P ? f2h_sat(acc[8 * t + e] + c) : f2h(0.0f);
+      }
+    }
+  } else {                                // out^T = W^T X^T: rows = channels, lane = position
+#pragma unroll
+    for (int t = 0; t < KS; ++t) acc = mfma32(*reinterpret_cast<const f16x8*>(wop + t * 512), X[t], acc);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      // channels slot_x(t, g, 0..7): two runs of four
+      const f32x4 c0 = *reinterpret_cast<const f32x4*>(cbk + 16 * t + 4 * g);
+      const f32x4 c1 = *reinterpret_cast<const f32x4*>(cbk + 16 * t + 8 + 4 * g);
+      if (tensor <= 1) {
+        // q (scale folded into its columns) and k; padded positions keep
+        // finite values: every sweep drops keys past P, and queries past
+        // P are never stored
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          res.o[t][e] = f2h_sat(acc[8 * t + e] + c0[e]);
+          res.o[t][4 + e] = f2h_sat(acc[8 * t + 4 + e] + c1[e]);
+        }
+      } else {                            // gate: sigmoid, same layout as q
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          res.o[t][e] = f2h(sigmoid_from_log2(acc[8 * t + e] + c0[e]));
+          res.o[t][4 + e] = f2h(sigmoid_from_log2(acc[8 * t + 4 + e] + c1[e]));
+        }
+      }
+    }
+  }
+  return res;
+}
+__device__ __forceinline__ void qkvg_store(const QkvgOut& b) {
+  if (b.dst == nullptr) return;
+  st16(b.dst, b.o[0]);
+  st16(b.dst + 512, b.o[1]);
+}
+
 template <int C_IN, int HD, int NCOL, int MODE>
 __global__ __launch_bounds__(kProjThreads) void proj_kernel(
     const bf16* __restrict__ x, int64_t xs_r, int64_t xs_p, int tile_rmajor, const bf16* __restrict__ gamma,
@@ -234,35 +380,9 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
   const int nb = Pp / 32;
   const int64_t ntiles = (int64_t)nb * nrows;
   const int64_t stride = (int64_t)gridDim.x * NW;
-  // tile -> (row, first position): row-major when positions are contiguous
-  // in memory, else position-block-major, so that the waves running at the
-  // same time read neighbouring bytes of x.
-  auto tile_rp = [&](int64_t tile, int& r, int& p0) {
-    if (tile_rmajor) {
-      r = (int)(tile / nb);
-      p0 = (int)(tile % nb) * 32;
-    } else {
-      r = (int)(tile % nrows);
-      p0 = (int)(tile / nrows) * 32;
-    }
-  };
-  // element offset of this lane's position and channel half within a tile
-  // (the tile's own offset is wave-uniform and computed on the scalar unit)
   const int64_t lane_off = (int64_t)lq * xs_p + g * 8;
-  auto load_tile = [&](int64_t tile, bf16x8* raw) {
-    if (tile < ntiles) {
-      int r, p0;
-      tile_rp(tile, r, p0);
-      const int p = p0 + lq;
-      if (p < P) {
-        const bf16* src = x + ((int64_t)r * xs_r + (int64_t)p0 * xs_p) + lane_off;
-#pragma unroll
-        for (int t = 0; t < KS; ++t) raw[t] = ld16(src + t * 16);
-        return;
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < KS; ++t) raw[t] = bf16x8{};
+  auto load_tile = [&](int64_t tile, bf16x8 (&raw)[KS]) {
+    proj_load_tile<KS>(x, xs_r, xs_p, lane_off, tile, ntiles, nb, nrows, tile_rmajor, P, lq, raw);
   };
 
   constexpr int PF = SH::PF;
@@ -278,107 +398,21 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
 #pragma unroll
    for (int u = 0; u < PF; ++u) {
     if (tile >= ntiles) break;
-    const bf16x8* raw = pre[u];
 
     int r, p0;
-    tile_rp(tile, r, p0);
+    proj_tile_rp(tile, nb, nrows, tile_rmajor, r, p0);
     const int p = p0 + lq;
     const bool valid = p < P;
 
-    // ---- LayerNorm in registers (two passes, fp32); affine map folded into W ----
-    float s = 0.0f;
-#pragma unroll
-    for (int t = 0; t < KS; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s += bf2f(raw[t][e]);
-    s += __shfl_xor(s, 32, 64);
-    const float mean = s * (1.0f / C_IN);
-    float s2 = 0.0f;
-#pragma unroll
-    for (int t = 0; t < KS; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float d = bf2f(raw[t][e]) - mean;
-        s2 += d * d;
-      }
-    s2 += __shfl_xor(s2, 32, 64);
-    const float rstd = 1.0f / __builtin_sqrtf(s2 * (1.0f / C_IN) + eps);
-    // |x - mean| * rstd <= sqrt(C_IN - 1) < 16 for any row: no saturation needed
     f16x8 X[KS];
-#pragma unroll
-    for (int t = 0; t < KS; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) X[t][e] = f2h((bf2f(raw[t][e]) - mean) * rstd);
+    proj_layernorm<KS>(pre[u], eps, X);
     load_tile(tile + PF * stride, pre[u]);
 
     // ---- q | k | v | g column blocks ----
-    // Register 8t+e of lane half g holds accumulator row slot_x(t, g, e), so
-    // registers 8t..8t+7 are exactly this lane's 16-byte slot of chunk t of
-    // the operand image: every chunk is written as one contiguous 1 KB store.
 #pragma unroll 4
-    for (int b = 0; b < SH::NBLK; ++b) {
-      const int col = col0 + b * 32;
-      const int tensor = col / HD;            // 0 q, 1 k, 2 v, 3 g
-      // a NULL plane is not wanted (partial attention projects the query and
-      // the key pairs separately)
-      if ((tensor == 0 ? q_ws : tensor == 1 ? k_ws : tensor == 2 ? v_ws : g_ws) == nullptr) continue;
-      const int hcol = col - tensor * HD;     // first column within the tensor
-      const int64_t rh = (int64_t)r * H + hcol / 32;
-      const int64_t chunk0 = (rh * nb + (p0 >> 5)) * 2;   // chunk of (rh, position block), t = 0
-      const f16* wop = w_lds + (b * KS) * 512 + lane * 8;
-      const float* cbk = cb + b * 32;
-      f32x16 acc = {};
-      if (tensor == 2) {                      // v = X W: rows = positions, lane = channel lq
-#pragma unroll
-        for (int t = 0; t < KS; ++t) acc = mfma32(X[t], *reinterpret_cast<const f16x8*>(wop + t * 512), acc);
-        const float c = cbk[lq];
-        const bool full_tile = p0 + 32 <= P;   // uniform: no padded position in this tile
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          f16x8 o;
-          if (full_tile) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = f2h_sat(acc[8 * t + e] + c);
-          } else {   // padded positions (keys past P) hold zeros: their weight is 0, so P.V must see 0
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              o[e] = p0 + slot_x(t, g, e) < P ? f2h_sat(acc[8 * t + e] + c) : f2h(0.0f);
-          }
-          PA_DCHECK((chunk0 + t + 1) * 512 <= (int64_t)nrows * H * nb * 1024, 4);
-          st16(v_ws + (chunk0 + t) * 512 + lane * 8, o);
-        }
-      } else {                                // out^T = W^T X^T: rows = channels, lane = position
-#pragma unroll
-        for (int t = 0; t < KS; ++t) acc = mfma32(*reinterpret_cast<const f16x8*>(wop + t * 512), X[t], acc);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          // channels slot_x(t, g, 0..7): two runs of four
-          const f32x4 c0 = *reinterpret_cast<const f32x4*>(cbk + 16 * t + 4 * g);
-          const f32x4 c1 = *reinterpret_cast<const f32x4*>(cbk + 16 * t + 8 + 4 * g);
-          f16x8 o;
-          if (tensor <= 1) {
-            // q (scale folded into its columns) and k; padded positions keep
-            // finite values: every sweep drops keys past P, and queries past
-            // P are never stored
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              o[e] = f2h_sat(acc[8 * t + e] + c0[e]);
-              o[4 + e] = f2h_sat(acc[8 * t + 4 + e] + c1[e]);
-            }
-            PA_DCHECK((chunk0 + t + 1) * 512 <= (int64_t)nrows * H * nb * 1024, 4);
-            st16((tensor == 0 ? q_ws : k_ws) + (chunk0 + t) * 512 + lane * 8, o);
-          } else {                            // gate: sigmoid, same layout as q
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              o[e] = f2h(sigmoid_from_log2(acc[8 * t + e] + c0[e]));
-              o[4 + e] = f2h(sigmoid_from_log2(acc[8 * t + 4 + e] + c1[e]));
-            }
-            PA_DCHECK((chunk0 + t + 1) * 512 <= (int64_t)nrows * H * nb * 1024, 4);
-            st16(g_ws + (chunk0 + t) * 512 + lane * 8, o);
-          }
-        }
-      }
-    }
+    for (int b = 0; b < SH::NBLK; ++b)
+      qkvg_store(qkvg_block<KS, HD>(X, w_lds + (b * KS) * 512 + lane * 8, cb + b * 32, col0 + b * 32, r, p0, P, H,
+                                    nb, nrows, lane, q_ws, k_ws, v_ws, g_ws));
 
     // ---- pair bias: rows = heads (zero beyond H), columns = positions ----
     if (do_bias) {
@@ -408,6 +442,113 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(
     }
     tile += stride;
    }
+  }
+}
+
+// LayerNorm + q|k|v|g where the operands of all 4*HD columns exceed the LDS
+// (C_IN = 256: 512 KB).  proj_kernel would split the columns over workgroups
+// and normalise every tile once per group; here a workgroup normalises a
+// batch of 8 position tiles once (one per wave, held in registers) and
+// streams the packed operand through LDS in slices of 4 column blocks,
+// double-buffered: the copy of slice s+1 (8 KB per wave, global -> LDS
+// without registers) is issued at the start of slice s and waited for at its
+// end, where one barrier hands both buffers over.  Each wave holds back the
+// stores of a slice's last block until after that barrier, so that the wait
+// finds only stores issued a block or more earlier.
+template <int C_IN, int HD>
+struct ProjStreamShape {
+  static constexpr int KS = C_IN / 16;
+  static constexpr int SBLK = 4;                   // 32-column blocks per slice
+  static constexpr int NS = 4 * HD / 32 / SBLK;    // slices
+  static constexpr int SLICE = SBLK * KS * 512;    // halfs per slice
+  static constexpr int LDS = 2 * SLICE * 2 + 4 * HD * 4;
+  static_assert(NS % 2 == 0, "slice s lives in buffer s % 2 across batches");
+  static_assert(SLICE * 2 % (kProjThreads * 16) == 0, "a slice is whole rounds of 16 bytes per thread");
+  static_assert(LDS <= 160 * 1024, "slice buffers exceed LDS");
+};
+
+template <int C_IN, int HD>
+__global__ __launch_bounds__(kProjThreads) void proj_stream_kernel(
+    const bf16* __restrict__ x, int64_t xs_r, int64_t xs_p, int tile_rmajor, float eps,
+    const f16* __restrict__ wimg, const float* __restrict__ cst, f16* __restrict__ q_ws, f16* __restrict__ k_ws,
+    f16* __restrict__ v_ws, f16* __restrict__ g_ws, int nrows, int P, int Pp, int H) {
+  using SH = ProjStreamShape<C_IN, HD>;
+  constexpr int KS = SH::KS, SBLK = SH::SBLK, NS = SH::NS, SLICE = SH::SLICE;
+  constexpr int NW = kProjThreads / kWave;
+  constexpr int ROUNDS = SLICE * 2 / (kProjThreads * 16);   // 16-byte copies per thread and slice
+  __shared__ __attribute__((aligned(1024))) f16 w_lds[2 * SLICE];
+  __shared__ float cb[4 * HD];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int lq = lane & 31, g = lane >> 5;
+  const int nb = Pp / 32;
+  const int64_t ntiles = (int64_t)nb * nrows;
+  const int64_t nbatch = (ntiles + NW - 1) / NW;
+  int64_t batch = blockIdx.x;
+  if (batch >= nbatch) return;   // the whole workgroup
+
+  // slice s of the packed image (column blocks s*SBLK ..) into buffer s % 2:
+  // a round of a wave is one contiguous 1 KB in the image and in LDS
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)w_lds;
+  auto copy_slice = [&](int s) {
+    const char* src = reinterpret_cast<const char*>(wimg + (int64_t)s * SLICE) + wave * 1024;
+    const uint32_t dst = lds0 + (uint32_t)((s & 1) * SLICE * 2 + wave * 1024);
+#pragma unroll
+    for (int k = 0; k < ROUNDS; ++k) {
+      PA_DCHECK((int64_t)s * SLICE * 2 + k * kProjThreads * 16 + wave * 1024 + 1024 <= (int64_t)NS * SLICE * 2, 6);
+      g2lds16_sbase(src + k * kProjThreads * 16, lane * 16, dst + k * kProjThreads * 16);
+    }
+  };
+  auto handover = [&]() {   // this wave's copies, stores and loads done, then the workgroup's
+    wait_vm0();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  const int64_t lane_off = (int64_t)lq * xs_p + g * 8;
+  auto load_tile = [&](int64_t tile, bf16x8 (&raw)[KS]) {
+    proj_load_tile<KS>(x, xs_r, xs_p, lane_off, tile, ntiles, nb, nrows, tile_rmajor, P, lq, raw);
+  };
+
+  for (int n = tid; n < 4 * HD; n += kProjThreads) cb[n] = cst[n];
+  copy_slice(0);
+  bf16x8 raw[KS];
+  load_tile(batch * NW + wave, raw);
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the constants are in LDS
+  handover();
+
+  for (; batch < nbatch; batch += gridDim.x) {
+    const int64_t tile = batch * NW + wave;
+    const bool more = batch + gridDim.x < nbatch;   // workgroup-uniform
+    const bool mine = tile < ntiles;                // wave-uniform
+    int r = 0, p0 = 0;
+    if (mine) proj_tile_rp(tile, nb, nrows, tile_rmajor, r, p0);
+    f16x8 X[KS];
+    proj_layernorm<KS>(raw, eps, X);
+    if (more) load_tile(tile + (int64_t)gridDim.x * NW, raw);
+    QkvgOut held;
+    held.dst = nullptr;
+    for (int s = 0; s < NS; ++s) {
+      if (s + 1 < NS) copy_slice(s + 1);
+      else if (more) copy_slice(0);
+      qkvg_store(held);   // the last block of the slice before (issued after its handover)
+      held.dst = nullptr;
+      if (mine) {
+        const f16* wbuf = w_lds + (s & 1) * SLICE + lane * 8;
+#pragma unroll
+        for (int j = 0; j < SBLK; ++j) {
+          const int b = s * SBLK + j;
+          const QkvgOut o = qkvg_block<KS, HD>(X, wbuf + j * KS * 512, cb + b * 32, b * 32, r, p0, P, H, nb, nrows,
+                                               lane, q_ws, k_ws, v_ws, g_ws);
+          if (j + 1 < SBLK) qkvg_store(o);
+          else held = o;
+        }
+      }
+      handover();   // slice s+1 in its buffer; every wave is done with buffer s % 2
+    }
+    qkvg_store(held);
   }
 }
 
@@ -482,25 +623,40 @@ hipError_t launch_pack_bf16(const PackArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// resident workgroups of a kernel per CU (registers and LDS), asked once per
+// instance; concurrent first calls ask the same question and store the same
+// answer
+template <typename K>
+static int resident_per_cu(K kernel, std::atomic<int>& cache) {
+  int n = cache.load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kProjThreads, 0) != hipSuccess || n < 1) n = 1;
+    cache.store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int C_IN, int HD, int MODE>
 static hipError_t proj_dispatch(const ProjArgs& a, int num_cu, hipStream_t s) {
   // columns per group: all of q|k|v|g when their operands fit in 128 KB of LDS
   constexpr int NCOL = MODE == 2 ? 0 : std::min(4 * HD, 65536 / C_IN);
   constexpr int groups = MODE == 2 ? 1 : 4 * HD / NCOL;
   const int64_t ntiles = (int64_t)(a.Pp / 32) * a.nrows;
-  // resident workgroups per CU (registers and LDS), asked once per instance;
-  // concurrent first calls ask the same question and store the same answer
-  static std::atomic<int> wg_cache{0};
-  int wg_per_cu = wg_cache.load(std::memory_order_relaxed);
-  if (wg_per_cu == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, proj_kernel<C_IN, HD, NCOL, MODE>, kProjThreads, 0) !=
-            hipSuccess ||
-        n < 1)
-      n = 1;
-    wg_per_cu = n;
-    wg_cache.store(n, std::memory_order_relaxed);
+  if constexpr (MODE == 0 && groups > 1) {
+    // q|k|v|g only, operands larger than the LDS: one normalisation per tile
+    // with the operand streamed (persistent, batches of 8 tiles)
+    static std::atomic<int> wg_cache{0};
+    const int wg_per_cu = resident_per_cu(proj_stream_kernel<C_IN, HD>, wg_cache);
+    const int64_t nbatch = (ntiles + kProjThreads / kWave - 1) / (kProjThreads / kWave);
+    const int grid_x = (int)std::max<int64_t>(1, std::min<int64_t>(nbatch, (int64_t)num_cu * wg_per_cu));
+    const int rmajor = a.xs_p <= a.xs_r ? 1 : 0;
+    hipLaunchKernelGGL((proj_stream_kernel<C_IN, HD>), dim3(grid_x), dim3(kProjThreads), 0, s, (const bf16*)a.x,
+                       a.xs_r, a.xs_p, rmajor, a.eps, (const f16*)a.wT, a.cst, (f16*)a.q_ws, (f16*)a.k_ws,
+                       (f16*)a.v_ws, (f16*)a.g_ws, a.nrows, a.P, a.Pp, a.H);
+    return hipGetLastError();
   }
+  static std::atomic<int> wg_cache{0};
+  const int wg_per_cu = resident_per_cu(proj_kernel<C_IN, HD, NCOL, MODE>, wg_cache);
   const int64_t want = (ntiles + kProjThreads / kWave - 1) / (kProjThreads / kWave);
   // one resident wave of workgroups: the column groups of a position range
   // run at the same time (their reads of x meet in the caches) and each CU

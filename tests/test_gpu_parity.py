@@ -261,6 +261,26 @@ def test_msa_small(mask):
     check(got, ref, "bf16", f"msa small mask={mask}")
 
 
+@pytest.mark.parametrize("c_m,H", [(256, 4), (128, 8)])
+@pytest.mark.parametrize("S,I", [(5, 37), (200, 384)])
+def test_msa_other_widths(c_m, H, S, I):
+    """Widths whose q|k|v|g operands exceed the LDS (4*H*32 columns of c_m
+    channels over 128 KB) take the streamed projection: one LayerNorm per
+    position tile, the operand in slices through LDS.  S = 5, I = 37 leaves
+    waves without a tile in the last batch; S = 200, I = 384 (2400 tiles)
+    gives workgroups more than one batch."""
+    case = inputs.make_msa_case(S=S, I=I, c_m=c_m, c_z=128, H=H, d=32, dtype="bf16", mask="bernoulli",
+                                seed=23 + c_m + H + I, affine=True, biases=True)
+    got = gpu_to_f64(_dev().MsaRunner(case.m, case.z, case.mask, case.params, H, "bf16")())
+    if S <= 8:
+        ref = oracle.msa_row(case.m, case.z, case.mask, case.params.as_dict(), H)
+        check(got, ref, "bf16", f"msa c_m={c_m} H={H} S={S} I={I}")
+    else:
+        seqs = _sample(S, 6, np.random.default_rng(2))
+        ref = oracle.msa_row(case.m, case.z, case.mask, case.params.as_dict(), H, seqs=seqs)
+        check(got[seqs], ref, "bf16", f"msa c_m={c_m} H={H} S={S} I={I}")
+
+
 def test_msa_small_fp32():
     case = inputs.make_msa_case(S=4, I=21, c_m=64, c_z=64, H=4, d=32, dtype="f32", mask="bernoulli", seed=19,
                                 affine=True, biases=True)
