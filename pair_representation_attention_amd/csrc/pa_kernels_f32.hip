@@ -78,7 +78,9 @@ __device__ __forceinline__ f32x16 mfma3(const f16x8& ah, const f16x8& al, const 
 // Block b of the packed list is columns b*32..+31 of q|k|v|g (each H*32
 // wide).  Lane l of K-step t holds column l%32 and channels t*16 + (l/32)*8
 // .. +7 (the activation operand uses the same slots).
-// cst[n] = beta . W[:, n] (+ b_g for gate columns).
+// cst[n] = beta . W[:, n] (+ b_g for gate columns): one wave per column,
+// fp32 partial sums over the lanes, then a wave reduction (blockIdx.y = 1;
+// blockIdx.y = 0 packs the operands).
 // W_o is packed as the B operand of out = og . W_o: lane l of (c block cb,
 // head hh, chunk t) holds output column cb*32 + l%32 and, in element e, the
 // head channel slot_x(t, l/32, e), the order in which an O^T accumulator
@@ -91,11 +93,22 @@ __global__ void pack_f32_kernel(const float* __restrict__ wq, const float* __res
                                 f16* __restrict__ w_hi, f16* __restrict__ w_lo,
                                 float* __restrict__ cst, const float* __restrict__ wo, f16* __restrict__ wo_hi,
                                 f16* __restrict__ wo_lo, int c_out) {
+  if (blockIdx.y == 1) {
+    const int n = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (n >= nqkvg * 32) return;   // the whole wave
+    const int tsr = n / hd, cc = n % hd;
+    const float* src = tsr == 0 ? wq : tsr == 1 ? wk : tsr == 2 ? wv : wg;
+    float acc = 0.0f;
+    for (int k = lane; k < c_in; k += kWave) acc = __builtin_fmaf(beta[k], src[(int64_t)k * hd + cc], acc);
+    acc = group_sum<kWave>(acc);
+    if (lane == 0) cst[n] = acc + (tsr == 3 && b_g != nullptr ? b_g[cc] : 0.0f);
+    return;
+  }
   const int ks = c_in / 16;
   const int64_t n_w = (int64_t)nqkvg * ks * 64;    // 8-element slots of the projection operands
-  const int64_t n_c = (int64_t)nqkvg * 32;          // column constants
   const int64_t n_o = wo != nullptr ? (int64_t)(c_out / 32) * H * 2 * 64 : 0;
-  const int64_t total = n_w + n_c + n_o;
+  const int64_t total = n_w + n_o;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     if (i < n_w) {
       const int l = (int)(i & 63), t = (int)((i >> 6) % ks), b = (int)((i >> 6) / ks);
@@ -110,16 +123,8 @@ __global__ void pack_f32_kernel(const float* __restrict__ wq, const float* __res
       split8(w, hi, lo);
       *reinterpret_cast<f16x8*>(w_hi + i * 8) = hi;
       *reinterpret_cast<f16x8*>(w_lo + i * 8) = lo;
-    } else if (i < n_w + n_c) {
-      const int n = (int)(i - n_w);
-      const int tsr = n / hd, cc = n % hd;
-      const float* src = tsr == 0 ? wq : tsr == 1 ? wk : tsr == 2 ? wv : wg;
-      float acc = 0.0f;
-      for (int k = 0; k < c_in; ++k) acc = __builtin_fmaf(beta[k], src[(int64_t)k * hd + cc], acc);
-      if (tsr == 3 && b_g != nullptr) acc += b_g[cc];
-      cst[n] = acc;
     } else {
-      const int64_t j = i - n_w - n_c;
+      const int64_t j = i - n_w;
       const int l = (int)(j & 63), t = (int)((j >> 6) & 1), hh = (int)((j >> 7) % H), cb = (int)((j >> 7) / H);
       const int col = cb * 32 + (l & 31);
       float w[8];
@@ -210,11 +215,14 @@ __global__ __launch_bounds__(ProjF32Shape<C_IN>::THREADS) void proj_f32_kernel(
       *reinterpret_cast<f16x8*>(wl_lo + i * 8) = lo;
     }
   }
-  if (with_bias && tid < 8) {
-    float acc = 0.0f;
-    if (tid < H)
-      for (int k = 0; k < C_IN; ++k) acc = __builtin_fmaf(beta[k], wb[(int64_t)k * H + tid], acc);
-    cstb[tid] = acc;
+  if (with_bias) {   // beta . w_b per head: a wave per head, partial sums over the lanes
+    for (int hh = wave; hh < 8; hh += NW) {
+      float acc = 0.0f;
+      if (hh < H)
+        for (int k = lane; k < C_IN; k += kWave) acc = __builtin_fmaf(beta[k], wb[(int64_t)k * H + hh], acc);
+      acc = group_sum<kWave>(acc);
+      if (lane == 0) cstb[hh] = acc;
+    }
   }
   __syncthreads();
 
@@ -916,11 +924,11 @@ __global__ __launch_bounds__(H * 64) void attn_f32_finish_kernel(
 // ---------------------------------------------------------------------------
 hipError_t launch_pack_f32(const PackF32Args& a, hipStream_t s) {
   const int64_t n_w = (int64_t)a.nqkvg * (a.c_in / 16) * 64;
-  const int64_t n_c = (int64_t)a.nqkvg * 32;
   const int64_t n_o = a.wo != nullptr ? (int64_t)(a.c_out / 32) * a.H * 2 * 64 : 0;
-  const int64_t total = n_w + n_c + n_o;
-  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 4096));
-  hipLaunchKernelGGL(pack_f32_kernel, dim3(blocks), dim3(256), 0, s, (const float*)a.wq, (const float*)a.wk,
+  const int64_t total = n_w + n_o;
+  const int64_t blocks_c = ((int64_t)a.nqkvg * 32 + 3) / 4;   // 4 waves (columns) per block
+  const int blocks = (int)std::max<int64_t>({int64_t(1), blocks_c, std::min<int64_t>((total + 255) / 256, 4096)});
+  hipLaunchKernelGGL(pack_f32_kernel, dim3(blocks, 2), dim3(256), 0, s, (const float*)a.wq, (const float*)a.wk,
                      (const float*)a.wv, (const float*)a.wg, (const float*)a.gamma, (const float*)a.beta,
                      (const float*)a.b_g, a.c_in, a.hd, a.H, a.nqkvg, (f16*)a.w_hi, (f16*)a.w_lo, a.cst, (const float*)a.wo, (f16*)a.wo_hi, (f16*)a.wo_lo, a.c_out);
   return hipGetLastError();
