@@ -293,13 +293,13 @@ int pairattn_calibrate_exp2(float *out, int64_t iters, void *stream);
 /* Index checks of the debug build (libpairattn_debug.so, built with
  * -DPA_DEBUG; not part of the method).  There every kernel checks the
  * indices it computes (copy sources and LDS stages of the attention, its
- * q / gate tiles and staged output, the projection's stores, the keep-bits
- * words) against the extents its shape arguments give, and a failed check
- * sets a bit in a device flag word instead of trapping.  This call waits for
- * the device, then writes the OR of those bits since the last call to
- * *flags (bit 0 K/V copy source, 1 bias copy source, 2 LDS stage, 3 q /
- * gate tile, 4 projection store, 5 pair-bias store, 6 keep-bits word, 7
- * staged output tile) and clears them; *checking is 1 in the debug build.
+ * q / gate tiles and staged output, the projection's stores and operand
+ * copies, the keep-bits words) against the extents its shape arguments give,
+ * and a failed check sets a bit in a device flag word instead of trapping.
+ * This call waits for the device, then writes the OR of those bits since the
+ * last call to *flags (bit 0 K/V copy source, 1 bias copy source, 2 LDS
+ * stage, 3 q / gate tile, 4 projection store, 5 pair-bias store, 6 keep-bits
+ * word, 7 staged output tile, 8 projection operand slice) and clears them; *checking is 1 in the debug build.
  * The release build writes 0 to both.  Either pointer may be NULL.  Returns
  * PAIRATTN_OK or PAIRATTN_ERR_HIP. */
 int pairattn_debug_status(uint32_t *flags, int32_t *checking);

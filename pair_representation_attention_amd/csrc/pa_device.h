@@ -138,6 +138,7 @@ __device__ __forceinline__ int64_t b16_chunk(int h, int nbq, int nbk, int qb, in
 //   0 K/V copy source   1 bias copy source   2 LDS stage address
 //   3 q / gate tile     4 projection store   5 pair-bias store
 //   6 keep-bits word    7 staged output tile in LDS
+//   8 projection operand slice copy source
 // In the release build the checks compile to nothing.
 #ifdef PA_DEBUG
 static __device__ unsigned int pa_dbg_flags;

@@ -496,7 +496,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_stream_kernel(
     const uint32_t dst = lds0 + (uint32_t)((s & 1) * SLICE * 2 + wave * 1024);
 #pragma unroll
     for (int k = 0; k < ROUNDS; ++k) {
-      PA_DCHECK((int64_t)s * SLICE * 2 + k * kProjThreads * 16 + wave * 1024 + 1024 <= (int64_t)NS * SLICE * 2, 6);
+      PA_DCHECK((int64_t)s * SLICE * 2 + k * kProjThreads * 16 + wave * 1024 + 1024 <= (int64_t)NS * SLICE * 2, 8);
       g2lds16_sbase(src + k * kProjThreads * 16, lane * 16, dst + k * kProjThreads * 16);
     }
   };

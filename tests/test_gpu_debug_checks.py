@@ -83,6 +83,20 @@ def test_debug_msa(_debug_library, mask):
     check(got, oracle.msa_row(case.m, case.z, case.mask, case.params.as_dict(), 8), "bf16", f"debug msa {mask}")
 
 
+def test_debug_msa_streamed_projection_batches(_debug_library):
+    """c_m = 256: the streamed projection, with more batches of 8 tiles (300)
+    than workgroups, so that the copies of the next batch's first operand
+    slice and the loads of its rows run under the current batch."""
+    lib = _debug_library
+    case = inputs.make_msa_case(S=200, I=384, c_m=256, c_z=128, H=4, d=32, dtype="bf16", mask="bernoulli",
+                                seed=641, affine=True, biases=True)
+    got = gpu_to_f64(_dev().MsaRunner(case.m, case.z, case.mask, case.params, 4, "bf16")())
+    _no_failed_check(lib, "msa streamed projection")
+    seqs = np.array([0, 77, 199])
+    ref = oracle.msa_row(case.m, case.z, case.mask, case.params.as_dict(), 4, seqs=seqs)
+    check(got[seqs], ref, "bf16", "debug msa streamed projection")
+
+
 def test_debug_chunked(_debug_library):
     lib = _debug_library
     case = inputs.make_tri_case(I=90, c=64, H=4, d=32, dtype="bf16", mask="random", seed=660, affine=True,
