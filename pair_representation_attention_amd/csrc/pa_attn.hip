@@ -1281,8 +1281,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       const int rr = row / NQ, qi = row % NQ;
       const int r = r0 + rr, q = qb0_wg * 32 + qi;
       if (r < nrows && q < P)
-        *reinterpret_cast<bf16x8*>(out + (int64_t)r * os_r + (int64_t)q * os_p + ch * 8) =
-            *reinterpret_cast<const bf16x8*>(st_lds + row * SP + ch * 8);
+        st16(out + (int64_t)r * os_r + (int64_t)q * os_p + ch * 8,
+             *reinterpret_cast<const bf16x8*>(st_lds + row * SP + ch * 8));
     }
   } else {
 #pragma unroll

@@ -38,7 +38,16 @@ __device__ __forceinline__ bf16x8 ld16(const bf16* p) { return *reinterpret_cast
 __device__ __forceinline__ f16x8 ld16(const f16* p) { return *reinterpret_cast<const f16x8*>(p); }
 __device__ __forceinline__ void st8(bf16* p, const bf16x4& v) { *reinterpret_cast<bf16x4*>(p) = v; }
 __device__ __forceinline__ void st8(f16* p, const f16x4& v) { *reinterpret_cast<f16x4*>(p) = v; }
-__device__ __forceinline__ void st16(f16* p, const f16x8& v) { *reinterpret_cast<f16x8*>(p) = v; }
+// 16-byte global stores of data that only a later kernel reads, after more
+// bytes than the caches hold have passed through them (projection planes,
+// attention output rows): non-temporal, so the lines do not displace the
+// cached K/V, bias and input lines on their way to HBM.
+__device__ __forceinline__ void st16(f16* p, const f16x8& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f16x8*>(p));
+}
+__device__ __forceinline__ void st16(bf16* p, const bf16x8& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(p));
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
