@@ -420,7 +420,7 @@ def main() -> int:
     proj_bytes = proj_kernel_bytes(I, I, c, H, d)
     proj_gbs = proj_bytes / (proj_ms * 1e-3) / 1e9
     roof_proj = {
-        "kernel": "proj_kernel<128,128,512,1> (LayerNorm + q|k|v|g + pair bias)",
+        "kernel": "proj_kernel<128,128,512,1,2> (LayerNorm + q|k|v|g + pair bias)",
         "bound": "hbm",
         "achieved": proj_gbs,
         "peak": PEAK_HBM_GBS,
