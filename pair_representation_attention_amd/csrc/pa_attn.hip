@@ -226,7 +226,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const f16* __restrict__ q_ws, const f16* __restrict__ k_ws, const f16* __restrict__ v_ws,
     const f16* __restrict__ g_ws, const f16* __restrict__ bias, const uint32_t* __restrict__ mask_bits,
     const int* __restrict__ mask_range, const f16* __restrict__ woT, const bf16* __restrict__ b_o, bf16* __restrict__ out, int64_t os_r,
-    int64_t os_p, int nrows, int P, int Pp, int n_qg, int n_rg, int nbq_in, int Pk_in, int nbk_in,
+    int64_t os_p, int nrows, int P, int Pp, int n_qg, int n_rg, int qgb, int nbq_in, int Pk_in, int nbk_in,
     float* __restrict__ o_part, float* __restrict__ lse_part) {
   static_assert(MODE >= 0 && MODE <= 2, "mode");
   static_assert(H == 4 || H == 8, "4 or 8 heads");
@@ -251,14 +251,15 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
   // XCD-aware tile order: consecutive workgroup ids are spread round-robin
   // over the 8 XCDs, so give each XCD a contiguous range of logical tiles,
-  // and walk tiles in super-columns of QGB query groups, so the workgroups
-  // that run together on one XCD share rows (K/V) and query groups (bias).
+  // and walk tiles in super-columns of QGB query groups (chosen by the host),
+  // so the workgroups that run together on one XCD share rows (K/V) and
+  // query groups (bias).
   int L = blockIdx.x;
   {
     const int n = gridDim.x, per = n / 8;
     if (L < per * 8) L = (L % 8) * per + L / 8;
   }
-  constexpr int QGB = H == 4 ? 4 : 16;
+  const int QGB = qgb;
   const int sc = L / (n_rg * QGB);
   const int sc_w = min(QGB, n_qg - sc * QGB);
   const int rem = L - sc * n_rg * QGB;
@@ -1396,6 +1397,27 @@ hipError_t launch_finish_bf16(const AttnArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// Query groups per super-column of the workgroup order.  The XCD of a
+// workgroup takes a contiguous range of n_qg * n_rg / 8 logical tiles; a
+// super-column holds n_rg * w of them.  Measured at H = 4: super-columns that
+// are whole multiples or whole fractions of an XCD range are faster than
+// ones that straddle range boundaries (I = 1536, 12 query groups: w = 3, 6,
+// 12 beat 4, 5, 8 by 1-2%, 6 best), and the first such width from 4 up was
+// the fastest measured (4096 residues, 32 groups: 4 = 8, then 16, 32;
+// 16384 in blocks of 1024 rows, 128 groups: 4, then 8, 16).  So: the first
+// w in 4..8 that divides the query groups and lines up with the ranges,
+// else 4.  At H = 8 (MSA rows) one super-column of up to 16 groups.
+static int super_column_width(int H, int n_qg, int n_rg) {
+  if (H != 4) return 16;
+  const int64_t per = (int64_t)n_qg * n_rg / 8;
+  for (int w = 4; w <= 8; ++w) {
+    if (n_qg % w != 0) continue;
+    const int64_t t = (int64_t)n_rg * w;
+    if (per > 0 && (t % per == 0 || per % t == 0)) return w;
+  }
+  return 4;
+}
+
 template <int H, int C_OUT, bool HAS_MASK, int MODE>
 static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
   using SH = AttnShape<H>;
@@ -1414,7 +1436,8 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((attn_kernel<H, C_OUT, HAS_MASK, MODE>), dim3((unsigned)n), dim3(512), 0, s,
                      (const f16*)a.q_ws, (const f16*)a.k_ws, (const f16*)a.v_ws, (const f16*)a.g_ws,
                      (const f16*)a.bias, a.mask_bits, a.mask_range, (const f16*)a.woT, (const bf16*)a.b_o, (bf16*)a.out, a.os_r,
-                     a.os_p, a.nrows, a.P, a.Pp, n_qg, n_rg, nbq, Pk, nbk, a.o_part, a.lse_part);
+                     a.os_p, a.nrows, a.P, a.Pp, n_qg, n_rg, super_column_width(H, n_qg, n_rg), nbq, Pk, nbk,
+                     a.o_part, a.lse_part);
   return hipGetLastError();
 }
 

@@ -289,25 +289,37 @@ def test_msa_small_fp32():
     check(got, ref, "f32", "msa small fp32")
 
 
+def _super_column_width(n_qg, n_rg):
+    """Query groups per super-column at H = 4, as the launch chooses them: the
+    first width in 4..8 that divides the query groups and whose super-columns
+    are whole multiples or whole fractions of an XCD's range of tiles, else 4."""
+    per = n_qg * n_rg // 8
+    for w in range(4, 9):
+        if n_qg % w == 0 and per > 0 and ((n_rg * w) % per == 0 or per % (n_rg * w) == 0):
+            return w
+    return 4
+
+
 def _attn_tiles_hit(rows, I, H=4):
     """(XCD, super-column) pairs of the bf16 attention's tile order that the
     sampled rows reach, every query of each row being checked.  Mirrors the
     launch: workgroups of 2 rows x 4 query blocks (H = 4), logical tile
     L' = (L % 8) * (n / 8) + L / 8 for L < 8 * (n / 8) (each XCD takes a
-    contiguous range), tiles walked in super-columns of 4 query groups."""
+    contiguous range), tiles walked in super-columns of w query groups."""
     n_qg = ((I + 31) // 32 + 3) // 4
     n_rg = (I + 1) // 2
+    w = _super_column_width(n_qg, n_rg)
     n = n_qg * n_rg
     per = n // 8
     hit = set()
     for L in range(n):
         Lp = (L % 8) * per + L // 8 if L < per * 8 else L
-        sc = Lp // (n_rg * 4)
-        sc_w = min(4, n_qg - sc * 4)
-        rgi = (Lp - sc * n_rg * 4) // sc_w
+        sc = Lp // (n_rg * w)
+        sc_w = min(w, n_qg - sc * w)
+        rgi = (Lp - sc * n_rg * w) // sc_w
         if 2 * rgi in rows or 2 * rgi + 1 in rows:
             hit.add((L % 8, sc))
-    return hit, n_qg
+    return hit, -(-n_qg // w)
 
 
 def test_cfg_tri_bf16_i1536_sampled():
@@ -320,9 +332,9 @@ def test_cfg_tri_bf16_i1536_sampled():
     dev = _dev()
     I = case.I
     rows = np.array([0, 1, 200, 201, 574, 575, 576, 577, 800, 801, 1150, 1151, 1152, 1153, 1534, 1535])
-    hit, n_qg = _attn_tiles_hit(set(rows.tolist()), I)
+    hit, n_sc = _attn_tiles_hit(set(rows.tolist()), I)
     assert {x for x, _ in hit} == set(range(8)), hit          # all 8 XCD tile ranges
-    assert {sc for _, sc in hit} == set(range((n_qg + 3) // 4)), hit   # all super-columns
+    assert {sc for _, sc in hit} == set(range(n_sc)), hit     # all super-columns
     for ori, p in ((0, case.params_start), (1, case.params_end)):
         out = dev.TriRunner(case.z, case.mask, p, 4, "bf16")(ori)
         if ori == 0:
