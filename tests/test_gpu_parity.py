@@ -347,6 +347,48 @@ def test_cfg_tri_bf16_i1536_sampled():
         del out
 
 
+def _rows_covering_tiles(I):
+    """One row of a row group in each (XCD, super-column) pair of the bf16
+    attention's tile order, plus the last row."""
+    n_qg = ((I + 31) // 32 + 3) // 4
+    n_rg = (I + 1) // 2
+    rows = {I - 1}
+    seen = set()
+    for rg in range(n_rg):
+        hit, _ = _attn_tiles_hit({2 * rg}, I)
+        if hit - seen:
+            rows.add(2 * rg)
+            seen |= hit
+    return np.array(sorted(rows)), seen
+
+
+@pytest.mark.parametrize("I,width", [(1280, 5), (1792, 7)])
+def test_super_column_widths_write_every_tile(I, width):
+    """Query-group counts whose super-column width is neither 4 nor 6 (10
+    groups: 5; 14 groups: 7).  The output starts as NaN: every element must be
+    written, in both orientations, and sampled rows and columns that reach
+    every XCD range and super-column match the oracle."""
+    n_qg = ((I + 31) // 32 + 3) // 4
+    assert _super_column_width(n_qg, (I + 1) // 2) == width
+    case = inputs.make_tri_case(I=I, c=128, H=4, d=32, dtype="bf16", mask="none", seed=31)
+    rows, seen = _rows_covering_tiles(I)
+    hit, n_sc = _attn_tiles_hit(set(rows.tolist()), I)
+    assert {x for x, _ in hit} == set(range(8)) and {sc for _, sc in hit} == set(range(n_sc)), hit
+    for ori, p in ((0, case.params_start), (1, case.params_end)):
+        run = _dev().TriRunner(case.z, None, p, 4, "bf16")
+        run.out.fill_(float("nan"))
+        out = run(ori)
+        assert bool(torch.isfinite(out).all()), f"I={I} ori={ori}: output elements left unwritten"
+        if ori == 0:
+            got = gpu_to_f64(out[torch.as_tensor(rows, device=out.device)])
+            ref = oracle.tri_start(case.z, None, p.as_dict(), 4, rows=rows)
+        else:
+            got = gpu_to_f64(out[:, torch.as_tensor(rows, device=out.device)])
+            ref = oracle.tri_end(case.z, None, p.as_dict(), 4, cols=rows)
+        check(got, ref, "bf16", f"I={I} width={width} ori={ori} rows={rows.tolist()}")
+        del out, run
+
+
 def test_cfg_tri_bf16_i1536_end_is_start_on_transpose_bitwise():
     """The whole ending-node output of Z[1536,1536,128] against the starting-
     node output of Z^T with the same weights, bit for bit: every tile of both
